@@ -1,0 +1,271 @@
+/*
+ * qlin.h -- C ABI of libqlin, the outlier-aware quantized linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is assembled from three methods described on public pages:
+ *   - "Quaff: Quantized Parameter-Efficient Fine-Tuning under Outlier Spatial
+ *     Stability Hypothesis" (paper notes): INT8 weight-activation quantization,
+ *     the decoupled form Y = X^(sW) = X^W + X^_{:,O}(s_O - 1)W_O with a sparse
+ *     compensation term on a fixed outlier channel set O, and targeted momentum
+ *     scaling s_t = gamma s_{t-1} + (1 - gamma) beta ("key design").
+ *   - "QQQ: Quality Quattuor-Bit Quantization for Large Language Models"
+ *     (review): W4A8 GEMMs, per-channel (INT4 -> INT8 by a left shift of 4,
+ *     INT8 GEMM, INT32 -> FP16) and per-group (INT4 -> FP16, fused
+ *     dequant-quant with the group/channel scale ratio, FP16 -> INT8, INT8
+ *     GEMM, INT32 -> FP16) ("technical architecture", W4A8 GEMM kernels).
+ *   - "OffQ: Taming Structured Outliers in LLM Quantization by Offsetting":
+ *     a partially random Hadamard matrix with an all-ones first row turns the
+ *     concentrated outlier channel of a group into a constant offset that the
+ *     zero point of asymmetric quantization absorbs (methodology).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
+ *     and allocates every buffer; the library keeps no pointer after return.
+ *   - Tensors are row-major and contiguous.  fp16 values are passed as their
+ *     uint16_t bit patterns.  X is [M x K] (tokens x input channels), W is
+ *     [K x N] (input x output channels), Y is [M x N].
+ *   - Every pointer must be 16-byte aligned (QLIN_ERR_ALIGN otherwise).
+ *   - Shapes: M >= 0 (M == 0 returns QLIN_OK and launches nothing);
+ *     K > 0 and K % 128 == 0; N > 0 and N % 64 == 0 (QLIN_ERR_SHAPE otherwise).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Nothing is synchronised; results are ready when the stream is.
+ *   - Arguments are validated before any HIP call; a non-zero status means
+ *     nothing was launched and no output was touched, except QLIN_ERR_HIP,
+ *     which reports a failed launch.  qlin_last_error() gives a message.
+ *   - No entry point allocates device memory or retains state between calls;
+ *     calls on different streams touching disjoint outputs may overlap.
+ *   - Rounding: every float -> integer decision is round-half-to-even in IEEE
+ *     float32 (float16 where stated), one rounding per operation, no fused
+ *     multiply-add, correctly rounded division and square root.
+ */
+#ifndef QLIN_H
+#define QLIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t qlin_status;
+#define QLIN_OK 0
+#define QLIN_ERR_INVALID_ARG 1 /* null pointer, negative size, bad enum value      */
+#define QLIN_ERR_SHAPE 2       /* K % 128, N % 64, nO > K, block/group != 128       */
+#define QLIN_ERR_ALIGN 3       /* a pointer is not 16-byte aligned                  */
+#define QLIN_ERR_UNSUPPORTED 4 /* a group size / bit width / block not provided     */
+#define QLIN_ERR_HIP 5         /* the HIP runtime reported an error at launch       */
+
+#define QLIN_ABI_VERSION 1
+
+/* Weight layouts accepted by qlin_pack_weight / qlin_packed_bytes. */
+#define QLIN_LAYOUT_W8 1  /* int8 codes for qlin_gemm_w8a8                         */
+#define QLIN_LAYOUT_W4S 2 /* signed int4 codes [-8,7] for qlin_gemm_w4a8            */
+#define QLIN_LAYOUT_W4U 3 /* unsigned int4 codes [0,15] for qlin_gemm_w4a4          */
+
+/* Version of this ABI (QLIN_ABI_VERSION). Host only. */
+int32_t qlin_abi_version(void);
+/* Static name of a status code. Host only. */
+const char* qlin_status_string(qlin_status status);
+/* Message describing the last non-zero status returned on this host thread. */
+const char* qlin_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Activation side
+ * --------------------------------------------------------------------- */
+
+/*
+ * qlin_quant_act -- per-token symmetric int8 quantization, optionally of X*r.
+ * Quaff notes, "key design" (INT8 activations; with momentum scaling the
+ * quantized operand is X^ = Q(X / s), here X times r = 1/s) and QQQ review,
+ * "technical architecture" (8-bit per-token activations).
+ *   x      fp16 [M x K]
+ *   r      fp32 [K] per-channel multiplier, or NULL for none
+ *   q      int8 [M x K] out: clamp(rint(v * inv), -127, 127) with v = x * r,
+ *          a = max_k |v|, inv = 127 / a (0 if a == 0)
+ *   scale  fp32 [M] out: a / 127 (0 if a == 0)
+ *   O, nO  optional int32 [nO] channel indices; qO int8 [M x nO] out: q[:, O]
+ *          (needed by the compensation term); an index outside [0, K) gives
+ *          code 0.  O and qO must both be NULL when nO == 0.
+ */
+qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, const float* r,
+                           int8_t* q, float* scale, const int32_t* O, int32_t nO, int8_t* qO,
+                           void* stream);
+
+/*
+ * qlin_hadamard_offset -- OffQ activation path (OffQ, methodology,
+ * "absorption via offsetting").  Per token and per group of `block` channels:
+ * t = (x * d) H_block, with H the natural-order Sylvester matrix (row 0 all
+ * ones), evaluated exactly and rounded once to fp32.  Then per token:
+ * rng = max t - min t, inv = 15 / rng, step = rng / 15 (both 1 if rng == 0),
+ * z = rint(-min t * inv), code = clamp(rint(t * inv) + z, 0, 15).
+ *   x       fp16 [M x K]
+ *   signs   int8 [K]: a negative entry means -1, any other +1; OffQ's all-ones
+ *           first row needs signs[block*b] == +1 (not checked)
+ *   block   128 (the only size provided)
+ *   q4      uint8 [M x K/2] out: two codes per byte, low nibble = even k
+ *   scale   fp32 [M] out: step
+ *   zero    int32 [M] out: z
+ *   rowsum  int32 [M] out: sum_k code (used by the W4A4 zero-point epilogue)
+ *   t       fp32 [M x K] out, or NULL: the transformed values (for checking)
+ */
+qlin_status qlin_hadamard_offset(const uint16_t* x, int64_t M, int64_t K, const int8_t* signs,
+                                 int32_t block, uint8_t* q4, float* scale, int32_t* zero,
+                                 int32_t* rowsum, float* t, void* stream);
+
+/*
+ * qlin_momentum_update -- Quaff targeted momentum scaling, one step
+ * (Quaff notes, "key design"): for o in O, c = max_m |x[m,o]|,
+ * beta = max(1, sqrt(c / wmax_O[o])) (beta = 1 if wmax_O[o] == 0 or M == 0),
+ * s[o] = (gamma * s[o]) + ((1 - gamma) * beta); then r[k] = 1 / s[k] for all k.
+ * Channels outside O keep their s (the caller starts from s = 1).  M may be 0
+ * (then beta = 1 for every o).
+ *   x       fp16 [M x K] the current batch (unscaled)
+ *   O, nO   int32 [nO], strictly increasing (not checked on the host: entries
+ *           outside [0, K) are skipped, and a decreasing or repeated entry
+ *           leaves s and r unspecified but in bounds); nO may be 0
+ *   wmax_O  fp32 [nO]: max_n |W[O[j], n]| (qlin_weight_row_absmax)
+ *   gamma   momentum in [0, 1]
+ *   s       fp32 [K] in/out;  r fp32 [K] out
+ */
+qlin_status qlin_momentum_update(const uint16_t* x, int64_t M, int64_t K, const int32_t* O,
+                                 int32_t nO, const float* wmax_O, float gamma, float* s, float* r,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * Weight preparation (offline; W is frozen)
+ * --------------------------------------------------------------------- */
+
+/*
+ * qlin_quant_weight_sym -- symmetric per-output-channel weights (QQQ review,
+ * "technical architecture", per-channel W4A8; Quaff notes, "overall
+ * framework", W_int).  a_n = max_k |W[k,n]|, step_n = fp16(a_n / qmax),
+ * code = clamp(rint(W / step_n), lo, qmax); (qmax, lo) = (127, -127) for
+ * bits = 8 and (7, -8) for bits = 4; a zero step gives zero codes.
+ *   w      fp16 [K x N];  codes int8 [K x N] out;  scale fp16 [N] out
+ */
+qlin_status qlin_quant_weight_sym(const uint16_t* w, int64_t K, int64_t N, int32_t bits,
+                                  int8_t* codes, uint16_t* scale, void* stream);
+
+/*
+ * qlin_quant_weight_group -- QQQ per-group int4 weights with the folded
+ * requantization ratio (QQQ review, "technical architecture", per-group W4A8
+ * GEMM and FusedDequantQuant).  s_g = fp16(max_{k in g}|W| / 7),
+ * code = clamp(rint(W / s_g), -8, 7), s_c = fp16(max_k |W| / 127),
+ * ratio = fp16(s_g / s_c) (0 where s_c == 0).
+ *   group   128 (the only size provided)
+ *   codes   int8 [K x N] out;  group_scale fp16 [K/group x N] out;
+ *   channel_scale fp16 [N] out;  ratio fp16 [K/group x N] out
+ */
+qlin_status qlin_quant_weight_group(const uint16_t* w, int64_t K, int64_t N, int32_t group,
+                                    int8_t* codes, uint16_t* group_scale,
+                                    uint16_t* channel_scale, uint16_t* ratio, void* stream);
+
+/*
+ * qlin_quant_weight_offq -- OffQ weight side: W'' = blockdiag(H'^-1) W with
+ * H' = diag(signs) H_block and H'^-1 = H_block diag(signs) / block, exact,
+ * rounded once to fp32; then per output channel the asymmetric int4 rule of
+ * qlin_hadamard_offset over k.  (x H')(H'^-1 W) = x W, so the layer output is
+ * preserved (OffQ, methodology).
+ *   codes  uint8 [K x N] out (0..15, one per byte);  scale fp32 [N];
+ *   zero int32 [N];  colsum int32 [N] (sum_k code)
+ */
+qlin_status qlin_quant_weight_offq(const uint16_t* w, int64_t K, int64_t N, const int8_t* signs,
+                                   int32_t block, uint8_t* codes, float* scale, int32_t* zero,
+                                   int32_t* colsum, void* stream);
+
+/*
+ * qlin_weight_row_absmax -- out[i] = max_n |w_rows[i, n]| (fp32), the max|W_i|
+ * of Quaff's beta for the rows W_O (Quaff notes, "key design").
+ *   w_rows fp16 [R x N] (R >= 0);  out fp32 [R]
+ */
+qlin_status qlin_weight_row_absmax(const uint16_t* w_rows, int64_t R, int64_t N, float* out,
+                                   void* stream);
+
+/* Bytes of a packed weight buffer for `layout` (0 for invalid arguments). Host only. */
+size_t qlin_packed_bytes(int32_t layout, int64_t K, int64_t N);
+
+/*
+ * qlin_pack_weight -- reorder one-code-per-byte weights [K x N] into the
+ * tiled layout the GEMMs read (int4 layouts hold two codes per byte, eight per
+ * 32-bit word).  The layout is private to the library: only pass the result to
+ * the matching GEMM.  codes: int8 [K x N] for W8 / W4S, uint8 for W4U.
+ *   packed: qlin_packed_bytes(layout, K, N) bytes out.
+ */
+qlin_status qlin_pack_weight(int32_t layout, const void* codes, int64_t K, int64_t N, void* packed,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
+ * GEMMs with fused epilogues
+ * --------------------------------------------------------------------- */
+
+/*
+ * qlin_gemm_w8a8 -- int8 x int8 -> int32, fused dequant, optional fused Quaff
+ * compensation (Quaff notes, "key design", decoupled WAQ).
+ *   acc[m,n] = sum_k qa[m,k] * W8[k,n]
+ *   y[m,n]   = fp16(sa[m] * (acc[m,n] * sw[n] + sum_j qO[m,j] * (s[O[j]] - 1) * WO[j,n]))
+ * The compensation term is the sparse X^_{:,O}(s_O - 1)W_O with
+ * X^_{m,o} = qO[m,o] * sa[m]; it is skipped when nO == 0 (then qO, O, s, WO
+ * must be NULL).
+ *   qa  int8 [M x K];  sa fp32 [M];  w8 packed QLIN_LAYOUT_W8;  sw fp16 [N]
+ *   qO  int8 [M x nO];  O int32 [nO] (entries outside [0, K) contribute 0);
+ *   s fp32 [K];  WO fp16 [nO x N]
+ *   y   fp16 [M x N] out;  acc int32 [M x N] out or NULL
+ */
+qlin_status qlin_gemm_w8a8(const int8_t* qa, const float* sa, const void* w8, const uint16_t* sw,
+                           int64_t M, int64_t N, int64_t K, const int8_t* qO, const int32_t* O,
+                           int32_t nO, const float* s, const uint16_t* WO, uint16_t* y,
+                           int32_t* acc, void* stream);
+
+/*
+ * qlin_gemm_w4a8 -- QQQ W4A8 (QQQ review, "technical architecture").
+ * group == 0, per channel: each int4 weight is moved to the high half of a
+ * byte (a left shift by 4, i.e. 16 * q4 as int8), multiplied in int8, and the
+ * sum is divided by 16 exactly: acc = sum_k qa * q4;  y = fp16(acc * sa * sw).
+ * group == 128, per group: w8 = clamp(rint(fp16(q4 * ratio[k/128, n])), -127, 127)
+ * (one fp16 rounding of the exact product, then round half to even) inside
+ * the K loop; acc = sum_k qa * w8;  y = fp16(acc * sa * sw) with sw = s_c.
+ *   qa int8 [M x K];  sa fp32 [M];  w4 packed QLIN_LAYOUT_W4S;  sw fp16 [N]
+ *   ratio fp16 [K/128 x N] (group == 128) or NULL (group == 0)
+ *   y fp16 [M x N] out;  acc int32 [M x N] out or NULL
+ */
+qlin_status qlin_gemm_w4a8(const int8_t* qa, const float* sa, const void* w4, const uint16_t* sw,
+                           const uint16_t* ratio, int32_t group, int64_t M, int64_t N, int64_t K,
+                           uint16_t* y, int32_t* acc, void* stream);
+
+/*
+ * qlin_gemm_w4a4 -- asymmetric int4 x int4 on int8 matrix cores with the
+ * zero-point correction in the epilogue (OffQ: uniform 4-bit weights and
+ * activations with zero points, methodology and "core contributions").
+ *   raw = sum_k qa * qw (codes 0..15)
+ *   acc = raw - zw[n]*rowsum[m] - za[m]*colsum[n] + K*za[m]*zw[n]
+ *       = sum_k (qa - za[m]) (qw - zw[n])           (int32)
+ *   y   = fp16(acc * sa[m] * sw[n])
+ * Precondition: every term above fits int32 (true whenever |za|,|zw| < 2^12
+ * at K <= 2^14); not checked on the device.
+ *   qa4 uint8 [M x K/2] (low nibble = even k), sa fp32 [M], za int32 [M],
+ *   rowsum int32 [M];  w4 packed QLIN_LAYOUT_W4U;  sw fp32 [N], zw int32 [N],
+ *   colsum int32 [N];  y fp16 [M x N] out;  acc int32 [M x N] out or NULL
+ */
+qlin_status qlin_gemm_w4a4(const uint8_t* qa4, const float* sa, const int32_t* za,
+                           const int32_t* rowsum, const void* w4, const float* sw,
+                           const int32_t* zw, const int32_t* colsum, int64_t M, int64_t N,
+                           int64_t K, uint16_t* y, int32_t* acc, void* stream);
+
+/*
+ * qlin_outlier_comp -- the sparse compensation term on its own, added to an
+ * existing output (Quaff notes, "key design"):
+ *   y[m,n] = fp16(y[m,n] + sa[m] * sum_j qO[m,j] * (s[O[j]] - 1) * WO[j,n])
+ *   qO int8 [M x nO];  sa fp32 [M];  O int32 [nO];  s fp32 [K];
+ *   WO fp16 [nO x N];  y fp16 [M x N] in/out.  nO == 0 leaves y unchanged.
+ *   K is the length of s (used to check O).
+ */
+qlin_status qlin_outlier_comp(const int8_t* qO, const float* sa, const int32_t* O, int32_t nO,
+                              const float* s, int64_t K, const uint16_t* WO, int64_t M, int64_t N,
+                              uint16_t* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLIN_H */

@@ -1,0 +1,324 @@
+// Activation-side kernels of libqlin (gfx950):
+//   qlin_quant_act        per-token symmetric int8 (optionally of X * r)
+//   qlin_hadamard_offset  OffQ block Hadamard (all-ones first row) + per-token
+//                         asymmetric int4 with the offset in the zero point
+//
+// Both are HBM-bound streaming kernels: one workgroup per token, 16-byte
+// loads of 8 fp16 values, the per-token reduction as a wavefront butterfly
+// plus one LDS exchange between waves, and packed stores.
+#include "common.hpp"
+
+namespace qlin {
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr int kQuantRegChunks = 8;  // 8-value chunks held in registers per thread
+
+__device__ __forceinline__ void load8_f16(const uint16_t* p, float (&v)[8]) {
+  const uint4 raw = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = h2f(static_cast<uint16_t>(w[i] & 0xffffu));
+    v[2 * i + 1] = h2f(static_cast<uint16_t>(w[i] >> 16));
+  }
+}
+
+template <bool HAS_R>
+__device__ __forceinline__ void load_chunk(const uint16_t* xr, const float* r, int c, float (&v)[8]) {
+  load8_f16(xr + c * 8, v);
+  if constexpr (HAS_R) {
+    const float4 r0 = *reinterpret_cast<const float4*>(r + c * 8);
+    const float4 r1 = *reinterpret_cast<const float4*>(r + c * 8 + 4);
+    const float rr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = mul_rn(v[i], rr[i]);
+  }
+}
+
+__device__ __forceinline__ int sym_code(float v, float inv) {
+  float t = rint_f(mul_rn(v, inv));
+  t = fminf(fmaxf(t, -127.0f), 127.0f);
+  return static_cast<int>(t);
+}
+
+// Per-token symmetric int8: a = max|v|, inv = 127/a, q = clamp(rint(v*inv)).
+template <bool HAS_R>
+__global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
+    const uint16_t* __restrict__ x, int64_t K, const float* __restrict__ r, int8_t* __restrict__ q,
+    float* __restrict__ scale, const int32_t* __restrict__ O, int nO, int8_t* __restrict__ qO) {
+  __shared__ float red[kQuantThreads / 64];
+  const int64_t m = blockIdx.x;
+  const uint16_t* xr = x + m * K;
+  const int nchunks = static_cast<int>(K / 8);
+
+  float v[kQuantRegChunks][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kQuantRegChunks; ++i) {
+    const int c = threadIdx.x + i * kQuantThreads;
+    if (c < nchunks) {
+      load_chunk<HAS_R>(xr, r, c, v[i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+    }
+  }
+  for (int c = threadIdx.x + kQuantRegChunks * kQuantThreads; c < nchunks; c += kQuantThreads) {
+    float t[8];
+    load_chunk<HAS_R>(xr, r, c, t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(t[j]));
+  }
+  const float a = block_max<kQuantThreads / 64>(amax, red);
+  const float inv = (a == 0.0f) ? 0.0f : div_rn(127.0f, a);
+  if (threadIdx.x == 0) scale[m] = (a == 0.0f) ? 0.0f : div_rn(a, 127.0f);
+
+  int8_t* qr = q + m * K;
+#pragma unroll
+  for (int i = 0; i < kQuantRegChunks; ++i) {
+    const int c = threadIdx.x + i * kQuantThreads;
+    if (c < nchunks) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo |= (static_cast<uint32_t>(sym_code(v[i][j], inv)) & 0xffu) << (8 * j);
+        hi |= (static_cast<uint32_t>(sym_code(v[i][j + 4], inv)) & 0xffu) << (8 * j);
+      }
+      *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(lo, hi);
+    }
+  }
+  for (int c = threadIdx.x + kQuantRegChunks * kQuantThreads; c < nchunks; c += kQuantThreads) {
+    float t[8];
+    load_chunk<HAS_R>(xr, r, c, t);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= (static_cast<uint32_t>(sym_code(t[j], inv)) & 0xffu) << (8 * j);
+      hi |= (static_cast<uint32_t>(sym_code(t[j + 4], inv)) & 0xffu) << (8 * j);
+    }
+    *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(lo, hi);
+  }
+
+  // Compact copy of the outlier columns: the same code, recomputed for O[j].
+  if (qO != nullptr) {
+    for (int j = threadIdx.x; j < nO; j += kQuantThreads) {
+      const int o = O[j];
+      int code = 0;
+      if (o >= 0 && o < K) {
+        float vv = h2f(xr[o]);
+        if constexpr (HAS_R) vv = mul_rn(vv, r[o]);
+        code = sym_code(vv, inv);
+      }
+      qO[m * nO + j] = static_cast<int8_t>(code);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// OffQ: t = (x*d) H_128 per group, exact (float64 butterflies; inputs are fp16
+// so every partial sum has at most 47 significant bits), rounded once to fp32;
+// then per-token asymmetric int4.
+//
+// Work split: a 128-channel group is held by 4 consecutive lanes, 32 channels
+// each.  Butterflies of span 1..16 stay in the lane; spans 32 and 64 pair the
+// lanes of a quad.
+// ---------------------------------------------------------------------------
+constexpr int kHadThreads = 128;
+constexpr int kHadRegChunks = 2;  // 32-channel chunks held in registers per thread
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// Transforms the 32-channel chunk c (group c/4, quarter c%4, with c%4 == lane%4).
+__device__ __forceinline__ void hadamard_chunk(const uint16_t* xr, const int8_t* signs, int c,
+                                               float (&t)[32]) {
+  double u[32];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    float f[8];
+    load8_f16(xr + c * 32 + p * 8, f);
+    const uint2 sraw = *reinterpret_cast<const uint2*>(signs + c * 32 + p * 8);
+    const uint32_t sw[2] = {sraw.x, sraw.y};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int8_t d = static_cast<int8_t>((sw[j >> 2] >> (8 * (j & 3))) & 0xffu);
+      const double xv = static_cast<double>(f[j]);
+      u[p * 8 + j] = (d < 0) ? -xv : xv;
+    }
+  }
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      if ((e & h) == 0) {
+        const double a = u[e], b = u[e + h];
+        u[e] = a + b;
+        u[e + h] = a - b;
+      }
+    }
+  }
+  const int quarter = c & 3;
+#pragma unroll
+  for (int step = 1; step < 4; step <<= 1) {  // spans 32 and 64: lanes xor 1, xor 2
+    const bool upper = (quarter & step) != 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const double other = shfl_xor_f64(u[e], step);
+      u[e] = upper ? (other - u[e]) : (u[e] + other);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 32; ++e) t[e] = static_cast<float>(u[e]);
+}
+
+__device__ __forceinline__ int asym_code(float t, float inv, int z) {
+  int c = static_cast<int>(rint_f(mul_rn(t, inv))) + z;
+  return c < 0 ? 0 : (c > 15 ? 15 : c);
+}
+
+__device__ __forceinline__ uint4 pack_codes(const float (&t)[32], float inv, int z, int& sum) {
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const int code = asym_code(t[e], inv, z);
+    sum += code;
+    w[e >> 3] |= static_cast<uint32_t>(code) << (4 * (e & 7));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ __launch_bounds__(kHadThreads) void hadamard_offset_kernel(
+    const uint16_t* __restrict__ x, int64_t K, const int8_t* __restrict__ signs,
+    uint8_t* __restrict__ q4, float* __restrict__ scale, int32_t* __restrict__ zero,
+    int32_t* __restrict__ rowsum, float* __restrict__ tout) {
+  __shared__ float redf[kHadThreads / 64];
+  __shared__ int redi[kHadThreads / 64];
+  const int64_t m = blockIdx.x;
+  const uint16_t* xr = x + m * K;
+  const int nchunks = static_cast<int>(K / 32);
+
+  float t[kHadRegChunks][32];
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kHadRegChunks; ++i) {
+    const int c = threadIdx.x + i * kHadThreads;
+    if (i * kHadThreads < nchunks) {  // uniform per wave group: all quads take part
+      const int cc = c < nchunks ? c : (c & 3);
+      hadamard_chunk(xr, signs, cc, t[i]);
+      if (c < nchunks) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          mn = fminf(mn, t[i][e]);
+          mx = fmaxf(mx, t[i][e]);
+        }
+        if (tout != nullptr) {
+          float* dst = tout + m * K + static_cast<int64_t>(c) * 32;
+#pragma unroll
+          for (int e = 0; e < 32; e += 4)
+            *reinterpret_cast<float4*>(dst + e) = make_float4(t[i][e], t[i][e + 1], t[i][e + 2], t[i][e + 3]);
+        }
+      }
+    }
+  }
+  for (int base = kHadRegChunks * kHadThreads; base < nchunks; base += kHadThreads) {
+    const int c = base + threadIdx.x;
+    const int cc = c < nchunks ? c : (c & 3);
+    float tt[32];
+    hadamard_chunk(xr, signs, cc, tt);
+    if (c < nchunks) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        mn = fminf(mn, tt[e]);
+        mx = fmaxf(mx, tt[e]);
+      }
+      if (tout != nullptr) {
+        float* dst = tout + m * K + static_cast<int64_t>(c) * 32;
+#pragma unroll
+        for (int e = 0; e < 32; e += 4)
+          *reinterpret_cast<float4*>(dst + e) = make_float4(tt[e], tt[e + 1], tt[e + 2], tt[e + 3]);
+      }
+    }
+  }
+  mn = block_min<kHadThreads / 64>(mn, redf);
+  mx = block_max<kHadThreads / 64>(mx, redf);
+  const float rng = sub_rn(mx, mn);
+  const float inv = (rng == 0.0f) ? 1.0f : div_rn(15.0f, rng);
+  const float step = (rng == 0.0f) ? 1.0f : div_rn(rng, 15.0f);
+  const int z = static_cast<int>(rint_f(mul_rn(-mn, inv)));
+
+  int sum = 0;
+  uint8_t* qr = q4 + m * (K / 2);
+#pragma unroll
+  for (int i = 0; i < kHadRegChunks; ++i) {
+    const int c = threadIdx.x + i * kHadThreads;
+    if (c < nchunks) *reinterpret_cast<uint4*>(qr + static_cast<int64_t>(c) * 16) = pack_codes(t[i], inv, z, sum);
+  }
+  for (int base = kHadRegChunks * kHadThreads; base < nchunks; base += kHadThreads) {
+    const int c = base + threadIdx.x;
+    const int cc = c < nchunks ? c : (c & 3);
+    float tt[32];
+    hadamard_chunk(xr, signs, cc, tt);
+    if (c < nchunks) *reinterpret_cast<uint4*>(qr + static_cast<int64_t>(c) * 16) = pack_codes(tt, inv, z, sum);
+  }
+  sum = block_sum<kHadThreads / 64>(sum, redi);
+  if (threadIdx.x == 0) {
+    scale[m] = step;
+    zero[m] = z;
+    rowsum[m] = sum;
+  }
+}
+
+}  // namespace
+}  // namespace qlin
+
+using namespace qlin;
+
+extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, const float* r,
+                                      int8_t* q, float* scale, const int32_t* O, int32_t nO,
+                                      int8_t* qO, void* stream) {
+  QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
+  QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
+  QLIN_PTR(x);
+  QLIN_PTR(q);
+  QLIN_PTR(scale);
+  QLIN_OPT_PTR(r);
+  if (nO > 0) {
+    QLIN_PTR(O);
+    QLIN_PTR(qO);
+  } else {
+    QLIN_REQUIRE(O == nullptr && qO == nullptr, QLIN_ERR_INVALID_ARG, "O and qO must be NULL when nO == 0");
+  }
+  if (M == 0) return QLIN_OK;
+  QLIN_REQUIRE(M <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
+  const dim3 grid(static_cast<unsigned>(M));
+  if (r != nullptr)
+    quant_act_kernel<true><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, K, r, q, scale, O, nO, qO);
+  else
+    quant_act_kernel<false><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, K, r, q, scale, O, nO, qO);
+  QLIN_LAUNCH_CHECK("quant_act_kernel");
+  return QLIN_OK;
+}
+
+extern "C" qlin_status qlin_hadamard_offset(const uint16_t* x, int64_t M, int64_t K,
+                                            const int8_t* signs, int32_t block, uint8_t* q4,
+                                            float* scale, int32_t* zero, int32_t* rowsum,
+                                            float* t, void* stream) {
+  QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
+  QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_REQUIRE(block == 128, QLIN_ERR_UNSUPPORTED, "block=%d: only 128 is provided", block);
+  QLIN_PTR(x);
+  QLIN_PTR(signs);
+  QLIN_PTR(q4);
+  QLIN_PTR(scale);
+  QLIN_PTR(zero);
+  QLIN_PTR(rowsum);
+  QLIN_OPT_PTR(t);
+  if (M == 0) return QLIN_OK;
+  QLIN_REQUIRE(M <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
+  hadamard_offset_kernel<<<dim3(static_cast<unsigned>(M)), kHadThreads, 0, as_stream(stream)>>>(
+      x, K, signs, q4, scale, zero, rowsum, t);
+  QLIN_LAUNCH_CHECK("hadamard_offset_kernel");
+  return QLIN_OK;
+}

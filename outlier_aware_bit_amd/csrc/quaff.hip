@@ -1,0 +1,179 @@
+// Quaff kernels of libqlin (gfx950):
+//   qlin_momentum_update    targeted momentum scaling on the fixed outlier set O
+//   qlin_weight_row_absmax  max_n |W_O[o, n]| for beta
+//   qlin_outlier_comp       the sparse compensation term added to Y
+//
+// Source: "Quaff: Quantized Parameter-Efficient Fine-Tuning under Outlier
+// Spatial Stability Hypothesis" (paper notes), "key design".
+#include "common.hpp"
+#include "comp.hpp"
+
+namespace qlin {
+namespace {
+
+constexpr int kMomThreads = 256;
+
+// One workgroup per outlier channel O[j]: c = max_m |x[m, O[j]]|, then
+// beta = max(1, sqrt(c / wmax)), s = gamma*s + (1-gamma)*beta, r = 1/s.  The
+// same workgroup writes r = 1/s for the channels between O[j-1] and O[j]
+// (and after the last one), so r covers every channel in one launch.
+__global__ __launch_bounds__(kMomThreads) void momentum_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const int32_t* __restrict__ O, int nO,
+    const float* __restrict__ wmax, float gamma, float* __restrict__ s, float* __restrict__ r) {
+  __shared__ float red[kMomThreads / 64];
+  const int j = blockIdx.x;
+  const int o = O[j];
+  const bool valid = (o >= 0 && o < K);
+  float c = 0.0f;
+  if (valid) {
+    const uint16_t* col = x + o;
+#pragma unroll 8
+    for (int64_t m = threadIdx.x; m < M; m += kMomThreads) c = fmaxf(c, fabsf(h2f(col[m * K])));
+  }
+  c = block_max<kMomThreads / 64>(c, red);
+  if (threadIdx.x == 0 && valid) {
+    const float w = wmax[j];
+    float beta = 1.0f;
+    if (w != 0.0f) beta = fmaxf(1.0f, sqrt_rn(div_rn(c, w)));
+    const float g1 = sub_rn(1.0f, gamma);
+    const float sn = add_rn(mul_rn(gamma, s[o]), mul_rn(g1, beta));
+    s[o] = sn;
+    r[o] = div_rn(1.0f, sn);
+  }
+  // Channels strictly between the previous outlier and this one.
+  int64_t lo = (j == 0) ? 0 : static_cast<int64_t>(O[j - 1]) + 1;
+  int64_t hi = static_cast<int64_t>(o);
+  lo = lo < 0 ? 0 : (lo > K ? K : lo);
+  hi = hi < 0 ? 0 : (hi > K ? K : hi);
+  for (int64_t k = lo + threadIdx.x; k < hi; k += kMomThreads) r[k] = div_rn(1.0f, s[k]);
+  if (j == nO - 1) {
+    int64_t t0 = static_cast<int64_t>(o) + 1;
+    t0 = t0 < 0 ? 0 : (t0 > K ? K : t0);
+    for (int64_t k = t0 + threadIdx.x; k < K; k += kMomThreads) r[k] = div_rn(1.0f, s[k]);
+  }
+}
+
+__global__ __launch_bounds__(kMomThreads) void reciprocal_kernel(const float* __restrict__ s,
+                                                                 float* __restrict__ r, int64_t K) {
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * kMomThreads + threadIdx.x;
+  if (k < K) r[k] = div_rn(1.0f, s[k]);
+}
+
+__global__ __launch_bounds__(kMomThreads) void row_absmax_kernel(const uint16_t* __restrict__ w,
+                                                                 int64_t N, float* __restrict__ out) {
+  __shared__ float red[kMomThreads / 64];
+  const int64_t i = blockIdx.x;
+  const uint16_t* row = w + i * N;
+  float a = 0.0f;
+  for (int64_t c = threadIdx.x; c < N / 8; c += kMomThreads) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(row + c * 8);
+    const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a = fmaxf(a, fabsf(h2f(static_cast<uint16_t>(v[q] & 0xffffu))));
+      a = fmaxf(a, fabsf(h2f(static_cast<uint16_t>(v[q] >> 16))));
+    }
+  }
+  a = block_max<kMomThreads / 64>(a, red);
+  if (threadIdx.x == 0) out[i] = a;
+}
+
+// Standalone compensation: y = fp16(y + sa * sum_j fp16(qO*(s-1)) * WO), on
+// 128 x 128 tiles with four waves of 64 x 64.
+constexpr int kCompBM = 128, kCompBN = 128, kCompThreads = 256;
+
+__global__ __launch_bounds__(kCompThreads) void outlier_comp_kernel(
+    const int8_t* __restrict__ qO, const float* __restrict__ sa, const int32_t* __restrict__ O,
+    int nO, const float* __restrict__ s, int64_t K, const uint16_t* __restrict__ WO, int64_t M,
+    int64_t N, uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[comp_lds_bytes<kCompBM, kCompBN>()];
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kCompBM;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kCompBN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wrow0 = (wave >> 1) * 64, wcol0 = (wave & 1) * 64;
+  v4f acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  comp_accumulate<kCompBM, kCompBN, kCompThreads, 4, 4>(acc, qO, O, nO, s, WO, M, N, K, m0, n0,
+                                                         wrow0, wcol0, lds);
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + wrow0 + tm * 16 + 4 * (lane >> 4) + i;
+      if (m >= M) continue;
+      const float sam = sa[m];
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) {
+        const int64_t n = n0 + wcol0 + tn * 16 + (lane & 15);
+        if (n >= N) continue;
+        uint16_t* p = y + m * N + n;
+        *p = f2h(h2f(*p) + sam * acc[tm][tn][i]);
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace qlin
+
+using namespace qlin;
+
+extern "C" qlin_status qlin_momentum_update(const uint16_t* x, int64_t M, int64_t K,
+                                            const int32_t* O, int32_t nO, const float* wmax_O,
+                                            float gamma, float* s, float* r, void* stream) {
+  QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
+  QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
+  QLIN_REQUIRE(gamma >= 0.0f && gamma <= 1.0f, QLIN_ERR_INVALID_ARG, "gamma=%g must be in [0, 1]", (double)gamma);
+  QLIN_PTR(s);
+  QLIN_PTR(r);
+  if (nO > 0) {
+    QLIN_PTR(O);
+    QLIN_PTR(wmax_O);
+    if (M > 0) QLIN_PTR(x);
+    momentum_kernel<<<dim3(nO), kMomThreads, 0, as_stream(stream)>>>(x, M, K, O, nO, wmax_O, gamma, s, r);
+  } else {
+    reciprocal_kernel<<<dim3(static_cast<unsigned>((K + kMomThreads - 1) / kMomThreads)), kMomThreads, 0,
+                        as_stream(stream)>>>(s, r, K);
+  }
+  QLIN_LAUNCH_CHECK("momentum_kernel");
+  return QLIN_OK;
+}
+
+extern "C" qlin_status qlin_weight_row_absmax(const uint16_t* w_rows, int64_t R, int64_t N,
+                                              float* out, void* stream) {
+  QLIN_REQUIRE(R >= 0, QLIN_ERR_INVALID_ARG, "R=%lld is negative", (long long)R);
+  QLIN_REQUIRE(N > 0 && N % 64 == 0, QLIN_ERR_SHAPE, "N=%lld must be a positive multiple of 64", (long long)N);
+  if (R == 0) return QLIN_OK;
+  QLIN_PTR(w_rows);
+  QLIN_PTR(out);
+  QLIN_REQUIRE(R <= 0x7fffffffLL, QLIN_ERR_SHAPE, "R too large");
+  row_absmax_kernel<<<dim3(static_cast<unsigned>(R)), kMomThreads, 0, as_stream(stream)>>>(w_rows, N, out);
+  QLIN_LAUNCH_CHECK("row_absmax_kernel");
+  return QLIN_OK;
+}
+
+extern "C" qlin_status qlin_outlier_comp(const int8_t* qO, const float* sa, const int32_t* O,
+                                         int32_t nO, const float* s, int64_t K, const uint16_t* WO,
+                                         int64_t M, int64_t N, uint16_t* y, void* stream) {
+  QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
+  QLIN_K_N(K, N);
+  QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
+  if (M == 0 || nO == 0) return QLIN_OK;
+  QLIN_REQUIRE(qO != nullptr && O != nullptr && s != nullptr && WO != nullptr && sa != nullptr && y != nullptr,
+               QLIN_ERR_INVALID_ARG, "null pointer");
+  QLIN_PTR(WO);
+  QLIN_PTR(y);
+  QLIN_PTR(sa);
+  QLIN_PTR(s);
+  QLIN_PTR(O);
+  QLIN_PTR(qO);
+  QLIN_REQUIRE((M + kCompBM - 1) / kCompBM <= 65535, QLIN_ERR_SHAPE, "M too large");
+  const dim3 grid(static_cast<unsigned>((N + kCompBN - 1) / kCompBN), static_cast<unsigned>((M + kCompBM - 1) / kCompBM));
+  outlier_comp_kernel<<<grid, kCompThreads, 0, as_stream(stream)>>>(qO, sa, O, nO, s, K, WO, M, N, y);
+  QLIN_LAUNCH_CHECK("outlier_comp_kernel");
+  return QLIN_OK;
+}

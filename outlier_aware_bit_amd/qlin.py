@@ -1,0 +1,252 @@
+"""Thin PyTorch binding of libqlin: one function per C entry point, same names.
+
+Each function checks dtypes, devices and contiguity, allocates outputs with
+torch when the caller does not pass them, and calls the C ABI with raw device
+pointers and the current HIP stream.  Every step of the layer runs in the HIP
+kernels; nothing here computes.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import QLIN_LAYOUT_W4S, QLIN_LAYOUT_W4U, QLIN_LAYOUT_W8, QlinError  # noqa: F401
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _req(t, name, dtype, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _opt(t, name, dtype, shape=None):
+    return None if t is None else _req(t, name, dtype, shape)
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def qlin_abi_version() -> int:
+    return _lib.load().qlin_abi_version()
+
+
+def qlin_quant_act(x, r=None, O=None, q=None, scale=None, qO=None):
+    """Per-token symmetric int8 of x (optionally x * r).  Returns (q, scale, qO)."""
+    lib = _lib.load()
+    _req(x, "x", torch.float16)
+    M, K = x.shape
+    _opt(r, "r", torch.float32, (K,))
+    q = _req(q, "q", torch.int8, (M, K)) if q is not None else _empty((M, K), torch.int8, x)
+    scale = _req(scale, "scale", torch.float32, (M,)) if scale is not None else _empty((M,), torch.float32, x)
+    nO = 0
+    if O is not None:
+        _req(O, "O", torch.int32)
+        nO = O.numel()
+        qO = _req(qO, "qO", torch.int8, (M, nO)) if qO is not None else _empty((M, nO), torch.int8, x)
+        if nO == 0:
+            O_p = qO_p = None
+        else:
+            O_p, qO_p = O.data_ptr(), qO.data_ptr()
+    else:
+        O_p = qO_p = None
+    _lib.check("qlin_quant_act", lib.qlin_quant_act(x.data_ptr(), M, K, _ptr(r), q.data_ptr(), scale.data_ptr(),
+                                                    O_p, nO, qO_p, _stream()))
+    return q, scale, qO
+
+
+def qlin_hadamard_offset(x, signs, block=128, want_t=False):
+    """OffQ block Hadamard + per-token asymmetric int4.
+    Returns (q4 uint8 [M, K/2], scale, zero, rowsum, t or None)."""
+    lib = _lib.load()
+    _req(x, "x", torch.float16)
+    M, K = x.shape
+    _req(signs, "signs", torch.int8, (K,))
+    q4 = _empty((M, K // 2), torch.uint8, x)
+    scale = _empty((M,), torch.float32, x)
+    zero = _empty((M,), torch.int32, x)
+    rowsum = _empty((M,), torch.int32, x)
+    t = _empty((M, K), torch.float32, x) if want_t else None
+    _lib.check("qlin_hadamard_offset", lib.qlin_hadamard_offset(
+        x.data_ptr(), M, K, signs.data_ptr(), block, q4.data_ptr(), scale.data_ptr(), zero.data_ptr(),
+        rowsum.data_ptr(), _ptr(t), _stream()))
+    return q4, scale, zero, rowsum, t
+
+
+def qlin_momentum_update(x, O, wmax_O, gamma, s, r):
+    """One step of Quaff's momentum scaling; updates s in place and writes r."""
+    lib = _lib.load()
+    _req(x, "x", torch.float16)
+    M, K = x.shape
+    _req(O, "O", torch.int32)
+    nO = O.numel()
+    _req(wmax_O, "wmax_O", torch.float32, (nO,))
+    _req(s, "s", torch.float32, (K,))
+    _req(r, "r", torch.float32, (K,))
+    _lib.check("qlin_momentum_update", lib.qlin_momentum_update(
+        x.data_ptr(), M, K, O.data_ptr() if nO else None, nO, wmax_O.data_ptr() if nO else None,
+        float(gamma), s.data_ptr(), r.data_ptr(), _stream()))
+    return s, r
+
+
+def qlin_weight_row_absmax(w_rows, out=None):
+    lib = _lib.load()
+    _req(w_rows, "w_rows", torch.float16)
+    R, N = w_rows.shape
+    out = out if out is not None else _empty((R,), torch.float32, w_rows)
+    _req(out, "out", torch.float32, (R,))
+    _lib.check("qlin_weight_row_absmax", lib.qlin_weight_row_absmax(
+        w_rows.data_ptr() if R else None, R, N, out.data_ptr() if R else None, _stream()))
+    return out
+
+
+def qlin_quant_weight_sym(w, bits):
+    lib = _lib.load()
+    _req(w, "w", torch.float16)
+    K, N = w.shape
+    codes = _empty((K, N), torch.int8, w)
+    scale = _empty((N,), torch.float16, w)
+    _lib.check("qlin_quant_weight_sym", lib.qlin_quant_weight_sym(
+        w.data_ptr(), K, N, bits, codes.data_ptr(), scale.data_ptr(), _stream()))
+    return codes, scale
+
+
+def qlin_quant_weight_group(w, group=128):
+    lib = _lib.load()
+    _req(w, "w", torch.float16)
+    K, N = w.shape
+    codes = _empty((K, N), torch.int8, w)
+    gs = _empty((K // group, N), torch.float16, w)
+    cs = _empty((N,), torch.float16, w)
+    ratio = _empty((K // group, N), torch.float16, w)
+    _lib.check("qlin_quant_weight_group", lib.qlin_quant_weight_group(
+        w.data_ptr(), K, N, group, codes.data_ptr(), gs.data_ptr(), cs.data_ptr(), ratio.data_ptr(), _stream()))
+    return codes, gs, cs, ratio
+
+
+def qlin_quant_weight_offq(w, signs, block=128):
+    lib = _lib.load()
+    _req(w, "w", torch.float16)
+    K, N = w.shape
+    _req(signs, "signs", torch.int8, (K,))
+    codes = _empty((K, N), torch.uint8, w)
+    scale = _empty((N,), torch.float32, w)
+    zero = _empty((N,), torch.int32, w)
+    colsum = _empty((N,), torch.int32, w)
+    _lib.check("qlin_quant_weight_offq", lib.qlin_quant_weight_offq(
+        w.data_ptr(), K, N, signs.data_ptr(), block, codes.data_ptr(), scale.data_ptr(), zero.data_ptr(),
+        colsum.data_ptr(), _stream()))
+    return codes, scale, zero, colsum
+
+
+def qlin_packed_bytes(layout, K, N) -> int:
+    return int(_lib.load().qlin_packed_bytes(layout, K, N))
+
+
+def qlin_pack_weight(layout, codes, out=None):
+    lib = _lib.load()
+    dt = torch.uint8 if layout == QLIN_LAYOUT_W4U else torch.int8
+    _req(codes, "codes", dt)
+    K, N = codes.shape
+    nbytes = qlin_packed_bytes(layout, K, N)
+    out = out if out is not None else _empty((nbytes,), torch.uint8, codes)
+    _req(out, "packed", torch.uint8, (nbytes,))
+    _lib.check("qlin_pack_weight", lib.qlin_pack_weight(layout, codes.data_ptr(), K, N, out.data_ptr(), _stream()))
+    return out
+
+
+def qlin_gemm_w8a8(qa, sa, w8, sw, N, qO=None, O=None, s=None, WO=None, want_acc=False, y=None):
+    """y = fp16(sa * (acc * sw + compensation)); returns (y, acc or None)."""
+    lib = _lib.load()
+    _req(qa, "qa", torch.int8)
+    M, K = qa.shape
+    _req(sa, "sa", torch.float32, (M,))
+    _req(w8, "w8", torch.uint8)
+    _req(sw, "sw", torch.float16, (N,))
+    nO = 0 if O is None else O.numel()
+    if nO:
+        _req(qO, "qO", torch.int8, (M, nO))
+        _req(O, "O", torch.int32, (nO,))
+        _req(s, "s", torch.float32, (K,))
+        _req(WO, "WO", torch.float16, (nO, N))
+    else:
+        qO = O = s = WO = None
+    y = y if y is not None else _empty((M, N), torch.float16, qa)
+    _req(y, "y", torch.float16, (M, N))
+    acc = _empty((M, N), torch.int32, qa) if want_acc else None
+    _lib.check("qlin_gemm_w8a8", lib.qlin_gemm_w8a8(
+        qa.data_ptr(), sa.data_ptr(), w8.data_ptr(), sw.data_ptr(), M, N, K, _ptr(qO), _ptr(O), nO, _ptr(s),
+        _ptr(WO), y.data_ptr(), _ptr(acc), _stream()))
+    return y, acc
+
+
+def qlin_gemm_w4a8(qa, sa, w4, sw, N, ratio=None, group=0, want_acc=False, y=None):
+    lib = _lib.load()
+    _req(qa, "qa", torch.int8)
+    M, K = qa.shape
+    _req(sa, "sa", torch.float32, (M,))
+    _req(w4, "w4", torch.uint8)
+    _req(sw, "sw", torch.float16, (N,))
+    if group:
+        _req(ratio, "ratio", torch.float16, (K // group, N))
+    y = y if y is not None else _empty((M, N), torch.float16, qa)
+    _req(y, "y", torch.float16, (M, N))
+    acc = _empty((M, N), torch.int32, qa) if want_acc else None
+    _lib.check("qlin_gemm_w4a8", lib.qlin_gemm_w4a8(
+        qa.data_ptr(), sa.data_ptr(), w4.data_ptr(), sw.data_ptr(), _ptr(ratio) if group else None, group, M, N, K,
+        y.data_ptr(), _ptr(acc), _stream()))
+    return y, acc
+
+
+def qlin_gemm_w4a4(qa4, sa, za, rowsum, w4, sw, zw, colsum, N, want_acc=False, y=None):
+    lib = _lib.load()
+    _req(qa4, "qa4", torch.uint8)
+    M, K2 = qa4.shape
+    K = 2 * K2
+    for t, n, d, sh in [(sa, "sa", torch.float32, (M,)), (za, "za", torch.int32, (M,)),
+                        (rowsum, "rowsum", torch.int32, (M,)), (sw, "sw", torch.float32, (N,)),
+                        (zw, "zw", torch.int32, (N,)), (colsum, "colsum", torch.int32, (N,))]:
+        _req(t, n, d, sh)
+    _req(w4, "w4", torch.uint8)
+    y = y if y is not None else _empty((M, N), torch.float16, qa4)
+    _req(y, "y", torch.float16, (M, N))
+    acc = _empty((M, N), torch.int32, qa4) if want_acc else None
+    _lib.check("qlin_gemm_w4a4", lib.qlin_gemm_w4a4(
+        qa4.data_ptr(), sa.data_ptr(), za.data_ptr(), rowsum.data_ptr(), w4.data_ptr(), sw.data_ptr(), zw.data_ptr(),
+        colsum.data_ptr(), M, N, K, y.data_ptr(), _ptr(acc), _stream()))
+    return y, acc
+
+
+def qlin_outlier_comp(qO, sa, O, s, WO, y):
+    """y += sa * sum_j qO * (s[O] - 1) * WO, in place."""
+    lib = _lib.load()
+    _req(y, "y", torch.float16)
+    M, N = y.shape
+    _req(s, "s", torch.float32)
+    K = s.numel()
+    nO = O.numel()
+    if nO:
+        _req(qO, "qO", torch.int8, (M, nO))
+        _req(sa, "sa", torch.float32, (M,))
+        _req(O, "O", torch.int32, (nO,))
+        _req(WO, "WO", torch.float16, (nO, N))
+    _lib.check("qlin_outlier_comp", lib.qlin_outlier_comp(
+        _ptr(qO) if nO else None, sa.data_ptr(), _ptr(O) if nO else None, nO, s.data_ptr(), K,
+        _ptr(WO) if nO else None, M, N, y.data_ptr(), _stream()))
+    return y

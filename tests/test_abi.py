@@ -1,0 +1,152 @@
+"""The C ABI: libqlin loads, exports every function include/qlin.h declares with
+the argument count the binding uses, and its host-side validation returns the
+documented status before any HIP call (CPU only, no kernel is launched)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from outlier_aware_bit_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlin.h")
+
+
+def _declarations():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    decls = {}
+    for m in re.finditer(r"\b(qlin_\w+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S):
+        params = m.group(2).strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        decls[m.group(1)] = n
+    return decls
+
+
+def test_header_declares_the_entry_points():
+    d = _declarations()
+    for name in ["qlin_quant_act", "qlin_hadamard_offset", "qlin_gemm_w8a8", "qlin_gemm_w4a8",
+                 "qlin_outlier_comp", "qlin_momentum_update", "qlin_gemm_w4a4", "qlin_pack_weight"]:
+        assert name in d
+
+
+def test_library_exports_every_declared_symbol_with_matching_arity():
+    lib = _lib.load()
+    decls = _declarations()
+    assert set(decls) == set(_lib.SIGNATURES), set(decls) ^ set(_lib.SIGNATURES)
+    for name, nargs in decls.items():
+        assert hasattr(lib, name), name
+        assert len(_lib.SIGNATURES[name][1]) == nargs, name
+
+
+def test_exported_symbols_via_nm_style_lookup():
+    # dlsym through a fresh handle, independent of the binding's table.
+    handle = C.CDLL(_lib.LIB_PATH)
+    for name in _declarations():
+        assert C.cast(getattr(handle, name), C.c_void_p).value
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    assert lib.qlin_abi_version() == 1
+    names = [lib.qlin_status_string(i).decode() for i in range(6)]
+    assert names == ["QLIN_OK", "QLIN_ERR_INVALID_ARG", "QLIN_ERR_SHAPE", "QLIN_ERR_ALIGN",
+                     "QLIN_ERR_UNSUPPORTED", "QLIN_ERR_HIP"]
+    assert lib.qlin_status_string(99).decode() == "QLIN_ERR_UNKNOWN"
+
+
+def test_packed_bytes():
+    lib = _lib.load()
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8, 4096, 4096) == 4096 * 4096
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W4S, 4096, 11008) == 4096 * 11008 // 2
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W4U, 4096, 14336) == 4096 * 14336 // 2
+    assert lib.qlin_packed_bytes(7, 4096, 4096) == 0
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8, 100, 4096) == 0
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8, 4096, 100) == 0
+
+
+# Fake but 16-byte aligned "device" addresses: validation never dereferences
+# them, and every case below fails (or returns for M == 0) before a HIP call.
+A = 0x10000
+B = 0x20000
+MIS = 0x10008  # 8-byte aligned only
+
+
+def _err(status, code):
+    assert status == code, (_lib.load().qlin_status_string(status), _lib.load().qlin_last_error())
+
+
+def test_quant_act_validation():
+    lib = _lib.load()
+    _err(lib.qlin_quant_act(None, 4, 256, None, B, A, None, 0, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    assert b"x" in lib.qlin_last_error()
+    _err(lib.qlin_quant_act(A, 4, 200, None, B, A, None, 0, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_quant_act(A, -1, 256, None, B, A, None, 0, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_quant_act(MIS, 4, 256, None, B, A, None, 0, None, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_quant_act(A, 4, 256, MIS, B, A, None, 0, None, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_quant_act(A, 4, 256, None, B, A, A, 0, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_quant_act(A, 4, 256, None, B, A, None, 3, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_quant_act(A, 4, 256, None, B, A, A, 300, B, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_quant_act(A, 0, 256, None, B, A, None, 0, None, None), _lib.QLIN_OK)
+
+
+def test_hadamard_validation():
+    lib = _lib.load()
+    args = [A, 4, 256, B, 128, A, A, A, A, None, None]
+    _err(lib.qlin_hadamard_offset(*args[:4], 64, *args[5:]), _lib.QLIN_ERR_UNSUPPORTED)
+    _err(lib.qlin_hadamard_offset(A, 4, 192, B, 128, A, A, A, A, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_hadamard_offset(A, 4, 256, None, 128, A, A, A, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_hadamard_offset(A, 4, 256, B, 128, A, A, A, A, MIS, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_hadamard_offset(A, 0, 256, B, 128, A, A, A, A, None, None), _lib.QLIN_OK)
+
+
+def test_momentum_validation():
+    lib = _lib.load()
+    _err(lib.qlin_momentum_update(A, 8, 256, A, 4, A, 1.5, A, B, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_momentum_update(A, 8, 256, A, 400, A, 0.9, A, B, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_momentum_update(A, 8, 256, None, 4, A, 0.9, A, B, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_momentum_update(A, 8, 256, A, 4, A, 0.9, None, B, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_momentum_update(A, -2, 256, A, 4, A, 0.9, A, B, None), _lib.QLIN_ERR_INVALID_ARG)
+
+
+def test_weight_prep_validation():
+    lib = _lib.load()
+    _err(lib.qlin_quant_weight_sym(A, 256, 128, 3, A, B, None), _lib.QLIN_ERR_UNSUPPORTED)
+    _err(lib.qlin_quant_weight_sym(A, 256, 100, 8, A, B, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_quant_weight_group(A, 256, 128, 64, A, B, A, B, None), _lib.QLIN_ERR_UNSUPPORTED)
+    _err(lib.qlin_quant_weight_offq(A, 256, 128, None, 128, A, B, A, B, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_pack_weight(9, A, 256, 128, B, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_pack_weight(_lib.QLIN_LAYOUT_W8, A, 256, 128, MIS, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_weight_row_absmax(A, 0, 128, None, None), _lib.QLIN_OK)
+
+
+def test_gemm_validation():
+    lib = _lib.load()
+    ok = [A, A, B, A, 16, 128, 256, None, None, 0, None, None, A, None, None]
+    _err(lib.qlin_gemm_w8a8(*ok[:4], 16, 100, 256, *ok[7:]), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_gemm_w8a8(*ok[:4], 16, 128, 250, *ok[7:]), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_gemm_w8a8(None, *ok[1:]), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w8a8(*ok[:7], A, A, 5, A, None, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w8a8(*ok[:7], None, A, 0, None, None, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w8a8(*ok[:12], A, MIS, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_gemm_w8a8(*ok[:4], 0, *ok[5:]), _lib.QLIN_OK)
+    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 64, 16, 128, 256, A, None, None), _lib.QLIN_ERR_UNSUPPORTED)
+    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 128, 16, 128, 256, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w4a8(A, A, B, A, A, 0, 16, 128, 256, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 0, 0, 128, 256, A, None, None), _lib.QLIN_OK)
+    _err(lib.qlin_gemm_w4a4(A, A, A, A, B, A, A, None, 16, 128, 256, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w4a4(A, A, A, A, B, A, A, A, 16, 128, 384 + 64, A, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_gemm_w4a4(A, A, A, A, B, A, A, A, 0, 128, 256, A, None, None), _lib.QLIN_OK)
+    _err(lib.qlin_outlier_comp(A, A, A, 4, A, 256, A, 16, 100, A, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_outlier_comp(None, A, A, 4, A, 256, A, 16, 128, A, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_outlier_comp(A, A, A, 0, A, 256, A, 16, 128, A, None), _lib.QLIN_OK)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from outlier_aware_bit_amd import qlin
+    with pytest.raises(ValueError):
+        qlin.qlin_quant_act(torch.zeros((4, 256), dtype=torch.float16))
+    with pytest.raises(TypeError):
+        qlin.qlin_quant_act(torch.zeros((4, 256), dtype=torch.float32))

@@ -1,0 +1,266 @@
+"""GPU parity of every libqlin entry point against the CPU oracle, called through
+the C ABI (via the thin binding) on seeded synthetic inputs.
+
+Integer results (codes, zero points, row/column sums, int32 accumulators) and
+the fp32 scales, s and r must match bit for bit; fp16 outputs must be within a
+normwise relative error of 1e-3 of the oracle's float64 value computed from
+the same codes.  Shapes span several tiles with ragged tails (M not a multiple
+of the tile, N a multiple of 64 but not of 128, K a multiple of 128 only).
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import gemm, hadamard, layer, quant, quaff
+from tests.gpu_helpers import assert_close, assert_equal, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+    assert torch.cuda.is_available()
+    from outlier_aware_bit_amd import qlin
+    return qlin
+
+
+# ------------------------------------------------------------ activations
+@pytest.mark.parametrize("M,K,n_out,use_r", [
+    (16, 256, 8, False), (1, 4096, 41, False), (37, 384, 3, True), (300, 1024, 10, True),
+    (5, 11008, 110, False), (3, 16384 + 2048, 5, True),
+])
+def test_quant_act(q, M, K, n_out, use_r):
+    log(f"quant_act M={M} K={K} r={use_r}")
+    lin = synth.plain_linear(M, K, 64, seed=100 + M, n_outliers=n_out)
+    r = None
+    if use_r:
+        r = np.random.default_rng(M).uniform(0.01, 1.5, K).astype(np.float32)
+    want_q, want_s = quant.quant_act_sym_int8(lin.x, r)
+    O = lin.outliers
+    qq, ss, qO = q.qlin_quant_act(dev(lin.x), None if r is None else dev(r), dev(O))
+    assert_equal(host(qq), want_q, "q")
+    assert_equal(host(ss), want_s, "scale")
+    assert_equal(host(qO), want_q[:, O], "qO")
+
+
+def test_quant_act_zero_rows_and_empty(q):
+    x = np.zeros((4, 256), np.float16)
+    x[2, 7] = -3.0
+    qq, ss, _ = q.qlin_quant_act(dev(x))
+    want_q, want_s = quant.quant_act_sym_int8(x)
+    assert_equal(host(qq), want_q, "q")
+    assert_equal(host(ss), want_s, "scale")
+    import torch
+    qq, ss, _ = q.qlin_quant_act(torch.zeros((0, 256), dtype=torch.float16, device="cuda"))
+    assert qq.shape == (0, 256)
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (37, 512), (300, 4096), (6, 11008)])
+def test_hadamard_offset(q, M, K):
+    log(f"hadamard_offset M={M} K={K}")
+    lin = synth.offq_inputs(M=M, K=K, N=64, seed=7 + M)
+    signs = lin.extra["signs"]
+    want_q, want_s, want_z, want_rs, want_t = quant.hadamard_offset_int4(lin.x, signs)
+    q4, ss, zz, rs, t = q.qlin_hadamard_offset(dev(lin.x), dev(signs), want_t=True)
+    assert_equal(host(t), want_t, "t")
+    packed = host(q4)
+    codes = np.empty((M, K), np.uint8)
+    codes[:, 0::2] = packed & 0xF
+    codes[:, 1::2] = packed >> 4
+    assert_equal(codes, want_q, "codes")
+    assert_equal(host(ss), want_s, "scale")
+    assert_equal(host(zz), want_z, "zero")
+    assert_equal(host(rs), want_rs, "rowsum")
+
+
+def test_hadamard_offset_constant_tokens(q):
+    # Only channel 0 of a single group set: the token is constant after the
+    # transform (range 0), the degenerate branch of the quantizer.
+    x = np.zeros((3, 128), np.float16)
+    x[:, 0] = [5.0, -2.5, 0.0]
+    signs = np.ones(128, np.int8)
+    want = quant.hadamard_offset_int4(x, signs)
+    q4, ss, zz, rs, t = q.qlin_hadamard_offset(dev(x), dev(signs), want_t=True)
+    assert_equal(host(t), want[4], "t")
+    assert_equal(host(ss), want[1], "scale")
+    assert_equal(host(zz), want[2], "zero")
+    assert_equal(host(rs), want[3], "rowsum")
+
+
+# ------------------------------------------------------------ Quaff
+@pytest.mark.parametrize("M,nO", [(300, 51), (1, 1), (0, 4), (64, 0)])
+def test_momentum_ten_steps(q, M, nO):
+    import torch
+    log(f"momentum M={M} nO={nO}")
+    K = 1024
+    d = synth.quaff_steps(M=max(M, 1), K=K, N=64, n_outliers=max(nO, 1), steps=10, seed=3)
+    O = d.outliers[:nO]
+    wmax = (np.random.default_rng(1).uniform(0.0, 0.1, nO)).astype(np.float32)
+    if nO > 1:
+        wmax[0] = 0.0
+    s_ref = np.ones(K, np.float32)
+    s = torch.ones(K, dtype=torch.float32, device="cuda")
+    r = torch.empty(K, dtype=torch.float32, device="cuda")
+    Od, wd = dev(O.astype(np.int32)), dev(wmax)
+    for t in range(10):
+        x = d.xs[t][:M]
+        s_ref, r_ref = quaff.momentum_update(x, O, wmax, 0.9, s_ref)
+        q.qlin_momentum_update(dev(x), Od, wd, 0.9, s, r)
+        assert_equal(host(s), s_ref, f"s step {t}")
+        assert_equal(host(r), r_ref, f"r step {t}")
+
+
+def test_weight_row_absmax(q):
+    w = (np.random.default_rng(2).standard_normal((37, 192)) * 0.02).astype(np.float16)
+    w[5] = 0
+    assert_equal(host(q.qlin_weight_row_absmax(dev(w))), quaff.weight_row_absmax(w), "wmax")
+
+
+# ------------------------------------------------------------ weights
+@pytest.mark.parametrize("K,N", [(256, 128), (384, 192), (1024, 64)])
+def test_weight_quantizers(q, K, N):
+    log(f"weights K={K} N={N}")
+    rng = np.random.default_rng(K + N)
+    w = (rng.standard_normal((K, N)) * 0.02).astype(np.float16)
+    w[:, 3] = 0
+    w[:128, 5] *= 50
+    for bits in (8, 4):
+        want_c, want_s = quant.quant_weight_sym(w, bits)
+        c, s = q.qlin_quant_weight_sym(dev(w), bits)
+        assert_equal(host(c), want_c, f"codes{bits}")
+        assert_equal(host(s).view(np.uint16), want_s.view(np.uint16), f"scale{bits}")
+    want = quant.quant_weight_group(w, 128)
+    got = q.qlin_quant_weight_group(dev(w), 128)
+    for g, wv, name in zip(got, want, ["codes", "group_scale", "channel_scale", "ratio"]):
+        if wv.dtype == np.float16:
+            assert_equal(host(g).view(np.uint16), wv.view(np.uint16), name)
+        else:
+            assert_equal(host(g), wv, name)
+    signs = rng.choice(np.array([-1, 1], np.int8), K)
+    signs[::128] = 1
+    want = quant.offq_weight(w, signs)
+    got = q.qlin_quant_weight_offq(dev(w), dev(signs))
+    for g, wv, name in zip(got, want, ["codes", "scale", "zero", "colsum"]):
+        assert_equal(host(g), wv, name)
+
+
+# ------------------------------------------------------------ GEMMs
+GEMM_SHAPES = [(1, 256, 128), (7, 384, 192), (16, 256, 128), (33, 512, 64), (64, 1024, 256),
+               (65, 256, 192), (200, 384, 320), (256, 512, 128)]
+
+
+@pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
+def test_gemm_w8a8(q, M, K, N):
+    log(f"w8a8 M={M} K={K} N={N}")
+    lin = synth.plain_linear(M, K, N, seed=M * 7 + K, n_outliers=3)
+    ref = layer.w8a8_forward(lin.x, lin.w)
+    codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 8)
+    w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
+    qa, sa, _ = q.qlin_quant_act(dev(lin.x))
+    y, acc = q.qlin_gemm_w8a8(qa, sa, w8, sw, N, want_acc=True)
+    assert_equal(host(acc), ref["acc"], "acc")
+    assert_close(host(y), ref["y"], "y")
+
+
+@pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
+def test_gemm_w4a8_channel(q, M, K, N):
+    log(f"w4a8 channel M={M} K={K} N={N}")
+    lin = synth.plain_linear(M, K, N, seed=M * 11 + K, n_outliers=2)
+    ref = layer.w4a8_channel_forward(lin.x, lin.w)
+    codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 4)
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes)
+    qa, sa, _ = q.qlin_quant_act(dev(lin.x))
+    y, acc = q.qlin_gemm_w4a8(qa, sa, w4, sw, N, want_acc=True)
+    assert_equal(host(acc), ref["acc"], "acc")
+    assert_close(host(y), ref["y"], "y")
+
+
+@pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
+def test_gemm_w4a8_group(q, M, K, N):
+    log(f"w4a8 group M={M} K={K} N={N}")
+    lin = synth.plain_linear(M, K, N, seed=M * 13 + K)
+    ref = layer.w4a8_group_forward(lin.x, lin.w)
+    codes, gs, cs, ratio = q.qlin_quant_weight_group(dev(lin.w), 128)
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes)
+    qa, sa, _ = q.qlin_quant_act(dev(lin.x))
+    y, acc = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128, want_acc=True)
+    assert_equal(host(acc), ref["acc"], "acc")
+    assert_close(host(y), ref["y"], "y")
+
+
+def test_gemm_w4a8_group_requant_edge_ratios(q):
+    # Hand-picked ratios (ties, clamping, fp16 rounding that changes the integer)
+    # and every int4 code, including -8, checked through the GEMM accumulator
+    # with one-hot activations: acc[m, n] is exactly the requantized weight.
+    K, N = 128, 64
+    rng = np.random.default_rng(0)
+    codes = np.tile(np.arange(-8, 8, dtype=np.int8), K // 16)[:, None].repeat(N, 1)
+    rg = np.zeros((1, N), np.float16)
+    rg[0, :8] = [0.2142333984375, 16.5, 18.5, 16.0, 3.0, 0.0, 18.140625, 1e-7]
+    rg[0, 8:] = rng.uniform(0, 18.2, N - 8).astype(np.float16)
+    want_w8 = quant.requant_group(codes, rg, 128)
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, dev(codes))
+    qa = np.eye(K, dtype=np.int8)
+    y, acc = q.qlin_gemm_w4a8(dev(qa), dev(np.ones(K, np.float32)), w4, dev(np.ones(N, np.float16)), N,
+                              ratio=dev(rg), group=128, want_acc=True)
+    assert_equal(host(acc), want_w8.astype(np.int32), "requantized weights")
+
+
+@pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
+def test_gemm_w4a4(q, M, K, N):
+    log(f"w4a4 M={M} K={K} N={N}")
+    lin = synth.offq_inputs(M=M, K=K, N=N, seed=M * 17 + K)
+    signs = lin.extra["signs"]
+    ref = layer.offq_forward(lin.x, lin.w, signs)
+    qa4, sa, za, rs, _ = q.qlin_hadamard_offset(dev(lin.x), dev(signs))
+    codes, sw, zw, cs = q.qlin_quant_weight_offq(dev(lin.w), dev(signs))
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, codes)
+    y, acc = q.qlin_gemm_w4a4(qa4, sa, za, rs, w4, sw, zw, cs, N, want_acc=True)
+    assert_equal(host(acc), ref["acc"], "acc")
+    assert_close(host(y), ref["y"], "y")
+
+
+@pytest.mark.parametrize("M,K,N,nO", [(16, 256, 128, 13), (200, 512, 192, 64), (130, 384, 64, 33)])
+def test_quaff_fused_and_standalone_compensation(q, M, K, N, nO):
+    import torch
+    log(f"quaff comp M={M} K={K} N={N} nO={nO}")
+    d = synth.quaff_steps(M=M, K=K, N=N, n_outliers=nO, steps=3, seed=M + nO)
+    prep = layer.quaff_prepare(d.w, d.outliers)
+    s_ref = np.ones(K, np.float32)
+    O = dev(d.outliers)
+    codes, sw = q.qlin_quant_weight_sym(dev(d.w), 8)
+    w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
+    WO = dev(np.ascontiguousarray(d.w[d.outliers]))
+    wmax = q.qlin_weight_row_absmax(WO)
+    assert_equal(host(wmax), prep["wmax"], "wmax")
+    s = torch.ones(K, dtype=torch.float32, device="cuda")
+    r = torch.empty(K, dtype=torch.float32, device="cuda")
+    for t, x in enumerate(d.xs):
+        ref = layer.quaff_step(x, prep, d.outliers, s_ref)
+        s_ref = ref["s"]
+        xd = dev(x)
+        q.qlin_momentum_update(xd, O, wmax, 0.9, s, r)
+        qa, sa, qO = q.qlin_quant_act(xd, r, O)
+        assert_equal(host(s), ref["s"], "s")
+        assert_equal(host(qa), ref["q"], "q")
+        y, acc = q.qlin_gemm_w8a8(qa, sa, w8, sw, N, qO=qO, O=O, s=s, WO=WO, want_acc=True)
+        assert_equal(host(acc), ref["acc"], "acc")
+        assert_close(host(y), ref["y"], f"fused y step {t}")
+        y2, _ = q.qlin_gemm_w8a8(qa, sa, w8, sw, N)
+        q.qlin_outlier_comp(qO, sa, O, s, WO, y2)
+        assert_close(host(y2), ref["y"], f"standalone y step {t}")
+
+
+def test_gemm_w8a8_single_tile_identity(q):
+    # acc[m, n] = sum_k qa[m, k] * w[k, n] with qa = identity rows: the output
+    # reproduces W's codes, which pins the fragment row/column layout.
+    K, N, M = 256, 128, 128
+    rng = np.random.default_rng(5)
+    codes = rng.integers(-127, 128, (K, N)).astype(np.int8)
+    w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, dev(codes))
+    qa = np.zeros((M, K), np.int8)
+    qa[np.arange(M), np.arange(M)] = 1
+    y, acc = q.qlin_gemm_w8a8(dev(qa), dev(np.ones(M, np.float32)), w8, dev(np.ones(N, np.float16)), N,
+                              want_acc=True)
+    assert_equal(host(acc), codes[:M].astype(np.int32), "acc")
