@@ -1,0 +1,330 @@
+"""Benchmark of the outlier-aware quantized linear layer on one MI355X.
+
+The headline workload is the Quaff W8A8 layer at LLaMA-7B q_proj shape:
+X [2048 x 4096] fp16 with a fixed 5% outlier channel set (205 channels at
+50-150x, drifting 5% per step over 10 activation batches), W [4096 x 4096]
+pre-quantized to int8 per output channel, fp16 rows W_O on the outlier set,
+momentum gamma = 0.9.  One step is one forward of the layer on one batch:
+  momentum update of s on O  ->  per-token int8 quantization of X / s
+  ->  W8A8 int8-MFMA GEMM with the fused compensation term  ->  Y fp16.
+
+Printed: one JSON line with the step throughput (TOPS of the layer's
+algorithmic work), the roofline of the dominant kernel (the fused GEMM) timed
+with HIP events on its own stream, the CPU oracle timed on the host on a
+bounded sample, and per-kernel measurements of the other steps of the path at
+their own workload shapes ("rows").
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-rows]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized-linear TOPS and HBM GB/s at LLaMA-7B layer shapes; % of roofline"
+PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_FP16_TFLOPS = 2500.0  # dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0      # HBM3E, 8 TB/s
+MALL_BYTES = 256 << 20
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def time_launches(fn, reps, trials=5, warm=3):
+    """Median over trials of the mean per-launch time (ms) of `reps`
+    back-to-back calls, timed with HIP events on the current stream."""
+    import torch
+    for _ in range(warm):
+        fn(0)
+    torch.cuda.synchronize()
+    res = []
+    for t in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        e1.synchronize()
+        res.append(e0.elapsed_time(e1) / reps)
+    return statistics.median(res)
+
+
+# ------------------------------------------------------------------ headline
+class QuaffLayer:
+    def __init__(self, q, M=2048, K=4096, N=4096, n_outliers=205, batches=10, gamma=0.9, seed=1):
+        import torch
+        self.q = q
+        self.M, self.K, self.N, self.gamma = M, K, N, gamma
+        log(f"generating Quaff q_proj inputs M={M} K={K} N={N} |O|={n_outliers} batches={batches}")
+        import synth
+        d = self.data = synth.quaff_steps(M=M, K=K, N=N, n_outliers=n_outliers, steps=batches, seed=seed)
+        self.xs = [dev(x) for x in d.xs]
+        self.O = dev(d.outliers)
+        self.nO = int(d.outliers.size)
+        w = dev(d.w)
+        codes, self.sw = q.qlin_quant_weight_sym(w, 8)
+        self.w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
+        self.WO = dev(np.ascontiguousarray(d.w[d.outliers]))
+        self.wmax = q.qlin_weight_row_absmax(self.WO)
+        self.s = torch.ones(K, dtype=torch.float32, device="cuda")
+        self.r = torch.empty_like(self.s)
+        self.qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        self.sa = torch.empty((M,), dtype=torch.float32, device="cuda")
+        self.qO = torch.empty((M, self.nO), dtype=torch.int8, device="cuda")
+        self.y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        del w, codes
+        torch.cuda.synchronize()
+
+    def momentum(self, x):
+        self.q.qlin_momentum_update(x, self.O, self.wmax, self.gamma, self.s, self.r)
+
+    def quant(self, x):
+        self.q.qlin_quant_act(x, self.r, self.O, q=self.qa, scale=self.sa, qO=self.qO)
+
+    def gemm(self):
+        self.q.qlin_gemm_w8a8(self.qa, self.sa, self.w8, self.sw, self.N, qO=self.qO, O=self.O, s=self.s,
+                              WO=self.WO, y=self.y)
+
+    def step(self, t, ev=None):
+        x = self.xs[t % len(self.xs)]
+        self.momentum(x)
+        self.quant(x)
+        if ev is not None:
+            ev[0].record()
+        self.gemm()
+        if ev is not None:
+            ev[1].record()
+
+    def int8_ops(self):
+        return 2 * self.M * self.K * self.N
+
+    def fp16_flops(self):
+        return 2 * self.M * self.nO * self.N
+
+    def gemm_bytes(self):
+        M, K, N, nO = self.M, self.K, self.N, self.nO
+        return M * K + K * N + 4 * M + 2 * N + M * nO + 4 * nO + 4 * K + 2 * nO * N + 2 * M * N
+
+
+def cpu_baseline(layer, budget_s=12.0, rows=128):
+    """The oracle as it stands, on the host: the momentum update over the full
+    batch, then quantization, the exact int8 GEMM (float64 BLAS) and the
+    compensation term on a sample of `rows` tokens; repeated until `budget_s`."""
+    from oracle import layer as ol
+    from threadpoolctl import threadpool_info
+    d = layer.data
+    prep = ol.quaff_prepare(d.w, d.outliers)
+    s = np.ones(layer.K, np.float32)
+    x_full = d.xs[0]
+    from oracle import quaff, quant, gemm
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        s, r = quaff.momentum_update(x_full, d.outliers, prep["wmax"], layer.gamma, s)
+        x = x_full[:rows]
+        qa, sa = quant.quant_act_sym_int8(x, r)
+        acc, y = gemm.w8a8(qa, sa, prep["qw"], prep["sw"].astype(np.float32))
+        y = y + quaff.compensation(qa[:, d.outliers], sa, s[d.outliers], prep["w_o"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    ops = n * (2 * rows * layer.K * layer.N + 2 * rows * layer.nO * layer.N)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": ops / el / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+        "sample": f"{n} oracle layer steps on {rows} of {layer.M} tokens (momentum over all {layer.M}); "
+                  f"{el:.1f} s; ops counted for the sampled rows only",
+    }
+
+
+# ------------------------------------------------------------------ rows
+def rows_measurements(q, layer):
+    import torch
+    out = {}
+    M, K, N, nO = layer.M, layer.K, layer.N, layer.nO
+
+    x = layer.xs[0]
+    t = time_launches(lambda i: layer.momentum(layer.xs[i % len(layer.xs)]), 200)
+    b = 2 * M * nO + 4 * nO * 3 + 4 * K * 2
+    out["A1_momentum_update"] = dict(workload=f"quaff M={M} K={K} |O|={nO}", ms=t, bytes=b, gbs=b / t / 1e6,
+                                     frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm")
+    t = time_launches(lambda i: layer.quant(layer.xs[i % len(layer.xs)]), 200)
+    b = 2 * M * K + M * K + 4 * M + 4 * K + M * nO
+    out["A2_quant_act"] = dict(workload=f"quaff M={M} K={K} with r and qO", ms=t, bytes=b, gbs=b / t / 1e6,
+                               frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm")
+    t = time_launches(lambda i: layer.gemm(), 100)
+    ops = layer.int8_ops() + 2 * layer.fp16_flops()
+    out["A4A5_gemm_w8a8_fused_comp"] = dict(workload=f"{M}x{K}x{N} + |O|={nO}", ms=t, int8_equiv_ops=ops,
+                                            tops=ops / t / 1e9, frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma")
+    t = time_launches(lambda i: q.qlin_gemm_w8a8(layer.qa, layer.sa, layer.w8, layer.sw, N, y=layer.y), 100)
+    ops = layer.int8_ops()
+    out["A4_gemm_w8a8"] = dict(workload=f"{M}x{K}x{N}", ms=t, ops=ops, tops=ops / t / 1e9,
+                               frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma")
+    y2 = layer.y.clone()
+    t = time_launches(lambda i: q.qlin_outlier_comp(layer.qO, layer.sa, layer.O, layer.s, layer.WO, y2), 100)
+    fl = layer.fp16_flops()
+    out["A5_outlier_comp_standalone"] = dict(workload=f"{M}x{nO}x{N}", ms=t, flops=fl, tflops=fl / t / 1e9,
+                                             frac=fl / t / 1e9 / PEAK_FP16_TFLOPS, bound="mfma")
+    del y2
+
+    # QQQ W4A8 per-channel decode, weights rotated through >= 2x the MALL.
+    import synth
+    K3, N3 = 4096, 11008
+    lin = synth.qqq_decode(M=64, K=K3, N=N3, seed=2)
+    w = dev(lin.w)
+    codes, sw = q.qlin_quant_weight_sym(w, 4)
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes)
+    copies = max(2, (2 * MALL_BYTES) // w4.numel() + 1)
+    bufs = [w4.clone() for _ in range(copies)]
+    del w, codes
+    for m in (1, 16, 64):
+        qa, sa, _ = q.qlin_quant_act(dev(lin.x[:m]))
+        y = torch.empty((m, N3), dtype=torch.float16, device="cuda")
+        t = time_launches(lambda i: q.qlin_gemm_w4a8(qa, sa, bufs[i % copies], sw, N3, y=y), 240)
+        b = K3 * N3 // 2 + m * K3 + 2 * N3 + 4 * m + 2 * m * N3
+        out[f"A6_gemm_w4a8_channel_M{m}"] = dict(workload=f"{m}x{K3}x{N3} ({copies} rotating weight copies)",
+                                                 ms=t, bytes=b, gbs=b / t / 1e6, frac=b / t / 1e6 / PEAK_HBM_GBS,
+                                                 tops=2 * m * K3 * N3 / t / 1e9, bound="hbm")
+    del bufs, w4
+
+    # QQQ W4A8 per-group prefill at down_proj shape.
+    M4, K4, N4 = 4096, 11008, 4096
+    lin = synth.qqq_prefill(M=M4, K=K4, N=N4, seed=3)
+    codes, gs, cs, ratio = q.qlin_quant_weight_group(dev(lin.w), 128)
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes)
+    xq = dev(lin.x)
+    qa, sa, _ = q.qlin_quant_act(xq)
+    t = time_launches(lambda i: q.qlin_quant_act(xq, q=qa, scale=sa), 50)
+    b = 3 * M4 * K4 + 4 * M4
+    out["A2_quant_act_prefill"] = dict(workload=f"{M4}x{K4}", ms=t, bytes=b, gbs=b / t / 1e6,
+                                       frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm")
+    y = torch.empty((M4, N4), dtype=torch.float16, device="cuda")
+    t = time_launches(lambda i: q.qlin_gemm_w4a8(qa, sa, w4, cs, N4, ratio=ratio, group=128, y=y), 20)
+    ops = 2 * M4 * K4 * N4
+    out["A7_gemm_w4a8_group128"] = dict(workload=f"{M4}x{K4}x{N4}", ms=t, ops=ops, tops=ops / t / 1e9,
+                                        frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma")
+    del codes, w4, xq, qa, y
+
+    # OffQ W4A4 at LLaMA-3-8B up_proj shape.
+    M5, K5, N5 = 2048, 4096, 14336
+    lin = synth.offq_inputs(M=M5, K=K5, N=N5, seed=4)
+    signs = dev(lin.extra["signs"])
+    xo = dev(lin.x)
+    qa4, sa, za, rs, _ = q.qlin_hadamard_offset(xo, signs)
+    t = time_launches(lambda i: q.qlin_hadamard_offset(xo, signs), 50)
+    b = 2 * M5 * K5 + M5 * K5 // 2 + 12 * M5 + K5
+    out["A3_hadamard_offset"] = dict(workload=f"{M5}x{K5}", ms=t, bytes=b, gbs=b / t / 1e6,
+                                     frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm")
+    cw, swf, zw, cs = q.qlin_quant_weight_offq(dev(lin.w), signs)
+    w4u = q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, cw)
+    y = torch.empty((M5, N5), dtype=torch.float16, device="cuda")
+    t = time_launches(lambda i: q.qlin_gemm_w4a4(qa4, sa, za, rs, w4u, swf, zw, cs, N5, y=y), 20)
+    ops = 2 * M5 * K5 * N5
+    out["A8_gemm_w4a4"] = dict(workload=f"{M5}x{K5}x{N5}", ms=t, ops=ops, tops=ops / t / 1e9,
+                               frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma")
+    del cw, w4u, y, xo
+
+    # Tiny W8A8 (latency only).
+    lin = synth.tiny_w8a8(seed=0)
+    codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 8)
+    w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
+    xt = dev(lin.x)
+    qa, sa, _ = q.qlin_quant_act(xt)
+    t = time_launches(lambda i: (q.qlin_quant_act(xt, q=qa, scale=sa), q.qlin_gemm_w8a8(qa, sa, w8, sw, 128)), 200)
+    out["tiny_w8a8_quant_plus_gemm"] = dict(workload="16x256x128", ms=t, bound="launch")
+    torch.cuda.synchronize()
+    for v in out.values():
+        for k in list(v):
+            if isinstance(v[k], float):
+                v[k] = round(v[k], 6)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    a = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE={world}); "
+              "the layer is data-parallel over tokens with no communication, so N GPUs would run N "
+              "independent copies of this single-GPU measurement.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from outlier_aware_bit_amd import qlin as q
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    layer = QuaffLayer(q)
+
+    for t in range(a.warmup):
+        layer.step(t)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(a.steps):
+        layer.step(a.warmup + t, evs[t])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_step = el * 1e3 / a.steps
+    gemm_ms = statistics.mean(e0.elapsed_time(e1) for e0, e1 in evs)
+    ops_step = layer.int8_ops() + layer.fp16_flops()
+    eq_ops = layer.int8_ops() + 2 * layer.fp16_flops()
+    achieved = eq_ops / (gemm_ms * 1e-3) / 1e12
+    log(f"step {ms_step:.4f} ms, fused GEMM {gemm_ms:.4f} ms ({achieved:.1f} int8-equivalent TOPS)")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(ops_step / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "quaff_w8a8_outlier_comp_q_proj", "M_tokens": layer.M, "K": layer.K,
+                   "N": layer.N, "n_outliers": layer.nO, "gamma": layer.gamma, "activation_batches": 10,
+                   "step": "momentum_update + quant_act + gemm_w8a8(fused compensation)"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_tile<W8,I8,comp>", "achieved": round(achieved, 2),
+                     "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": None, "launch_ms": round(gemm_ms, 5),
+                     "work": "int8 MACs x2 plus fp16 compensation flops x2 (fp16 peak is half the int8 peak)"},
+    }
+    if not a.no_rows:
+        rec["rows"] = rows_measurements(q, layer)
+    if not a.no_cpu:
+        log("timing the CPU oracle")
+        rec["cpu_baseline"] = cpu_baseline(layer, budget_s=a.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,7 +25,8 @@
  *     uint16_t bit patterns.  X is [M x K] (tokens x input channels), W is
  *     [K x N] (input x output channels), Y is [M x N].
  *   - Every pointer must be 16-byte aligned (QLIN_ERR_ALIGN otherwise).
- *   - Shapes: M >= 0 (M == 0 returns QLIN_OK and launches nothing);
+ *   - Shapes: M >= 0 (M == 0 returns QLIN_OK after the shape checks, reads no
+ *     pointer and launches nothing, except qlin_momentum_update);
  *     K > 0 and K % 128 == 0; N > 0 and N % 64 == 0 (QLIN_ERR_SHAPE otherwise).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream).  Nothing is synchronised; results are ready when the stream is.

@@ -57,6 +57,11 @@ def load() -> C.CDLL:
             raise ImportError(
                 f"{LIB_PATH} is missing: build it with `python -m outlier_aware_bit_amd.build` "
                 "(hipcc --offload-arch=gfx950); there is no fallback implementation")
+        # One HIP runtime per process: torch ships its own libamdhip64 (same
+        # SONAME as ROCm's).  Loading torch first makes libqlin bind to the
+        # runtime that owns torch's allocations and streams; loading libqlin
+        # first would pull in a second runtime beside torch's.
+        import torch  # noqa: F401
         lib = C.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)

@@ -280,6 +280,7 @@ extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, c
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
   QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
+  if (M == 0) return QLIN_OK;
   QLIN_PTR(x);
   QLIN_PTR(q);
   QLIN_PTR(scale);
@@ -290,7 +291,6 @@ extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, c
   } else {
     QLIN_REQUIRE(O == nullptr && qO == nullptr, QLIN_ERR_INVALID_ARG, "O and qO must be NULL when nO == 0");
   }
-  if (M == 0) return QLIN_OK;
   QLIN_REQUIRE(M <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
   const dim3 grid(static_cast<unsigned>(M));
   if (r != nullptr)
@@ -308,6 +308,7 @@ extern "C" qlin_status qlin_hadamard_offset(const uint16_t* x, int64_t M, int64_
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
   QLIN_REQUIRE(block == 128, QLIN_ERR_UNSUPPORTED, "block=%d: only 128 is provided", block);
+  if (M == 0) return QLIN_OK;
   QLIN_PTR(x);
   QLIN_PTR(signs);
   QLIN_PTR(q4);
@@ -315,7 +316,6 @@ extern "C" qlin_status qlin_hadamard_offset(const uint16_t* x, int64_t M, int64_
   QLIN_PTR(zero);
   QLIN_PTR(rowsum);
   QLIN_OPT_PTR(t);
-  if (M == 0) return QLIN_OK;
   QLIN_REQUIRE(M <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
   hadamard_offset_kernel<<<dim3(static_cast<unsigned>(M)), kHadThreads, 0, as_stream(stream)>>>(
       x, K, signs, q4, scale, zero, rowsum, t);

@@ -65,8 +65,12 @@ __device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
 __device__ __forceinline__ float mul_rn(float a, float b) { return __fmul_rn(a, b); }
 __device__ __forceinline__ float add_rn(float a, float b) { return __fadd_rn(a, b); }
 __device__ __forceinline__ float sub_rn(float a, float b) { return __fsub_rn(a, b); }
-__device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, b); }
-__device__ __forceinline__ float sqrt_rn(float a) { return __fsqrt_rn(a); }
+__device__ __forceinline__ float div_rn(float a, float b) { return a / b; }
+// HIP's __fsqrt_rn maps to the approximate native square root unless OCML's
+// rounded operations are enabled; the sqrtf builtin is lowered to the
+// correctly rounded sequence (v_sqrt_f32 plus residual checks of both
+// neighbours), and '/' to the IEEE division sequence.
+__device__ __forceinline__ float sqrt_rn(float a) { return __builtin_sqrtf(a); }
 __device__ __forceinline__ float rint_f(float a) { return __builtin_rintf(a); }
 
 // Wavefront (64 lanes) reductions.

@@ -458,6 +458,7 @@ extern "C" qlin_status qlin_gemm_w8a8(const int8_t* qa, const float* sa, const v
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_K_N(K, N);
   QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
+  if (M == 0) return QLIN_OK;
   QLIN_PTR(qa);
   QLIN_PTR(sa);
   QLIN_PTR(w8);
@@ -473,7 +474,6 @@ extern "C" qlin_status qlin_gemm_w8a8(const int8_t* qa, const float* sa, const v
     QLIN_REQUIRE(qO == nullptr && O == nullptr && s == nullptr && WO == nullptr, QLIN_ERR_INVALID_ARG,
                  "qO, O, s and WO must be NULL when nO == 0");
   }
-  if (M == 0) return QLIN_OK;
   GemmArgs g = base_args(M, N, K, y, acc);
   g.a = qa;
   g.sa = sa;
@@ -494,6 +494,7 @@ extern "C" qlin_status qlin_gemm_w4a8(const int8_t* qa, const float* sa, const v
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_K_N(K, N);
   QLIN_REQUIRE(group == 0 || group == 128, QLIN_ERR_UNSUPPORTED, "group=%d: only 0 and 128 are provided", group);
+  if (M == 0) return QLIN_OK;
   QLIN_PTR(qa);
   QLIN_PTR(sa);
   QLIN_PTR(w4);
@@ -504,7 +505,6 @@ extern "C" qlin_status qlin_gemm_w4a8(const int8_t* qa, const float* sa, const v
     QLIN_PTR(ratio);
   else
     QLIN_REQUIRE(ratio == nullptr, QLIN_ERR_INVALID_ARG, "ratio must be NULL when group == 0");
-  if (M == 0) return QLIN_OK;
   GemmArgs g = base_args(M, N, K, y, acc);
   g.a = qa;
   g.sa = sa;
@@ -521,6 +521,7 @@ extern "C" qlin_status qlin_gemm_w4a4(const uint8_t* qa4, const float* sa, const
                                       int64_t K, uint16_t* y, int32_t* acc, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_K_N(K, N);
+  if (M == 0) return QLIN_OK;
   QLIN_PTR(qa4);
   QLIN_PTR(sa);
   QLIN_PTR(za);
@@ -531,7 +532,6 @@ extern "C" qlin_status qlin_gemm_w4a4(const uint8_t* qa4, const float* sa, const
   QLIN_PTR(colsum);
   QLIN_PTR(y);
   QLIN_OPT_PTR(acc);
-  if (M == 0) return QLIN_OK;
   GemmArgs g = base_args(M, N, K, y, acc);
   g.a = qa4;
   g.sa = sa;
