@@ -81,26 +81,27 @@ class QuaffLayer:
         w = dev(d.w)
         codes, self.sw = q.qlin_quant_weight_sym(w, 8)
         self.w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
-        self.WO = dev(np.ascontiguousarray(d.w[d.outliers]))
-        self.wmax = q.qlin_weight_row_absmax(self.WO)
+        WO = dev(np.ascontiguousarray(d.w[d.outliers]))
+        self.WOp = q.qlin_pack_weight(q.QLIN_LAYOUT_WO, WO)
+        self.wmax = q.qlin_weight_row_absmax(WO)
         self.s = torch.ones(K, dtype=torch.float32, device="cuda")
         self.r = torch.empty_like(self.s)
         self.qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
         self.sa = torch.empty((M,), dtype=torch.float32, device="cuda")
-        self.qO = torch.empty((M, self.nO), dtype=torch.int8, device="cuda")
+        self.xO = torch.empty((M, q.qlin_outlier_ld(self.nO)), dtype=torch.float16, device="cuda")
         self.y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-        del w, codes
+        del w, codes, WO
         torch.cuda.synchronize()
 
     def momentum(self, x):
         self.q.qlin_momentum_update(x, self.O, self.wmax, self.gamma, self.s, self.r)
 
     def quant(self, x):
-        self.q.qlin_quant_act(x, self.r, self.O, q=self.qa, scale=self.sa, qO=self.qO)
+        self.q.qlin_quant_act(x, self.r, self.O, s=self.s, q=self.qa, scale=self.sa, xO=self.xO, want_qO=False)
 
     def gemm(self):
-        self.q.qlin_gemm_w8a8(self.qa, self.sa, self.w8, self.sw, self.N, qO=self.qO, O=self.O, s=self.s,
-                              WO=self.WO, y=self.y)
+        self.q.qlin_gemm_w8a8(self.qa, self.sa, self.w8, self.sw, self.N, xO=self.xO, nO=self.nO, WO=self.WOp,
+                              y=self.y)
 
     def step(self, t, ev=None):
         x = self.xs[t % len(self.xs)]
@@ -167,8 +168,8 @@ def rows_measurements(q, layer):
     out["A1_momentum_update"] = dict(workload=f"quaff M={M} K={K} |O|={nO}", ms=t, bytes=b, gbs=b / t / 1e6,
                                      frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm")
     t = time_launches(lambda i: layer.quant(layer.xs[i % len(layer.xs)]), 200)
-    b = 2 * M * K + M * K + 4 * M + 4 * K + M * nO
-    out["A2_quant_act"] = dict(workload=f"quaff M={M} K={K} with r and qO", ms=t, bytes=b, gbs=b / t / 1e6,
+    b = 2 * M * K + M * K + 4 * M + 4 * K + 2 * M * nO
+    out["A2_quant_act"] = dict(workload=f"quaff M={M} K={K} with r and xO", ms=t, bytes=b, gbs=b / t / 1e6,
                                frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm")
     t = time_launches(lambda i: layer.gemm(), 100)
     ops = layer.int8_ops() + 2 * layer.fp16_flops()
@@ -179,7 +180,7 @@ def rows_measurements(q, layer):
     out["A4_gemm_w8a8"] = dict(workload=f"{M}x{K}x{N}", ms=t, ops=ops, tops=ops / t / 1e9,
                                frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma")
     y2 = layer.y.clone()
-    t = time_launches(lambda i: q.qlin_outlier_comp(layer.qO, layer.sa, layer.O, layer.s, layer.WO, y2), 100)
+    t = time_launches(lambda i: q.qlin_outlier_comp(layer.xO, layer.sa, nO, layer.WOp, y2), 100)
     fl = layer.fp16_flops()
     out["A5_outlier_comp_standalone"] = dict(workload=f"{M}x{nO}x{N}", ms=t, flops=fl, tflops=fl / t / 1e9,
                                              frac=fl / t / 1e9 / PEAK_FP16_TFLOPS, bound="mfma")
@@ -196,7 +197,7 @@ def rows_measurements(q, layer):
     bufs = [w4.clone() for _ in range(copies)]
     del w, codes
     for m in (1, 16, 64):
-        qa, sa, _ = q.qlin_quant_act(dev(lin.x[:m]))
+        qa, sa, _, _ = q.qlin_quant_act(dev(lin.x[:m]))
         y = torch.empty((m, N3), dtype=torch.float16, device="cuda")
         t = time_launches(lambda i: q.qlin_gemm_w4a8(qa, sa, bufs[i % copies], sw, N3, y=y), 240)
         b = K3 * N3 // 2 + m * K3 + 2 * N3 + 4 * m + 2 * m * N3
@@ -211,7 +212,7 @@ def rows_measurements(q, layer):
     codes, gs, cs, ratio = q.qlin_quant_weight_group(dev(lin.w), 128)
     w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes)
     xq = dev(lin.x)
-    qa, sa, _ = q.qlin_quant_act(xq)
+    qa, sa, _, _ = q.qlin_quant_act(xq)
     t = time_launches(lambda i: q.qlin_quant_act(xq, q=qa, scale=sa), 50)
     b = 3 * M4 * K4 + 4 * M4
     out["A2_quant_act_prefill"] = dict(workload=f"{M4}x{K4}", ms=t, bytes=b, gbs=b / t / 1e6,
@@ -247,7 +248,7 @@ def rows_measurements(q, layer):
     codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 8)
     w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
     xt = dev(lin.x)
-    qa, sa, _ = q.qlin_quant_act(xt)
+    qa, sa, _, _ = q.qlin_quant_act(xt)
     t = time_launches(lambda i: (q.qlin_quant_act(xt, q=qa, scale=sa), q.qlin_gemm_w8a8(qa, sa, w8, sw, 128)), 200)
     out["tiny_w8a8_quant_plus_gemm"] = dict(workload="16x256x128", ms=t, bound="launch")
     torch.cuda.synchronize()

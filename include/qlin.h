@@ -63,6 +63,7 @@ typedef int32_t qlin_status;
 #define QLIN_LAYOUT_W8 1  /* int8 codes for qlin_gemm_w8a8                         */
 #define QLIN_LAYOUT_W4S 2 /* signed int4 codes [-8,7] for qlin_gemm_w4a8            */
 #define QLIN_LAYOUT_W4U 3 /* unsigned int4 codes [0,15] for qlin_gemm_w4a4          */
+#define QLIN_LAYOUT_WO 4  /* fp16 rows W_O [nO x N] for the compensation term       */
 
 /* Version of this ABI (QLIN_ABI_VERSION). Host only. */
 int32_t qlin_abi_version(void);
@@ -70,6 +71,8 @@ int32_t qlin_abi_version(void);
 const char* qlin_status_string(qlin_status status);
 /* Message describing the last non-zero status returned on this host thread. */
 const char* qlin_last_error(void);
+/* Row stride of the per-outlier arrays qO / xO: nO rounded up to a multiple of 16. Host only. */
+int32_t qlin_outlier_ld(int32_t nO);
 
 /* ------------------------------------------------------------------------
  * Activation side
@@ -85,13 +88,18 @@ const char* qlin_last_error(void);
  *   q      int8 [M x K] out: clamp(rint(v * inv), -127, 127) with v = x * r,
  *          a = max_k |v|, inv = 127 / a (0 if a == 0)
  *   scale  fp32 [M] out: a / 127 (0 if a == 0)
- *   O, nO  optional int32 [nO] channel indices; qO int8 [M x nO] out: q[:, O]
- *          (needed by the compensation term); an index outside [0, K) gives
- *          code 0.  O and qO must both be NULL when nO == 0.
+ * Outlier columns (for the Quaff compensation term), written with the row
+ * stride ldO = qlin_outlier_ld(nO), columns nO..ldO-1 zero:
+ *   O, nO  int32 [nO] channel indices (an index outside [0, K) gives 0)
+ *   qO     int8 [M x ldO] out or NULL: q[:, O]
+ *   xO     fp16 [M x ldO] out or NULL: fp16(q[:, O] * (s[O] - 1)), the operand
+ *          X^_{:,O}(s_O - 1) of the compensation term without the token step
+ *   s      fp32 [K] (required with xO)
+ * With nO == 0, O, qO and xO must be NULL; with nO > 0, qO or xO is required.
  */
 qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, const float* r,
-                           int8_t* q, float* scale, const int32_t* O, int32_t nO, int8_t* qO,
-                           void* stream);
+                           int8_t* q, float* scale, const int32_t* O, int32_t nO, const float* s,
+                           int8_t* qO, uint16_t* xO, void* stream);
 
 /*
  * qlin_hadamard_offset -- OffQ activation path (OffQ, methodology,
@@ -190,7 +198,9 @@ size_t qlin_packed_bytes(int32_t layout, int64_t K, int64_t N);
  * qlin_pack_weight -- reorder one-code-per-byte weights [K x N] into the
  * tiled layout the GEMMs read (int4 layouts hold two codes per byte, eight per
  * 32-bit word).  The layout is private to the library: only pass the result to
- * the matching GEMM.  codes: int8 [K x N] for W8 / W4S, uint8 for W4U.
+ * the matching GEMM.  codes: int8 [K x N] for W8 / W4S, uint8 for W4U, fp16
+ * [nO x N] for WO (then K = nO, any positive value, rows padded to
+ * qlin_outlier_ld(nO) with zeros).
  *   packed: qlin_packed_bytes(layout, K, N) bytes out.
  */
 qlin_status qlin_pack_weight(int32_t layout, const void* codes, int64_t K, int64_t N, void* packed,
@@ -204,19 +214,18 @@ qlin_status qlin_pack_weight(int32_t layout, const void* codes, int64_t K, int64
  * qlin_gemm_w8a8 -- int8 x int8 -> int32, fused dequant, optional fused Quaff
  * compensation (Quaff notes, "key design", decoupled WAQ).
  *   acc[m,n] = sum_k qa[m,k] * W8[k,n]
- *   y[m,n]   = fp16(sa[m] * (acc[m,n] * sw[n] + sum_j qO[m,j] * (s[O[j]] - 1) * WO[j,n]))
- * The compensation term is the sparse X^_{:,O}(s_O - 1)W_O with
- * X^_{m,o} = qO[m,o] * sa[m]; it is skipped when nO == 0 (then qO, O, s, WO
- * must be NULL).
+ *   y[m,n]   = fp16(sa[m] * (acc[m,n] * sw[n] + sum_j xO[m,j] * WO[j,n]))
+ * The second term is the sparse X^_{:,O}(s_O - 1)W_O with
+ * X^_{m,o} = q[m,o] * sa[m] and xO = fp16(q[:, O] * (s[O] - 1)) from
+ * qlin_quant_act; it is skipped when nO == 0 (then xO and WO must be NULL).
+ * fp32 accumulation of fp16 products.
  *   qa  int8 [M x K];  sa fp32 [M];  w8 packed QLIN_LAYOUT_W8;  sw fp16 [N]
- *   qO  int8 [M x nO];  O int32 [nO] (entries outside [0, K) contribute 0);
- *   s fp32 [K];  WO fp16 [nO x N]
+ *   xO  fp16 [M x qlin_outlier_ld(nO)];  WO packed QLIN_LAYOUT_WO (nO rows)
  *   y   fp16 [M x N] out;  acc int32 [M x N] out or NULL
  */
 qlin_status qlin_gemm_w8a8(const int8_t* qa, const float* sa, const void* w8, const uint16_t* sw,
-                           int64_t M, int64_t N, int64_t K, const int8_t* qO, const int32_t* O,
-                           int32_t nO, const float* s, const uint16_t* WO, uint16_t* y,
-                           int32_t* acc, void* stream);
+                           int64_t M, int64_t N, int64_t K, const uint16_t* xO, int32_t nO,
+                           const void* WO, uint16_t* y, int32_t* acc, void* stream);
 
 /*
  * qlin_gemm_w4a8 -- QQQ W4A8 (QQQ review, "technical architecture").
@@ -256,14 +265,12 @@ qlin_status qlin_gemm_w4a4(const uint8_t* qa4, const float* sa, const int32_t* z
 /*
  * qlin_outlier_comp -- the sparse compensation term on its own, added to an
  * existing output (Quaff notes, "key design"):
- *   y[m,n] = fp16(y[m,n] + sa[m] * sum_j qO[m,j] * (s[O[j]] - 1) * WO[j,n])
- *   qO int8 [M x nO];  sa fp32 [M];  O int32 [nO];  s fp32 [K];
- *   WO fp16 [nO x N];  y fp16 [M x N] in/out.  nO == 0 leaves y unchanged.
- *   K is the length of s (used to check O).
+ *   y[m,n] = fp16(y[m,n] + sa[m] * sum_j xO[m,j] * WO[j,n])
+ *   xO fp16 [M x qlin_outlier_ld(nO)] (from qlin_quant_act);  sa fp32 [M];
+ *   WO packed QLIN_LAYOUT_WO;  y fp16 [M x N] in/out.  nO == 0 leaves y unchanged.
  */
-qlin_status qlin_outlier_comp(const int8_t* qO, const float* sa, const int32_t* O, int32_t nO,
-                              const float* s, int64_t K, const uint16_t* WO, int64_t M, int64_t N,
-                              uint16_t* y, void* stream);
+qlin_status qlin_outlier_comp(const uint16_t* xO, const float* sa, int32_t nO, const void* WO,
+                              int64_t M, int64_t N, uint16_t* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,8 @@ SIGNATURES = {
     "qlin_abi_version": (i32, []),
     "qlin_status_string": (C.c_char_p, [i32]),
     "qlin_last_error": (C.c_char_p, []),
-    "qlin_quant_act": (i32, [p, i64, i64, p, p, p, p, i32, p, p]),
+    "qlin_outlier_ld": (i32, [i32]),
+    "qlin_quant_act": (i32, [p, i64, i64, p, p, p, p, i32, p, p, p, p]),
     "qlin_hadamard_offset": (i32, [p, i64, i64, p, i32, p, p, p, p, p, p]),
     "qlin_momentum_update": (i32, [p, i64, i64, p, i32, p, f32, p, p, p]),
     "qlin_quant_weight_sym": (i32, [p, i64, i64, i32, p, p, p]),
@@ -30,10 +31,10 @@ SIGNATURES = {
     "qlin_weight_row_absmax": (i32, [p, i64, i64, p, p]),
     "qlin_packed_bytes": (C.c_size_t, [i32, i64, i64]),
     "qlin_pack_weight": (i32, [i32, p, i64, i64, p, p]),
-    "qlin_gemm_w8a8": (i32, [p, p, p, p, i64, i64, i64, p, p, i32, p, p, p, p, p]),
+    "qlin_gemm_w8a8": (i32, [p, p, p, p, i64, i64, i64, p, i32, p, p, p, p]),
     "qlin_gemm_w4a8": (i32, [p, p, p, p, p, i32, i64, i64, i64, p, p, p]),
     "qlin_gemm_w4a4": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p, p]),
-    "qlin_outlier_comp": (i32, [p, p, p, i32, p, i64, p, i64, i64, p, p]),
+    "qlin_outlier_comp": (i32, [p, p, i32, p, i64, i64, p, p]),
 }
 
 QLIN_OK = 0
@@ -45,6 +46,7 @@ QLIN_ERR_HIP = 5
 QLIN_LAYOUT_W8 = 1
 QLIN_LAYOUT_W4S = 2
 QLIN_LAYOUT_W4U = 3
+QLIN_LAYOUT_WO = 4
 
 _lib = None
 

@@ -7,6 +7,7 @@
 // loads of 8 fp16 values, the per-token reduction as a wavefront butterfly
 // plus one LDS exchange between waves, and packed stores.
 #include "common.hpp"
+#include "layout.hpp"
 
 namespace qlin {
 namespace {
@@ -46,7 +47,8 @@ __device__ __forceinline__ int sym_code(float v, float inv) {
 template <bool HAS_R>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     const uint16_t* __restrict__ x, int64_t K, const float* __restrict__ r, int8_t* __restrict__ q,
-    float* __restrict__ scale, const int32_t* __restrict__ O, int nO, int8_t* __restrict__ qO) {
+    float* __restrict__ scale, const int32_t* __restrict__ O, int nO, int ldO,
+    const float* __restrict__ s, int8_t* __restrict__ qO, uint16_t* __restrict__ xO) {
   __shared__ float red[kQuantThreads / 64];
   const int64_t m = blockIdx.x;
   const uint16_t* xr = x + m * K;
@@ -99,17 +101,21 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(lo, hi);
   }
 
-  // Compact copy of the outlier columns: the same code, recomputed for O[j].
-  if (qO != nullptr) {
-    for (int j = threadIdx.x; j < nO; j += kQuantThreads) {
-      const int o = O[j];
+  // Outlier columns (row stride ldO, zero padded): the code, recomputed for
+  // O[j], and the compensation operand fp16(code * (s[O[j]] - 1)).
+  if (ldO > 0) {
+    for (int j = threadIdx.x; j < ldO; j += kQuantThreads) {
+      const int o = j < nO ? O[j] : -1;
       int code = 0;
+      float sm1 = 0.0f;
       if (o >= 0 && o < K) {
         float vv = h2f(xr[o]);
         if constexpr (HAS_R) vv = mul_rn(vv, r[o]);
         code = sym_code(vv, inv);
+        if (xO != nullptr) sm1 = sub_rn(s[o], 1.0f);
       }
-      qO[m * nO + j] = static_cast<int8_t>(code);
+      if (qO != nullptr) qO[m * ldO + j] = static_cast<int8_t>(code);
+      if (xO != nullptr) xO[m * ldO + j] = f2h(mul_rn(static_cast<float>(code), sm1));
     }
   }
 }
@@ -276,7 +282,7 @@ using namespace qlin;
 
 extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, const float* r,
                                       int8_t* q, float* scale, const int32_t* O, int32_t nO,
-                                      int8_t* qO, void* stream) {
+                                      const float* s, int8_t* qO, uint16_t* xO, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
   QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
@@ -287,16 +293,21 @@ extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, c
   QLIN_OPT_PTR(r);
   if (nO > 0) {
     QLIN_PTR(O);
-    QLIN_PTR(qO);
+    QLIN_REQUIRE(qO != nullptr || xO != nullptr, QLIN_ERR_INVALID_ARG, "nO > 0 needs qO or xO");
+    QLIN_OPT_PTR(qO);
+    QLIN_OPT_PTR(xO);
+    if (xO != nullptr) QLIN_PTR(s);
   } else {
-    QLIN_REQUIRE(O == nullptr && qO == nullptr, QLIN_ERR_INVALID_ARG, "O and qO must be NULL when nO == 0");
+    QLIN_REQUIRE(O == nullptr && qO == nullptr && xO == nullptr, QLIN_ERR_INVALID_ARG,
+                 "O, qO and xO must be NULL when nO == 0");
   }
+  const int ldO = static_cast<int>(outlier_ld(nO));
   QLIN_REQUIRE(M <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
   const dim3 grid(static_cast<unsigned>(M));
   if (r != nullptr)
-    quant_act_kernel<true><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, K, r, q, scale, O, nO, qO);
+    quant_act_kernel<true><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, K, r, q, scale, O, nO, ldO, s, qO, xO);
   else
-    quant_act_kernel<false><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, K, r, q, scale, O, nO, qO);
+    quant_act_kernel<false><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, K, r, q, scale, O, nO, ldO, s, qO, xO);
   QLIN_LAUNCH_CHECK("quant_act_kernel");
   return QLIN_OK;
 }

@@ -53,6 +53,12 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Row of register v of a 32 x 32 matrix-core accumulator fragment in lane l
+// (the column is l & 31).
+__device__ __forceinline__ int frag_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
 __device__ __forceinline__ float h2f(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));

@@ -1,21 +1,30 @@
-// Integer GEMMs of libqlin on gfx950 int8 matrix cores (v_mfma_i32_16x16x64_i8):
+// Integer GEMMs of libqlin on gfx950 matrix cores (v_mfma_i32_32x32x32_i8):
 //   qlin_gemm_w8a8  int8 x int8, fused dequant, optional fused Quaff compensation
 //   qlin_gemm_w4a8  QQQ W4A8: per channel (shift-by-4 unpack) or per group of
-//                   128 (fused fp16 dequant-quant in the K loop)
+//                   128 (fused fp16 dequant-quant inside the K loop)
 //   qlin_gemm_w4a4  OffQ-style asymmetric int4 x int4 with the zero-point
 //                   correction in the epilogue
 //
-// Two kernels serve all of them, specialised by an operand policy:
-//   * gemm_tile: 128 x 128 output tiles, four waves of 64 x 64, K in stages of
-//     128.  Each stage is fetched with 16-byte global loads into registers
-//     (while the previous stage is multiplied), unpacked to int8 on the way
-//     into LDS (double buffered, 16-byte chunks XOR-swizzled by row so the
-//     fragment reads of 8 consecutive rows hit distinct banks), then read back
-//     as MFMA fragments.
-//   * gemm_skinny: M <= 64 (decode).  Weight bound: each workgroup owns NT
-//     16-column tiles, its waves split K, every weight byte is loaded exactly
-//     once straight into MFMA fragments (the packed layout is fragment
-//     ordered), and the waves' int32 partial sums meet in LDS.
+// Two kernels serve all of them, specialised by an operand policy.
+//
+// gemm_tile (M > 64): a workgroup computes a (32*TM) x 256 tile with four
+// waves side by side, each owning 64 distinct output columns (32*TM x 64
+// per wave, 2*TM accumulator fragments of 32 x 32).
+//   * Weights never touch LDS: the packed layout is in MFMA fragment order, so
+//     each wave streams its own columns straight from memory into registers
+//     with one 16-byte load per lane per fragment (int4 weights at half the
+//     bytes), one K stage ahead of use, and unpacks them in registers.
+//   * Activations, shared by the four waves, go global -> registers -> LDS
+//     (double buffered, one stage of 128 k ahead), stored as 16-byte chunks
+//     XOR-swizzled by row so fragment reads of 8 consecutive rows hit
+//     distinct banks.
+//   * Workgroups are mapped to tiles in groups of 4 tile rows, with each
+//     XCD (every 8th workgroup) given a contiguous block of tiles so the
+//     operands it streams stay in its own L2.
+// gemm_skinny (M <= 64, decode): bound by the weight stream.  A workgroup
+// owns NT 32-column tiles, its waves split K, every weight byte is loaded
+// once straight into MFMA fragments with U units of 64 k in flight per lane,
+// and the waves' int32 partial sums meet in LDS.
 #include "common.hpp"
 #include "comp.hpp"
 #include "layout.hpp"
@@ -27,29 +36,27 @@ enum class BOp { W8, W4Shift, W4Group, W4U };
 enum class AOp { I8, U4 };
 
 struct GemmArgs {
-  const void* a;           // int8 [M x K] or packed uint4 [M x K/2]
-  const float* sa;         // [M]
-  const uint8_t* b;        // packed weights
-  const uint16_t* sw_h;    // fp16 [N] (W8A8, W4A8)
-  const float* sw_f;       // fp32 [N] (W4A4)
-  const uint16_t* ratio;   // fp16 [K/128 x N] (per group)
-  const int32_t* za;       // [M]  (W4A4)
-  const int32_t* rowsum;   // [M]
-  const int32_t* zw;       // [N]
-  const int32_t* colsum;   // [N]
-  const int8_t* qO;        // compensation (W8A8)
-  const int32_t* O;
-  int nO;
-  const float* s;
-  const uint16_t* WO;
+  const void* a;          // int8 [M x K] or packed uint4 [M x K/2]
+  const float* sa;        // [M]
+  const uint8_t* b;       // packed weights
+  const uint16_t* sw_h;   // fp16 [N] (W8A8, W4A8)
+  const float* sw_f;      // fp32 [N] (W4A4)
+  const uint16_t* ratio;  // fp16 [K/128 x N] (per group)
+  const int32_t* za;      // [M]  (W4A4)
+  const int32_t* rowsum;  // [M]
+  const int32_t* zw;      // [N]
+  const int32_t* colsum;  // [N]
+  const uint16_t* xO;     // fp16 [M x ldO] compensation operand (W8A8)
+  const uint8_t* WOp;     // packed fp16 W_O
+  int ldO;
   uint16_t* y;
   int32_t* acc;
   int64_t M, N, K;
 };
 
 // ---------------------------------------------------------------- unpacking
-// int4 pairs -> int8 bytes.  Shift path: the nibble lands in the high half of
-// the byte, i.e. the signed byte reads 16*q4 (QQQ's INT4 -> INT8 left shift).
+// Shift path: the nibble lands in the high half of the byte, i.e. the signed
+// byte reads 16*q4 (QQQ's INT4 -> INT8 left shift).
 __device__ __forceinline__ uint32_t shift_lo(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t shift_hi(uint32_t w) { return w & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t mask_lo(uint32_t w) { return w & 0x0F0F0F0Fu; }
@@ -58,24 +65,26 @@ __device__ __forceinline__ uint32_t mask_hi(uint32_t w) { return (w >> 4) & 0x0F
 // QQQ per-group requantization of one 32-bit word of the W4S layout (8 signed
 // nibbles) into 8 int8 values in natural k order (two words):
 //   w8 = clamp(rint(fp16(q4 * r)), -127, 127).
-// Packed fp16 arithmetic, two values per instruction:
-//   nibble ^ 8 in the low mantissa bits of 1024.0 gives 1024 + q4 + 8, minus
-//   1032 gives q4 exactly; one fp16 multiply by r rounds the exact product
-//   once; after clamping, adding 1536.0 (spacing 1 on [1024, 2048)) rounds to
-//   an integer n with ties to even and leaves n's two's complement in the low
-//   byte of the fp16 pattern.
+// Packed fp16 arithmetic, two values per instruction: nibble ^ 8 in the low
+// mantissa bits of 1024.0 gives 1024 + q4 + 8, minus 1032 gives q4 exactly;
+// one fp16 multiply by r rounds the exact product once; after clamping, adding
+// 1536.0 (spacing 1 on [1024, 2048)) rounds to an integer n with ties to even
+// and leaves n's two's complement in the low byte of the fp16 pattern.
 __device__ __forceinline__ void requant_word(uint32_t w, v2h rr, uint32_t& out_lo, uint32_t& out_hi) {
   const uint32_t xw = w ^ 0x88888888u;
+  const v2h off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+  const v2h lo = {static_cast<_Float16>(-127.0f), static_cast<_Float16>(-127.0f)};
+  const v2h hi = {static_cast<_Float16>(127.0f), static_cast<_Float16>(127.0f)};
+  const v2h magic = {static_cast<_Float16>(1536.0f), static_cast<_Float16>(1536.0f)};
   uint32_t pr[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const uint32_t bits = ((xw >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
     v2h h = __builtin_bit_cast(v2h, bits);
-    h = h - v2h{static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+    h = h - off;
     h = h * rr;
-    h = __builtin_elementwise_max(h, v2h{static_cast<_Float16>(-127.0f), static_cast<_Float16>(-127.0f)});
-    h = __builtin_elementwise_min(h, v2h{static_cast<_Float16>(127.0f), static_cast<_Float16>(127.0f)});
-    h = h + v2h{static_cast<_Float16>(1536.0f), static_cast<_Float16>(1536.0f)};
+    h = __builtin_elementwise_min(__builtin_elementwise_max(h, lo), hi);
+    h = h + magic;
     pr[p] = __builtin_bit_cast(uint32_t, h);
   }
   // Nibble p of the word holds k = {0,4,1,5}[p] (low half) and {2,6,3,7}[p]
@@ -84,7 +93,7 @@ __device__ __forceinline__ void requant_word(uint32_t w, v2h rr, uint32_t& out_l
   out_hi = __builtin_amdgcn_perm(pr[3], pr[1], 0x06020400u);  // k 4,5,6,7
 }
 
-// 16 packed bytes of a W4 lane chunk -> two 16-byte int8 chunks (k steps 0, 1).
+// 16 packed bytes of a W4 lane chunk -> the int8 B fragments of k steps 0 and 1.
 template <BOp B>
 __device__ __forceinline__ void unpack_w4(uint4 raw, v2h rr, v4i& c0, v4i& c1) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -111,12 +120,11 @@ __device__ __forceinline__ v4i unpack_a4(uint32_t w0, uint32_t w1) {
   return v4i{(int)mask_lo(w0), (int)mask_hi(w0), (int)mask_lo(w1), (int)mask_hi(w1)};
 }
 
-__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+__device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- epilogue
-// Per output element: int32 accumulator -> fp16 (and the optional raw int32).
 template <BOp B>
 __device__ __forceinline__ int32_t finish_acc(int32_t raw, const GemmArgs& g, int64_t m, int64_t n) {
   if constexpr (B == BOp::W4Shift) {
@@ -138,247 +146,313 @@ __device__ __forceinline__ float col_scale(const GemmArgs& g, int64_t n) {
     return h2f(g.sw_h[n]);
 }
 
+__device__ __forceinline__ void lds_barrier() {
+  // Waits for this wave's LDS traffic, then for every wave of the group.
+  // Outstanding global loads (the prefetched stages) are not waited for.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ============================================================ tiled kernel
-constexpr int kBM = 128, kBN = 128, kBK = 128, kTileThreads = 256;
-constexpr int kTM = 4, kTN = 4;  // 16x16 fragments per wave (64 x 64)
-constexpr int kStageBytes = (kBM + kBN) * kBK;
+constexpr int kBN = 256, kBK = 128, kTileThreads = 256;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
 
-template <BOp B, AOp A>
-struct TileLoader {
-  // Registers holding one stage between its global load and its LDS store.
-  static constexpr int kAChunks = (A == AOp::I8) ? (kBM * 8) / kTileThreads : (kBM * 4) / kTileThreads;
-  static constexpr int kBChunks = (B == BOp::W8) ? (kBN / 16 * 128) / kTileThreads : (kBN / 16 * 64) / kTileThreads;
-  uint4 ra[kAChunks];
-  uint4 rb[kBChunks];
-  v2h rr[kBChunks];
-
-  __device__ __forceinline__ void load(const GemmArgs& g, int64_t m0, int64_t n0, int s) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-      const int q = tid + i * kTileThreads;
-      if constexpr (A == AOp::I8) {
-        const int row = q >> 3, c = q & 7;
-        const int64_t m = m0 + row;
-        ra[i] = (m < g.M) ? *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(g.a) + m * g.K + s * kBK + c * 16)
-                          : make_uint4(0, 0, 0, 0);
-      } else {
-        const int row = q >> 2, c = q & 3;
-        const int64_t m = m0 + row;
-        ra[i] = (m < g.M) ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(g.a) + m * (g.K / 2) + s * (kBK / 2) + c * 16)
-                          : make_uint4(0, 0, 0, 0);
-      }
-    }
-    const int64_t ntiles = g.N / 16;
-#pragma unroll
-    for (int i = 0; i < kBChunks; ++i) {
-      const int q = tid + i * kTileThreads;
-      if constexpr (B == BOp::W8) {
-        const int nt = q >> 7, ks = (q >> 6) & 1, lane = q & 63;
-        const int64_t gnt = n0 / 16 + nt;
-        rb[i] = (gnt < ntiles) ? *reinterpret_cast<const uint4*>(g.b + ((static_cast<int64_t>(2 * s + ks) * ntiles + gnt) << 10) + lane * 16)
-                               : make_uint4(0, 0, 0, 0);
-      } else {
-        const int nt = q >> 6, lane = q & 63;
-        const int64_t gnt = n0 / 16 + nt;
-        rb[i] = (gnt < ntiles) ? *reinterpret_cast<const uint4*>(g.b + ((static_cast<int64_t>(s) * ntiles + gnt) << 10) + lane * 16)
-                               : make_uint4(0, 0, 0, 0);
-        if constexpr (B == BOp::W4Group) {
-          const int64_t n = gnt * 16 + (lane & 15);
-          const uint16_t r16 = (gnt < ntiles) ? g.ratio[static_cast<int64_t>(s) * g.N + n] : 0;
-          const _Float16 r = __builtin_bit_cast(_Float16, r16);
-          rr[i] = v2h{r, r};
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint8_t* lds) const {
-    const int tid = threadIdx.x;
-    uint8_t* la = lds;
-    uint8_t* lb = lds + kBM * kBK;
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-      const int q = tid + i * kTileThreads;
-      if constexpr (A == AOp::I8) {
-        const int row = q >> 3, c = q & 7;
-        *reinterpret_cast<uint4*>(la + swz(row, c)) = ra[i];
-      } else {
-        const int row = q >> 2, c = q & 3;
-        *reinterpret_cast<v4i*>(la + swz(row, 2 * c)) = unpack_a4(ra[i].x, ra[i].y);
-        *reinterpret_cast<v4i*>(la + swz(row, 2 * c + 1)) = unpack_a4(ra[i].z, ra[i].w);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kBChunks; ++i) {
-      const int q = tid + i * kTileThreads;
-      if constexpr (B == BOp::W8) {
-        const int nt = q >> 7, ks = (q >> 6) & 1, lane = q & 63;
-        const int col = nt * 16 + (lane & 15);
-        *reinterpret_cast<uint4*>(lb + swz(col, ks * 4 + (lane >> 4))) = rb[i];
-      } else {
-        const int nt = q >> 6, lane = q & 63;
-        const int col = nt * 16 + (lane & 15);
-        v4i c0, c1;
-        unpack_w4<B>(rb[i], rr[i], c0, c1);
-        *reinterpret_cast<v4i*>(lb + swz(col, lane >> 4)) = c0;
-        *reinterpret_cast<v4i*>(lb + swz(col, 4 + (lane >> 4))) = c1;
-      }
-    }
-  }
+template <BOp B, AOp A, int TM>
+struct Tile {
+  static constexpr int BM = 32 * TM;
+  static constexpr int kStage = BM * kBK;  // LDS bytes of one A stage (int8)
+  static constexpr int kAChunks = (A == AOp::I8) ? BM * 8 / kTileThreads : BM * 4 / kTileThreads;
+  static constexpr int kNB = (B == BOp::W8) ? 8 : 4;  // 16-byte B loads per lane per stage
 };
 
-template <BOp B, AOp A, bool COMP>
-__global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kBN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wrow0 = (wave >> 1) * 64, wcol0 = (wave & 1) * 64;
-
-  v4i acc[kTM][kTN];
+template <BOp B, AOp A, int TM>
+__device__ __forceinline__ void load_a(const GemmArgs& g, int64_t m0, int s, uint4 (&ra)[Tile<B, A, TM>::kAChunks]) {
 #pragma unroll
-  for (int a = 0; a < kTM; ++a)
-#pragma unroll
-    for (int b = 0; b < kTN; ++b) acc[a][b] = v4i{0, 0, 0, 0};
-
-  const int S = static_cast<int>(g.K / kBK);
-  TileLoader<B, A> ld;
-  ld.load(g, m0, n0, 0);
-  ld.store(lds);
-  __syncthreads();
-  for (int s = 0; s < S; ++s) {
-    const uint8_t* cur = lds + (s & 1) * kStageBytes;
-    if (s + 1 < S) ld.load(g, m0, n0, s + 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v4i af[kTM], bf[kTN];
-      const int chunk = ks * 4 + (lane >> 4);
-#pragma unroll
-      for (int tm = 0; tm < kTM; ++tm)
-        af[tm] = *reinterpret_cast<const v4i*>(cur + swz(wrow0 + tm * 16 + (lane & 15), chunk));
-#pragma unroll
-      for (int tn = 0; tn < kTN; ++tn)
-        bf[tn] = *reinterpret_cast<const v4i*>(cur + kBM * kBK + swz(wcol0 + tn * 16 + (lane & 15), chunk));
-#pragma unroll
-      for (int tm = 0; tm < kTM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < kTN; ++tn) acc[tm][tn] = mfma_i8(af[tm], bf[tn], acc[tm][tn]);
+  for (int i = 0; i < Tile<B, A, TM>::kAChunks; ++i) {
+    const int q = threadIdx.x + i * kTileThreads;
+    if constexpr (A == AOp::I8) {
+      const int row = q >> 3, c = q & 7;
+      int64_t m = m0 + row;
+      m = m < g.M ? m : g.M - 1;
+      ra[i] = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(g.a) + m * g.K + s * kBK + c * 16);
+    } else {
+      const int row = q >> 2, c = q & 3;
+      int64_t m = m0 + row;
+      m = m < g.M ? m : g.M - 1;
+      ra[i] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(g.a) + m * (g.K / 2) + s * (kBK / 2) + c * 16);
     }
-    if (s + 1 < S) ld.store(lds + ((s + 1) & 1) * kStageBytes);
-    __syncthreads();
   }
+}
 
-  // Epilogue.  Fragment (tm, tn), register i of lane l holds
-  // row wrow0 + 16 tm + 4 (l >> 4) + i, column wcol0 + 16 tn + (l & 15).
-  v4f accf[kTM][kTN];
+template <BOp B, AOp A, int TM>
+__device__ __forceinline__ void store_a(uint8_t* buf, const uint4 (&ra)[Tile<B, A, TM>::kAChunks]) {
 #pragma unroll
-  for (int tm = 0; tm < kTM; ++tm)
+  for (int i = 0; i < Tile<B, A, TM>::kAChunks; ++i) {
+    const int q = threadIdx.x + i * kTileThreads;
+    if constexpr (A == AOp::I8) {
+      const int row = q >> 3, c = q & 7;
+      *reinterpret_cast<uint4*>(buf + swz(row, c)) = ra[i];
+    } else {
+      const int row = q >> 2, c = q & 3;
+      *reinterpret_cast<v4i*>(buf + swz(row, 2 * c)) = unpack_a4(ra[i].x, ra[i].y);
+      *reinterpret_cast<v4i*>(buf + swz(row, 2 * c + 1)) = unpack_a4(ra[i].z, ra[i].w);
+    }
+  }
+}
+
+// B of stage s for this wave: columns nt32 and nt32 + 1 (32 each).
+template <BOp B, AOp A, int TM>
+__device__ __forceinline__ void load_b(const GemmArgs& g, int64_t nt32, bool live, int s,
+                                       uint4 (&rb)[Tile<B, A, TM>::kNB], v2h (&rr)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tiles_n = g.N / 32;
+  if (!live) {
 #pragma unroll
-    for (int tn = 0; tn < kTN; ++tn) {
-      const int64_t n = n0 + wcol0 + tn * 16 + (lane & 15);
-      const float sw = (n < g.N) ? col_scale<B>(g, n) : 0.0f;
+    for (int i = 0; i < Tile<B, A, TM>::kNB; ++i) rb[i] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  if constexpr (B == BOp::W8) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + wrow0 + tm * 16 + 4 * (lane >> 4) + i;
-        int32_t v = acc[tm][tn][i];
-        if (m < g.M && n < g.N) {
-          v = finish_acc<B>(v, g, m, n);
-          if (g.acc != nullptr) g.acc[m * g.N + n] = v;
-        }
-        accf[tm][tn][i] = static_cast<float>(v) * sw;
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        rb[ks * 2 + nt] = *reinterpret_cast<const uint4*>(
+            g.b + (((static_cast<int64_t>(4 * s + ks) * tiles_n) + nt32 + nt) << 10) + lane * 16);
+  } else {
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        rb[kp * 2 + nt] = *reinterpret_cast<const uint4*>(
+            g.b + (((static_cast<int64_t>(2 * s + kp) * tiles_n) + nt32 + nt) << 10) + lane * 16);
+    if constexpr (B == BOp::W4Group) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const _Float16 r = __builtin_bit_cast(_Float16, g.ratio[static_cast<int64_t>(s) * g.N + (nt32 + nt) * 32 + (lane & 31)]);
+        rr[nt] = v2h{r, r};
       }
     }
+  }
+}
+
+template <BOp B, AOp A, int TM>
+__device__ __forceinline__ void compute_stage(const uint8_t* buf, const uint4 (&rb)[Tile<B, A, TM>::kNB],
+                                              const v2h (&rr)[2], v16i (&acc)[TM][2]) {
+  const int lane = threadIdx.x & 63;
+  const int arow = lane & 31, ahalf = lane >> 5;
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) {
+    v4i bf[2][2];  // [nt][k step within the pair]
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if constexpr (B == BOp::W8) {
+        const uint4 r0 = rb[(2 * kp) * 2 + nt], r1 = rb[(2 * kp + 1) * 2 + nt];
+        bf[nt][0] = v4i{(int)r0.x, (int)r0.y, (int)r0.z, (int)r0.w};
+        bf[nt][1] = v4i{(int)r1.x, (int)r1.y, (int)r1.z, (int)r1.w};
+      } else {
+        unpack_w4<B>(rb[kp * 2 + nt], rr[nt], bf[nt][0], bf[nt][1]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ks = 2 * kp + h;
+      v4i af[TM];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        af[tm] = *reinterpret_cast<const v4i*>(buf + swz(tm * 32 + arow, 2 * ks + ahalf));
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[tm][nt] = mfma_i8(af[tm], bf[nt][h], acc[tm][nt]);
+    }
+  }
+}
+
+// Tile index -> (tile row, tile column): XCD-contiguous blocks, groups of 4 rows.
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm_idx, int64_t& tn_idx) {
+  const int64_t T = tiles_m * tiles_n;
+  int64_t bid = blockIdx.x;
+  if (T % 8 == 0) bid = (bid % 8) * (T / 8) + bid / 8;
+  constexpr int64_t G = 4;
+  const int64_t per_group = G * tiles_n;
+  const int64_t group = bid / per_group;
+  const int64_t first_m = group * G;
+  const int64_t gm = (tiles_m - first_m) < G ? (tiles_m - first_m) : G;
+  const int64_t r = bid % per_group;
+  tm_idx = first_m + r % gm;
+  tn_idx = r / gm;
+}
+
+template <BOp B, AOp A, int TM, bool COMP>
+__global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
+  using T = Tile<B, A, TM>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * T::kStage];
+  const int64_t tiles_m = (g.M + T::BM - 1) / T::BM, tiles_n = (g.N + kBN - 1) / kBN;
+  int64_t tmi, tni;
+  tile_coords(tiles_m, tiles_n, tmi, tni);
+  const int64_t m0 = tmi * T::BM, n0 = tni * kBN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t wcol0 = n0 + 64 * wave;
+  const bool live = wcol0 < g.N;  // N % 64 == 0: a wave is all in or all out
+  const int64_t nt32 = wcol0 / 32;
+
+  v16i acc[TM][2];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = v16i{};
+
+  const int S = static_cast<int>(g.K / kBK);
+  uint4 ra[T::kAChunks];
+  uint4 rb0[T::kNB], rb1[T::kNB];
+  v2h rr0[2], rr1[2];
+  load_a<B, A, TM>(g, m0, 0, ra);
+  load_b<B, A, TM>(g, nt32, live, 0, rb0, rr0);
+  store_a<B, A, TM>(lds, ra);
+  if (S > 1) load_a<B, A, TM>(g, m0, 1, ra);
+  lds_barrier();
+
+  // Stage s: prefetch B(s+1) into the other register set, compute from LDS
+  // buffer s&1, store A(s+1) into the other LDS buffer, prefetch A(s+2).
+  // S is even for the shapes that matter (K % 256 == 0); an odd tail stage
+  // is handled by the guards.
+  for (int s = 0; s < S; s += 2) {
+    if (s + 1 < S) load_b<B, A, TM>(g, nt32, live, s + 1, rb1, rr1);
+    compute_stage<B, A, TM>(lds, rb0, rr0, acc);
+    if (s + 1 < S) {
+      store_a<B, A, TM>(lds + T::kStage, ra);
+      if (s + 2 < S) load_a<B, A, TM>(g, m0, s + 2, ra);
+    }
+    lds_barrier();
+    if (s + 1 >= S) break;
+    if (s + 2 < S) load_b<B, A, TM>(g, nt32, live, s + 2, rb0, rr0);
+    compute_stage<B, A, TM>(lds + T::kStage, rb1, rr1, acc);
+    if (s + 2 < S) {
+      store_a<B, A, TM>(lds, ra);
+      if (s + 3 < S) load_a<B, A, TM>(g, m0, s + 3, ra);
+    }
+    lds_barrier();
+  }
+
+  if (!live) return;
+  // Epilogue: finish the integer accumulator, scale by the column step, add
+  // the compensation term, scale by the token step, store fp16.
+  [[maybe_unused]] v16f cf[COMP ? TM : 1][2];
   if constexpr (COMP) {
-    comp_accumulate<kBM, kBN, kTileThreads, kTM, kTN>(accf, g.qO, g.O, g.nO, g.s, g.WO, g.M, g.N, g.K,
-                                                       m0, n0, wrow0, wcol0, lds);
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) cf[a][b] = v16f{};
+    comp_accumulate<TM, 2>(cf, g.xO, g.ldO, g.WOp, g.M, g.N, m0, nt32);
+  }
+  float swv[2];
+  int64_t ncol[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    ncol[nt] = wcol0 + 32 * nt + (lane & 31);
+    swv[nt] = col_scale<B>(g, ncol[nt]);
   }
 #pragma unroll
-  for (int tm = 0; tm < kTM; ++tm)
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + wrow0 + tm * 16 + 4 * (lane >> 4) + i;
+    for (int v = 0; v < 16; ++v) {
+      const int64_t m = m0 + 32 * tm + frag_row(v, lane);
       if (m >= g.M) continue;
       const float sam = g.sa[m];
 #pragma unroll
-      for (int tn = 0; tn < kTN; ++tn) {
-        const int64_t n = n0 + wcol0 + tn * 16 + (lane & 15);
-        if (n < g.N) g.y[m * g.N + n] = f2h(accf[tm][tn][i] * sam);
+      for (int nt = 0; nt < 2; ++nt) {
+        const int32_t val = finish_acc<B>(acc[tm][nt][v], g, m, ncol[nt]);
+        if (g.acc != nullptr) g.acc[m * g.N + ncol[nt]] = val;
+        float f = static_cast<float>(val) * swv[nt];
+        if constexpr (COMP) f += cf[tm][nt][v];
+        g.y[m * g.N + ncol[nt]] = f2h(f * sam);
       }
     }
 }
 
 // ============================================================ skinny kernel
-// M <= 16*MT.  Workgroup: WAVES waves, NT 16-column tiles; wave w takes the
-// K stages s = w, w + WAVES, ...
-template <BOp B, AOp A, int MT, int NT, int WAVES>
+// M <= 32*MT.  Workgroup: WAVES waves and NT 32-column tiles; wave w takes the
+// 64-k units u = w, w + WAVES, ...; U units are loaded before any is used.
+template <BOp B, AOp A, int MT, int NT, int WAVES, int U>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny(GemmArgs g) {
-  __shared__ int red[MT * NT * 4][64];
+  __shared__ int red[MT * NT * 16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t nt0 = static_cast<int64_t>(blockIdx.x) * NT;
-  const int64_t ntiles = g.N / 16;
-  const int S = static_cast<int>(g.K / 128);
+  const int64_t tiles_n = g.N / 32;
+  const int KU = static_cast<int>(g.K / 64);
+  const int arow = lane & 31, ahalf = lane >> 5;
 
-  for (int i = threadIdx.x; i < MT * NT * 4 * 64; i += 64 * WAVES) (&red[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < MT * NT * 16 * 64; i += 64 * WAVES) (&red[0][0])[i] = 0;
 
-  v4i acc[MT][NT];
+  v16i acc[MT][NT];
 #pragma unroll
   for (int a = 0; a < MT; ++a)
 #pragma unroll
-    for (int b = 0; b < NT; ++b) acc[a][b] = v4i{0, 0, 0, 0};
+    for (int b = 0; b < NT; ++b) acc[a][b] = v16i{};
 
-  const int row = lane & 15, grp = lane >> 4;
-  for (int s = wave; s < S; s += WAVES) {
-    v4i bf[NT][2];
+  for (int base = wave; base < KU; base += WAVES * U) {
+    constexpr int NBU = (B == BOp::W8) ? 2 : 1;
+    uint4 rb[U][NT][NBU];
+    v2h rr[U][NT];
+    v4i af[U][MT][2];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int64_t gnt = nt0 + nt;
-      const bool ok = gnt < ntiles;
-      if constexpr (B == BOp::W8) {
+    for (int uu = 0; uu < U; ++uu) {
+      const int u = base + WAVES * uu;
+      const bool ok_u = u < KU;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const uint4 raw = ok ? *reinterpret_cast<const uint4*>(g.b + ((static_cast<int64_t>(2 * s + ks) * ntiles + gnt) << 10) + lane * 16)
-                               : make_uint4(0, 0, 0, 0);
-          bf[nt][ks] = v4i{(int)raw.x, (int)raw.y, (int)raw.z, (int)raw.w};
-        }
-      } else {
-        const uint4 raw = ok ? *reinterpret_cast<const uint4*>(g.b + ((static_cast<int64_t>(s) * ntiles + gnt) << 10) + lane * 16)
+      for (int nt = 0; nt < NT; ++nt) {
+        const bool ok = ok_u && (nt0 + nt) < tiles_n;
+#pragma unroll
+        for (int h = 0; h < NBU; ++h) {
+          const int64_t tile_k = (B == BOp::W8) ? (2 * static_cast<int64_t>(u) + h) : static_cast<int64_t>(u);
+          rb[uu][nt][h] = ok ? *reinterpret_cast<const uint4*>(g.b + ((tile_k * tiles_n + nt0 + nt) << 10) + lane * 16)
                              : make_uint4(0, 0, 0, 0);
-        v2h rr = v2h{static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f)};
+        }
+        rr[uu][nt] = v2h{static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f)};
         if constexpr (B == BOp::W4Group) {
-          const uint16_t r16 = ok ? g.ratio[static_cast<int64_t>(s) * g.N + gnt * 16 + row] : 0;
-          const _Float16 r = __builtin_bit_cast(_Float16, r16);
-          rr = v2h{r, r};
+          if (ok) {
+            const _Float16 r = __builtin_bit_cast(_Float16, g.ratio[static_cast<int64_t>(u / 2) * g.N + (nt0 + nt) * 32 + arow]);
+            rr[uu][nt] = v2h{r, r};
+          }
         }
-        unpack_w4<B>(raw, rr, bf[nt][0], bf[nt][1]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m = mt * 32 + arow;
+        const bool ok = ok_u && m < g.M;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t k = 64 * static_cast<int64_t>(u) + 32 * h + 16 * ahalf;
+          if constexpr (A == AOp::I8) {
+            const uint4 raw = ok ? *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(g.a) + m * g.K + k)
+                                 : make_uint4(0, 0, 0, 0);
+            af[uu][mt][h] = v4i{(int)raw.x, (int)raw.y, (int)raw.z, (int)raw.w};
+          } else {
+            const uint2 raw = ok ? *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(g.a) + m * (g.K / 2) + k / 2)
+                                 : make_uint2(0, 0);
+            af[uu][mt][h] = unpack_a4(raw.x, raw.y);
+          }
+        }
       }
     }
-    v4i af[MT][2];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int64_t m = mt * 16 + row;
-      const bool ok = m < g.M;
+    for (int uu = 0; uu < U; ++uu) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if constexpr (A == AOp::I8) {
-          const uint4 raw = ok ? *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(g.a) + m * g.K + s * 128 + ks * 64 + grp * 16)
-                               : make_uint4(0, 0, 0, 0);
-          af[mt][ks] = v4i{(int)raw.x, (int)raw.y, (int)raw.z, (int)raw.w};
+      for (int nt = 0; nt < NT; ++nt) {
+        v4i bf[2];
+        if constexpr (B == BOp::W8) {
+          bf[0] = v4i{(int)rb[uu][nt][0].x, (int)rb[uu][nt][0].y, (int)rb[uu][nt][0].z, (int)rb[uu][nt][0].w};
+          bf[1] = v4i{(int)rb[uu][nt][NBU - 1].x, (int)rb[uu][nt][NBU - 1].y, (int)rb[uu][nt][NBU - 1].z,
+                      (int)rb[uu][nt][NBU - 1].w};
         } else {
-          const uint2 raw = ok ? *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(g.a) + m * (g.K / 2) + (s * 128 + ks * 64 + grp * 16) / 2)
-                               : make_uint2(0, 0);
-          af[mt][ks] = unpack_a4(raw.x, raw.y);
+          unpack_w4<B>(rb[uu][nt][0], rr[uu][nt], bf[0], bf[1]);
         }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma_i8(af[uu][mt][h], bf[h], acc[mt][nt]);
       }
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_i8(af[mt][ks], bf[nt][ks], acc[mt][nt]);
   }
 
   __syncthreads();
@@ -387,53 +461,55 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny(GemmArgs g) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) atomicAdd(&red[(mt * NT + nt) * 4 + i][lane], acc[mt][nt][i]);
+      for (int v = 0; v < 16; ++v) atomicAdd(&red[(mt * NT + nt) * 16 + v][lane], acc[mt][nt][v]);
   __syncthreads();
 
-  for (int f = wave; f < MT * NT; f += WAVES) {
-    const int mt = f / NT, nt = f % NT;
-    const int64_t n = (nt0 + nt) * 16 + row;
-    if (n >= g.N) continue;
+  for (int fi = wave; fi < MT * NT; fi += WAVES) {
+    const int mt = fi / NT, nt = fi % NT;
+    if (nt0 + nt >= tiles_n) continue;
+    const int64_t n = (nt0 + nt) * 32 + arow;
     const float sw = col_scale<B>(g, n);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = mt * 16 + 4 * grp + i;
+    for (int v = 0; v < 16; ++v) {
+      const int64_t m = mt * 32 + frag_row(v, lane);
       if (m >= g.M) continue;
-      const int32_t v = finish_acc<B>(red[f * 4 + i][lane], g, m, n);
-      if (g.acc != nullptr) g.acc[m * g.N + n] = v;
-      g.y[m * g.N + n] = f2h(static_cast<float>(v) * sw * g.sa[m]);
+      const int32_t val = finish_acc<B>(red[fi * 16 + v][lane], g, m, n);
+      if (g.acc != nullptr) g.acc[m * g.N + n] = val;
+      g.y[m * g.N + n] = f2h(static_cast<float>(val) * sw * g.sa[m]);
     }
   }
 }
 
 // ------------------------------------------------------------ dispatch
+template <BOp B, AOp A, int MT, int NT, int WAVES, int U>
+void launch_skinny(const GemmArgs& g, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((g.N / 32 + NT - 1) / NT));
+  gemm_skinny<B, A, MT, NT, WAVES, U><<<grid, 64 * WAVES, 0, st>>>(g);
+}
+
+template <BOp B, AOp A, int TM, bool COMP>
+qlin_status launch_tile(const GemmArgs& g, hipStream_t st) {
+  const int64_t tiles = ((g.M + 32 * TM - 1) / (32 * TM)) * ((g.N + kBN - 1) / kBN);
+  QLIN_REQUIRE(tiles <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M=%lld too large", (long long)g.M);
+  gemm_tile<B, A, TM, COMP><<<dim3(static_cast<unsigned>(tiles)), kTileThreads, 0, st>>>(g);
+  QLIN_LAUNCH_CHECK("gemm_tile");
+  return QLIN_OK;
+}
+
 template <BOp B, AOp A>
 qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
   if (!comp && g.M <= 64) {
-    constexpr int NT = 2, WAVES = 8;
-    const dim3 grid(static_cast<unsigned>((g.N / 16 + NT - 1) / NT));
-    if (g.M <= 16)
-      gemm_skinny<B, A, 1, NT, WAVES><<<grid, 64 * WAVES, 0, st>>>(g);
-    else if (g.M <= 32)
-      gemm_skinny<B, A, 2, NT, WAVES><<<grid, 64 * WAVES, 0, st>>>(g);
+    if (g.M <= 32)
+      launch_skinny<B, A, 1, 1, 8, 8>(g, st);
     else
-      gemm_skinny<B, A, 4, NT, WAVES><<<grid, 64 * WAVES, 0, st>>>(g);
+      launch_skinny<B, A, 2, 2, 8, 4>(g, st);
     QLIN_LAUNCH_CHECK("gemm_skinny");
     return QLIN_OK;
   }
-  const int64_t gy = (g.M + kBM - 1) / kBM;
-  QLIN_REQUIRE(gy <= 65535, QLIN_ERR_SHAPE, "M=%lld too large", (long long)g.M);
-  const dim3 grid(static_cast<unsigned>((g.N + kBN - 1) / kBN), static_cast<unsigned>(gy));
-  if constexpr (B == BOp::W8 && A == AOp::I8) {
-    if (comp) {
-      gemm_tile<B, A, true><<<grid, kTileThreads, 0, st>>>(g);
-      QLIN_LAUNCH_CHECK("gemm_tile");
-      return QLIN_OK;
-    }
+  if (comp) {
+    if constexpr (B == BOp::W8 && A == AOp::I8) return launch_tile<B, A, 4, true>(g, st);
   }
-  gemm_tile<B, A, false><<<grid, kTileThreads, 0, st>>>(g);
-  QLIN_LAUNCH_CHECK("gemm_tile");
-  return QLIN_OK;
+  return launch_tile<B, A, 4, false>(g, st);
 }
 
 GemmArgs base_args(int64_t M, int64_t N, int64_t K, uint16_t* y, int32_t* acc) {
@@ -453,8 +529,8 @@ using namespace qlin;
 
 extern "C" qlin_status qlin_gemm_w8a8(const int8_t* qa, const float* sa, const void* w8,
                                       const uint16_t* sw, int64_t M, int64_t N, int64_t K,
-                                      const int8_t* qO, const int32_t* O, int32_t nO, const float* s,
-                                      const uint16_t* WO, uint16_t* y, int32_t* acc, void* stream) {
+                                      const uint16_t* xO, int32_t nO, const void* WO, uint16_t* y,
+                                      int32_t* acc, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_K_N(K, N);
   QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
@@ -466,24 +542,19 @@ extern "C" qlin_status qlin_gemm_w8a8(const int8_t* qa, const float* sa, const v
   QLIN_PTR(y);
   QLIN_OPT_PTR(acc);
   if (nO > 0) {
-    QLIN_PTR(qO);
-    QLIN_PTR(O);
-    QLIN_PTR(s);
+    QLIN_PTR(xO);
     QLIN_PTR(WO);
   } else {
-    QLIN_REQUIRE(qO == nullptr && O == nullptr && s == nullptr && WO == nullptr, QLIN_ERR_INVALID_ARG,
-                 "qO, O, s and WO must be NULL when nO == 0");
+    QLIN_REQUIRE(xO == nullptr && WO == nullptr, QLIN_ERR_INVALID_ARG, "xO and WO must be NULL when nO == 0");
   }
   GemmArgs g = base_args(M, N, K, y, acc);
   g.a = qa;
   g.sa = sa;
   g.b = static_cast<const uint8_t*>(w8);
   g.sw_h = sw;
-  g.qO = qO;
-  g.O = O;
-  g.nO = nO;
-  g.s = s;
-  g.WO = WO;
+  g.xO = xO;
+  g.WOp = static_cast<const uint8_t*>(WO);
+  g.ldO = static_cast<int>(outlier_ld(nO));
   return launch<BOp::W8, AOp::I8>(g, nO > 0, as_stream(stream));
 }
 

@@ -7,6 +7,7 @@
 // Spatial Stability Hypothesis" (paper notes), "key design".
 #include "common.hpp"
 #include "comp.hpp"
+#include "layout.hpp"
 
 namespace qlin {
 namespace {
@@ -78,42 +79,37 @@ __global__ __launch_bounds__(kMomThreads) void row_absmax_kernel(const uint16_t*
   if (threadIdx.x == 0) out[i] = a;
 }
 
-// Standalone compensation: y = fp16(y + sa * sum_j fp16(qO*(s-1)) * WO), on
-// 128 x 128 tiles with four waves of 64 x 64.
-constexpr int kCompBM = 128, kCompBN = 128, kCompThreads = 256;
+// Standalone compensation: y = fp16(y + sa * sum_j xO[m,j] * WO[j,n]) on
+// 128 x 256 tiles, four waves of 128 x 64 (no LDS: both operands arrive in
+// fragment order).
+constexpr int kCompTM = 4, kCompThreads = 256;
 
 __global__ __launch_bounds__(kCompThreads) void outlier_comp_kernel(
-    const int8_t* __restrict__ qO, const float* __restrict__ sa, const int32_t* __restrict__ O,
-    int nO, const float* __restrict__ s, int64_t K, const uint16_t* __restrict__ WO, int64_t M,
-    int64_t N, uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[comp_lds_bytes<kCompBM, kCompBN>()];
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kCompBM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kCompBN;
+    const uint16_t* __restrict__ xO, int ldO, const float* __restrict__ sa,
+    const uint8_t* __restrict__ WOp, int64_t M, int64_t N, uint16_t* __restrict__ y) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wrow0 = (wave >> 1) * 64, wcol0 = (wave & 1) * 64;
-  v4f acc[4][4];
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 32 * kCompTM;
+  const int64_t wcol0 = static_cast<int64_t>(blockIdx.x) * 256 + 64 * wave;
+  if (wcol0 >= N) return;
+  v16f f[kCompTM][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kCompTM; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  comp_accumulate<kCompBM, kCompBN, kCompThreads, 4, 4>(acc, qO, O, nO, s, WO, M, N, K, m0, n0,
-                                                         wrow0, wcol0, lds);
+    for (int b = 0; b < 2; ++b) f[a][b] = v16f{};
+  comp_accumulate<kCompTM, 2>(f, xO, ldO, WOp, M, N, m0, wcol0 / 32);
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm) {
+  for (int tm = 0; tm < kCompTM; ++tm)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + wrow0 + tm * 16 + 4 * (lane >> 4) + i;
+    for (int v = 0; v < 16; ++v) {
+      const int64_t m = m0 + 32 * tm + frag_row(v, lane);
       if (m >= M) continue;
       const float sam = sa[m];
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-        const int64_t n = n0 + wcol0 + tn * 16 + (lane & 15);
-        if (n >= N) continue;
-        uint16_t* p = y + m * N + n;
-        *p = f2h(h2f(*p) + sam * acc[tm][tn][i]);
+      for (int nt = 0; nt < 2; ++nt) {
+        uint16_t* p = y + m * N + wcol0 + 32 * nt + (lane & 31);
+        *p = f2h(h2f(*p) + sam * f[tm][nt][v]);
       }
     }
-  }
 }
 
 }  // namespace
@@ -156,24 +152,22 @@ extern "C" qlin_status qlin_weight_row_absmax(const uint16_t* w_rows, int64_t R,
   return QLIN_OK;
 }
 
-extern "C" qlin_status qlin_outlier_comp(const int8_t* qO, const float* sa, const int32_t* O,
-                                         int32_t nO, const float* s, int64_t K, const uint16_t* WO,
-                                         int64_t M, int64_t N, uint16_t* y, void* stream) {
+extern "C" qlin_status qlin_outlier_comp(const uint16_t* xO, const float* sa, int32_t nO,
+                                         const void* WO, int64_t M, int64_t N, uint16_t* y,
+                                         void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
-  QLIN_K_N(K, N);
-  QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
+  QLIN_REQUIRE(N > 0 && N % 64 == 0, QLIN_ERR_SHAPE, "N=%lld must be a positive multiple of 64", (long long)N);
+  QLIN_REQUIRE(nO >= 0, QLIN_ERR_INVALID_ARG, "nO=%d is negative", nO);
   if (M == 0 || nO == 0) return QLIN_OK;
-  QLIN_REQUIRE(qO != nullptr && O != nullptr && s != nullptr && WO != nullptr && sa != nullptr && y != nullptr,
-               QLIN_ERR_INVALID_ARG, "null pointer");
+  QLIN_PTR(xO);
+  QLIN_PTR(sa);
   QLIN_PTR(WO);
   QLIN_PTR(y);
-  QLIN_PTR(sa);
-  QLIN_PTR(s);
-  QLIN_PTR(O);
-  QLIN_PTR(qO);
-  QLIN_REQUIRE((M + kCompBM - 1) / kCompBM <= 65535, QLIN_ERR_SHAPE, "M too large");
-  const dim3 grid(static_cast<unsigned>((N + kCompBN - 1) / kCompBN), static_cast<unsigned>((M + kCompBM - 1) / kCompBM));
-  outlier_comp_kernel<<<grid, kCompThreads, 0, as_stream(stream)>>>(qO, sa, O, nO, s, K, WO, M, N, y);
+  const int64_t gy = (M + 32 * kCompTM - 1) / (32 * kCompTM);
+  QLIN_REQUIRE(gy <= 65535, QLIN_ERR_SHAPE, "M too large");
+  const dim3 grid(static_cast<unsigned>((N + 255) / 256), static_cast<unsigned>(gy));
+  outlier_comp_kernel<<<grid, kCompThreads, 0, as_stream(stream)>>>(
+      xO, static_cast<int>(outlier_ld(nO)), sa, static_cast<const uint8_t*>(WO), M, N, y);
   QLIN_LAUNCH_CHECK("outlier_comp_kernel");
   return QLIN_OK;
 }

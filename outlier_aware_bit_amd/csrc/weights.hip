@@ -160,20 +160,19 @@ __global__ __launch_bounds__(kColThreads) void quant_offq_kernel(
 }
 
 // ---------------------------------------------------------------- packing
-// One thread writes one 16-byte lane chunk of the packed layout.
+// One thread writes one 16-byte lane chunk of the packed layout (layout.hpp).
 __global__ void pack_w8_kernel(const int8_t* __restrict__ codes, int64_t K, int64_t N,
                                uint8_t* __restrict__ out) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = K * N / 16;
-  if (q >= total) return;
+  if (q >= K * N / 16) return;
   const int lane = static_cast<int>(q & 63);
-  const int64_t nt = (q >> 6) % (N / 16);
-  const int64_t s = (q >> 6) / (N / 16);
-  const int64_t n = nt * 16 + (lane & 15);
-  const int64_t kb = s * 64 + 16 * (lane >> 4);
+  const int64_t nt = (q >> 6) % (N / 32);
+  const int64_t s = (q >> 6) / (N / 32);
+  const int64_t n = nt * 32 + (lane & 31);
+  const int64_t kb = s * 32 + 16 * (lane >> 5);
   uint32_t word[4] = {0, 0, 0, 0};
   for (int j = 0; j < 16; ++j)
-    word[j >> 2] |= (static_cast<uint32_t>(static_cast<uint8_t>(codes[(kb + j) * N + n]))) << (8 * (j & 3));
+    word[j >> 2] |= static_cast<uint32_t>(static_cast<uint8_t>(codes[(kb + j) * N + n])) << (8 * (j & 3));
   *reinterpret_cast<uint4*>(out + q * 16) = make_uint4(word[0], word[1], word[2], word[3]);
 }
 
@@ -181,29 +180,43 @@ template <bool SIGNED_SHIFT>
 __global__ void pack_w4_kernel(const uint8_t* __restrict__ codes, int64_t K, int64_t N,
                                uint8_t* __restrict__ out) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = K * N / 32;
-  if (q >= total) return;
+  if (q >= K * N / 32) return;
   const int lane = static_cast<int>(q & 63);
-  const int64_t nt = (q >> 6) % (N / 16);
-  const int64_t s = (q >> 6) / (N / 16);
-  const int64_t n = nt * 16 + (lane & 15);
+  const int64_t nt = (q >> 6) % (N / 32);
+  const int64_t p = (q >> 6) / (N / 32);
+  const int64_t n = nt * 32 + (lane & 31);
   uint32_t word[4] = {0, 0, 0, 0};
   for (int half = 0; half < 2; ++half) {
-    const int64_t kb = s * 128 + half * 64 + 16 * (lane >> 4);
+    const int64_t kb = p * 64 + half * 32 + 16 * (lane >> 5);
     uint32_t nib[16];
     for (int j = 0; j < 16; ++j) nib[j] = static_cast<uint32_t>(codes[(kb + j) * N + n]) & 0xfu;
     for (int i = 0; i < 2; ++i) {
       uint32_t v = 0;
       for (int b = 0; b < 4; ++b) {
-        uint32_t byte;
-        if (SIGNED_SHIFT)
-          byte = nib[8 * i + b] | (nib[8 * i + 4 + b] << 4);
-        else
-          byte = nib[8 * i + 2 * b] | (nib[8 * i + 2 * b + 1] << 4);
+        const uint32_t byte = SIGNED_SHIFT ? (nib[8 * i + b] | (nib[8 * i + 4 + b] << 4))
+                                           : (nib[8 * i + 2 * b] | (nib[8 * i + 2 * b + 1] << 4));
         v |= byte << (8 * b);
       }
       word[2 * half + i] = v;
     }
+  }
+  *reinterpret_cast<uint4*>(out + q * 16) = make_uint4(word[0], word[1], word[2], word[3]);
+}
+
+// W_O fp16 [nO x N] -> lane tiles of 32 columns x 16 rows (zero rows past nO).
+__global__ void pack_wo_kernel(const uint16_t* __restrict__ wo, int64_t nO, int64_t ldO, int64_t N,
+                               uint8_t* __restrict__ out) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q >= ldO * N / 8) return;
+  const int lane = static_cast<int>(q & 63);
+  const int64_t nt = (q >> 6) % (N / 32);
+  const int64_t s = (q >> 6) / (N / 32);
+  const int64_t n = nt * 32 + (lane & 31);
+  const int64_t jb = s * 16 + 8 * (lane >> 5);
+  uint32_t word[4] = {0, 0, 0, 0};
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t v = (jb + i < nO) ? wo[(jb + i) * N + n] : 0u;
+    word[i >> 1] |= v << (16 * (i & 1));
   }
   *reinterpret_cast<uint4*>(out + q * 16) = make_uint4(word[0], word[1], word[2], word[3]);
 }
@@ -262,37 +275,53 @@ extern "C" qlin_status qlin_quant_weight_offq(const uint16_t* w, int64_t K, int6
   return QLIN_OK;
 }
 
+extern "C" int32_t qlin_outlier_ld(int32_t nO) {
+  return nO < 0 ? 0 : static_cast<int32_t>(outlier_ld(nO));
+}
+
 extern "C" size_t qlin_packed_bytes(int32_t layout, int64_t K, int64_t N) {
-  if (K <= 0 || K % 128 || N <= 0 || N % 64) return 0;
+  if (N <= 0 || N % 64) return 0;
+  if (layout == QLIN_LAYOUT_WO) return K <= 0 ? 0 : static_cast<size_t>(outlier_ld(K) * N * 2);
+  if (K <= 0 || K % 128) return 0;
   switch (layout) {
-    case QLIN_LAYOUT_W8: return static_cast<size_t>(packed_bytes_w8(K, N));
+    case QLIN_LAYOUT_W8: return static_cast<size_t>(K * N);
     case QLIN_LAYOUT_W4S:
-    case QLIN_LAYOUT_W4U: return static_cast<size_t>(packed_bytes_w4(K, N));
+    case QLIN_LAYOUT_W4U: return static_cast<size_t>(K * N / 2);
     default: return 0;
   }
 }
 
 extern "C" qlin_status qlin_pack_weight(int32_t layout, const void* codes, int64_t K, int64_t N,
                                         void* packed, void* stream) {
-  QLIN_K_N(K, N);
-  QLIN_REQUIRE(layout == QLIN_LAYOUT_W8 || layout == QLIN_LAYOUT_W4S || layout == QLIN_LAYOUT_W4U,
+  QLIN_REQUIRE(layout == QLIN_LAYOUT_W8 || layout == QLIN_LAYOUT_W4S || layout == QLIN_LAYOUT_W4U ||
+                   layout == QLIN_LAYOUT_WO,
                QLIN_ERR_INVALID_ARG, "layout=%d is not a QLIN_LAYOUT_* value", layout);
+  if (layout == QLIN_LAYOUT_WO) {
+    QLIN_REQUIRE(K > 0, QLIN_ERR_SHAPE, "nO=%lld must be positive", (long long)K);
+    QLIN_REQUIRE(N > 0 && N % 64 == 0, QLIN_ERR_SHAPE, "N=%lld must be a positive multiple of 64", (long long)N);
+  } else {
+    QLIN_K_N(K, N);
+  }
   QLIN_PTR(codes);
   QLIN_PTR(packed);
   constexpr int T = 256;
+  hipStream_t st = as_stream(stream);
   if (layout == QLIN_LAYOUT_W8) {
     const int64_t total = K * N / 16;
-    pack_w8_kernel<<<dim3(static_cast<unsigned>((total + T - 1) / T)), T, 0, as_stream(stream)>>>(
+    pack_w8_kernel<<<dim3(static_cast<unsigned>((total + T - 1) / T)), T, 0, st>>>(
         static_cast<const int8_t*>(codes), K, N, static_cast<uint8_t*>(packed));
+  } else if (layout == QLIN_LAYOUT_WO) {
+    const int64_t ldO = outlier_ld(K);
+    const int64_t total = ldO * N / 8;
+    pack_wo_kernel<<<dim3(static_cast<unsigned>((total + T - 1) / T)), T, 0, st>>>(
+        static_cast<const uint16_t*>(codes), K, ldO, N, static_cast<uint8_t*>(packed));
   } else {
     const int64_t total = K * N / 32;
     const dim3 grid(static_cast<unsigned>((total + T - 1) / T));
     if (layout == QLIN_LAYOUT_W4S)
-      pack_w4_kernel<true><<<grid, T, 0, as_stream(stream)>>>(static_cast<const uint8_t*>(codes), K, N,
-                                                              static_cast<uint8_t*>(packed));
+      pack_w4_kernel<true><<<grid, T, 0, st>>>(static_cast<const uint8_t*>(codes), K, N, static_cast<uint8_t*>(packed));
     else
-      pack_w4_kernel<false><<<grid, T, 0, as_stream(stream)>>>(static_cast<const uint8_t*>(codes), K, N,
-                                                               static_cast<uint8_t*>(packed));
+      pack_w4_kernel<false><<<grid, T, 0, st>>>(static_cast<const uint8_t*>(codes), K, N, static_cast<uint8_t*>(packed));
   }
   QLIN_LAUNCH_CHECK("pack_weight");
   return QLIN_OK;

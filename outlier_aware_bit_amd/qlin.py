@@ -10,7 +10,7 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import QLIN_LAYOUT_W4S, QLIN_LAYOUT_W4U, QLIN_LAYOUT_W8, QlinError  # noqa: F401
+from ._lib import QLIN_LAYOUT_W4S, QLIN_LAYOUT_W4U, QLIN_LAYOUT_W8, QLIN_LAYOUT_WO, QlinError  # noqa: F401
 
 
 def _stream():
@@ -47,8 +47,15 @@ def qlin_abi_version() -> int:
     return _lib.load().qlin_abi_version()
 
 
-def qlin_quant_act(x, r=None, O=None, q=None, scale=None, qO=None):
-    """Per-token symmetric int8 of x (optionally x * r).  Returns (q, scale, qO)."""
+def qlin_outlier_ld(nO) -> int:
+    return int(_lib.load().qlin_outlier_ld(nO))
+
+
+def qlin_quant_act(x, r=None, O=None, s=None, q=None, scale=None, qO=None, xO=None, want_qO=True,
+                   want_xO=None):
+    """Per-token symmetric int8 of x (optionally x * r).  With O, also the
+    outlier columns qO = q[:, O] and, with s, xO = fp16(q[:, O] * (s[O] - 1)),
+    both [M, qlin_outlier_ld(nO)].  Returns (q, scale, qO, xO)."""
     lib = _lib.load()
     _req(x, "x", torch.float16)
     M, K = x.shape
@@ -59,16 +66,22 @@ def qlin_quant_act(x, r=None, O=None, q=None, scale=None, qO=None):
     if O is not None:
         _req(O, "O", torch.int32)
         nO = O.numel()
-        qO = _req(qO, "qO", torch.int8, (M, nO)) if qO is not None else _empty((M, nO), torch.int8, x)
-        if nO == 0:
-            O_p = qO_p = None
-        else:
-            O_p, qO_p = O.data_ptr(), qO.data_ptr()
-    else:
-        O_p = qO_p = None
+    if nO == 0:
+        _lib.check("qlin_quant_act", lib.qlin_quant_act(x.data_ptr(), M, K, _ptr(r), q.data_ptr(),
+                                                        scale.data_ptr(), None, 0, None, None, None, _stream()))
+        return q, scale, None, None
+    ld = qlin_outlier_ld(nO)
+    if want_xO is None:
+        want_xO = s is not None
+    if want_qO or qO is not None:
+        qO = _req(qO, "qO", torch.int8, (M, ld)) if qO is not None else _empty((M, ld), torch.int8, x)
+    if want_xO or xO is not None:
+        _req(s, "s", torch.float32, (K,))
+        xO = _req(xO, "xO", torch.float16, (M, ld)) if xO is not None else _empty((M, ld), torch.float16, x)
     _lib.check("qlin_quant_act", lib.qlin_quant_act(x.data_ptr(), M, K, _ptr(r), q.data_ptr(), scale.data_ptr(),
-                                                    O_p, nO, qO_p, _stream()))
-    return q, scale, qO
+                                                    O.data_ptr(), nO, _ptr(s) if xO is not None else None,
+                                                    _ptr(qO), _ptr(xO), _stream()))
+    return q, scale, qO, xO
 
 
 def qlin_hadamard_offset(x, signs, block=128, want_t=False):
@@ -160,8 +173,9 @@ def qlin_packed_bytes(layout, K, N) -> int:
 
 
 def qlin_pack_weight(layout, codes, out=None):
+    """Pack weights (int8 codes for W8/W4S, uint8 for W4U, fp16 rows for WO)."""
     lib = _lib.load()
-    dt = torch.uint8 if layout == QLIN_LAYOUT_W4U else torch.int8
+    dt = {QLIN_LAYOUT_W4U: torch.uint8, QLIN_LAYOUT_WO: torch.float16}.get(layout, torch.int8)
     _req(codes, "codes", dt)
     K, N = codes.shape
     nbytes = qlin_packed_bytes(layout, K, N)
@@ -171,28 +185,26 @@ def qlin_pack_weight(layout, codes, out=None):
     return out
 
 
-def qlin_gemm_w8a8(qa, sa, w8, sw, N, qO=None, O=None, s=None, WO=None, want_acc=False, y=None):
-    """y = fp16(sa * (acc * sw + compensation)); returns (y, acc or None)."""
+def qlin_gemm_w8a8(qa, sa, w8, sw, N, xO=None, nO=0, WO=None, want_acc=False, y=None):
+    """y = fp16(sa * (acc * sw + xO @ W_O)); returns (y, acc or None).
+    WO is the packed W_O (qlin_pack_weight(QLIN_LAYOUT_WO, ...)) of nO rows."""
     lib = _lib.load()
     _req(qa, "qa", torch.int8)
     M, K = qa.shape
     _req(sa, "sa", torch.float32, (M,))
     _req(w8, "w8", torch.uint8)
     _req(sw, "sw", torch.float16, (N,))
-    nO = 0 if O is None else O.numel()
     if nO:
-        _req(qO, "qO", torch.int8, (M, nO))
-        _req(O, "O", torch.int32, (nO,))
-        _req(s, "s", torch.float32, (K,))
-        _req(WO, "WO", torch.float16, (nO, N))
+        _req(xO, "xO", torch.float16, (M, qlin_outlier_ld(nO)))
+        _req(WO, "WO", torch.uint8, (qlin_packed_bytes(QLIN_LAYOUT_WO, nO, N),))
     else:
-        qO = O = s = WO = None
+        xO = WO = None
     y = y if y is not None else _empty((M, N), torch.float16, qa)
     _req(y, "y", torch.float16, (M, N))
     acc = _empty((M, N), torch.int32, qa) if want_acc else None
     _lib.check("qlin_gemm_w8a8", lib.qlin_gemm_w8a8(
-        qa.data_ptr(), sa.data_ptr(), w8.data_ptr(), sw.data_ptr(), M, N, K, _ptr(qO), _ptr(O), nO, _ptr(s),
-        _ptr(WO), y.data_ptr(), _ptr(acc), _stream()))
+        qa.data_ptr(), sa.data_ptr(), w8.data_ptr(), sw.data_ptr(), M, N, K, _ptr(xO), nO, _ptr(WO),
+        y.data_ptr(), _ptr(acc), _stream()))
     return y, acc
 
 
@@ -233,20 +245,16 @@ def qlin_gemm_w4a4(qa4, sa, za, rowsum, w4, sw, zw, colsum, N, want_acc=False, y
     return y, acc
 
 
-def qlin_outlier_comp(qO, sa, O, s, WO, y):
-    """y += sa * sum_j qO * (s[O] - 1) * WO, in place."""
+def qlin_outlier_comp(xO, sa, nO, WO, y):
+    """y += sa * (xO @ W_O), in place (WO packed, nO rows)."""
     lib = _lib.load()
     _req(y, "y", torch.float16)
     M, N = y.shape
-    _req(s, "s", torch.float32)
-    K = s.numel()
-    nO = O.numel()
     if nO:
-        _req(qO, "qO", torch.int8, (M, nO))
+        _req(xO, "xO", torch.float16, (M, qlin_outlier_ld(nO)))
         _req(sa, "sa", torch.float32, (M,))
-        _req(O, "O", torch.int32, (nO,))
-        _req(WO, "WO", torch.float16, (nO, N))
+        _req(WO, "WO", torch.uint8, (qlin_packed_bytes(QLIN_LAYOUT_WO, nO, N),))
     _lib.check("qlin_outlier_comp", lib.qlin_outlier_comp(
-        _ptr(qO) if nO else None, sa.data_ptr(), _ptr(O) if nO else None, nO, s.data_ptr(), K,
-        _ptr(WO) if nO else None, M, N, y.data_ptr(), _stream()))
+        _ptr(xO) if nO else None, _ptr(sa) if nO else None, nO, _ptr(WO) if nO else None, M, N,
+        y.data_ptr(), _stream()))
     return y

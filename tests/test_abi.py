@@ -64,6 +64,9 @@ def test_packed_bytes():
     assert lib.qlin_packed_bytes(7, 4096, 4096) == 0
     assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8, 100, 4096) == 0
     assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8, 4096, 100) == 0
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_WO, 205, 4096) == 208 * 4096 * 2
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_WO, 0, 4096) == 0
+    assert [lib.qlin_outlier_ld(n) for n in (0, 1, 16, 17, 205)] == [0, 16, 16, 32, 208]
 
 
 # Fake but 16-byte aligned "device" addresses: validation never dereferences
@@ -79,16 +82,20 @@ def _err(status, code):
 
 def test_quant_act_validation():
     lib = _lib.load()
-    _err(lib.qlin_quant_act(None, 4, 256, None, B, A, None, 0, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    def qa(*head, O=None, nO=0, s=None, qO=None, xO=None):
+        return lib.qlin_quant_act(*head, O, nO, s, qO, xO, None)
+    _err(qa(None, 4, 256, None, B, A), _lib.QLIN_ERR_INVALID_ARG)
     assert b"x" in lib.qlin_last_error()
-    _err(lib.qlin_quant_act(A, 4, 200, None, B, A, None, 0, None, None), _lib.QLIN_ERR_SHAPE)
-    _err(lib.qlin_quant_act(A, -1, 256, None, B, A, None, 0, None, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_quant_act(MIS, 4, 256, None, B, A, None, 0, None, None), _lib.QLIN_ERR_ALIGN)
-    _err(lib.qlin_quant_act(A, 4, 256, MIS, B, A, None, 0, None, None), _lib.QLIN_ERR_ALIGN)
-    _err(lib.qlin_quant_act(A, 4, 256, None, B, A, A, 0, None, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_quant_act(A, 4, 256, None, B, A, None, 3, None, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_quant_act(A, 4, 256, None, B, A, A, 300, B, None), _lib.QLIN_ERR_SHAPE)
-    _err(lib.qlin_quant_act(A, 0, 256, None, B, A, None, 0, None, None), _lib.QLIN_OK)
+    _err(qa(A, 4, 200, None, B, A), _lib.QLIN_ERR_SHAPE)
+    _err(qa(A, -1, 256, None, B, A), _lib.QLIN_ERR_INVALID_ARG)
+    _err(qa(MIS, 4, 256, None, B, A), _lib.QLIN_ERR_ALIGN)
+    _err(qa(A, 4, 256, MIS, B, A), _lib.QLIN_ERR_ALIGN)
+    _err(qa(A, 4, 256, None, B, A, O=A), _lib.QLIN_ERR_INVALID_ARG)
+    _err(qa(A, 4, 256, None, B, A, nO=3), _lib.QLIN_ERR_INVALID_ARG)
+    _err(qa(A, 4, 256, None, B, A, O=A, nO=3), _lib.QLIN_ERR_INVALID_ARG)
+    _err(qa(A, 4, 256, None, B, A, O=A, nO=3, xO=B), _lib.QLIN_ERR_INVALID_ARG)
+    _err(qa(A, 4, 256, None, B, A, O=A, nO=300, qO=B), _lib.QLIN_ERR_SHAPE)
+    _err(qa(A, 0, 256, None, B, A), _lib.QLIN_OK)
 
 
 def test_hadamard_validation():
@@ -123,13 +130,14 @@ def test_weight_prep_validation():
 
 def test_gemm_validation():
     lib = _lib.load()
-    ok = [A, A, B, A, 16, 128, 256, None, None, 0, None, None, A, None, None]
+    ok = [A, A, B, A, 16, 128, 256, None, 0, None, A, None, None]
     _err(lib.qlin_gemm_w8a8(*ok[:4], 16, 100, 256, *ok[7:]), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_gemm_w8a8(*ok[:4], 16, 128, 250, *ok[7:]), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_gemm_w8a8(None, *ok[1:]), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_gemm_w8a8(*ok[:7], A, A, 5, A, None, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_gemm_w8a8(*ok[:7], None, A, 0, None, None, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_gemm_w8a8(*ok[:12], A, MIS, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_gemm_w8a8(*ok[:7], A, 5, None, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w8a8(*ok[:7], A, 0, None, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w8a8(*ok[:7], None, 300, None, A, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_gemm_w8a8(*ok[:10], A, MIS, None), _lib.QLIN_ERR_ALIGN)
     _err(lib.qlin_gemm_w8a8(*ok[:4], 0, *ok[5:]), _lib.QLIN_OK)
     _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 64, 16, 128, 256, A, None, None), _lib.QLIN_ERR_UNSUPPORTED)
     _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 128, 16, 128, 256, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
@@ -138,9 +146,11 @@ def test_gemm_validation():
     _err(lib.qlin_gemm_w4a4(A, A, A, A, B, A, A, None, 16, 128, 256, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
     _err(lib.qlin_gemm_w4a4(A, A, A, A, B, A, A, A, 16, 128, 384 + 64, A, None, None), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_gemm_w4a4(A, A, A, A, B, A, A, A, 0, 128, 256, A, None, None), _lib.QLIN_OK)
-    _err(lib.qlin_outlier_comp(A, A, A, 4, A, 256, A, 16, 100, A, None), _lib.QLIN_ERR_SHAPE)
-    _err(lib.qlin_outlier_comp(None, A, A, 4, A, 256, A, 16, 128, A, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_outlier_comp(A, A, A, 0, A, 256, A, 16, 128, A, None), _lib.QLIN_OK)
+    _err(lib.qlin_outlier_comp(A, A, 4, A, 16, 100, A, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_outlier_comp(None, A, 4, A, 16, 128, A, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_outlier_comp(A, A, 4, MIS, 16, 128, A, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_outlier_comp(A, A, 0, A, 16, 128, A, None), _lib.QLIN_OK)
+    _err(lib.qlin_pack_weight(_lib.QLIN_LAYOUT_WO, A, 0, 128, B, None), _lib.QLIN_ERR_SHAPE)
 
 
 def test_binding_refuses_cpu_tensors():

@@ -38,21 +38,28 @@ def test_quant_act(q, M, K, n_out, use_r):
         r = np.random.default_rng(M).uniform(0.01, 1.5, K).astype(np.float32)
     want_q, want_s = quant.quant_act_sym_int8(lin.x, r)
     O = lin.outliers
-    qq, ss, qO = q.qlin_quant_act(dev(lin.x), None if r is None else dev(r), dev(O))
+    s = np.random.default_rng(K).uniform(1.0, 60.0, K).astype(np.float32)
+    qq, ss, qO, xO = q.qlin_quant_act(dev(lin.x), None if r is None else dev(r), dev(O), s=dev(s))
     assert_equal(host(qq), want_q, "q")
     assert_equal(host(ss), want_s, "scale")
-    assert_equal(host(qO), want_q[:, O], "qO")
+    ld = q.qlin_outlier_ld(O.size)
+    assert qO.shape == (M, ld) and xO.shape == (M, ld)
+    assert_equal(host(qO)[:, :O.size], want_q[:, O], "qO")
+    assert np.all(host(qO)[:, O.size:] == 0) and np.all(host(xO)[:, O.size:] == 0)
+    # xO is the compensation operand fp16(q * (s - 1)) in fp32 arithmetic.
+    want_x = (want_q[:, O].astype(np.float32) * (s[O] - np.float32(1))).astype(np.float16)
+    assert_equal(host(xO)[:, :O.size].view(np.uint16), want_x.view(np.uint16), "xO")
 
 
 def test_quant_act_zero_rows_and_empty(q):
     x = np.zeros((4, 256), np.float16)
     x[2, 7] = -3.0
-    qq, ss, _ = q.qlin_quant_act(dev(x))
+    qq, ss, _, _ = q.qlin_quant_act(dev(x))
     want_q, want_s = quant.quant_act_sym_int8(x)
     assert_equal(host(qq), want_q, "q")
     assert_equal(host(ss), want_s, "scale")
     import torch
-    qq, ss, _ = q.qlin_quant_act(torch.zeros((0, 256), dtype=torch.float16, device="cuda"))
+    qq, ss, _, _ = q.qlin_quant_act(torch.zeros((0, 256), dtype=torch.float16, device="cuda"))
     assert qq.shape == (0, 256)
 
 
@@ -147,7 +154,7 @@ def test_weight_quantizers(q, K, N):
 
 # ------------------------------------------------------------ GEMMs
 GEMM_SHAPES = [(1, 256, 128), (7, 384, 192), (16, 256, 128), (33, 512, 64), (64, 1024, 256),
-               (65, 256, 192), (200, 384, 320), (256, 512, 128)]
+               (65, 256, 192), (200, 384, 320), (256, 512, 128), (1000, 512, 1024)]
 
 
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
@@ -157,7 +164,7 @@ def test_gemm_w8a8(q, M, K, N):
     ref = layer.w8a8_forward(lin.x, lin.w)
     codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 8)
     w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
-    qa, sa, _ = q.qlin_quant_act(dev(lin.x))
+    qa, sa, _, _ = q.qlin_quant_act(dev(lin.x))
     y, acc = q.qlin_gemm_w8a8(qa, sa, w8, sw, N, want_acc=True)
     assert_equal(host(acc), ref["acc"], "acc")
     assert_close(host(y), ref["y"], "y")
@@ -170,7 +177,7 @@ def test_gemm_w4a8_channel(q, M, K, N):
     ref = layer.w4a8_channel_forward(lin.x, lin.w)
     codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 4)
     w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes)
-    qa, sa, _ = q.qlin_quant_act(dev(lin.x))
+    qa, sa, _, _ = q.qlin_quant_act(dev(lin.x))
     y, acc = q.qlin_gemm_w4a8(qa, sa, w4, sw, N, want_acc=True)
     assert_equal(host(acc), ref["acc"], "acc")
     assert_close(host(y), ref["y"], "y")
@@ -183,7 +190,7 @@ def test_gemm_w4a8_group(q, M, K, N):
     ref = layer.w4a8_group_forward(lin.x, lin.w)
     codes, gs, cs, ratio = q.qlin_quant_weight_group(dev(lin.w), 128)
     w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes)
-    qa, sa, _ = q.qlin_quant_act(dev(lin.x))
+    qa, sa, _, _ = q.qlin_quant_act(dev(lin.x))
     y, acc = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128, want_acc=True)
     assert_equal(host(acc), ref["acc"], "acc")
     assert_close(host(y), ref["y"], "y")
@@ -221,7 +228,8 @@ def test_gemm_w4a4(q, M, K, N):
     assert_close(host(y), ref["y"], "y")
 
 
-@pytest.mark.parametrize("M,K,N,nO", [(16, 256, 128, 13), (200, 512, 192, 64), (130, 384, 64, 33)])
+@pytest.mark.parametrize("M,K,N,nO", [(16, 256, 128, 13), (200, 512, 192, 64), (130, 384, 64, 33),
+                                       (300, 256, 320, 16)])
 def test_quaff_fused_and_standalone_compensation(q, M, K, N, nO):
     import torch
     log(f"quaff comp M={M} K={K} N={N} nO={nO}")
@@ -232,6 +240,7 @@ def test_quaff_fused_and_standalone_compensation(q, M, K, N, nO):
     codes, sw = q.qlin_quant_weight_sym(dev(d.w), 8)
     w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
     WO = dev(np.ascontiguousarray(d.w[d.outliers]))
+    WOp = q.qlin_pack_weight(q.QLIN_LAYOUT_WO, WO)
     wmax = q.qlin_weight_row_absmax(WO)
     assert_equal(host(wmax), prep["wmax"], "wmax")
     s = torch.ones(K, dtype=torch.float32, device="cuda")
@@ -241,14 +250,15 @@ def test_quaff_fused_and_standalone_compensation(q, M, K, N, nO):
         s_ref = ref["s"]
         xd = dev(x)
         q.qlin_momentum_update(xd, O, wmax, 0.9, s, r)
-        qa, sa, qO = q.qlin_quant_act(xd, r, O)
+        qa, sa, qO, xO = q.qlin_quant_act(xd, r, O, s=s)
         assert_equal(host(s), ref["s"], "s")
         assert_equal(host(qa), ref["q"], "q")
-        y, acc = q.qlin_gemm_w8a8(qa, sa, w8, sw, N, qO=qO, O=O, s=s, WO=WO, want_acc=True)
+        assert_equal(host(qO)[:, :nO], ref["q"][:, d.outliers], "qO")
+        y, acc = q.qlin_gemm_w8a8(qa, sa, w8, sw, N, xO=xO, nO=nO, WO=WOp, want_acc=True)
         assert_equal(host(acc), ref["acc"], "acc")
         assert_close(host(y), ref["y"], f"fused y step {t}")
         y2, _ = q.qlin_gemm_w8a8(qa, sa, w8, sw, N)
-        q.qlin_outlier_comp(qO, sa, O, s, WO, y2)
+        q.qlin_outlier_comp(xO, sa, nO, WOp, y2)
         assert_close(host(y2), ref["y"], f"standalone y step {t}")
 
 
