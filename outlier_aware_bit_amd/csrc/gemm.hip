@@ -14,6 +14,9 @@
 //     each wave streams its own columns straight from memory into registers
 //     with one 16-byte load per lane per fragment (int4 weights at half the
 //     bytes), one K stage ahead of use, and unpacks them in registers.
+//   * The K loop takes two stages per iteration with no branches inside (the
+//     prefetch indices are clamped), so the accumulators stay in place in the
+//     accumulation registers.
 //   * Activations, shared by the four waves, go global -> registers -> LDS
 //     (double buffered, one stage of 128 k ahead), stored as 16-byte chunks
 //     XOR-swizzled by row so fragment reads of 8 consecutive rows hit
@@ -114,6 +117,11 @@ __device__ __forceinline__ void unpack_w4(uint4 raw, v2h rr, v4i& c0, v4i& c1) {
   c1 = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
 }
 
+template <BOp B>
+__device__ __forceinline__ void unpack_w4v(v4i raw, v2h rr, v4i& c0, v4i& c1) {
+  unpack_w4<B>(make_uint4(raw[0], raw[1], raw[2], raw[3]), rr, c0, c1);
+}
+
 // 8 packed bytes of int4 activations (natural packing) -> 16 int8 values in
 // the same k order as unpack_w4<W4U>.
 __device__ __forceinline__ v4i unpack_a4(uint32_t w0, uint32_t w1) {
@@ -163,72 +171,84 @@ struct Tile {
   static constexpr int kStage = BM * kBK;  // LDS bytes of one A stage (int8)
   static constexpr int kAChunks = (A == AOp::I8) ? BM * 8 / kTileThreads : BM * 4 / kTileThreads;
   static constexpr int kNB = (B == BOp::W8) ? 8 : 4;  // 16-byte B loads per lane per stage
+  static constexpr int kARowStep = (A == AOp::I8) ? kTileThreads / 8 : kTileThreads / 4;  // rows between chunks
+};
+
+// Per-thread operand pointers, computed once.  A chunk i of a stage is row
+// (r0 + i * kARowStep), 16-byte column c0; B tile t of a stage is
+// bptr + t_offset (uniform) for this lane.
+template <BOp B, AOp A, int TM>
+struct TilePtrs {
+  const uint8_t* a[Tile<B, A, TM>::kAChunks];  // stage 0 addresses of this thread's A chunks
+  int lds_a;                                   // LDS byte offset of chunk 0 (chunk i adds i * kARowStep * kBK)
+  const uint8_t* b;                            // this lane's B address in tile (0, nt32)
+  const uint16_t* ratio;                       // this lane's ratio column (W4Group)
 };
 
 template <BOp B, AOp A, int TM>
-__device__ __forceinline__ void load_a(const GemmArgs& g, int64_t m0, int s, uint4 (&ra)[Tile<B, A, TM>::kAChunks]) {
+__device__ __forceinline__ void tile_ptrs(const GemmArgs& g, int64_t m0, int64_t nt32, TilePtrs<B, A, TM>& p) {
+  using T = Tile<B, A, TM>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int row0 = (A == AOp::I8) ? (tid >> 3) : (tid >> 2);
+  const int c0 = (A == AOp::I8) ? (tid & 7) : (tid & 3);
+  const int64_t lda = (A == AOp::I8) ? g.K : g.K / 2;
 #pragma unroll
-  for (int i = 0; i < Tile<B, A, TM>::kAChunks; ++i) {
-    const int q = threadIdx.x + i * kTileThreads;
+  for (int i = 0; i < T::kAChunks; ++i) {
+    int64_t m = m0 + row0 + i * T::kARowStep;
+    m = m < g.M ? m : g.M - 1;
+    p.a[i] = static_cast<const uint8_t*>(g.a) + m * lda + c0 * 16;
+  }
+  p.lds_a = (A == AOp::I8) ? swz(row0, c0) : swz(row0, 2 * c0);
+  p.b = g.b + (nt32 << 10) + lane * 16;
+  p.ratio = g.ratio + nt32 * 32 + (lane & 31);
+}
+
+template <BOp B, AOp A, int TM>
+__device__ __forceinline__ void load_a(const TilePtrs<B, A, TM>& p, int s, v4i (&ra)[Tile<B, A, TM>::kAChunks]) {
+  constexpr int stage_bytes = (A == AOp::I8) ? kBK : kBK / 2;
+#pragma unroll
+  for (int i = 0; i < Tile<B, A, TM>::kAChunks; ++i)
+    ra[i] = *reinterpret_cast<const v4i*>(p.a[i] + static_cast<int64_t>(s) * stage_bytes);
+}
+
+template <BOp B, AOp A, int TM>
+__device__ __forceinline__ void store_a(uint8_t* buf, int lds_a, const v4i (&ra)[Tile<B, A, TM>::kAChunks]) {
+  using T = Tile<B, A, TM>;
+#pragma unroll
+  for (int i = 0; i < T::kAChunks; ++i) {
+    // Rows of chunk i differ from chunk 0 by a multiple of 32: same swizzle.
+    uint8_t* d = buf + lds_a + i * T::kARowStep * kBK;
     if constexpr (A == AOp::I8) {
-      const int row = q >> 3, c = q & 7;
-      int64_t m = m0 + row;
-      m = m < g.M ? m : g.M - 1;
-      ra[i] = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(g.a) + m * g.K + s * kBK + c * 16);
+      *reinterpret_cast<v4i*>(d) = ra[i];
     } else {
-      const int row = q >> 2, c = q & 3;
-      int64_t m = m0 + row;
-      m = m < g.M ? m : g.M - 1;
-      ra[i] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(g.a) + m * (g.K / 2) + s * (kBK / 2) + c * 16);
+      // swz(row, 2c + 1) is swz(row, 2c) with the chunk bit 0 flipped.
+      const int base = lds_a + i * T::kARowStep * kBK;
+      *reinterpret_cast<v4i*>(buf + base) = unpack_a4(ra[i][0], ra[i][1]);
+      *reinterpret_cast<v4i*>(buf + (base ^ 16)) = unpack_a4(ra[i][2], ra[i][3]);
     }
   }
 }
 
+// B of stage s for this wave: 32-column tiles nt32 and nt32 + 1.
 template <BOp B, AOp A, int TM>
-__device__ __forceinline__ void store_a(uint8_t* buf, const uint4 (&ra)[Tile<B, A, TM>::kAChunks]) {
-#pragma unroll
-  for (int i = 0; i < Tile<B, A, TM>::kAChunks; ++i) {
-    const int q = threadIdx.x + i * kTileThreads;
-    if constexpr (A == AOp::I8) {
-      const int row = q >> 3, c = q & 7;
-      *reinterpret_cast<uint4*>(buf + swz(row, c)) = ra[i];
-    } else {
-      const int row = q >> 2, c = q & 3;
-      *reinterpret_cast<v4i*>(buf + swz(row, 2 * c)) = unpack_a4(ra[i].x, ra[i].y);
-      *reinterpret_cast<v4i*>(buf + swz(row, 2 * c + 1)) = unpack_a4(ra[i].z, ra[i].w);
-    }
-  }
-}
-
-// B of stage s for this wave: columns nt32 and nt32 + 1 (32 each).
-template <BOp B, AOp A, int TM>
-__device__ __forceinline__ void load_b(const GemmArgs& g, int64_t nt32, bool live, int s,
-                                       uint4 (&rb)[Tile<B, A, TM>::kNB], v2h (&rr)[2]) {
-  const int lane = threadIdx.x & 63;
-  const int64_t tiles_n = g.N / 32;
-  if (!live) {
-#pragma unroll
-    for (int i = 0; i < Tile<B, A, TM>::kNB; ++i) rb[i] = make_uint4(0, 0, 0, 0);
-    return;
-  }
+__device__ __forceinline__ void load_b(const TilePtrs<B, A, TM>& p, int64_t tiles_n, int64_t N, int s,
+                                       v4i (&rb)[Tile<B, A, TM>::kNB], v2h (&rr)[2]) {
   if constexpr (B == BOp::W8) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        rb[ks * 2 + nt] = *reinterpret_cast<const uint4*>(
-            g.b + (((static_cast<int64_t>(4 * s + ks) * tiles_n) + nt32 + nt) << 10) + lane * 16);
+        rb[ks * 2 + nt] = *reinterpret_cast<const v4i*>(p.b + ((static_cast<int64_t>(4 * s + ks) * tiles_n + nt) << 10));
   } else {
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        rb[kp * 2 + nt] = *reinterpret_cast<const uint4*>(
-            g.b + (((static_cast<int64_t>(2 * s + kp) * tiles_n) + nt32 + nt) << 10) + lane * 16);
+        rb[kp * 2 + nt] = *reinterpret_cast<const v4i*>(p.b + ((static_cast<int64_t>(2 * s + kp) * tiles_n + nt) << 10));
     if constexpr (B == BOp::W4Group) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const _Float16 r = __builtin_bit_cast(_Float16, g.ratio[static_cast<int64_t>(s) * g.N + (nt32 + nt) * 32 + (lane & 31)]);
+        const _Float16 r = __builtin_bit_cast(_Float16, p.ratio[static_cast<int64_t>(s) * N + nt * 32]);
         rr[nt] = v2h{r, r};
       }
     }
@@ -236,35 +256,38 @@ __device__ __forceinline__ void load_b(const GemmArgs& g, int64_t nt32, bool liv
 }
 
 template <BOp B, AOp A, int TM>
-__device__ __forceinline__ void compute_stage(const uint8_t* buf, const uint4 (&rb)[Tile<B, A, TM>::kNB],
+__device__ __forceinline__ void compute_stage(const uint8_t* buf, const v4i (&rb)[Tile<B, A, TM>::kNB],
                                               const v2h (&rr)[2], v16i (&acc)[TM][2]) {
   const int lane = threadIdx.x & 63;
   const int arow = lane & 31, ahalf = lane >> 5;
+  const uint8_t* abuf = buf + arow * kBK;
+  v4i bf[2][4];  // [nt][k step]
 #pragma unroll
-  for (int kp = 0; kp < 2; ++kp) {
-    v4i bf[2][2];  // [nt][k step within the pair]
+  for (int nt = 0; nt < 2; ++nt) {
+    if constexpr (B == BOp::W8) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      if constexpr (B == BOp::W8) {
-        const uint4 r0 = rb[(2 * kp) * 2 + nt], r1 = rb[(2 * kp + 1) * 2 + nt];
-        bf[nt][0] = v4i{(int)r0.x, (int)r0.y, (int)r0.z, (int)r0.w};
-        bf[nt][1] = v4i{(int)r1.x, (int)r1.y, (int)r1.z, (int)r1.w};
-      } else {
-        unpack_w4<B>(rb[kp * 2 + nt], rr[nt], bf[nt][0], bf[nt][1]);
-      }
+      for (int ks = 0; ks < 4; ++ks) bf[nt][ks] = rb[ks * 2 + nt];
+    } else {
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) unpack_w4v<B>(rb[kp * 2 + nt], rr[nt], bf[nt][2 * kp], bf[nt][2 * kp + 1]);
     }
+  }
+  v4i af[2][TM];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ks = 2 * kp + h;
-      v4i af[TM];
+  for (int tm = 0; tm < TM; ++tm)
+    af[0][tm] = *reinterpret_cast<const v4i*>(abuf + tm * 32 * kBK + ((ahalf ^ (arow & 7)) << 4));
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks + 1 < 4) {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
-        af[tm] = *reinterpret_cast<const v4i*>(buf + swz(tm * 32 + arow, 2 * ks + ahalf));
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[tm][nt] = mfma_i8(af[tm], bf[nt][h], acc[tm][nt]);
+        af[(ks + 1) & 1][tm] =
+            *reinterpret_cast<const v4i*>(abuf + tm * 32 * kBK + (((2 * (ks + 1) + ahalf) ^ (arow & 7)) << 4));
     }
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[tm][nt] = mfma_i8(af[ks & 1][tm], bf[nt][ks], acc[tm][nt]);
   }
 }
 
@@ -292,9 +315,16 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
   tile_coords(tiles_m, tiles_n, tmi, tni);
   const int64_t m0 = tmi * T::BM, n0 = tni * kBN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t wcol0 = n0 + 64 * wave;
-  const bool live = wcol0 < g.N;  // N % 64 == 0: a wave is all in or all out
-  const int64_t nt32 = wcol0 / 32;
+  // N % 64 == 0: a wave's 64 columns are all in range or all out.  A wave
+  // out of range still streams (clamped, in-bounds) weights so that every
+  // wave takes part in every barrier; it stores nothing.
+  int64_t wcol0 = n0 + 64 * wave;
+  const bool live = wcol0 < g.N;
+  const int64_t nt32 = (live ? wcol0 : g.N - 64) / 32;
+  const int64_t b_tiles = g.N / 32;
+
+  TilePtrs<B, A, TM> p;
+  tile_ptrs<B, A, TM>(g, m0, nt32, p);
 
   v16i acc[TM][2];
 #pragma unroll
@@ -303,36 +333,36 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
     for (int b = 0; b < 2; ++b) acc[a][b] = v16i{};
 
   const int S = static_cast<int>(g.K / kBK);
-  uint4 ra[T::kAChunks];
-  uint4 rb0[T::kNB], rb1[T::kNB];
+  uint8_t* buf0 = lds;
+  uint8_t* buf1 = lds + T::kStage;
+  v4i ra[T::kAChunks];
+  v4i rb0[T::kNB], rb1[T::kNB];
   v2h rr0[2], rr1[2];
-  load_a<B, A, TM>(g, m0, 0, ra);
-  load_b<B, A, TM>(g, nt32, live, 0, rb0, rr0);
-  store_a<B, A, TM>(lds, ra);
-  if (S > 1) load_a<B, A, TM>(g, m0, 1, ra);
+  load_a<B, A, TM>(p, 0, ra);
+  load_b<B, A, TM>(p, b_tiles, g.N, 0, rb0, rr0);
+  store_a<B, A, TM>(buf0, p.lds_a, ra);
+  load_a<B, A, TM>(p, S > 1 ? 1 : 0, ra);
   lds_barrier();
 
-  // Stage s: prefetch B(s+1) into the other register set, compute from LDS
-  // buffer s&1, store A(s+1) into the other LDS buffer, prefetch A(s+2).
-  // S is even for the shapes that matter (K % 256 == 0); an odd tail stage
-  // is handled by the guards.
-  for (int s = 0; s < S; s += 2) {
-    if (s + 1 < S) load_b<B, A, TM>(g, nt32, live, s + 1, rb1, rr1);
-    compute_stage<B, A, TM>(lds, rb0, rr0, acc);
-    if (s + 1 < S) {
-      store_a<B, A, TM>(lds + T::kStage, ra);
-      if (s + 2 < S) load_a<B, A, TM>(g, m0, s + 2, ra);
-    }
+  // Two stages per iteration, no branches inside: prefetch stage indices are
+  // clamped to S - 1, so past the end they reload the last stage (in bounds)
+  // into buffers that are not read again.
+  int s = 0;
+  for (; s + 1 < S; s += 2) {
+    const int s2 = (s + 2 < S) ? s + 2 : S - 1;
+    const int s3 = (s + 3 < S) ? s + 3 : S - 1;
+    load_b<B, A, TM>(p, b_tiles, g.N, s + 1, rb1, rr1);
+    compute_stage<B, A, TM>(buf0, rb0, rr0, acc);
+    store_a<B, A, TM>(buf1, p.lds_a, ra);
+    load_a<B, A, TM>(p, s2, ra);
     lds_barrier();
-    if (s + 1 >= S) break;
-    if (s + 2 < S) load_b<B, A, TM>(g, nt32, live, s + 2, rb0, rr0);
-    compute_stage<B, A, TM>(lds + T::kStage, rb1, rr1, acc);
-    if (s + 2 < S) {
-      store_a<B, A, TM>(lds, ra);
-      if (s + 3 < S) load_a<B, A, TM>(g, m0, s + 3, ra);
-    }
+    load_b<B, A, TM>(p, b_tiles, g.N, s2, rb0, rr0);
+    compute_stage<B, A, TM>(buf1, rb1, rr1, acc);
+    store_a<B, A, TM>(buf0, p.lds_a, ra);
+    load_a<B, A, TM>(p, s3, ra);
     lds_barrier();
   }
+  if (s < S) compute_stage<B, A, TM>(buf0, rb0, rr0, acc);  // odd S: the last stage
 
   if (!live) return;
   // Epilogue: finish the integer accumulator, scale by the column step, add
@@ -345,13 +375,9 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
       for (int b = 0; b < 2; ++b) cf[a][b] = v16f{};
     comp_accumulate<TM, 2>(cf, g.xO, g.ldO, g.WOp, g.M, g.N, m0, nt32);
   }
-  float swv[2];
-  int64_t ncol[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    ncol[nt] = wcol0 + 32 * nt + (lane & 31);
-    swv[nt] = col_scale<B>(g, ncol[nt]);
-  }
+  const int64_t n_lane = wcol0 + (lane & 31);
+  const float sw0 = col_scale<B>(g, n_lane), sw1 = col_scale<B>(g, n_lane + 32);
+  const bool want_acc = g.acc != nullptr;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -359,13 +385,20 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
       const int64_t m = m0 + 32 * tm + frag_row(v, lane);
       if (m >= g.M) continue;
       const float sam = g.sa[m];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int32_t val = finish_acc<B>(acc[tm][nt][v], g, m, ncol[nt]);
-        if (g.acc != nullptr) g.acc[m * g.N + ncol[nt]] = val;
-        float f = static_cast<float>(val) * swv[nt];
-        if constexpr (COMP) f += cf[tm][nt][v];
-        g.y[m * g.N + ncol[nt]] = f2h(f * sam);
+      uint16_t* yrow = g.y + m * g.N + n_lane;
+      const int32_t v0 = finish_acc<B>(acc[tm][0][v], g, m, n_lane);
+      const int32_t v1 = finish_acc<B>(acc[tm][1][v], g, m, n_lane + 32);
+      float f0 = static_cast<float>(v0) * sw0, f1 = static_cast<float>(v1) * sw1;
+      if constexpr (COMP) {
+        f0 += cf[tm][0][v];
+        f1 += cf[tm][1][v];
+      }
+      yrow[0] = f2h(f0 * sam);
+      yrow[32] = f2h(f1 * sam);
+      if (want_acc) {
+        int32_t* arow = g.acc + m * g.N + n_lane;
+        arow[0] = v0;
+        arow[32] = v1;
       }
     }
 }
@@ -509,6 +542,10 @@ qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
   if (comp) {
     if constexpr (B == BOp::W8 && A == AOp::I8) return launch_tile<B, A, 4, true>(g, st);
   }
+  // 256-row tiles when they still give every CU a tile: per weight byte
+  // streamed (and unpacked) they do twice the matrix-core work.
+  const int64_t tiles_n = (g.N + kBN - 1) / kBN;
+  if (((g.M + 255) / 256) * tiles_n >= 256) return launch_tile<B, A, 8, false>(g, st);
   return launch_tile<B, A, 4, false>(g, st);
 }
 
