@@ -12,22 +12,24 @@
 namespace qlin {
 namespace {
 
-constexpr int kQuantThreads = 256;
-constexpr int kQuantRegChunks = 8;  // 8-value chunks held in registers per thread
+constexpr int kQuantThreads = 256;  // four wavefronts, one token each
+constexpr int kQuantRegChunks = 16;  // 8-value chunks per lane held in registers (K <= 8192)
 
-__device__ __forceinline__ void load8_f16(const uint16_t* p, float (&v)[8]) {
-  const uint4 raw = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+__device__ __forceinline__ void unpack8_f16(v4i raw, float (&v)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    v[2 * i] = h2f(static_cast<uint16_t>(w[i] & 0xffffu));
-    v[2 * i + 1] = h2f(static_cast<uint16_t>(w[i] >> 16));
+    const uint32_t w = static_cast<uint32_t>(raw[i]);
+    v[2 * i] = h2f(static_cast<uint16_t>(w & 0xffffu));
+    v[2 * i + 1] = h2f(static_cast<uint16_t>(w >> 16));
   }
 }
 
+__device__ __forceinline__ void load8_f16(const uint16_t* p, float (&v)[8]) {
+  unpack8_f16(*reinterpret_cast<const v4i*>(p), v);
+}
+
 template <bool HAS_R>
-__device__ __forceinline__ void load_chunk(const uint16_t* xr, const float* r, int c, float (&v)[8]) {
-  load8_f16(xr + c * 8, v);
+__device__ __forceinline__ void scale_chunk(const float* r, int c, float (&v)[8]) {
   if constexpr (HAS_R) {
     const float4 r0 = *reinterpret_cast<const float4*>(r + c * 8);
     const float4 r1 = *reinterpret_cast<const float4*>(r + c * 8 + 4);
@@ -43,80 +45,93 @@ __device__ __forceinline__ int sym_code(float v, float inv) {
   return static_cast<int>(t);
 }
 
+template <bool HAS_R>
+__device__ __forceinline__ uint2 sym_codes8(const float (&v)[8], float inv) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lo |= (static_cast<uint32_t>(sym_code(v[j], inv)) & 0xffu) << (8 * j);
+    hi |= (static_cast<uint32_t>(sym_code(v[j + 4], inv)) & 0xffu) << (8 * j);
+  }
+  return make_uint2(lo, hi);
+}
+
 // Per-token symmetric int8: a = max|v|, inv = 127/a, q = clamp(rint(v*inv)).
+// One wavefront per token: the row stays in registers as raw fp16 (up to
+// 16 chunks of 8 per lane), the absmax is a wavefront butterfly, and there is
+// no LDS traffic or block barrier.  Longer rows re-read the tail from cache.
 template <bool HAS_R>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
-    const uint16_t* __restrict__ x, int64_t K, const float* __restrict__ r, int8_t* __restrict__ q,
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ r, int8_t* __restrict__ q,
     float* __restrict__ scale, const int32_t* __restrict__ O, int nO, int ldO,
     const float* __restrict__ s, int8_t* __restrict__ qO, uint16_t* __restrict__ xO) {
-  __shared__ float red[kQuantThreads / 64];
-  const int64_t m = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * (kQuantThreads / 64) + (threadIdx.x >> 6);
+  if (m >= M) return;
   const uint16_t* xr = x + m * K;
   const int nchunks = static_cast<int>(K / 8);
 
-  float v[kQuantRegChunks][8];
+  v4i raw[kQuantRegChunks];
+#pragma unroll
+  for (int i = 0; i < kQuantRegChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nchunks) raw[i] = *reinterpret_cast<const v4i*>(xr + c * 8);
+  }
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < kQuantRegChunks; ++i) {
-    const int c = threadIdx.x + i * kQuantThreads;
+    const int c = lane + 64 * i;
     if (c < nchunks) {
-      load_chunk<HAS_R>(xr, r, c, v[i]);
+      float v[8];
+      unpack8_f16(raw[i], v);
+      scale_chunk<HAS_R>(r, c, v);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
     }
   }
-  for (int c = threadIdx.x + kQuantRegChunks * kQuantThreads; c < nchunks; c += kQuantThreads) {
-    float t[8];
-    load_chunk<HAS_R>(xr, r, c, t);
+  for (int c = lane + 64 * kQuantRegChunks; c < nchunks; c += 64) {
+    float v[8];
+    load8_f16(xr + c * 8, v);
+    scale_chunk<HAS_R>(r, c, v);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(t[j]));
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
   }
-  const float a = block_max<kQuantThreads / 64>(amax, red);
+  const float a = wave_max(amax);
   const float inv = (a == 0.0f) ? 0.0f : div_rn(127.0f, a);
-  if (threadIdx.x == 0) scale[m] = (a == 0.0f) ? 0.0f : div_rn(a, 127.0f);
+  if (lane == 0) scale[m] = (a == 0.0f) ? 0.0f : div_rn(a, 127.0f);
 
   int8_t* qr = q + m * K;
 #pragma unroll
   for (int i = 0; i < kQuantRegChunks; ++i) {
-    const int c = threadIdx.x + i * kQuantThreads;
+    const int c = lane + 64 * i;
     if (c < nchunks) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lo |= (static_cast<uint32_t>(sym_code(v[i][j], inv)) & 0xffu) << (8 * j);
-        hi |= (static_cast<uint32_t>(sym_code(v[i][j + 4], inv)) & 0xffu) << (8 * j);
-      }
-      *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(lo, hi);
+      float v[8];
+      unpack8_f16(raw[i], v);
+      scale_chunk<HAS_R>(r, c, v);
+      *reinterpret_cast<uint2*>(qr + c * 8) = sym_codes8<HAS_R>(v, inv);
     }
   }
-  for (int c = threadIdx.x + kQuantRegChunks * kQuantThreads; c < nchunks; c += kQuantThreads) {
-    float t[8];
-    load_chunk<HAS_R>(xr, r, c, t);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo |= (static_cast<uint32_t>(sym_code(t[j], inv)) & 0xffu) << (8 * j);
-      hi |= (static_cast<uint32_t>(sym_code(t[j + 4], inv)) & 0xffu) << (8 * j);
-    }
-    *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(lo, hi);
+  for (int c = lane + 64 * kQuantRegChunks; c < nchunks; c += 64) {
+    float v[8];
+    load8_f16(xr + c * 8, v);
+    scale_chunk<HAS_R>(r, c, v);
+    *reinterpret_cast<uint2*>(qr + c * 8) = sym_codes8<HAS_R>(v, inv);
   }
 
   // Outlier columns (row stride ldO, zero padded): the code, recomputed for
   // O[j], and the compensation operand fp16(code * (s[O[j]] - 1)).
-  if (ldO > 0) {
-    for (int j = threadIdx.x; j < ldO; j += kQuantThreads) {
-      const int o = j < nO ? O[j] : -1;
-      int code = 0;
-      float sm1 = 0.0f;
-      if (o >= 0 && o < K) {
-        float vv = h2f(xr[o]);
-        if constexpr (HAS_R) vv = mul_rn(vv, r[o]);
-        code = sym_code(vv, inv);
-        if (xO != nullptr) sm1 = sub_rn(s[o], 1.0f);
-      }
-      if (qO != nullptr) qO[m * ldO + j] = static_cast<int8_t>(code);
-      if (xO != nullptr) xO[m * ldO + j] = f2h(mul_rn(static_cast<float>(code), sm1));
+  for (int j = lane; j < ldO; j += 64) {
+    const int o = j < nO ? O[j] : -1;
+    int code = 0;
+    float sm1 = 0.0f;
+    if (o >= 0 && o < K) {
+      float vv = h2f(xr[o]);
+      if constexpr (HAS_R) vv = mul_rn(vv, r[o]);
+      code = sym_code(vv, inv);
+      if (xO != nullptr) sm1 = sub_rn(s[o], 1.0f);
     }
+    if (qO != nullptr) qO[m * ldO + j] = static_cast<int8_t>(code);
+    if (xO != nullptr) xO[m * ldO + j] = f2h(mul_rn(static_cast<float>(code), sm1));
   }
 }
 
@@ -132,8 +147,15 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
 constexpr int kHadThreads = 128;
 constexpr int kHadRegChunks = 2;  // 32-channel chunks held in registers per thread
 
-__device__ __forceinline__ double shfl_xor_f64(double v, int mask) {
-  return __shfl_xor(v, mask, 64);
+// Value of lane ^ 1 (MASK == 1) or lane ^ 2 (MASK == 2) within each quad, by
+// DPP quad permutes of the two halves (no LDS round trip).
+template <int MASK>
+__device__ __forceinline__ double quad_xor_f64(double v) {
+  constexpr int ctrl = (MASK == 1) ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b & 0xffffffffu), ctrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), ctrl, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo));
 }
 
 // Transforms the 32-channel chunk c (group c/4, quarter c%4, with c%4 == lane%4).
@@ -165,12 +187,19 @@ __device__ __forceinline__ void hadamard_chunk(const uint16_t* xr, const int8_t*
     }
   }
   const int quarter = c & 3;
-#pragma unroll
-  for (int step = 1; step < 4; step <<= 1) {  // spans 32 and 64: lanes xor 1, xor 2
-    const bool upper = (quarter & step) != 0;
+  {  // span 32: lanes xor 1
+    const bool upper = (quarter & 1) != 0;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      const double other = shfl_xor_f64(u[e], step);
+      const double other = quad_xor_f64<1>(u[e]);
+      u[e] = upper ? (other - u[e]) : (u[e] + other);
+    }
+  }
+  {  // span 64: lanes xor 2
+    const bool upper = (quarter & 2) != 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const double other = quad_xor_f64<2>(u[e]);
       u[e] = upper ? (other - u[e]) : (u[e] + other);
     }
   }
@@ -302,12 +331,13 @@ extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, c
                  "O, qO and xO must be NULL when nO == 0");
   }
   const int ldO = static_cast<int>(outlier_ld(nO));
-  QLIN_REQUIRE(M <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
-  const dim3 grid(static_cast<unsigned>(M));
+  constexpr int rows_per_block = kQuantThreads / 64;
+  QLIN_REQUIRE(M / rows_per_block < 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
+  const dim3 grid(static_cast<unsigned>((M + rows_per_block - 1) / rows_per_block));
   if (r != nullptr)
-    quant_act_kernel<true><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, K, r, q, scale, O, nO, ldO, s, qO, xO);
+    quant_act_kernel<true><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, M, K, r, q, scale, O, nO, ldO, s, qO, xO);
   else
-    quant_act_kernel<false><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, K, r, q, scale, O, nO, ldO, s, qO, xO);
+    quant_act_kernel<false><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, M, K, r, q, scale, O, nO, ldO, s, qO, xO);
   QLIN_LAUNCH_CHECK("quant_act_kernel");
   return QLIN_OK;
 }

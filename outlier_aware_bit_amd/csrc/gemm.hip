@@ -13,14 +13,14 @@
 //   * Weights never touch LDS: the packed layout is in MFMA fragment order, so
 //     each wave streams its own columns straight from memory into registers
 //     with one 16-byte load per lane per fragment (int4 weights at half the
-//     bytes), one K stage ahead of use, and unpacks them in registers.
-//   * The K loop takes two stages per iteration with no branches inside (the
-//     prefetch indices are clamped), so the accumulators stay in place in the
-//     accumulation registers.
+//     bytes), up to two K stages ahead of use, and unpacks them in registers.
+//   * The K loop is unrolled over the period of the register rotation with no
+//     branches inside (prefetch indices are clamped to the last stage), so
+//     the accumulators stay in place in the accumulation registers.
 //   * Activations, shared by the four waves, go global -> registers -> LDS
-//     (double buffered, one stage of 128 k ahead), stored as 16-byte chunks
-//     XOR-swizzled by row so fragment reads of 8 consecutive rows hit
-//     distinct banks.
+//     (double buffered, loaded two stages of 128 k ahead), stored as 16-byte chunks
+//     XOR-swizzled by row so that fragment reads and row stores are free of
+//     bank conflicts.
 //   * Workgroups are mapped to tiles in groups of 4 tile rows, with each
 //     XCD (every 8th workgroup) given a contiguous block of tiles so the
 //     operands it streams stay in its own L2.
@@ -28,6 +28,8 @@
 // owns NT 32-column tiles, its waves split K, every weight byte is loaded
 // once straight into MFMA fragments with U units of 64 k in flight per lane,
 // and the waves' int32 partial sums meet in LDS.
+#include <type_traits>
+
 #include "common.hpp"
 #include "comp.hpp"
 #include "layout.hpp"
@@ -163,7 +165,13 @@ __device__ __forceinline__ void lds_barrier() {
 // ============================================================ tiled kernel
 constexpr int kBN = 256, kBK = 128, kTileThreads = 256;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
+// LDS byte offset of 16-byte chunk `chunk` of A row `row`.  The chunk index is
+// XORed with (row >> 1) & 7: the LDS serves 16 lanes per cycle over 64 banks,
+// and a fragment read has lanes 0..15 on rows 0..15 at one logical chunk, so
+// rows of equal parity (which share a bank half) must land on 8 different
+// chunks.
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ swz_key(row)) << 4); }
 
 template <BOp B, AOp A, int TM>
 struct Tile {
@@ -216,7 +224,7 @@ __device__ __forceinline__ void store_a(uint8_t* buf, int lds_a, const v4i (&ra)
   using T = Tile<B, A, TM>;
 #pragma unroll
   for (int i = 0; i < T::kAChunks; ++i) {
-    // Rows of chunk i differ from chunk 0 by a multiple of 32: same swizzle.
+    // Rows of chunk i differ from chunk 0 by a multiple of 32: same swizzle key.
     uint8_t* d = buf + lds_a + i * T::kARowStep * kBK;
     if constexpr (A == AOp::I8) {
       *reinterpret_cast<v4i*>(d) = ra[i];
@@ -275,14 +283,14 @@ __device__ __forceinline__ void compute_stage(const uint8_t* buf, const v4i (&rb
   v4i af[2][TM];
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm)
-    af[0][tm] = *reinterpret_cast<const v4i*>(abuf + tm * 32 * kBK + ((ahalf ^ (arow & 7)) << 4));
+    af[0][tm] = *reinterpret_cast<const v4i*>(abuf + tm * 32 * kBK + ((ahalf ^ swz_key(arow)) << 4));
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (ks + 1 < 4) {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
         af[(ks + 1) & 1][tm] =
-            *reinterpret_cast<const v4i*>(abuf + tm * 32 * kBK + (((2 * (ks + 1) + ahalf) ^ (arow & 7)) << 4));
+            *reinterpret_cast<const v4i*>(abuf + tm * 32 * kBK + (((2 * (ks + 1) + ahalf) ^ swz_key(arow)) << 4));
     }
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
@@ -306,7 +314,7 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
   tn_idx = r / gm;
 }
 
-template <BOp B, AOp A, int TM, bool COMP>
+template <BOp B, AOp A, int TM, int BD, bool COMP>
 __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
   using T = Tile<B, A, TM>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * T::kStage];
@@ -333,36 +341,58 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
     for (int b = 0; b < 2; ++b) acc[a][b] = v16i{};
 
   const int S = static_cast<int>(g.K / kBK);
-  uint8_t* buf0 = lds;
-  uint8_t* buf1 = lds + T::kStage;
-  v4i ra[T::kAChunks];
-  v4i rb0[T::kNB], rb1[T::kNB];
-  v2h rr0[2], rr1[2];
-  load_a<B, A, TM>(p, 0, ra);
-  load_b<B, A, TM>(p, b_tiles, g.N, 0, rb0, rr0);
-  store_a<B, A, TM>(buf0, p.lds_a, ra);
-  load_a<B, A, TM>(p, S > 1 ? 1 : 0, ra);
+  // Operand t (stage t of K) lives in B register set t % NBS (NBS = BD + 1)
+  // and in A register set / LDS buffer t % 2.  Stage s loads B(s+BD) and
+  // A(s+2) before its matrix-core work and stores A(s+1) into LDS after it,
+  // so weight loads have BD stages and activation loads about two stages of
+  // work to arrive.
+  constexpr int NBS = BD + 1;
+  v4i ra[2][T::kAChunks];
+  v4i rb[NBS][T::kNB];
+  v2h rr[NBS][2];
+  load_a<B, A, TM>(p, 0, ra[0]);
+#pragma unroll
+  for (int j = 0; j < BD; ++j) load_b<B, A, TM>(p, b_tiles, g.N, j < S ? j : S - 1, rb[j], rr[j]);
+  load_a<B, A, TM>(p, S > 1 ? 1 : 0, ra[1]);
+  store_a<B, A, TM>(lds, p.lds_a, ra[0]);
   lds_barrier();
 
-  // Two stages per iteration, no branches inside: prefetch stage indices are
-  // clamped to S - 1, so past the end they reload the last stage (in bounds)
-  // into buffers that are not read again.
+  auto stage = [&](auto jb, auto ja, int st) __attribute__((always_inline)) {
+    constexpr int JB = decltype(jb)::value, JA = decltype(ja)::value;
+    const int sb = (st + BD < S) ? st + BD : S - 1;
+    const int s2 = (st + 2 < S) ? st + 2 : S - 1;
+    load_b<B, A, TM>(p, b_tiles, g.N, sb, rb[(JB + BD) % NBS], rr[(JB + BD) % NBS]);
+    load_a<B, A, TM>(p, s2, ra[JA]);
+    compute_stage<B, A, TM>(lds + JA * T::kStage, rb[JB], rr[JB], acc);
+    store_a<B, A, TM>(lds + (1 - JA) * T::kStage, p.lds_a, ra[1 - JA]);
+    lds_barrier();
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
   int s = 0;
-  for (; s + 1 < S; s += 2) {
-    const int s2 = (s + 2 < S) ? s + 2 : S - 1;
-    const int s3 = (s + 3 < S) ? s + 3 : S - 1;
-    load_b<B, A, TM>(p, b_tiles, g.N, s + 1, rb1, rr1);
-    compute_stage<B, A, TM>(buf0, rb0, rr0, acc);
-    store_a<B, A, TM>(buf1, p.lds_a, ra);
-    load_a<B, A, TM>(p, s2, ra);
-    lds_barrier();
-    load_b<B, A, TM>(p, b_tiles, g.N, s2, rb0, rr0);
-    compute_stage<B, A, TM>(buf1, rb1, rr1, acc);
-    store_a<B, A, TM>(buf0, p.lds_a, ra);
-    load_a<B, A, TM>(p, s3, ra);
-    lds_barrier();
+  if constexpr (BD == 2) {
+    for (; s + 5 < S; s += 6) {
+      stage(C0{}, C0{}, s);
+      stage(C1{}, C1{}, s + 1);
+      stage(C2{}, C0{}, s + 2);
+      stage(C0{}, C1{}, s + 3);
+      stage(C1{}, C0{}, s + 4);
+      stage(C2{}, C1{}, s + 5);
+    }
+    const int rem = S - s;  // 0..5 stages left, uniform
+    if (rem > 0) stage(C0{}, C0{}, s);
+    if (rem > 1) stage(C1{}, C1{}, s + 1);
+    if (rem > 2) stage(C2{}, C0{}, s + 2);
+    if (rem > 3) stage(C0{}, C1{}, s + 3);
+    if (rem > 4) stage(C1{}, C0{}, s + 4);
+  } else {
+    for (; s + 1 < S; s += 2) {
+      stage(C0{}, C0{}, s);
+      stage(C1{}, C1{}, s + 1);
+    }
+    if (s < S) stage(C0{}, C0{}, s);
   }
-  if (s < S) compute_stage<B, A, TM>(buf0, rb0, rr0, acc);  // odd S: the last stage
 
   if (!live) return;
   // Epilogue: finish the integer accumulator, scale by the column step, add
@@ -377,28 +407,47 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
   }
   const int64_t n_lane = wcol0 + (lane & 31);
   const float sw0 = col_scale<B>(g, n_lane), sw1 = col_scale<B>(g, n_lane + 32);
+  // W4A4 zero points: acc = raw - zw*(rowsum - K*za) - za*colsum, evaluated
+  // in wrapping 32-bit arithmetic (exact: the true value fits int32).
+  [[maybe_unused]] uint32_t zw0 = 0, zw1 = 0, cs0 = 0, cs1 = 0;
+  if constexpr (B == BOp::W4U) {
+    zw0 = static_cast<uint32_t>(g.zw[n_lane]);
+    zw1 = static_cast<uint32_t>(g.zw[n_lane + 32]);
+    cs0 = static_cast<uint32_t>(g.colsum[n_lane]);
+    cs1 = static_cast<uint32_t>(g.colsum[n_lane + 32]);
+  }
   const bool want_acc = g.acc != nullptr;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int64_t m = m0 + 32 * tm + frag_row(v, lane);
-      if (m >= g.M) continue;
-      const float sam = g.sa[m];
-      uint16_t* yrow = g.y + m * g.N + n_lane;
-      const int32_t v0 = finish_acc<B>(acc[tm][0][v], g, m, n_lane);
-      const int32_t v1 = finish_acc<B>(acc[tm][1][v], g, m, n_lane + 32);
+      const int64_t mc = m < g.M ? m : g.M - 1;
+      const float sam = g.sa[mc];
+      int32_t v0 = acc[tm][0][v], v1 = acc[tm][1][v];
+      if constexpr (B == BOp::W4Shift) {
+        v0 >>= 4;  // every product is 16 * q * q4: the division is exact
+        v1 >>= 4;
+      } else if constexpr (B == BOp::W4U) {
+        const uint32_t za = static_cast<uint32_t>(g.za[mc]);
+        const uint32_t rk = static_cast<uint32_t>(g.rowsum[mc]) - static_cast<uint32_t>(g.K) * za;
+        v0 = static_cast<int32_t>(static_cast<uint32_t>(v0) - zw0 * rk - za * cs0);
+        v1 = static_cast<int32_t>(static_cast<uint32_t>(v1) - zw1 * rk - za * cs1);
+      }
       float f0 = static_cast<float>(v0) * sw0, f1 = static_cast<float>(v1) * sw1;
       if constexpr (COMP) {
         f0 += cf[tm][0][v];
         f1 += cf[tm][1][v];
       }
-      yrow[0] = f2h(f0 * sam);
-      yrow[32] = f2h(f1 * sam);
-      if (want_acc) {
-        int32_t* arow = g.acc + m * g.N + n_lane;
-        arow[0] = v0;
-        arow[32] = v1;
+      if (m < g.M) {
+        uint16_t* yrow = g.y + m * g.N + n_lane;
+        yrow[0] = f2h(f0 * sam);
+        yrow[32] = f2h(f1 * sam);
+        if (want_acc) {
+          int32_t* arow = g.acc + m * g.N + n_lane;
+          arow[0] = v0;
+          arow[32] = v1;
+        }
       }
     }
 }
@@ -522,9 +571,12 @@ void launch_skinny(const GemmArgs& g, hipStream_t st) {
 
 template <BOp B, AOp A, int TM, bool COMP>
 qlin_status launch_tile(const GemmArgs& g, hipStream_t st) {
+  // Weight prefetch depth: two stages, except for the per-group requant at
+  // 256-row tiles, whose unpack temporaries leave room for one.
+  constexpr int BD = (B == BOp::W4Group && TM == 8) ? 1 : 2;
   const int64_t tiles = ((g.M + 32 * TM - 1) / (32 * TM)) * ((g.N + kBN - 1) / kBN);
   QLIN_REQUIRE(tiles <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M=%lld too large", (long long)g.M);
-  gemm_tile<B, A, TM, COMP><<<dim3(static_cast<unsigned>(tiles)), kTileThreads, 0, st>>>(g);
+  gemm_tile<B, A, TM, BD, COMP><<<dim3(static_cast<unsigned>(tiles)), kTileThreads, 0, st>>>(g);
   QLIN_LAUNCH_CHECK("gemm_tile");
   return QLIN_OK;
 }

@@ -27,9 +27,18 @@ __global__ __launch_bounds__(kMomThreads) void momentum_kernel(
   const bool valid = (o >= 0 && o < K);
   float c = 0.0f;
   if (valid) {
-    const uint16_t* col = x + o;
-#pragma unroll 8
-    for (int64_t m = threadIdx.x; m < M; m += kMomThreads) c = fmaxf(c, fabsf(h2f(col[m * K])));
+    // Eight rows per thread per pass, all loads issued before the reduction.
+    constexpr int R = 8;
+    const uint16_t* col = x + o + static_cast<int64_t>(threadIdx.x) * K;
+    const int64_t step = static_cast<int64_t>(kMomThreads) * K;
+    for (int64_t base = threadIdx.x; base < M; base += static_cast<int64_t>(kMomThreads) * R) {
+      uint16_t v[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) v[i] = (base + i * kMomThreads < M) ? col[i * step] : static_cast<uint16_t>(0);
+#pragma unroll
+      for (int i = 0; i < R; ++i) c = fmaxf(c, fabsf(h2f(v[i])));
+      col += R * step;
+    }
   }
   c = block_max<kMomThreads / 64>(c, red);
   if (threadIdx.x == 0 && valid) {
