@@ -1,0 +1,154 @@
+"""GPU parity at the full sizes of the five layer workloads, in the launch
+configurations bench.py times.
+
+Integer stages (codes, zero points, sums, the momentum state s and r) are
+compared in full, bit for bit.  GEMM accumulators and fp16 outputs are
+compared on sampled rows (the oracle's float64 product of the full matrices
+would take minutes): integer accumulators bit for bit, outputs within the
+normwise relative tolerance 1e-3 over the sample.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import gemm, layer, quant, quaff
+from tests.gpu_helpers import assert_close, assert_equal, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+    assert torch.cuda.is_available()
+    from outlier_aware_bit_amd import qlin
+    return qlin
+
+
+def _sample_rows(M, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(n, M), replace=False)]))
+    return rows.astype(np.int64)
+
+
+def test_tiny_w8a8_full(q):
+    lin = synth.tiny_w8a8(seed=0)
+    log("tiny W8A8 16x256x128")
+    ref = layer.w8a8_forward(lin.x, lin.w)
+    codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 8)
+    assert_equal(host(codes), ref["qw"], "weight codes")
+    w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
+    qa, sa, _, _ = q.qlin_quant_act(dev(lin.x))
+    assert_equal(host(qa), ref["q"], "activation codes")
+    assert_equal(host(sa), ref["sa"], "activation steps")
+    y, acc = q.qlin_gemm_w8a8(qa, sa, w8, sw, 128, want_acc=True)
+    assert_equal(host(acc), ref["acc"], "acc")
+    assert_close(host(y), ref["y"], "y")
+
+
+def test_quaff_q_proj_ten_steps(q):
+    import torch
+    M, K, N, nO = 2048, 4096, 4096, 205
+    log(f"Quaff q_proj {M}x{K}x{N} |O|={nO}, 10 steps")
+    d = synth.quaff_steps(M=M, K=K, N=N, n_outliers=nO, steps=10, seed=1)
+    prep = layer.quaff_prepare(d.w, d.outliers)
+    codes, sw = q.qlin_quant_weight_sym(dev(d.w), 8)
+    assert_equal(host(codes), prep["qw"], "weight codes")
+    assert_equal(host(sw).view(np.uint16), prep["sw"].view(np.uint16), "weight steps")
+    w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
+    O = dev(d.outliers)
+    WO = dev(np.ascontiguousarray(d.w[d.outliers]))
+    WOp = q.qlin_pack_weight(q.QLIN_LAYOUT_WO, WO)
+    wmax = q.qlin_weight_row_absmax(WO)
+    s = torch.ones(K, dtype=torch.float32, device="cuda")
+    r = torch.empty_like(s)
+    s_ref = np.ones(K, np.float32)
+    rows = _sample_rows(M, 48, 7)
+    o = d.outliers.astype(np.int64)
+    for t, x in enumerate(d.xs):
+        log(f"  step {t}")
+        s_ref, r_ref = quaff.momentum_update(x, o, prep["wmax"], 0.9, s_ref)
+        xd = dev(x)
+        q.qlin_momentum_update(xd, O, wmax, 0.9, s, r)
+        qa, sa, _, xO = q.qlin_quant_act(xd, r, O, s=s, want_qO=False)
+        y, acc = q.qlin_gemm_w8a8(qa, sa, w8, sw, N, xO=xO, nO=nO, WO=WOp, want_acc=True)
+        assert_equal(host(s), s_ref, f"s step {t}")
+        assert_equal(host(r), r_ref, f"r step {t}")
+        q_ref, sa_ref = quant.quant_act_sym_int8(x, r_ref)
+        assert_equal(host(qa), q_ref, f"codes step {t}")
+        assert_equal(host(sa), sa_ref, f"steps step {t}")
+        acc_ref, y_main = gemm.w8a8(q_ref[rows], sa_ref[rows], prep["qw"], prep["sw"].astype(np.float32))
+        y_ref = y_main + quaff.compensation(q_ref[rows][:, o], sa_ref[rows], s_ref[o], prep["w_o"])
+        assert_equal(host(acc)[rows], acc_ref, f"acc step {t}")
+        assert_close(host(y)[rows], y_ref, f"y step {t}")
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_qqq_decode_w4a8_channel_full(q, M):
+    K, N = 4096, 11008
+    log(f"QQQ decode W4A8 per channel M={M} K={K} N={N}")
+    lin = synth.qqq_decode(M=M, K=K, N=N, seed=2)
+    ref = layer.w4a8_channel_forward(lin.x, lin.w)
+    codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 4)
+    assert_equal(host(codes), ref["q4"], "weight codes")
+    assert_equal(host(sw).view(np.uint16), ref["sw"].view(np.uint16), "weight steps")
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes)
+    qa, sa, _, _ = q.qlin_quant_act(dev(lin.x))
+    assert_equal(host(qa), ref["q"], "activation codes")
+    y, acc = q.qlin_gemm_w4a8(qa, sa, w4, sw, N, want_acc=True)
+    assert_equal(host(acc), ref["acc"], "acc")
+    assert_close(host(y), ref["y"], "y")
+
+
+def test_qqq_prefill_w4a8_group_full(q):
+    M, K, N = 4096, 11008, 4096
+    log(f"QQQ prefill W4A8 g128 {M}x{K}x{N}")
+    lin = synth.qqq_prefill(M=M, K=K, N=N, seed=3)
+    q4, sg, sc, rg = quant.quant_weight_group(lin.w, 128)
+    codes, gs, cs, ratio = q.qlin_quant_weight_group(dev(lin.w), 128)
+    assert_equal(host(codes), q4, "weight codes")
+    assert_equal(host(gs).view(np.uint16), sg.view(np.uint16), "group scales")
+    assert_equal(host(cs).view(np.uint16), sc.view(np.uint16), "channel scales")
+    assert_equal(host(ratio).view(np.uint16), rg.view(np.uint16), "ratios")
+    w8 = quant.requant_group(q4, rg, 128)
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes)
+    qa, sa, _, _ = q.qlin_quant_act(dev(lin.x))
+    q_ref, sa_ref = quant.quant_act_sym_int8(lin.x)
+    assert_equal(host(qa), q_ref, "activation codes")
+    assert_equal(host(sa), sa_ref, "activation steps")
+    y, acc = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128, want_acc=True)
+    rows = _sample_rows(M, 40, 8)
+    acc_ref, y_ref = gemm.w4a8_group(q_ref[rows], sa_ref[rows], w8, sc.astype(np.float32))
+    assert_equal(host(acc)[rows], acc_ref, "acc")
+    assert_close(host(y)[rows], y_ref, "y")
+
+
+def test_offq_w4a4_full(q):
+    M, K, N = 2048, 4096, 14336
+    log(f"OffQ W4A4 {M}x{K}x{N}")
+    lin = synth.offq_inputs(M=M, K=K, N=N, seed=4)
+    signs = lin.extra["signs"]
+    qa_ref, sa_ref, za_ref, rs_ref, t_ref = quant.hadamard_offset_int4(lin.x, signs)
+    qw_ref, sw_ref, zw_ref, cs_ref = quant.offq_weight(lin.w, signs)
+    sd = dev(signs)
+    qa4, sa, za, rs, t = q.qlin_hadamard_offset(dev(lin.x), sd, want_t=True)
+    assert_equal(host(t), t_ref, "transformed activations")
+    packed = host(qa4)
+    codes = np.empty((M, K), np.uint8)
+    codes[:, 0::2] = packed & 0xF
+    codes[:, 1::2] = packed >> 4
+    assert_equal(codes, qa_ref, "activation codes")
+    assert_equal(host(sa), sa_ref, "activation steps")
+    assert_equal(host(za), za_ref, "activation zero points")
+    assert_equal(host(rs), rs_ref, "row sums")
+    cw, sw, zw, cs = q.qlin_quant_weight_offq(dev(lin.w), sd)
+    assert_equal(host(cw), qw_ref, "weight codes")
+    assert_equal(host(sw), sw_ref, "weight steps")
+    assert_equal(host(zw), zw_ref, "weight zero points")
+    assert_equal(host(cs), cs_ref, "column sums")
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, cw)
+    y, acc = q.qlin_gemm_w4a4(qa4, sa, za, rs, w4, sw, zw, cs, N, want_acc=True)
+    rows = _sample_rows(M, 32, 9)
+    acc_ref, y_ref = gemm.w4a4(qa_ref[rows], sa_ref[rows], za_ref[rows], qw_ref, sw_ref, zw_ref)
+    assert_equal(host(acc)[rows], acc_ref, "acc")
+    assert_close(host(y)[rows], y_ref, "y")
