@@ -15,12 +15,23 @@ bounded sample, and per-kernel measurements of the other steps of the path at
 their own workload shapes ("rows").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-rows]
+                       [--copy-calibration]
+
+--copy-calibration first runs a plain device-to-device copy of a known size
+(256 MiB read, 256 MiB written, three times) so that a counter run
+(rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE) can scale the GEMM's counter
+readings to bytes.  The scaled per-launch traffic is kept in
+profiles/gemm_w8a8_comp_q_proj_traffic.md together with a SHA-256 of the GEMM
+kernel's sources; roofline.traffic reports it only while the sources still
+hash to that value, and null otherwise.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -35,6 +46,47 @@ PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_FP16_TFLOPS = 2500.0  # dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0      # HBM3E, 8 TB/s
 MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_comp_q_proj_traffic.md")
+# Sources that make up the fused W8A8 GEMM kernel.
+GEMM_SOURCES = ["gemm.hip", "comp.hpp", "layout.hpp", "common.hpp"]
+COPY_CALIB_BYTES = 256 << 20
+
+
+def gemm_sources_sha256():
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "outlier_aware_bit_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Per-launch HBM bytes of the fused GEMM from the committed counter
+    summary, or None when it is absent or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    kv = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
+    if kv.get("kernel_sources_sha256") != gemm_sources_sha256():
+        return None
+    try:
+        return {"read": int(kv["read_bytes_per_launch"]), "write": int(kv["write_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain copy of COPY_CALIB_BYTES, three times, for counter scaling."""
+    import torch
+    src = torch.ones(COPY_CALIB_BYTES // 2, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def log(msg):
@@ -267,6 +319,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -279,6 +332,8 @@ def main():
     from outlier_aware_bit_amd import qlin as q
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if a.copy_calibration:
+        copy_calibration()
     layer = QuaffLayer(q)
 
     for t in range(a.warmup):
@@ -297,6 +352,7 @@ def main():
     eq_ops = layer.int8_ops() + 2 * layer.fp16_flops()
     achieved = eq_ops / (gemm_ms * 1e-3) / 1e12
     log(f"step {ms_step:.4f} ms, fused GEMM {gemm_ms:.4f} ms ({achieved:.1f} int8-equivalent TOPS)")
+    tr = recorded_traffic()
 
     rec = {
         "metric": METRIC,
@@ -316,7 +372,9 @@ def main():
                    "step": "momentum_update + quant_act + gemm_w8a8(fused compensation)"},
         "roofline": {"bound": "mfma", "kernel": "gemm_tile<W8,I8,comp>", "achieved": round(achieved, 2),
                      "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": None, "launch_ms": round(gemm_ms, 5),
+                     "traffic": (tr["read"] + tr["write"]) if tr else None,
+                     "traffic_read_write": [tr["read"], tr["write"]] if tr else None,
+                     "algorithmic_bytes": layer.gemm_bytes(), "launch_ms": round(gemm_ms, 5),
                      "work": "int8 MACs x2 plus fp16 compensation flops x2 (fp16 peak is half the int8 peak)"},
     }
     if not a.no_rows:

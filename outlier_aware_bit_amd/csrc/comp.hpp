@@ -16,7 +16,10 @@
 namespace qlin {
 
 // f[tm][nt]: fragments of rows m0 + 32 tm + [0, 32) and 32-column tiles
-// nt32 + nt.  Rows at or past M read row M - 1 (their results are discarded).
+// nt32 + nt, transposed like the integer accumulators (W_O is the first
+// operand): lane l holds row (l & 31), register v column
+// 8*(v>>2) + 4*(l>>5) + (v&3).  Rows at or past M read row M - 1 (their
+// results are discarded).
 template <int TM, int NT>
 __device__ __forceinline__ void comp_accumulate(v16f (&f)[TM][NT], const uint16_t* __restrict__ xO,
                                                 int ldO, const uint8_t* __restrict__ WOp, int64_t M,
@@ -41,7 +44,7 @@ __device__ __forceinline__ void comp_accumulate(v16f (&f)[TM][NT], const uint16_
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        f[tm][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[tm], bp[nt], f[tm][nt], 0, 0, 0);
+        f[tm][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bp[nt], ap[tm], f[tm][nt], 0, 0, 0);
   }
 }
 

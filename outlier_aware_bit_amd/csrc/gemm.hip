@@ -29,6 +29,7 @@
 // once straight into MFMA fragments with U units of 64 k in flight per lane,
 // and the waves' int32 partial sums meet in LDS.
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "comp.hpp"
@@ -295,8 +296,37 @@ __device__ __forceinline__ void compute_stage(const uint8_t* buf, const v4i (&rb
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[tm][nt] = mfma_i8(af[ks & 1][tm], bf[nt][ks], acc[tm][nt]);
+      for (int nt = 0; nt < 2; ++nt) acc[tm][nt] = mfma_i8(bf[nt][ks], af[ks & 1][tm], acc[tm][nt]);
   }
+}
+
+// Issue order of one K stage.  A wave is alone on its SIMD and issues in
+// order, so a burst of global loads or LDS traffic that fills a queue stalls
+// the matrix-core instructions behind it.  The scheduler is told to emit the
+// stage as pairs of MFMAs, each followed by its share of the stage's memory
+// instructions: the LDS fragment reads of the next k step, the global
+// prefetch loads and the LDS stores of the next activation stage.
+template <int Mask, int N>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(Mask, N, 0);
+}
+
+template <BOp B, AOp A, int TM, int P>
+__device__ __forceinline__ void sched_pair() {
+  using T = Tile<B, A, TM>;
+  constexpr int kPairs = 4 * TM;
+  constexpr int kVmem = T::kNB + T::kAChunks + (B == BOp::W4Group ? 2 : 0);
+  constexpr int kDsWrite = (A == AOp::I8) ? T::kAChunks : 2 * T::kAChunks;
+  sched_group<0x008, 2>();                                          // MFMA
+  sched_group<0x100, (P < 3 * TM) ? 1 : 0>();                       // LDS read
+  sched_group<0x020, (P + 1) * kVmem / kPairs - P * kVmem / kPairs>();        // global load
+  sched_group<0x200, (P + 1) * kDsWrite / kPairs - P * kDsWrite / kPairs>();  // LDS write
+}
+
+template <BOp B, AOp A, int TM, int... Ps>
+__device__ __forceinline__ void stage_schedule(std::integer_sequence<int, Ps...>) {
+  sched_group<0x100, TM>();  // the first k step's fragments
+  (sched_pair<B, A, TM, Ps>(), ...);
 }
 
 // Tile index -> (tile row, tile column): XCD-contiguous blocks, groups of 4 rows.
@@ -365,7 +395,10 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
     load_a<B, A, TM>(p, s2, ra[JA]);
     compute_stage<B, A, TM>(lds + JA * T::kStage, rb[JB], rr[JB], acc);
     store_a<B, A, TM>(lds + (1 - JA) * T::kStage, p.lds_a, ra[1 - JA]);
+    stage_schedule<B, A, TM>(std::make_integer_sequence<int, 4 * TM>{});
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
@@ -394,9 +427,14 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
     if (s < S) stage(C0{}, C0{}, s);
   }
 
-  if (!live) return;
-  // Epilogue: finish the integer accumulator, scale by the column step, add
-  // the compensation term, scale by the token step, store fp16.
+  // Epilogue.  The weight fragment is the first matrix-core operand, so each
+  // accumulator fragment is the transposed 32 x 32 block: lane l holds token
+  // row (l & 31) and, in register v, output column 8*(v>>2) + 4*(l>>5) + (v&3)
+  // -- runs of four adjacent columns.  Per 32 rows the wave finishes the
+  // integer accumulator, scales by the column step, adds the compensation
+  // term, scales by the token step, converts to fp16, stages the 32 x 64
+  // block in its own LDS rows and writes it out as full 128-byte row
+  // segments, 16 bytes per lane.
   [[maybe_unused]] v16f cf[COMP ? TM : 1][2];
   if constexpr (COMP) {
 #pragma unroll
@@ -405,51 +443,77 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
       for (int b = 0; b < 2; ++b) cf[a][b] = v16f{};
     comp_accumulate<TM, 2>(cf, g.xO, g.ldO, g.WOp, g.M, g.N, m0, nt32);
   }
-  const int64_t n_lane = wcol0 + (lane & 31);
-  const float sw0 = col_scale<B>(g, n_lane), sw1 = col_scale<B>(g, n_lane + 32);
-  // W4A4 zero points: acc = raw - zw*(rowsum - K*za) - za*colsum, evaluated
-  // in wrapping 32-bit arithmetic (exact: the true value fits int32).
-  [[maybe_unused]] uint32_t zw0 = 0, zw1 = 0, cs0 = 0, cs1 = 0;
-  if constexpr (B == BOp::W4U) {
-    zw0 = static_cast<uint32_t>(g.zw[n_lane]);
-    zw1 = static_cast<uint32_t>(g.zw[n_lane + 32]);
-    cs0 = static_cast<uint32_t>(g.colsum[n_lane]);
-    cs1 = static_cast<uint32_t>(g.colsum[n_lane + 32]);
-  }
+  lds_barrier();  // every wave has finished reading the activation stages
+  if (!live) return;
+  constexpr int kOutPitch = 144;  // bytes per staged row: 128 + 16 spreads rows over the banks
+  static_assert(4 * 32 * kOutPitch <= 2 * T::kStage, "output staging exceeds the LDS buffers");
+  uint8_t* const out_lds = lds + wave * 32 * kOutPitch;
+  const int r = lane & 31, h = lane >> 5;
   const bool want_acc = g.acc != nullptr;
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t m = m0 + 32 * tm + frag_row(v, lane);
-      const int64_t mc = m < g.M ? m : g.M - 1;
-      const float sam = g.sa[mc];
-      int32_t v0 = acc[tm][0][v], v1 = acc[tm][1][v];
-      if constexpr (B == BOp::W4Shift) {
-        v0 >>= 4;  // every product is 16 * q * q4: the division is exact
-        v1 >>= 4;
-      } else if constexpr (B == BOp::W4U) {
-        const uint32_t za = static_cast<uint32_t>(g.za[mc]);
-        const uint32_t rk = static_cast<uint32_t>(g.rowsum[mc]) - static_cast<uint32_t>(g.K) * za;
-        v0 = static_cast<int32_t>(static_cast<uint32_t>(v0) - zw0 * rk - za * cs0);
-        v1 = static_cast<int32_t>(static_cast<uint32_t>(v1) - zw1 * rk - za * cs1);
-      }
-      float f0 = static_cast<float>(v0) * sw0, f1 = static_cast<float>(v1) * sw1;
-      if constexpr (COMP) {
-        f0 += cf[tm][0][v];
-        f1 += cf[tm][1][v];
-      }
-      if (m < g.M) {
-        uint16_t* yrow = g.y + m * g.N + n_lane;
-        yrow[0] = f2h(f0 * sam);
-        yrow[32] = f2h(f1 * sam);
-        if (want_acc) {
-          int32_t* arow = g.acc + m * g.N + n_lane;
-          arow[0] = v0;
-          arow[32] = v1;
-        }
-      }
+  for (int tm = 0; tm < TM; ++tm) {
+    const int64_t m = m0 + 32 * tm + r;
+    const int64_t mc = m < g.M ? m : g.M - 1;
+    const float sam = g.sa[mc];
+    // W4A4 zero points: acc = raw - zw*(rowsum - K*za) - za*colsum, evaluated
+    // in wrapping 32-bit arithmetic (exact: the true value fits int32).
+    [[maybe_unused]] uint32_t za = 0, rk = 0;
+    if constexpr (B == BOp::W4U) {
+      za = static_cast<uint32_t>(g.za[mc]);
+      rk = static_cast<uint32_t>(g.rowsum[mc]) - static_cast<uint32_t>(g.K) * za;
     }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = wcol0 + 32 * nt + 8 * q + 4 * h;  // first of this lane's four columns
+        float sw[4];
+        [[maybe_unused]] v4i zw{}, cs{};
+        if constexpr (B == BOp::W4U) {
+          const v4f swv = *reinterpret_cast<const v4f*>(g.sw_f + n);
+          zw = *reinterpret_cast<const v4i*>(g.zw + n);
+          cs = *reinterpret_cast<const v4i*>(g.colsum + n);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sw[j] = swv[j];
+        } else {
+          const uint2 swh = *reinterpret_cast<const uint2*>(g.sw_h + n);
+          sw[0] = h2f(static_cast<uint16_t>(swh.x & 0xffffu));
+          sw[1] = h2f(static_cast<uint16_t>(swh.x >> 16));
+          sw[2] = h2f(static_cast<uint16_t>(swh.y & 0xffffu));
+          sw[3] = h2f(static_cast<uint16_t>(swh.y >> 16));
+        }
+        v4i iv;
+        uint16_t hv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int32_t val = acc[tm][nt][4 * q + j];
+          if constexpr (B == BOp::W4Shift) {
+            val >>= 4;  // every product is 16 * q * q4: the division is exact
+          } else if constexpr (B == BOp::W4U) {
+            val = static_cast<int32_t>(static_cast<uint32_t>(val) - static_cast<uint32_t>(zw[j]) * rk -
+                                       za * static_cast<uint32_t>(cs[j]));
+          }
+          iv[j] = val;
+          float f = static_cast<float>(val) * sw[j];
+          if constexpr (COMP) f += cf[tm][nt][4 * q + j];
+          hv[j] = f2h(f * sam);
+        }
+        *reinterpret_cast<uint2*>(out_lds + r * kOutPitch + (32 * nt + 8 * q + 4 * h) * 2) =
+            make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
+        if (want_acc && m < g.M) *reinterpret_cast<v4i*>(g.acc + m * g.N + n) = iv;
+      }
+    // The wave reads back only rows it wrote; LDS operations of one wave
+    // complete in order, so no barrier is needed, only a compiler fence.
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 3) + 8 * i, chunk = lane & 7;
+      const v4i d = *reinterpret_cast<const v4i*>(out_lds + row * kOutPitch + chunk * 16);
+      const int64_t mr = m0 + 32 * tm + row;
+      if (mr < g.M) *reinterpret_cast<v4i*>(g.y + mr * g.N + wcol0 + 8 * chunk) = d;
+    }
+    asm volatile("" ::: "memory");
+  }
 }
 
 // ============================================================ skinny kernel

@@ -106,19 +106,27 @@ __global__ __launch_bounds__(kCompThreads) void outlier_comp_kernel(
 #pragma unroll
     for (int b = 0; b < 2; ++b) f[a][b] = v16f{};
   comp_accumulate<kCompTM, 2>(f, xO, ldO, WOp, M, N, m0, wcol0 / 32);
+  // Lane l holds row (l & 31) and runs of four adjacent columns: 8-byte
+  // read-modify-write of y per run.
 #pragma unroll
-  for (int tm = 0; tm < kCompTM; ++tm)
+  for (int tm = 0; tm < kCompTM; ++tm) {
+    const int64_t m = m0 + 32 * tm + (lane & 31);
+    if (m >= M) continue;
+    const float sam = sa[m];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t m = m0 + 32 * tm + frag_row(v, lane);
-      if (m >= M) continue;
-      const float sam = sa[m];
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        uint16_t* p = y + m * N + wcol0 + 32 * nt + (lane & 31);
-        *p = f2h(h2f(*p) + sam * f[tm][nt][v]);
+      for (int q = 0; q < 4; ++q) {
+        uint2* p = reinterpret_cast<uint2*>(y + m * N + wcol0 + 32 * nt + 8 * q + 4 * (lane >> 5));
+        const uint2 old = *p;
+        const uint16_t in[4] = {static_cast<uint16_t>(old.x & 0xffffu), static_cast<uint16_t>(old.x >> 16),
+                                static_cast<uint16_t>(old.y & 0xffffu), static_cast<uint16_t>(old.y >> 16)};
+        uint16_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = f2h(h2f(in[j]) + sam * f[tm][nt][4 * q + j]);
+        *p = make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
       }
-    }
+  }
 }
 
 }  // namespace
