@@ -320,7 +320,12 @@ __device__ __forceinline__ void sched_pair() {
   sched_group<0x008, 2>();                                          // MFMA
   sched_group<0x100, (P < 3 * TM) ? 1 : 0>();                       // LDS read
   sched_group<0x020, (P + 1) * kVmem / kPairs - P * kVmem / kPairs>();        // global load
-  sched_group<0x200, (P + 1) * kDsWrite / kPairs - P * kDsWrite / kPairs>();  // LDS write
+  if constexpr (A == AOp::U4) {
+    constexpr int q0 = 3 * kPairs / 4, n = kPairs - q0;  // LDS writes in the last quarter
+    sched_group<0x200, (P < q0) ? 0 : ((P - q0 + 1) * kDsWrite / n - (P - q0) * kDsWrite / n)>();
+  } else {
+    sched_group<0x200, (P + 1) * kDsWrite / kPairs - P * kDsWrite / kPairs>();  // LDS write
+  }
 }
 
 template <BOp B, AOp A, int TM, int... Ps>
@@ -391,8 +396,15 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
     constexpr int JB = decltype(jb)::value, JA = decltype(ja)::value;
     const int sb = (st + BD < S) ? st + BD : S - 1;
     const int s2 = (st + 2 < S) ? st + 2 : S - 1;
-    load_b<B, A, TM>(p, b_tiles, g.N, sb, rb[(JB + BD) % NBS], rr[(JB + BD) % NBS]);
-    load_a<B, A, TM>(p, s2, ra[JA]);
+    if constexpr (A == AOp::U4) {
+      // int4 activations: their loads go first and their LDS stores last,
+      // which gives the stores a full stage of latency cover.
+      load_a<B, A, TM>(p, s2, ra[JA]);
+      load_b<B, A, TM>(p, b_tiles, g.N, sb, rb[(JB + BD) % NBS], rr[(JB + BD) % NBS]);
+    } else {
+      load_b<B, A, TM>(p, b_tiles, g.N, sb, rb[(JB + BD) % NBS], rr[(JB + BD) % NBS]);
+      load_a<B, A, TM>(p, s2, ra[JA]);
+    }
     compute_stage<B, A, TM>(lds + JA * T::kStage, rb[JB], rr[JB], acc);
     store_a<B, A, TM>(lds + (1 - JA) * T::kStage, p.lds_a, ra[1 - JA]);
     stage_schedule<B, A, TM>(std::make_integer_sequence<int, 4 * TM>{});
