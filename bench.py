@@ -165,6 +165,32 @@ class QuaffLayer:
         if ev is not None:
             ev[1].record()
 
+    def capture(self):
+        """HIP graphs of the step: per activation batch one graph of the
+        momentum update and the quantization, and one graph of the GEMM (the
+        same buffers for every batch), so the GEMM can still be timed with
+        events recorded between graph launches."""
+        import torch
+        self.g_pre = []
+        for x in self.xs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.momentum(x)
+                self.quant(x)
+            self.g_pre.append(g)
+        self.g_gemm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g_gemm):
+            self.gemm()
+        torch.cuda.synchronize()
+
+    def graph_step(self, t, ev=None):
+        self.g_pre[t % len(self.g_pre)].replay()
+        if ev is not None:
+            ev[0].record()
+        self.g_gemm.replay()
+        if ev is not None:
+            ev[1].record()
+
     def int8_ops(self):
         return 2 * self.M * self.K * self.N
 
@@ -320,6 +346,10 @@ def main():
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--graphs", action="store_true",
+                    help="launch the step as HIP graphs (slower than eager launches on ROCm 7)")
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="record the GEMM's timing events on every n-th timed step (event records cost host time)")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -335,15 +365,21 @@ def main():
     if a.copy_calibration:
         copy_calibration()
     layer = QuaffLayer(q)
+    run = layer.step
+    if a.graphs:
+        layer.capture()
+        run = layer.graph_step
 
     for t in range(a.warmup):
-        layer.step(t)
+        run(t)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    every = max(1, a.event_every)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range((a.steps + every - 1) // every)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for t in range(a.steps):
-        layer.step(a.warmup + t, evs[t])
+        run(a.warmup + t, evs[t // every] if t % every == 0 else None)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_step = el * 1e3 / a.steps
@@ -369,7 +405,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "quaff_w8a8_outlier_comp_q_proj", "M_tokens": layer.M, "K": layer.K,
                    "N": layer.N, "n_outliers": layer.nO, "gamma": layer.gamma, "activation_batches": 10,
-                   "step": "momentum_update + quant_act + gemm_w8a8(fused compensation)"},
+                   "step": "momentum_update + quant_act + gemm_w8a8(fused compensation)",
+                   "launch": "hip_graphs" if a.graphs else "eager"},
         "roofline": {"bound": "mfma", "kernel": "gemm_tile<W8,I8,comp>", "achieved": round(achieved, 2),
                      "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                      "traffic": (tr["read"] + tr["write"]) if tr else None,

@@ -24,6 +24,9 @@ template <int TM, int NT>
 __device__ __forceinline__ void comp_accumulate(v16f (&f)[TM][NT], const uint16_t* __restrict__ xO,
                                                 int ldO, const uint8_t* __restrict__ WOp, int64_t M,
                                                 int64_t N, int64_t m0, int64_t nt32) {
+  // Operands of D = 4 k steps are in flight while the matrix cores work on
+  // the oldest one; a step's registers are refilled right after its MFMAs.
+  constexpr int D = 4;
   const int lane = threadIdx.x & 63;
   const int64_t tiles32 = N / 32;
   const uint16_t* arow[TM];
@@ -33,18 +36,48 @@ __device__ __forceinline__ void comp_accumulate(v16f (&f)[TM][NT], const uint16_
     m = m < M ? m : M - 1;
     arow[tm] = xO + m * ldO + 8 * (lane >> 5);
   }
-  for (int js = 0; js < ldO / 16; ++js) {
-    v8h ap[TM], bp[NT];
+  const uint8_t* bcol = WOp + (nt32 << 10) + lane * 16;
+  auto load = [&](int js, v8h (&ap)[TM], v8h (&bp)[NT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) ap[tm] = *reinterpret_cast<const v8h*>(arow[tm] + 16 * js);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      bp[nt] = *reinterpret_cast<const v8h*>(WOp + ((static_cast<int64_t>(js) * tiles32 + nt32 + nt) << 10) + lane * 16);
+      bp[nt] = *reinterpret_cast<const v8h*>(bcol + ((static_cast<int64_t>(js) * tiles32 + nt) << 10));
+  };
+  auto mma = [&](const v8h (&ap)[TM], const v8h (&bp)[NT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         f[tm][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bp[nt], ap[tm], f[tm][nt], 0, 0, 0);
+  };
+  const int nj = ldO / 16;
+  const int nfull = nj / D * D;
+  v8h ap[D][TM], bp[D][NT];
+  if (nfull > 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      load(d, ap[d], bp[d]);
+      __builtin_amdgcn_sched_barrier(0);  // issue the slots in order: slot 0 arrives first
+    }
+    for (int j0 = 0; j0 < nfull; j0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        mma(ap[d], bp[d]);
+        const int nxt = j0 + D + d;
+        load(nxt < nfull ? nxt : nfull - 1, ap[d], bp[d]);  // past the end: a harmless reload
+      }
+      // Keep that order: each step's MFMAs, then the refill of its registers.
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * NT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, TM + NT, 0);
+      }
+    }
+  }
+  for (int js = nfull; js < nj; ++js) {
+    load(js, ap[0], bp[0]);
+    mma(ap[0], bp[0]);
   }
 }
 

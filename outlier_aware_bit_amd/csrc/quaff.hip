@@ -14,59 +14,88 @@ namespace {
 
 constexpr int kMomThreads = 256;
 
-// One workgroup per outlier channel O[j]: c = max_m |x[m, O[j]]|, then
-// beta = max(1, sqrt(c / wmax)), s = gamma*s + (1-gamma)*beta, r = 1/s.  The
-// same workgroup writes r = 1/s for the channels between O[j-1] and O[j]
-// (and after the last one), so r covers every channel in one launch.
-__global__ __launch_bounds__(kMomThreads) void momentum_kernel(
+// Momentum update, one workgroup per 64-channel strip of X (one 128-byte
+// line per token row).  The outliers of a strip share its lines, so reading
+// the whole strip once per row fetches every line of X that holds an outlier
+// exactly once, with no reduction across workgroups.  Strips without an
+// outlier read nothing from X.
+//   c_k   = max_m |x[m, k]| for the 64 channels k of the strip
+//   o in O in the strip:  beta = max(1, sqrt(c_o / wmax)) (1 if wmax == 0),
+//                         s_o = gamma*s_o + (1-gamma)*beta, r_o = 1/s_o
+//   other channels:       r_k = 1/s_k
+constexpr int kStripThreads = 1024;
+constexpr int kStripLoads = 16;                             // 16-byte loads in flight per thread
+constexpr int kStripRows = kStripThreads / 8 * kStripLoads;  // rows per pass (8 lanes per row)
+
+__global__ __launch_bounds__(kStripThreads) void momentum_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const int32_t* __restrict__ O, int nO,
     const float* __restrict__ wmax, float gamma, float* __restrict__ s, float* __restrict__ r) {
-  __shared__ float red[kMomThreads / 64];
-  const int j = blockIdx.x;
-  const int o = O[j];
-  const bool valid = (o >= 0 && o < K);
-  float c = 0.0f;
-  if (valid) {
-    // Eight rows per thread per pass, all loads issued before the reduction.
-    constexpr int R = 8;
-    const uint16_t* col = x + o + static_cast<int64_t>(threadIdx.x) * K;
-    const int64_t step = static_cast<int64_t>(kMomThreads) * K;
-    for (int64_t base = threadIdx.x; base < M; base += static_cast<int64_t>(kMomThreads) * R) {
-      uint16_t v[R];
+  __shared__ float red[kStripThreads / 64][64];
+  __shared__ int owner[64];  // 1 + index into O of the outlier at this channel, or 0
+  const int64_t strip = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < 64) owner[tid] = 0;
+  __syncthreads();
+  for (int j = tid; j < nO; j += kStripThreads) {
+    const int o = O[j];
+    if (o >= 0 && o < K && o / 64 == strip) owner[o % 64] = j + 1;
+  }
+  __syncthreads();
+  const bool any = __syncthreads_or(tid < 64 && owner[tid] != 0);
+
+  float cm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // channels 8*(tid&7) + [0, 8)
+  if (any) {
+    const uint16_t* col = x + strip * 64 + (tid & 7) * 8;
+    const int64_t row0 = tid >> 3;
+    for (int64_t mb = 0; mb < M; mb += kStripRows) {
+      v4i v[kStripLoads];
 #pragma unroll
-      for (int i = 0; i < R; ++i) v[i] = (base + i * kMomThreads < M) ? col[i * step] : static_cast<uint16_t>(0);
+      for (int i = 0; i < kStripLoads; ++i) {
+        const int64_t m = mb + row0 + static_cast<int64_t>(kStripThreads / 8) * i;
+        v[i] = (m < M) ? *reinterpret_cast<const v4i*>(col + m * K) : v4i{0, 0, 0, 0};
+      }
 #pragma unroll
-      for (int i = 0; i < R; ++i) c = fmaxf(c, fabsf(h2f(v[i])));
-      col += R * step;
+      for (int i = 0; i < kStripLoads; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t u = static_cast<uint32_t>(v[i][w]);
+          cm[2 * w] = fmaxf(cm[2 * w], fabsf(h2f(static_cast<uint16_t>(u & 0xffffu))));
+          cm[2 * w + 1] = fmaxf(cm[2 * w + 1], fabsf(h2f(static_cast<uint16_t>(u >> 16))));
+        }
     }
   }
-  c = block_max<kMomThreads / 64>(c, red);
-  if (threadIdx.x == 0 && valid) {
-    const float w = wmax[j];
-    float beta = 1.0f;
-    if (w != 0.0f) beta = fmaxf(1.0f, sqrt_rn(div_rn(c, w)));
-    const float g1 = sub_rn(1.0f, gamma);
-    const float sn = add_rn(mul_rn(gamma, s[o]), mul_rn(g1, beta));
-    s[o] = sn;
-    r[o] = div_rn(1.0f, sn);
+  // Lanes with equal (lane & 7) hold the same channels: combine over lane bits 3..5.
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float v = cm[c];
+    v = fmaxf(v, __shfl_xor(v, 8));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    cm[c] = v;
   }
-  // Channels strictly between the previous outlier and this one.
-  int64_t lo = (j == 0) ? 0 : static_cast<int64_t>(O[j - 1]) + 1;
-  int64_t hi = static_cast<int64_t>(o);
-  lo = lo < 0 ? 0 : (lo > K ? K : lo);
-  hi = hi < 0 ? 0 : (hi > K ? K : hi);
-  for (int64_t k = lo + threadIdx.x; k < hi; k += kMomThreads) r[k] = div_rn(1.0f, s[k]);
-  if (j == nO - 1) {
-    int64_t t0 = static_cast<int64_t>(o) + 1;
-    t0 = t0 < 0 ? 0 : (t0 > K ? K : t0);
-    for (int64_t k = t0 + threadIdx.x; k < K; k += kMomThreads) r[k] = div_rn(1.0f, s[k]);
+  if (lane < 8) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) red[wave][lane * 8 + c] = cm[c];
   }
-}
-
-__global__ __launch_bounds__(kMomThreads) void reciprocal_kernel(const float* __restrict__ s,
-                                                                 float* __restrict__ r, int64_t K) {
-  const int64_t k = static_cast<int64_t>(blockIdx.x) * kMomThreads + threadIdx.x;
-  if (k < K) r[k] = div_rn(1.0f, s[k]);
+  __syncthreads();
+  if (tid < 64) {
+    float c = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kStripThreads / 64; ++w) c = fmaxf(c, red[w][tid]);
+    const int64_t k = strip * 64 + tid;
+    const int own = owner[tid];
+    if (own != 0) {
+      const float wm = wmax[own - 1];
+      float beta = 1.0f;
+      if (wm != 0.0f) beta = fmaxf(1.0f, sqrt_rn(div_rn(c, wm)));
+      const float g1 = sub_rn(1.0f, gamma);
+      const float sn = add_rn(mul_rn(gamma, s[k]), mul_rn(g1, beta));
+      s[k] = sn;
+      r[k] = div_rn(1.0f, sn);
+    } else {
+      r[k] = div_rn(1.0f, s[k]);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kMomThreads) void row_absmax_kernel(const uint16_t* __restrict__ w,
@@ -147,11 +176,10 @@ extern "C" qlin_status qlin_momentum_update(const uint16_t* x, int64_t M, int64_
     QLIN_PTR(O);
     QLIN_PTR(wmax_O);
     if (M > 0) QLIN_PTR(x);
-    momentum_kernel<<<dim3(nO), kMomThreads, 0, as_stream(stream)>>>(x, M, K, O, nO, wmax_O, gamma, s, r);
-  } else {
-    reciprocal_kernel<<<dim3(static_cast<unsigned>((K + kMomThreads - 1) / kMomThreads)), kMomThreads, 0,
-                        as_stream(stream)>>>(s, r, K);
   }
+  QLIN_REQUIRE(K / 64 <= 0x7fffffffLL, QLIN_ERR_SHAPE, "K too large");
+  momentum_kernel<<<dim3(static_cast<unsigned>(K / 64)), kStripThreads, 0, as_stream(stream)>>>(
+      x, M, K, O, nO, wmax_O, gamma, s, r);
   QLIN_LAUNCH_CHECK("momentum_kernel");
   return QLIN_OK;
 }
