@@ -198,8 +198,12 @@ class QuaffLayer:
         return 2 * self.M * self.nO * self.N
 
     def gemm_bytes(self):
-        M, K, N, nO = self.M, self.K, self.N, self.nO
-        return M * K + K * N + 4 * M + 2 * N + M * nO + 4 * nO + 4 * K + 2 * nO * N + 2 * M * N
+        """Operands of the fused GEMM, each counted once: codes, packed int8
+        weights, token and column steps, the compensation operand xO and the
+        packed fp16 W_O (both padded to ldO rows), and the fp16 output."""
+        M, K, N = self.M, self.K, self.N
+        ldO = self.q.qlin_outlier_ld(self.nO)
+        return M * K + K * N + 4 * M + 2 * N + 2 * M * ldO + 2 * ldO * N + 2 * M * N
 
 
 def cpu_baseline(layer, budget_s=12.0, rows=128):
