@@ -7,9 +7,11 @@
 // quantization kernel as xO[m, j] = fp16(q[m, O[j]] * (s[O[j]] - 1)) with a
 // row stride ldO (a multiple of 16, zero padded), so each A fragment is one
 // 16-byte load; W_O arrives packed in fragment order (layout.hpp).  The
-// accumulation is fp32, added onto fragments that already hold acc * sw; the
+// accumulation is fp32, onto fragments that already hold acc * sw; the
 // caller multiplies by the token step sa[m] afterwards.
 #pragma once
+
+#include <utility>
 
 #include "common.hpp"
 
@@ -81,4 +83,62 @@ __device__ __forceinline__ void comp_accumulate(v16f (&f)[TM][NT], const uint16_
   }
 }
 
+// As comp_accumulate, with the activation side already staged in LDS: rows
+// m0 + [0, 32*TM) of xO at a pitch of `pitch` bytes (xlds), nj k steps of 16.
+// The steps run in blocks of D; the W_O fragments of block b + 1 are loaded
+// into the other register set before block b's matrix-core work, so each
+// load has a whole block of cover.  Steps past nj (padding up to an even
+// number of blocks) use zero activation fragments: adding 0 * w_O leaves an
+// fp32 sum unchanged.
+template <int TM, int NT>
+__device__ __forceinline__ void comp_accumulate_lds(v16f (&f)[TM][NT], const uint8_t* xlds, int pitch, int nj,
+                                                    const uint8_t* __restrict__ WOp, int64_t N, int64_t nt32) {
+  constexpr int D = 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t tiles32 = N / 32;
+  const uint8_t* arow = xlds + (lane & 31) * pitch + 16 * (lane >> 5);
+  const uint8_t* bcol = WOp + (nt32 << 10) + lane * 16;
+  auto load_block = [&](int blk, v8h (&bp)[D][NT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      int js = blk * D + d;
+      js = js < nj ? js : nj - 1;  // padding steps: a harmless reload
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        bp[d][nt] = *reinterpret_cast<const v8h*>(bcol + ((static_cast<int64_t>(js) * tiles32 + nt) << 10));
+    }
+  };
+  auto mma_block = [&](int blk, const v8h (&bp)[D][NT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int js = blk * D + d;
+      const bool real = js < nj;
+      const int jr = real ? js : nj - 1;
+      v8h ap[TM];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const v8h a = *reinterpret_cast<const v8h*>(arow + tm * 32 * pitch + 32 * jr);
+        ap[tm] = real ? a : v8h{};
+      }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          f[tm][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bp[d][nt], ap[tm], f[tm][nt], 0, 0, 0);
+    }
+  };
+  const int nb = (nj + D - 1) / D;
+  v8h b0[D][NT], b1[D][NT];
+  load_block(0, b0);
+  for (int blk = 0; blk < nb; blk += 2) {
+    load_block(blk + 1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_block(blk, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_block(blk + 2, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_block(blk + 1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 }  // namespace qlin

@@ -137,19 +137,6 @@ __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
 
 // ---------------------------------------------------------------- epilogue
 template <BOp B>
-__device__ __forceinline__ int32_t finish_acc(int32_t raw, const GemmArgs& g, int64_t m, int64_t n) {
-  if constexpr (B == BOp::W4Shift) {
-    return raw >> 4;  // every product is 16 * q * q4: the division is exact
-  } else if constexpr (B == BOp::W4U) {
-    const int64_t za = g.za[m], zw = g.zw[n];
-    const int64_t v = static_cast<int64_t>(raw) - zw * g.rowsum[m] - za * g.colsum[n] + g.K * za * zw;
-    return static_cast<int32_t>(v);
-  } else {
-    return raw;
-  }
-}
-
-template <BOp B>
 __device__ __forceinline__ float col_scale(const GemmArgs& g, int64_t n) {
   if constexpr (B == BOp::W4U)
     return g.sw_f[n];
@@ -238,100 +225,95 @@ __device__ __forceinline__ void store_a(uint8_t* buf, int lds_a, const v4i (&ra)
   }
 }
 
-// B of stage s for this wave: 32-column tiles nt32 and nt32 + 1.
-template <BOp B, AOp A, int TM>
-__device__ __forceinline__ void load_b(const TilePtrs<B, A, TM>& p, int64_t tiles_n, int64_t N, int s,
-                                       v4i (&rb)[Tile<B, A, TM>::kNB], v2h (&rr)[2]) {
+// Part KS (k step KS of the stage) of the B loads of stage s for this wave:
+// 32-column tiles nt32 and nt32 + 1.  int8 weights: one tile per k step and
+// column tile; int4 weights: one tile holds two k steps, so part KS loads
+// tile (kp = KS >> 1, nt = KS & 1), and the per-group ratios come with part 0.
+template <BOp B, AOp A, int TM, int KS>
+__device__ __forceinline__ void load_b_part(const TilePtrs<B, A, TM>& p, int64_t tiles_n, int64_t N, int s,
+                                            v4i (&rb)[Tile<B, A, TM>::kNB], v2h (&rr)[2]) {
   if constexpr (B == BOp::W8) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        rb[ks * 2 + nt] = *reinterpret_cast<const v4i*>(p.b + ((static_cast<int64_t>(4 * s + ks) * tiles_n + nt) << 10));
+    for (int nt = 0; nt < 2; ++nt)
+      rb[KS * 2 + nt] = *reinterpret_cast<const v4i*>(p.b + ((static_cast<int64_t>(4 * s + KS) * tiles_n + nt) << 10));
   } else {
+    constexpr int kp = KS >> 1, nt = KS & 1;
+    rb[kp * 2 + nt] = *reinterpret_cast<const v4i*>(p.b + ((static_cast<int64_t>(2 * s + kp) * tiles_n + nt) << 10));
+    if constexpr (B == BOp::W4Group && KS == 0) {
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        rb[kp * 2 + nt] = *reinterpret_cast<const v4i*>(p.b + ((static_cast<int64_t>(2 * s + kp) * tiles_n + nt) << 10));
-    if constexpr (B == BOp::W4Group) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const _Float16 r = __builtin_bit_cast(_Float16, p.ratio[static_cast<int64_t>(s) * N + nt * 32]);
-        rr[nt] = v2h{r, r};
+      for (int n2 = 0; n2 < 2; ++n2) {
+        const _Float16 r = __builtin_bit_cast(_Float16, p.ratio[static_cast<int64_t>(s) * N + n2 * 32]);
+        rr[n2] = v2h{r, r};
       }
     }
   }
 }
 
 template <BOp B, AOp A, int TM>
-__device__ __forceinline__ void compute_stage(const uint8_t* buf, const v4i (&rb)[Tile<B, A, TM>::kNB],
-                                              const v2h (&rr)[2], v16i (&acc)[TM][2]) {
-  const int lane = threadIdx.x & 63;
-  const int arow = lane & 31, ahalf = lane >> 5;
-  const uint8_t* abuf = buf + arow * kBK;
-  v4i bf[2][4];  // [nt][k step]
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    if constexpr (B == BOp::W8) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bf[nt][ks] = rb[ks * 2 + nt];
-    } else {
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp) unpack_w4v<B>(rb[kp * 2 + nt], rr[nt], bf[nt][2 * kp], bf[nt][2 * kp + 1]);
-    }
-  }
-  v4i af[2][TM];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-    af[0][tm] = *reinterpret_cast<const v4i*>(abuf + tm * 32 * kBK + ((ahalf ^ swz_key(arow)) << 4));
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (ks + 1 < 4) {
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-        af[(ks + 1) & 1][tm] =
-            *reinterpret_cast<const v4i*>(abuf + tm * 32 * kBK + (((2 * (ks + 1) + ahalf) ^ swz_key(arow)) << 4));
-    }
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[tm][nt] = mfma_i8(bf[nt][ks], af[ks & 1][tm], acc[tm][nt]);
-  }
+__device__ __forceinline__ void load_b(const TilePtrs<B, A, TM>& p, int64_t tiles_n, int64_t N, int s,
+                                       v4i (&rb)[Tile<B, A, TM>::kNB], v2h (&rr)[2]) {
+  load_b_part<B, A, TM, 0>(p, tiles_n, N, s, rb, rr);
+  load_b_part<B, A, TM, 1>(p, tiles_n, N, s, rb, rr);
+  load_b_part<B, A, TM, 2>(p, tiles_n, N, s, rb, rr);
+  load_b_part<B, A, TM, 3>(p, tiles_n, N, s, rb, rr);
 }
 
-// Issue order of one K stage.  A wave is alone on its SIMD and issues in
-// order, so a burst of global loads or LDS traffic that fills a queue stalls
-// the matrix-core instructions behind it.  The scheduler is told to emit the
-// stage as pairs of MFMAs, each followed by its share of the stage's memory
-// instructions: the LDS fragment reads of the next k step, the global
-// prefetch loads and the LDS stores of the next activation stage.
+// Chunks [P * n / 2, (P + 1) * n / 2) of this thread's A loads of stage s.
+template <BOp B, AOp A, int TM, int P>
+__device__ __forceinline__ void load_a_half(const TilePtrs<B, A, TM>& p, int s, v4i (&ra)[Tile<B, A, TM>::kAChunks]) {
+  constexpr int n = Tile<B, A, TM>::kAChunks, stage_bytes = (A == AOp::I8) ? kBK : kBK / 2;
+  static_assert(n % 2 == 0, "A chunks are loaded in two halves");
+#pragma unroll
+  for (int i = P * n / 2; i < (P + 1) * n / 2; ++i)
+    ra[i] = *reinterpret_cast<const v4i*>(p.a[i] + static_cast<int64_t>(s) * stage_bytes);
+}
+
+// A fragments of k step ks (32 k) of an LDS stage: rows 32*tm + (lane & 31),
+// 16-byte half (lane >> 5).
+template <int TM>
+__device__ __forceinline__ void read_frags(const uint8_t* buf, int ks, v4i (&af)[TM]) {
+  const int lane = threadIdx.x & 63;
+  const int arow = lane & 31, ahalf = lane >> 5;
+  const uint8_t* abuf = buf + arow * kBK + (((2 * ks + ahalf) ^ swz_key(arow)) << 4);
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) af[tm] = *reinterpret_cast<const v4i*>(abuf + tm * 32 * kBK);
+}
+
 template <int Mask, int N>
 __device__ __forceinline__ void sched_group() {
   if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(Mask, N, 0);
 }
 
-template <BOp B, AOp A, int TM, int P>
-__device__ __forceinline__ void sched_pair() {
-  using T = Tile<B, A, TM>;
-  constexpr int kPairs = 4 * TM;
-  constexpr int kVmem = T::kNB + T::kAChunks + (B == BOp::W4Group ? 2 : 0);
-  constexpr int kDsWrite = (A == AOp::I8) ? T::kAChunks : 2 * T::kAChunks;
-  sched_group<0x008, 2>();                                          // MFMA
-  sched_group<0x100, (P < 3 * TM) ? 1 : 0>();                       // LDS read
-  sched_group<0x020, (P + 1) * kVmem / kPairs - P * kVmem / kPairs>();        // global load
-  if constexpr (A == AOp::U4) {
-    constexpr int q0 = 3 * kPairs / 4, n = kPairs - q0;  // LDS writes in the last quarter
-    sched_group<0x200, (P < q0) ? 0 : ((P - q0 + 1) * kDsWrite / n - (P - q0) * kDsWrite / n)>();
-  } else {
-    sched_group<0x200, (P + 1) * kDsWrite / kPairs - P * kDsWrite / kPairs>();  // LDS write
-  }
+// Issue order of one k step (2*TM MFMAs).  A wave is alone on its SIMD and
+// issues in order, so a burst of memory instructions that fills a queue
+// stalls the matrix-core instructions behind it: the next k step's fragment
+// reads go first (a full k step of cover), then pairs of MFMAs, each pair
+// followed by its share of the global loads and LDS stores of the k step.
+template <int TM, int NVM, int NDS, int P>
+__device__ __forceinline__ void sched_kpair() {
+  sched_group<0x008, 2>();                                       // MFMA
+  sched_group<0x020, (P + 1) * NVM / TM - P * NVM / TM>();       // global load
+  sched_group<0x200, (P + 1) * NDS / TM - P * NDS / TM>();       // LDS write
 }
 
-template <BOp B, AOp A, int TM, int... Ps>
-__device__ __forceinline__ void stage_schedule(std::integer_sequence<int, Ps...>) {
-  sched_group<0x100, TM>();  // the first k step's fragments
-  (sched_pair<B, A, TM, Ps>(), ...);
+template <int TM, int NVM, int NDS, int... Ps>
+__device__ __forceinline__ void sched_kstep(std::integer_sequence<int, Ps...>) {
+  sched_group<0x100, TM>();  // LDS fragment reads of the next k step
+  (sched_kpair<TM, NVM, NDS, Ps>(), ...);
+}
+
+// Stage barrier.  The last TM LDS operations of the wave are the fragment
+// reads of the next stage (from a buffer completed before the previous
+// barrier) and may stay in flight; everything before them -- in particular
+// this stage's stores of a future stage -- has completed, since LDS
+// operations of a wave complete in order.
+template <int TM>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(TM == 4 || TM == 8, "lgkmcnt immediate");
+  if constexpr (TM == 4)
+    asm volatile("s_waitcnt lgkmcnt(4)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");
 }
 
 // Tile index -> (tile row, tile column): XCD-contiguous blocks, groups of 4 rows.
@@ -349,10 +331,27 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
   tn_idx = r / gm;
 }
 
-template <BOp B, AOp A, int TM, int BD, bool COMP>
+// COMP: 0 no compensation term; 1 compensation with xO read from memory;
+// 2 compensation with the tile's xO rows staged in LDS during the K loop
+// (ldO <= kXOMaxLd).
+constexpr int kXOMaxLd = 384;
+
+template <BOp B, AOp A, int TM, int BD, int COMP>
 __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
   using T = Tile<B, A, TM>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * T::kStage];
+  // Three activation stages, then the epilogue constants of the tile: the
+  // token steps (and W4A4 zero points / row sums) of its BM rows and the
+  // column steps (and W4A4 zero points / column sums) of its 256 columns.
+  constexpr int kRowC = (B == BOp::W4U) ? 3 : 1, kColC = (B == BOp::W4U) ? 3 : 1;
+  constexpr int kXO = (COMP == 2) ? T::BM * (2 * kXOMaxLd + 16) : 0;  // staged xO rows
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * T::kStage + kXO + 4 * (kRowC * T::BM + kColC * kBN)];
+  [[maybe_unused]] uint8_t* const xlds = lds + 3 * T::kStage;
+  float* const c_sa = reinterpret_cast<float*>(lds + 3 * T::kStage + kXO);
+  [[maybe_unused]] int32_t* const c_za = reinterpret_cast<int32_t*>(c_sa + T::BM);
+  [[maybe_unused]] int32_t* const c_rs = c_za + T::BM;
+  float* const c_sw = c_sa + kRowC * T::BM;
+  [[maybe_unused]] int32_t* const c_zw = reinterpret_cast<int32_t*>(c_sw + kBN);
+  [[maybe_unused]] int32_t* const c_cs = c_zw + kBN;
   const int64_t tiles_m = (g.M + T::BM - 1) / T::BM, tiles_n = (g.N + kBN - 1) / kBN;
   int64_t tmi, tni;
   tile_coords(tiles_m, tiles_n, tmi, tni);
@@ -376,67 +375,171 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
     for (int b = 0; b < 2; ++b) acc[a][b] = v16i{};
 
   const int S = static_cast<int>(g.K / kBK);
-  // Operand t (stage t of K) lives in B register set t % NBS (NBS = BD + 1)
-  // and in A register set / LDS buffer t % 2.  Stage s loads B(s+BD) and
-  // A(s+2) before its matrix-core work and stores A(s+1) into LDS after it,
-  // so weight loads have BD stages and activation loads about two stages of
-  // work to arrive.
+  // Stage t of K: its weights live in B register set t % NBS (NBS = BD + 1),
+  // loaded BD stages ahead; its activations in LDS buffer t % 3.  Stage s
+  // reads buffer s % 3 and, at its last k step, the first fragments of
+  // buffer (s+1) % 3; it stores A(s+2) (held in A register set s % 2 since
+  // the previous stage) into buffer (s+2) % 3, and loads A(s+3) into set
+  // (s+1) % 2.  The buffer written during stage s is read only after the
+  // barriers ending stages s and s+1, and the one it overwrites was last read
+  // before the barrier ending stage s-1.
   constexpr int NBS = BD + 1;
   v4i ra[2][T::kAChunks];
   v4i rb[NBS][T::kNB];
   v2h rr[NBS][2];
-  load_a<B, A, TM>(p, 0, ra[0]);
-#pragma unroll
-  for (int j = 0; j < BD; ++j) load_b<B, A, TM>(p, b_tiles, g.N, j < S ? j : S - 1, rb[j], rr[j]);
-  load_a<B, A, TM>(p, S > 1 ? 1 : 0, ra[1]);
-  store_a<B, A, TM>(lds, p.lds_a, ra[0]);
-  lds_barrier();
-
-  auto stage = [&](auto jb, auto ja, int st) __attribute__((always_inline)) {
-    constexpr int JB = decltype(jb)::value, JA = decltype(ja)::value;
-    const int sb = (st + BD < S) ? st + BD : S - 1;
-    const int s2 = (st + 2 < S) ? st + 2 : S - 1;
-    if constexpr (A == AOp::U4) {
-      // int4 activations: their loads go first and their LDS stores last,
-      // which gives the stores a full stage of latency cover.
-      load_a<B, A, TM>(p, s2, ra[JA]);
-      load_b<B, A, TM>(p, b_tiles, g.N, sb, rb[(JB + BD) % NBS], rr[(JB + BD) % NBS]);
+  v4i af[2][TM];
+  // The epilogue constants are fetched first, with the first operands: they
+  // arrive during the prologue instead of costing a round trip at the end.
+  // Thread t takes column n0 + t and, if t < BM, row m0 + t (both clamped).
+  float k_sa = 0.0f, k_sw;
+  [[maybe_unused]] int32_t k_za = 0, k_rs = 0, k_zw = 0, k_cs = 0;
+  {
+    const int t = threadIdx.x;
+    int64_t mc = m0 + (t < T::BM ? t : 0);
+    mc = mc < g.M ? mc : g.M - 1;
+    int64_t nc = n0 + t;
+    nc = nc < g.N ? nc : g.N - 1;
+    k_sa = g.sa[mc];
+    if constexpr (B == BOp::W4U) {
+      k_za = g.za[mc];
+      k_rs = g.rowsum[mc];
+      k_sw = g.sw_f[nc];
+      k_zw = g.zw[nc];
+      k_cs = g.colsum[nc];
     } else {
-      load_b<B, A, TM>(p, b_tiles, g.N, sb, rb[(JB + BD) % NBS], rr[(JB + BD) % NBS]);
-      load_a<B, A, TM>(p, s2, ra[JA]);
+      k_sw = h2f(g.sw_h[nc]);
     }
-    compute_stage<B, A, TM>(lds + JA * T::kStage, rb[JB], rr[JB], acc);
-    store_a<B, A, TM>(lds + (1 - JA) * T::kStage, p.lds_a, ra[1 - JA]);
-    stage_schedule<B, A, TM>(std::make_integer_sequence<int, 4 * TM>{});
-    __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();
+  }
+  auto clamp_s = [S](int t) { return t < S ? t : S - 1; };
+  load_a<B, A, TM>(p, 0, ra[0]);
+  load_a<B, A, TM>(p, clamp_s(1), ra[1]);
+#pragma unroll
+  for (int j = 0; j < BD; ++j) load_b<B, A, TM>(p, b_tiles, g.N, clamp_s(j), rb[j], rr[j]);
+  store_a<B, A, TM>(lds, p.lds_a, ra[0]);
+  store_a<B, A, TM>(lds + T::kStage, p.lds_a, ra[1]);
+  load_a<B, A, TM>(p, clamp_s(2), ra[0]);
+  {
+    const int t = threadIdx.x;
+    if (t < T::BM) {
+      c_sa[t] = k_sa;
+      if constexpr (B == BOp::W4U) {
+        c_za[t] = k_za;
+        c_rs[t] = k_rs;
+      }
+    }
+    c_sw[t] = k_sw;
+    if constexpr (B == BOp::W4U) {
+      c_zw[t] = k_zw;
+      c_cs[t] = k_cs;
+    }
+  }
+  // Compensation operand, COMP == 2: the tile's xO rows (BM x ldO fp16,
+  // 16 * ldO 16-byte chunks in row-major order) move into LDS one round of
+  // 256 chunks per stage, chunk 256 j + t of round j by thread t; the rows
+  // sit at a pitch of 2 ldO + 16 bytes, so the 16 rows of a fragment read
+  // fall on distinct banks.  Round j is loaded during stage j - 1 and stored
+  // during stage j (rounds past the last one repeat it).
+  [[maybe_unused]] const int xpitch = 2 * g.ldO + 16, xrounds = g.ldO / 16, xcpr = g.ldO / 8;
+  [[maybe_unused]] v4i xr[2];
+  auto xo_load = [&](int j, v4i& v) __attribute__((always_inline)) {
+    const int c = 256 * j + static_cast<int>(threadIdx.x), row = c / xcpr, cc = c - row * xcpr;
+    int64_t m = m0 + row;
+    m = m < g.M ? m : g.M - 1;
+    v = *reinterpret_cast<const v4i*>(g.xO + m * g.ldO + 8 * cc);
+  };
+  auto xo_store = [&](int j, const v4i& v) __attribute__((always_inline)) {
+    const int c = 256 * j + static_cast<int>(threadIdx.x), row = c / xcpr, cc = c - row * xcpr;
+    *reinterpret_cast<v4i*>(xlds + row * xpitch + 16 * cc) = v;
+  };
+  if constexpr (COMP == 2) xo_load(0, xr[1]);
+  lds_barrier();
+  read_frags<TM>(lds, 0, af[0]);
+
+  constexpr int kVmA = T::kAChunks / 2;                                  // A loads in k steps 0 and 1
+  constexpr int kVmB = (B == BOp::W8) ? 2 : 1;                           // B loads per k step
+  constexpr int kDsW = (A == AOp::I8) ? T::kAChunks : 2 * T::kAChunks;   // LDS stores in k step 2
+  auto stage = [&](auto jb, auto ja, auto jl, int st) __attribute__((always_inline)) {
+    constexpr int JB = decltype(jb)::value, JA = decltype(ja)::value, JL = decltype(jl)::value;
+    const int sb = clamp_s(st + BD), s3 = clamp_s(st + 3);
+    const uint8_t* const cur = lds + JL * T::kStage;
+    const uint8_t* const nxt = lds + ((JL + 1) % 3) * T::kStage;
+    uint8_t* const fut = lds + ((JL + 2) % 3) * T::kStage;
+    v4i (&rbn)[T::kNB] = rb[(JB + BD) % NBS];
+    v2h (&rrn)[2] = rr[(JB + BD) % NBS];
+    [[maybe_unused]] v4i bq[2][2];  // int4 weights: [nt][k step & 1], unpacked two k steps at a time
+    auto kstep = [&](auto ksc) __attribute__((always_inline)) {
+      constexpr int KS = decltype(ksc)::value;
+      if constexpr (KS < 3)
+        read_frags<TM>(cur, KS + 1, af[(KS + 1) & 1]);
+      else
+        read_frags<TM>(nxt, 0, af[0]);
+      load_b_part<B, A, TM, KS>(p, b_tiles, g.N, sb, rbn, rrn);
+      if constexpr (KS == 0) load_a_half<B, A, TM, 0>(p, s3, ra[1 - JA]);
+      if constexpr (KS == 1) load_a_half<B, A, TM, 1>(p, s3, ra[1 - JA]);
+      if constexpr (KS == 2) store_a<B, A, TM>(fut, p.lds_a, ra[JA]);
+      if constexpr (COMP == 2 && KS == 0) xo_load(st + 1 < xrounds ? st + 1 : xrounds - 1, xr[JA]);
+      if constexpr (COMP == 2 && KS == 2) xo_store(st < xrounds ? st : xrounds - 1, xr[1 - JA]);
+      v4i bf[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        if constexpr (B == BOp::W8) {
+          bf[nt] = rb[JB][KS * 2 + nt];
+        } else {
+          if constexpr ((KS & 1) == 0) unpack_w4v<B>(rb[JB][(KS >> 1) * 2 + nt], rr[JB][nt], bq[nt][0], bq[nt][1]);
+          bf[nt] = bq[nt][KS & 1];
+        }
+      }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[tm][nt] = mfma_i8(bf[nt], af[KS & 1][tm], acc[tm][nt]);
+      constexpr int nvm = kVmB + ((KS < 2) ? kVmA : 0) + ((B == BOp::W4Group && KS == 0) ? 2 : 0) +
+                          ((COMP == 2 && KS == 0) ? 1 : 0);
+      sched_kstep<TM, nvm, (KS == 2) ? kDsW + (COMP == 2 ? 1 : 0) : 0>(std::make_integer_sequence<int, TM>{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    kstep(std::integral_constant<int, 0>{});
+    kstep(std::integral_constant<int, 1>{});
+    kstep(std::integral_constant<int, 2>{});
+    kstep(std::integral_constant<int, 3>{});
+    stage_barrier<TM>();
     __builtin_amdgcn_sched_barrier(0);
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
+  // The register-set and buffer rotations repeat every 6 stages.
   int s = 0;
   if constexpr (BD == 2) {
     for (; s + 5 < S; s += 6) {
-      stage(C0{}, C0{}, s);
-      stage(C1{}, C1{}, s + 1);
-      stage(C2{}, C0{}, s + 2);
-      stage(C0{}, C1{}, s + 3);
-      stage(C1{}, C0{}, s + 4);
-      stage(C2{}, C1{}, s + 5);
+      stage(C0{}, C0{}, C0{}, s);
+      stage(C1{}, C1{}, C1{}, s + 1);
+      stage(C2{}, C0{}, C2{}, s + 2);
+      stage(C0{}, C1{}, C0{}, s + 3);
+      stage(C1{}, C0{}, C1{}, s + 4);
+      stage(C2{}, C1{}, C2{}, s + 5);
     }
     const int rem = S - s;  // 0..5 stages left, uniform
-    if (rem > 0) stage(C0{}, C0{}, s);
-    if (rem > 1) stage(C1{}, C1{}, s + 1);
-    if (rem > 2) stage(C2{}, C0{}, s + 2);
-    if (rem > 3) stage(C0{}, C1{}, s + 3);
-    if (rem > 4) stage(C1{}, C0{}, s + 4);
+    if (rem > 0) stage(C0{}, C0{}, C0{}, s);
+    if (rem > 1) stage(C1{}, C1{}, C1{}, s + 1);
+    if (rem > 2) stage(C2{}, C0{}, C2{}, s + 2);
+    if (rem > 3) stage(C0{}, C1{}, C0{}, s + 3);
+    if (rem > 4) stage(C1{}, C0{}, C1{}, s + 4);
   } else {
-    for (; s + 1 < S; s += 2) {
-      stage(C0{}, C0{}, s);
-      stage(C1{}, C1{}, s + 1);
+    for (; s + 5 < S; s += 6) {
+      stage(C0{}, C0{}, C0{}, s);
+      stage(C1{}, C1{}, C1{}, s + 1);
+      stage(C0{}, C0{}, C2{}, s + 2);
+      stage(C1{}, C1{}, C0{}, s + 3);
+      stage(C0{}, C0{}, C1{}, s + 4);
+      stage(C1{}, C1{}, C2{}, s + 5);
     }
-    if (s < S) stage(C0{}, C0{}, s);
+    const int rem = S - s;
+    if (rem > 0) stage(C0{}, C0{}, C0{}, s);
+    if (rem > 1) stage(C1{}, C1{}, C1{}, s + 1);
+    if (rem > 2) stage(C0{}, C0{}, C2{}, s + 2);
+    if (rem > 3) stage(C1{}, C1{}, C0{}, s + 3);
+    if (rem > 4) stage(C0{}, C0{}, C1{}, s + 4);
   }
 
   // Epilogue.  The weight fragment is the first matrix-core operand, so each
@@ -447,52 +550,68 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
   // term, scales by the token step, converts to fp16, stages the 32 x 64
   // block in its own LDS rows and writes it out as full 128-byte row
   // segments, 16 bytes per lane.
+  const int r = lane & 31, h = lane >> 5;
+  // With the compensation term, the (final, int8-weight) accumulators are
+  // reported if asked and then continue in fp32 as acc * sw, onto which the
+  // compensation products accumulate: only one set of accumulation
+  // registers is live at a time.
   [[maybe_unused]] v16f cf[COMP ? TM : 1][2];
-  if constexpr (COMP) {
+  if constexpr (COMP != 0) {
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+    for (int tm = 0; tm < TM; ++tm) {
+      const int64_t m = m0 + 32 * tm + r;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) cf[a][b] = v16f{};
-    comp_accumulate<TM, 2>(cf, g.xO, g.ldO, g.WOp, g.M, g.N, m0, nt32);
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4f sw = *reinterpret_cast<const v4f*>(c_sw + 64 * wave + 32 * nt + 8 * q + 4 * h);
+          const v4i iv = v4i{acc[tm][nt][4 * q], acc[tm][nt][4 * q + 1], acc[tm][nt][4 * q + 2], acc[tm][nt][4 * q + 3]};
+          if (g.acc != nullptr && live && m < g.M)
+            *reinterpret_cast<v4i*>(g.acc + m * g.N + wcol0 + 32 * nt + 8 * q + 4 * h) = iv;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cf[tm][nt][4 * q + j] = static_cast<float>(iv[j]) * sw[j];
+        }
+    }
+  }
+  if constexpr (COMP == 1) comp_accumulate<TM, 2>(cf, g.xO, g.ldO, g.WOp, g.M, g.N, m0, nt32);
+  if constexpr (COMP == 2) {
+    // Rounds the K loop was too short for (fewer stages than rounds).
+    for (int j = S; j < xrounds; ++j) {
+      v4i v;
+      xo_load(j, v);
+      xo_store(j, v);
+    }
+    lds_barrier();  // the staged xO rows are complete
+    comp_accumulate_lds<TM, 2>(cf, xlds, xpitch, xrounds, g.WOp, g.N, nt32);
   }
   lds_barrier();  // every wave has finished reading the activation stages
   if (!live) return;
   constexpr int kOutPitch = 144;  // bytes per staged row: 128 + 16 spreads rows over the banks
-  static_assert(4 * 32 * kOutPitch <= 2 * T::kStage, "output staging exceeds the LDS buffers");
+  static_assert(4 * 32 * kOutPitch <= 3 * T::kStage, "output staging exceeds the LDS buffers");
   uint8_t* const out_lds = lds + wave * 32 * kOutPitch;
-  const int r = lane & 31, h = lane >> 5;
   const bool want_acc = g.acc != nullptr;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const int64_t m = m0 + 32 * tm + r;
-    const int64_t mc = m < g.M ? m : g.M - 1;
-    const float sam = g.sa[mc];
     // W4A4 zero points: acc = raw - zw*(rowsum - K*za) - za*colsum, evaluated
     // in wrapping 32-bit arithmetic (exact: the true value fits int32).
-    [[maybe_unused]] uint32_t za = 0, rk = 0;
+    const float sam = c_sa[32 * tm + r];
+    [[maybe_unused]] uint32_t za = 0, rkt = 0;
     if constexpr (B == BOp::W4U) {
-      za = static_cast<uint32_t>(g.za[mc]);
-      rk = static_cast<uint32_t>(g.rowsum[mc]) - static_cast<uint32_t>(g.K) * za;
+      za = static_cast<uint32_t>(c_za[32 * tm + r]);
+      rkt = static_cast<uint32_t>(c_rs[32 * tm + r]) - static_cast<uint32_t>(g.K) * za;
     }
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t n = wcol0 + 32 * nt + 8 * q + 4 * h;  // first of this lane's four columns
-        float sw[4];
-        [[maybe_unused]] v4i zw{}, cs{};
+        const int cb = 64 * wave + 32 * nt + 8 * q + 4 * h;  // the same column within the tile
+        const v4f sw = *reinterpret_cast<const v4f*>(c_sw + cb);
+        [[maybe_unused]] v4i zw, cs;
         if constexpr (B == BOp::W4U) {
-          const v4f swv = *reinterpret_cast<const v4f*>(g.sw_f + n);
-          zw = *reinterpret_cast<const v4i*>(g.zw + n);
-          cs = *reinterpret_cast<const v4i*>(g.colsum + n);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sw[j] = swv[j];
-        } else {
-          const uint2 swh = *reinterpret_cast<const uint2*>(g.sw_h + n);
-          sw[0] = h2f(static_cast<uint16_t>(swh.x & 0xffffu));
-          sw[1] = h2f(static_cast<uint16_t>(swh.x >> 16));
-          sw[2] = h2f(static_cast<uint16_t>(swh.y & 0xffffu));
-          sw[3] = h2f(static_cast<uint16_t>(swh.y >> 16));
+          zw = *reinterpret_cast<const v4i*>(c_zw + cb);
+          cs = *reinterpret_cast<const v4i*>(c_cs + cb);
         }
         v4i iv;
         uint16_t hv[4];
@@ -502,17 +621,20 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
           if constexpr (B == BOp::W4Shift) {
             val >>= 4;  // every product is 16 * q * q4: the division is exact
           } else if constexpr (B == BOp::W4U) {
-            val = static_cast<int32_t>(static_cast<uint32_t>(val) - static_cast<uint32_t>(zw[j]) * rk -
+            val = static_cast<int32_t>(static_cast<uint32_t>(val) - static_cast<uint32_t>(zw[j]) * rkt -
                                        za * static_cast<uint32_t>(cs[j]));
           }
           iv[j] = val;
-          float f = static_cast<float>(val) * sw[j];
-          if constexpr (COMP) f += cf[tm][nt][4 * q + j];
+          float f;
+          if constexpr (COMP != 0)
+            f = cf[tm][nt][4 * q + j];  // acc * sw + compensation
+          else
+            f = static_cast<float>(val) * sw[j];
           hv[j] = f2h(f * sam);
         }
         *reinterpret_cast<uint2*>(out_lds + r * kOutPitch + (32 * nt + 8 * q + 4 * h) * 2) =
             make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
-        if (want_acc && m < g.M) *reinterpret_cast<v4i*>(g.acc + m * g.N + n) = iv;
+        if (COMP == 0 && want_acc && m < g.M) *reinterpret_cast<v4i*>(g.acc + m * g.N + n) = iv;
       }
     // The wave reads back only rows it wrote; LDS operations of one wave
     // complete in order, so no barrier is needed, only a compiler fence.
@@ -522,7 +644,8 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
       const int row = (lane >> 3) + 8 * i, chunk = lane & 7;
       const v4i d = *reinterpret_cast<const v4i*>(out_lds + row * kOutPitch + chunk * 16);
       const int64_t mr = m0 + 32 * tm + row;
-      if (mr < g.M) *reinterpret_cast<v4i*>(g.y + mr * g.N + wcol0 + 8 * chunk) = d;
+      // Streaming store: the output is not read again by this kernel.
+      if (mr < g.M) __builtin_nontemporal_store(d, reinterpret_cast<v4i*>(g.y + mr * g.N + wcol0 + 8 * chunk));
     }
     asm volatile("" ::: "memory");
   }
@@ -626,14 +749,42 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny(GemmArgs g) {
     const int mt = fi / NT, nt = fi % NT;
     if (nt0 + nt >= tiles_n) continue;
     const int64_t n = (nt0 + nt) * 32 + arow;
+    // All constants first, in one batch (a load after a store waits for its
+    // own round trip, since the store may alias it).
     const float sw = col_scale<B>(g, n);
+    float sam[16];
+    [[maybe_unused]] int32_t zam[16], rsm[16];
+    [[maybe_unused]] int32_t zwn = 0, csn = 0;
+    if constexpr (B == BOp::W4U) {
+      zwn = g.zw[n];
+      csn = g.colsum[n];
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      int64_t m = mt * 32 + frag_row(v, lane);
+      m = m < g.M ? m : g.M - 1;
+      sam[v] = g.sa[m];
+      if constexpr (B == BOp::W4U) {
+        zam[v] = g.za[m];
+        rsm[v] = g.rowsum[m];
+      }
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int64_t m = mt * 32 + frag_row(v, lane);
       if (m >= g.M) continue;
-      const int32_t val = finish_acc<B>(red[fi * 16 + v][lane], g, m, n);
+      int32_t val = red[fi * 16 + v][lane];
+      if constexpr (B == BOp::W4Shift) {
+        val >>= 4;  // every product is 16 * q * q4: the division is exact
+      } else if constexpr (B == BOp::W4U) {
+        // Zero-point correction in wrapping 32-bit arithmetic (exact: the
+        // true value fits int32).
+        const uint32_t za = static_cast<uint32_t>(zam[v]), zw = static_cast<uint32_t>(zwn);
+        val = static_cast<int32_t>(static_cast<uint32_t>(val) - zw * static_cast<uint32_t>(rsm[v]) -
+                                   za * static_cast<uint32_t>(csn) + static_cast<uint32_t>(g.K) * za * zw);
+      }
       if (g.acc != nullptr) g.acc[m * g.N + n] = val;
-      g.y[m * g.N + n] = f2h(static_cast<float>(val) * sw * g.sa[m]);
+      g.y[m * g.N + n] = f2h(static_cast<float>(val) * sw * sam[v]);
     }
   }
 }
@@ -645,11 +796,11 @@ void launch_skinny(const GemmArgs& g, hipStream_t st) {
   gemm_skinny<B, A, MT, NT, WAVES, U><<<grid, 64 * WAVES, 0, st>>>(g);
 }
 
-template <BOp B, AOp A, int TM, bool COMP>
+template <BOp B, AOp A, int TM, int COMP>
 qlin_status launch_tile(const GemmArgs& g, hipStream_t st) {
-  // Weight prefetch depth: two stages, except for the per-group requant at
-  // 256-row tiles, whose unpack temporaries leave room for one.
-  constexpr int BD = (B == BOp::W4Group && TM == 8) ? 1 : 2;
+  // Weight prefetch depth: two stages, except at 256-row tiles with int8 or
+  // per-group requantized weights, where register room leaves one.
+  constexpr int BD = ((B == BOp::W8 || B == BOp::W4Group) && TM == 8) ? 1 : 2;
   const int64_t tiles = ((g.M + 32 * TM - 1) / (32 * TM)) * ((g.N + kBN - 1) / kBN);
   QLIN_REQUIRE(tiles <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M=%lld too large", (long long)g.M);
   gemm_tile<B, A, TM, BD, COMP><<<dim3(static_cast<unsigned>(tiles)), kTileThreads, 0, st>>>(g);
@@ -668,13 +819,19 @@ qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
     return QLIN_OK;
   }
   if (comp) {
-    if constexpr (B == BOp::W8 && A == AOp::I8) return launch_tile<B, A, 4, true>(g, st);
+    if constexpr (B == BOp::W8 && A == AOp::I8) {
+      if (g.ldO <= kXOMaxLd) return launch_tile<B, A, 4, 2>(g, st);
+      return launch_tile<B, A, 4, 1>(g, st);
+    }
   }
   // 256-row tiles when they still give every CU a tile: per weight byte
   // streamed (and unpacked) they do twice the matrix-core work.
   const int64_t tiles_n = (g.N + kBN - 1) / kBN;
-  if (((g.M + 255) / 256) * tiles_n >= 256) return launch_tile<B, A, 8, false>(g, st);
-  return launch_tile<B, A, 4, false>(g, st);
+#if EXP_FORCE_TM4
+  return launch_tile<B, A, 4, 0>(g, st);
+#endif
+  if (((g.M + 255) / 256) * tiles_n >= 256) return launch_tile<B, A, 8, 0>(g, st);
+  return launch_tile<B, A, 4, 0>(g, st);
 }
 
 GemmArgs base_args(int64_t M, int64_t N, int64_t K, uint16_t* y, int32_t* acc) {

@@ -228,6 +228,44 @@ def test_gemm_w4a4(q, M, K, N):
     assert_close(host(y), ref["y"], "y")
 
 
+# The tiled kernels unroll their K loop by 6 stages of 128 k with register
+# and buffer rotations: every stage count from 1 to 13 (no full unrolled
+# period, one, two, with every remainder) on a ragged tile grid (M = 130: a
+# partial second tile row; N = 320: a second tile column with one live
+# column group).
+@pytest.mark.parametrize("stages", list(range(1, 14)))
+def test_gemm_tiled_k_depths(q, stages):
+    M, N, K = 130, 320, 128 * stages
+    log(f"tiled K depth: M={M} K={K} N={N}")
+    lin = synth.plain_linear(M, K, N, seed=500 + stages, n_outliers=2)
+    qa, sa, _, _ = q.qlin_quant_act(dev(lin.x))
+    ref = layer.w8a8_forward(lin.x, lin.w)
+    codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 8)
+    y, acc = q.qlin_gemm_w8a8(qa, sa, q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes), sw, N, want_acc=True)
+    assert_equal(host(acc), ref["acc"], "w8a8 acc")
+    assert_close(host(y), ref["y"], "w8a8 y")
+    ref = layer.w4a8_channel_forward(lin.x, lin.w)
+    codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 4)
+    y, acc = q.qlin_gemm_w4a8(qa, sa, q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes), sw, N, want_acc=True)
+    assert_equal(host(acc), ref["acc"], "w4a8 channel acc")
+    assert_close(host(y), ref["y"], "w4a8 channel y")
+    ref = layer.w4a8_group_forward(lin.x, lin.w)
+    codes, gs, cs, ratio = q.qlin_quant_weight_group(dev(lin.w), 128)
+    y, acc = q.qlin_gemm_w4a8(qa, sa, q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes), cs, N, ratio=ratio, group=128,
+                              want_acc=True)
+    assert_equal(host(acc), ref["acc"], "w4a8 group acc")
+    assert_close(host(y), ref["y"], "w4a8 group y")
+    lin = synth.offq_inputs(M=M, K=K, N=N, seed=600 + stages)
+    signs = lin.extra["signs"]
+    ref = layer.offq_forward(lin.x, lin.w, signs)
+    qa4, sa4, za, rs, _ = q.qlin_hadamard_offset(dev(lin.x), dev(signs))
+    codes, sw, zw, csum = q.qlin_quant_weight_offq(dev(lin.w), dev(signs))
+    y, acc = q.qlin_gemm_w4a4(qa4, sa4, za, rs, q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, codes), sw, zw, csum, N,
+                              want_acc=True)
+    assert_equal(host(acc), ref["acc"], "w4a4 acc")
+    assert_close(host(y), ref["y"], "w4a4 y")
+
+
 @pytest.mark.parametrize("M,K,N,nO", [(16, 256, 128, 13), (200, 512, 192, 64), (130, 384, 64, 33),
                                        (300, 256, 320, 16)])
 def test_quaff_fused_and_standalone_compensation(q, M, K, N, nO):
