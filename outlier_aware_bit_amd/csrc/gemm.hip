@@ -331,8 +331,9 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
   tn_idx = r / gm;
 }
 
-// COMP: 0 no compensation term; 1 compensation with xO read from memory;
-// 2 compensation with the tile's xO rows staged in LDS during the K loop
+// COMP: 0 no compensation term; 1 compensation after the K loop with xO read
+// from memory; 2 compensation before the K loop, while the loop's first
+// operands are in flight, with the tile's xO rows staged in LDS
 // (ldO <= kXOMaxLd).
 constexpr int kXOMaxLd = 384;
 
@@ -343,10 +344,13 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
   // token steps (and W4A4 zero points / row sums) of its BM rows and the
   // column steps (and W4A4 zero points / column sums) of its 256 columns.
   constexpr int kRowC = (B == BOp::W4U) ? 3 : 1, kColC = (B == BOp::W4U) ? 3 : 1;
-  constexpr int kXO = (COMP == 2) ? T::BM * (2 * kXOMaxLd + 16) : 0;  // staged xO rows
-  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * T::kStage + kXO + 4 * (kRowC * T::BM + kColC * kBN)];
-  [[maybe_unused]] uint8_t* const xlds = lds + 3 * T::kStage;
-  float* const c_sa = reinterpret_cast<float*>(lds + 3 * T::kStage + kXO);
+  // COMP == 2 stages the tile's xO rows (BM x ldO fp16, unpadded) in the
+  // same space before the activation stages are first written.
+  constexpr int kXO = (COMP == 2) ? T::BM * 2 * kXOMaxLd : 0;
+  constexpr int kMainBytes = (kXO > 3 * T::kStage) ? kXO : 3 * T::kStage;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kMainBytes + 4 * (kRowC * T::BM + kColC * kBN)];
+  [[maybe_unused]] uint8_t* const xlds = lds;
+  float* const c_sa = reinterpret_cast<float*>(lds + kMainBytes);
   [[maybe_unused]] int32_t* const c_za = reinterpret_cast<int32_t*>(c_sa + T::BM);
   [[maybe_unused]] int32_t* const c_rs = c_za + T::BM;
   float* const c_sw = c_sa + kRowC * T::BM;
@@ -411,10 +415,42 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
     }
   }
   auto clamp_s = [S](int t) { return t < S ? t : S - 1; };
+  [[maybe_unused]] v16f cf[COMP ? TM : 1][2];
+  if constexpr (COMP != 0) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) cf[a][b] = v16f{};
+  }
+  if constexpr (COMP == 2) {
+    // The tile's xO rows go straight from memory into LDS (16 * ldO chunks
+    // of 16 bytes in row-major order, 64 consecutive chunks per wave and
+    // load), ahead of the K loop's first operands.
+    const int xcpr = g.ldO / 8, xrounds = g.ldO / 16;
+    for (int j = 0; j < xrounds; ++j) {
+      const int c = 256 * j + 64 * wave + lane, row = c / xcpr, cc = c - row * xcpr;
+      int64_t m = m0 + row;
+      m = m < g.M ? m : g.M - 1;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(g.xO + m * g.ldO + 8 * cc),
+          (__attribute__((address_space(3))) void*)(xlds + (256 * j + 64 * wave) * 16), 16, 0, 0);
+    }
+  }
   load_a<B, A, TM>(p, 0, ra[0]);
   load_a<B, A, TM>(p, clamp_s(1), ra[1]);
 #pragma unroll
   for (int j = 0; j < BD; ++j) load_b<B, A, TM>(p, b_tiles, g.N, clamp_s(j), rb[j], rr[j]);
+  if constexpr (COMP == 2) {
+    // Wait for the xO chunks only: the K loop's loads issued after them may
+    // stay in flight while the compensation runs.
+    constexpr int younger = 2 * T::kAChunks + BD * T::kNB;
+    static_assert(younger < 64, "vmcnt immediate");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(((younger >> 4) << 14) | (15 << 8) | (7 << 4) | (younger & 15));
+    lds_barrier();
+    comp_accumulate_lds<TM, 2>(cf, xlds, 2 * g.ldO, g.ldO / 16, g.WOp, g.N, nt32);
+    lds_barrier();  // every wave has read the staged xO rows
+  }
   store_a<B, A, TM>(lds, p.lds_a, ra[0]);
   store_a<B, A, TM>(lds + T::kStage, p.lds_a, ra[1]);
   load_a<B, A, TM>(p, clamp_s(2), ra[0]);
@@ -433,25 +469,6 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
       c_cs[t] = k_cs;
     }
   }
-  // Compensation operand, COMP == 2: the tile's xO rows (BM x ldO fp16,
-  // 16 * ldO 16-byte chunks in row-major order) move into LDS one round of
-  // 256 chunks per stage, chunk 256 j + t of round j by thread t; the rows
-  // sit at a pitch of 2 ldO + 16 bytes, so the 16 rows of a fragment read
-  // fall on distinct banks.  Round j is loaded during stage j - 1 and stored
-  // during stage j (rounds past the last one repeat it).
-  [[maybe_unused]] const int xpitch = 2 * g.ldO + 16, xrounds = g.ldO / 16, xcpr = g.ldO / 8;
-  [[maybe_unused]] v4i xr[2];
-  auto xo_load = [&](int j, v4i& v) __attribute__((always_inline)) {
-    const int c = 256 * j + static_cast<int>(threadIdx.x), row = c / xcpr, cc = c - row * xcpr;
-    int64_t m = m0 + row;
-    m = m < g.M ? m : g.M - 1;
-    v = *reinterpret_cast<const v4i*>(g.xO + m * g.ldO + 8 * cc);
-  };
-  auto xo_store = [&](int j, const v4i& v) __attribute__((always_inline)) {
-    const int c = 256 * j + static_cast<int>(threadIdx.x), row = c / xcpr, cc = c - row * xcpr;
-    *reinterpret_cast<v4i*>(xlds + row * xpitch + 16 * cc) = v;
-  };
-  if constexpr (COMP == 2) xo_load(0, xr[1]);
   lds_barrier();
   read_frags<TM>(lds, 0, af[0]);
 
@@ -477,8 +494,6 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
       if constexpr (KS == 0) load_a_half<B, A, TM, 0>(p, s3, ra[1 - JA]);
       if constexpr (KS == 1) load_a_half<B, A, TM, 1>(p, s3, ra[1 - JA]);
       if constexpr (KS == 2) store_a<B, A, TM>(fut, p.lds_a, ra[JA]);
-      if constexpr (COMP == 2 && KS == 0) xo_load(st + 1 < xrounds ? st + 1 : xrounds - 1, xr[JA]);
-      if constexpr (COMP == 2 && KS == 2) xo_store(st < xrounds ? st : xrounds - 1, xr[1 - JA]);
       v4i bf[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -493,9 +508,8 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[tm][nt] = mfma_i8(bf[nt], af[KS & 1][tm], acc[tm][nt]);
-      constexpr int nvm = kVmB + ((KS < 2) ? kVmA : 0) + ((B == BOp::W4Group && KS == 0) ? 2 : 0) +
-                          ((COMP == 2 && KS == 0) ? 1 : 0);
-      sched_kstep<TM, nvm, (KS == 2) ? kDsW + (COMP == 2 ? 1 : 0) : 0>(std::make_integer_sequence<int, TM>{});
+      constexpr int nvm = kVmB + ((KS < 2) ? kVmA : 0) + ((B == BOp::W4Group && KS == 0) ? 2 : 0);
+      sched_kstep<TM, nvm, (KS == 2) ? kDsW : 0>(std::make_integer_sequence<int, TM>{});
       __builtin_amdgcn_sched_barrier(0);
     };
     kstep(std::integral_constant<int, 0>{});
@@ -551,12 +565,10 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
   // block in its own LDS rows and writes it out as full 128-byte row
   // segments, 16 bytes per lane.
   const int r = lane & 31, h = lane >> 5;
-  // With the compensation term, the (final, int8-weight) accumulators are
-  // reported if asked and then continue in fp32 as acc * sw, onto which the
-  // compensation products accumulate: only one set of accumulation
-  // registers is live at a time.
-  [[maybe_unused]] v16f cf[COMP ? TM : 1][2];
-  if constexpr (COMP != 0) {
+  // COMP == 1: the (final, int8-weight) accumulators are reported if asked
+  // and then continue in fp32 as acc * sw, onto which the compensation
+  // products accumulate, so that one set of accumulation registers is live.
+  if constexpr (COMP == 1) {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       const int64_t m = m0 + 32 * tm + r;
@@ -572,22 +584,12 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
           for (int j = 0; j < 4; ++j) cf[tm][nt][4 * q + j] = static_cast<float>(iv[j]) * sw[j];
         }
     }
-  }
-  if constexpr (COMP == 1) comp_accumulate<TM, 2>(cf, g.xO, g.ldO, g.WOp, g.M, g.N, m0, nt32);
-  if constexpr (COMP == 2) {
-    // Rounds the K loop was too short for (fewer stages than rounds).
-    for (int j = S; j < xrounds; ++j) {
-      v4i v;
-      xo_load(j, v);
-      xo_store(j, v);
-    }
-    lds_barrier();  // the staged xO rows are complete
-    comp_accumulate_lds<TM, 2>(cf, xlds, xpitch, xrounds, g.WOp, g.N, nt32);
+    comp_accumulate<TM, 2>(cf, g.xO, g.ldO, g.WOp, g.M, g.N, m0, nt32);
   }
   lds_barrier();  // every wave has finished reading the activation stages
   if (!live) return;
   constexpr int kOutPitch = 144;  // bytes per staged row: 128 + 16 spreads rows over the banks
-  static_assert(4 * 32 * kOutPitch <= 3 * T::kStage, "output staging exceeds the LDS buffers");
+  static_assert(4 * 32 * kOutPitch <= kMainBytes, "output staging exceeds the LDS buffers");
   uint8_t* const out_lds = lds + wave * 32 * kOutPitch;
   const bool want_acc = g.acc != nullptr;
 #pragma unroll
@@ -626,15 +628,17 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
           }
           iv[j] = val;
           float f;
-          if constexpr (COMP != 0)
+          if constexpr (COMP == 1)
             f = cf[tm][nt][4 * q + j];  // acc * sw + compensation
+          else if constexpr (COMP == 2)
+            f = static_cast<float>(val) * sw[j] + cf[tm][nt][4 * q + j];
           else
             f = static_cast<float>(val) * sw[j];
           hv[j] = f2h(f * sam);
         }
         *reinterpret_cast<uint2*>(out_lds + r * kOutPitch + (32 * nt + 8 * q + 4 * h) * 2) =
             make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
-        if (COMP == 0 && want_acc && m < g.M) *reinterpret_cast<v4i*>(g.acc + m * g.N + n) = iv;
+        if (COMP != 1 && want_acc && m < g.M) *reinterpret_cast<v4i*>(g.acc + m * g.N + n) = iv;
       }
     // The wave reads back only rows it wrote; LDS operations of one wave
     // complete in order, so no barrier is needed, only a compiler fence.
