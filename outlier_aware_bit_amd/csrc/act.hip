@@ -6,6 +6,8 @@
 // Both are HBM-bound streaming kernels: one workgroup per token, 16-byte
 // loads of 8 fp16 values, the per-token reduction as a wavefront butterfly
 // plus one LDS exchange between waves, and packed stores.
+#include <type_traits>
+
 #include "common.hpp"
 #include "layout.hpp"
 
@@ -57,29 +59,71 @@ __device__ __forceinline__ uint2 sym_codes8(const float (&v)[8], float inv) {
 }
 
 // Per-token symmetric int8: a = max|v|, inv = 127/a, q = clamp(rint(v*inv)).
-// One wavefront per token: the row stays in registers as raw fp16 (up to
-// 16 chunks of 8 per lane), the absmax is a wavefront butterfly, and there is
-// no LDS traffic or block barrier.  Longer rows re-read the tail from cache.
-template <bool HAS_R>
+// One wavefront per token: the row stays in registers as raw fp16 (CH chunks
+// of 8 per lane: 8 up to K = 4096, 16 up to 8192), the absmax is a wavefront
+// butterfly, and there is no block barrier.  Longer rows re-read the tail
+// from cache.
+//
+// Outlier columns (row stride ldO, zero padded): the code of x[m, O[j]], and
+// the compensation operand fp16(code * (s[O[j]] - 1)).  With OL (ldO <= 256
+// and 2K bytes of LDS per wave), O, r[O] and s[O] are fetched before the row
+// is needed, and the row is staged in the wave's own LDS so that its
+// outlier values are read from there; otherwise they are re-read from memory.
+constexpr int kOutlierLdMax = 256;
+
+template <bool HAS_R, bool OL, int CH>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ r, int8_t* __restrict__ q,
     float* __restrict__ scale, const int32_t* __restrict__ O, int nO, int ldO,
     const float* __restrict__ s, int8_t* __restrict__ qO, uint16_t* __restrict__ xO) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t qlds[];
   const int lane = threadIdx.x & 63;
   const int64_t m = static_cast<int64_t>(blockIdx.x) * (kQuantThreads / 64) + (threadIdx.x >> 6);
   if (m >= M) return;
   const uint16_t* xr = x + m * K;
   const int nchunks = static_cast<int>(K / 8);
 
-  v4i raw[kQuantRegChunks];
+  // The row first: chunks c = lane + 64 i (clamped to the row, so that every
+  // load is in range and unconditional).
+  v4i raw[CH];
 #pragma unroll
-  for (int i = 0; i < kQuantRegChunks; ++i) {
+  for (int i = 0; i < CH; ++i) {
     const int c = lane + 64 * i;
-    if (c < nchunks) raw[i] = *reinterpret_cast<const v4i*>(xr + c * 8);
+    raw[i] = *reinterpret_cast<const v4i*>(xr + (c < nchunks ? c : nchunks - 1) * 8);
   }
+  // Outlier bookkeeping of this lane (columns j = lane + 64 i), in flight
+  // with the row.
+  [[maybe_unused]] int oj[kOutlierLdMax / 64];
+  [[maybe_unused]] float rj[kOutlierLdMax / 64], sm1j[kOutlierLdMax / 64];
+  if constexpr (OL) {
+#pragma unroll
+    for (int i = 0; i < kOutlierLdMax / 64; ++i) {
+      const int j = lane + 64 * i;
+      const int o = j < nO ? O[j] : -1;
+      oj[i] = (o >= 0 && o < K) ? o : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kOutlierLdMax / 64; ++i) {
+      const int o = oj[i] >= 0 ? oj[i] : 0;
+      rj[i] = HAS_R ? r[o] : 1.0f;
+      sm1j[i] = (xO != nullptr && oj[i] >= 0) ? sub_rn(s[o], 1.0f) : 0.0f;
+    }
+    // The raw row goes to this wave's LDS for the outlier columns.
+    uint16_t* const rowl = reinterpret_cast<uint16_t*>(qlds + (threadIdx.x >> 6) * 2 * K);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunks) *reinterpret_cast<v4i*>(rowl + c * 8) = raw[i];
+    }
+    for (int c = lane + 64 * CH; c < nchunks; c += 64)
+      *reinterpret_cast<v4i*>(rowl + c * 8) = *reinterpret_cast<const v4i*>(xr + c * 8);
+  }
+
+  // v = x * r (HAS_R: held in registers between the two passes), absmax.
+  [[maybe_unused]] float vr[HAS_R ? CH : 1][8];
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kQuantRegChunks; ++i) {
+  for (int i = 0; i < CH; ++i) {
     const int c = lane + 64 * i;
     if (c < nchunks) {
       float v[8];
@@ -87,9 +131,13 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
       scale_chunk<HAS_R>(r, c, v);
 #pragma unroll
       for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      if constexpr (HAS_R) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vr[i][j] = v[j];
+      }
     }
   }
-  for (int c = lane + 64 * kQuantRegChunks; c < nchunks; c += 64) {
+  for (int c = lane + 64 * CH; c < nchunks; c += 64) {
     float v[8];
     load8_f16(xr + c * 8, v);
     scale_chunk<HAS_R>(r, c, v);
@@ -102,36 +150,60 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
 
   int8_t* qr = q + m * K;
 #pragma unroll
-  for (int i = 0; i < kQuantRegChunks; ++i) {
+  for (int i = 0; i < CH; ++i) {
     const int c = lane + 64 * i;
     if (c < nchunks) {
       float v[8];
-      unpack8_f16(raw[i], v);
-      scale_chunk<HAS_R>(r, c, v);
+      if constexpr (HAS_R) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = vr[i][j];
+      } else {
+        unpack8_f16(raw[i], v);
+      }
       *reinterpret_cast<uint2*>(qr + c * 8) = sym_codes8<HAS_R>(v, inv);
     }
   }
-  for (int c = lane + 64 * kQuantRegChunks; c < nchunks; c += 64) {
+  for (int c = lane + 64 * CH; c < nchunks; c += 64) {
     float v[8];
     load8_f16(xr + c * 8, v);
     scale_chunk<HAS_R>(r, c, v);
     *reinterpret_cast<uint2*>(qr + c * 8) = sym_codes8<HAS_R>(v, inv);
   }
+  if (ldO == 0) return;
 
-  // Outlier columns (row stride ldO, zero padded): the code, recomputed for
-  // O[j], and the compensation operand fp16(code * (s[O[j]] - 1)).
-  for (int j = lane; j < ldO; j += 64) {
-    const int o = j < nO ? O[j] : -1;
-    int code = 0;
-    float sm1 = 0.0f;
-    if (o >= 0 && o < K) {
-      float vv = h2f(xr[o]);
-      if constexpr (HAS_R) vv = mul_rn(vv, r[o]);
-      code = sym_code(vv, inv);
-      if (xO != nullptr) sm1 = sub_rn(s[o], 1.0f);
+  if constexpr (OL) {
+    // The wave reads back only what it wrote: LDS operations of one wave
+    // complete in order.
+    const uint16_t* const rowl = reinterpret_cast<const uint16_t*>(qlds + (threadIdx.x >> 6) * 2 * K);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < kOutlierLdMax / 64; ++i) {
+      const int j = lane + 64 * i;
+      if (j < ldO) {
+        int code = 0;
+        if (oj[i] >= 0) {
+          float vv = h2f(rowl[oj[i]]);
+          if constexpr (HAS_R) vv = mul_rn(vv, rj[i]);
+          code = sym_code(vv, inv);
+        }
+        if (qO != nullptr) qO[m * ldO + j] = static_cast<int8_t>(code);
+        if (xO != nullptr) xO[m * ldO + j] = f2h(mul_rn(static_cast<float>(code), sm1j[i]));
+      }
     }
-    if (qO != nullptr) qO[m * ldO + j] = static_cast<int8_t>(code);
-    if (xO != nullptr) xO[m * ldO + j] = f2h(mul_rn(static_cast<float>(code), sm1));
+  } else {
+    for (int j = lane; j < ldO; j += 64) {
+      const int o = j < nO ? O[j] : -1;
+      int code = 0;
+      float sm1 = 0.0f;
+      if (o >= 0 && o < K) {
+        float vv = h2f(xr[o]);
+        if constexpr (HAS_R) vv = mul_rn(vv, r[o]);
+        code = sym_code(vv, inv);
+        if (xO != nullptr) sm1 = sub_rn(s[o], 1.0f);
+      }
+      if (qO != nullptr) qO[m * ldO + j] = static_cast<int8_t>(code);
+      if (xO != nullptr) xO[m * ldO + j] = f2h(mul_rn(static_cast<float>(code), sm1));
+    }
   }
 }
 
@@ -334,10 +406,32 @@ extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, c
   constexpr int rows_per_block = kQuantThreads / 64;
   QLIN_REQUIRE(M / rows_per_block < 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
   const dim3 grid(static_cast<unsigned>((M + rows_per_block - 1) / rows_per_block));
+  // Outlier columns through LDS when they fit (2K bytes per wave).
+  const size_t ol_lds = static_cast<size_t>(rows_per_block) * 2 * static_cast<size_t>(K);
+  const bool ol = nO > 0 && ldO <= kOutlierLdMax && ol_lds <= 160 * 1024;
+  hipStream_t st = as_stream(stream);
+  auto go = [&](auto has_r, auto ol_c, auto ch) {
+    constexpr bool HR = decltype(has_r)::value, OLc = decltype(ol_c)::value;
+    constexpr int CH = decltype(ch)::value;
+    quant_act_kernel<HR, OLc, CH><<<grid, kQuantThreads, OLc ? ol_lds : 0, st>>>(x, M, K, r, q, scale, O, nO, ldO, s,
+                                                                                qO, xO);
+  };
+  auto go_ch = [&](auto has_r, auto ol_c) {
+    if (K <= 4096)
+      go(has_r, ol_c, std::integral_constant<int, 8>{});
+    else
+      go(has_r, ol_c, std::integral_constant<int, 16>{});
+  };
+  auto go_ol = [&](auto has_r) {
+    if (ol)
+      go_ch(has_r, std::true_type{});
+    else
+      go_ch(has_r, std::false_type{});
+  };
   if (r != nullptr)
-    quant_act_kernel<true><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, M, K, r, q, scale, O, nO, ldO, s, qO, xO);
+    go_ol(std::true_type{});
   else
-    quant_act_kernel<false><<<grid, kQuantThreads, 0, as_stream(stream)>>>(x, M, K, r, q, scale, O, nO, ldO, s, qO, xO);
+    go_ol(std::false_type{});
   QLIN_LAUNCH_CHECK("quant_act_kernel");
   return QLIN_OK;
 }
