@@ -98,23 +98,39 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def time_launches(fn, reps, trials=5, warm=3):
+def time_launches(fn, reps, trials=5, warm=3, graph_len=24):
     """Median over trials of the mean per-launch time (ms) of `reps`
-    back-to-back calls, timed with HIP events on the current stream."""
+    back-to-back calls, timed with HIP events on the current stream.
+
+    The calls are captured once into a HIP graph of `graph_len` launches
+    (call i uses fn(i)), which is replayed: the time is the device's, not that
+    of the Python argument checks of each call, which for a kernel of a few
+    microseconds would otherwise set the pace."""
     import torch
     for _ in range(warm):
         fn(0)
+    torch.cuda.synchronize()
+    n = max(1, min(graph_len, reps))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    replays = max(1, reps // n)
+    for _ in range(2):
+        g.replay()
     torch.cuda.synchronize()
     res = []
     for t in range(trials):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        for i in range(reps):
-            fn(i)
+        for _ in range(replays):
+            g.replay()
         e1.record()
         e1.synchronize()
-        res.append(e0.elapsed_time(e1) / reps)
+        res.append(e0.elapsed_time(e1) / (replays * n))
+    del g
     return statistics.median(res)
 
 
@@ -312,7 +328,7 @@ def rows_measurements(q, layer):
     signs = dev(lin.extra["signs"])
     xo = dev(lin.x)
     qa4, sa, za, rs, _ = q.qlin_hadamard_offset(xo, signs)
-    t = time_launches(lambda i: q.qlin_hadamard_offset(xo, signs), 50)
+    t = time_launches(lambda i: q.qlin_hadamard_offset(xo, signs, q4=qa4, scale=sa, zero=za, rowsum=rs), 50)
     b = 2 * M5 * K5 + M5 * K5 // 2 + 12 * M5 + K5
     out["A3_hadamard_offset"] = dict(workload=f"{M5}x{K5}", ms=t, bytes=b, gbs=b / t / 1e6,
                                      frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm")
@@ -331,7 +347,8 @@ def rows_measurements(q, layer):
     w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
     xt = dev(lin.x)
     qa, sa, _, _ = q.qlin_quant_act(xt)
-    t = time_launches(lambda i: (q.qlin_quant_act(xt, q=qa, scale=sa), q.qlin_gemm_w8a8(qa, sa, w8, sw, 128)), 200)
+    yt = torch.empty((16, 128), dtype=torch.float16, device="cuda")
+    t = time_launches(lambda i: (q.qlin_quant_act(xt, q=qa, scale=sa), q.qlin_gemm_w8a8(qa, sa, w8, sw, 128, y=yt)), 200)
     out["tiny_w8a8_quant_plus_gemm"] = dict(workload="16x256x128", ms=t, bound="launch")
     torch.cuda.synchronize()
     for v in out.values():

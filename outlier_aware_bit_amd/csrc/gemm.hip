@@ -195,7 +195,8 @@ __device__ __forceinline__ void tile_ptrs(const GemmArgs& g, int64_t m0, int64_t
     p.a[i] = static_cast<const uint8_t*>(g.a) + m * lda + c0 * 16;
   }
   p.lds_a = (A == AOp::I8) ? swz(row0, c0) : swz(row0, 2 * c0);
-  p.b = g.b + (nt32 << 10) + lane * 16;
+  const int64_t kt = (B == BOp::W8) ? g.K / 32 : g.K / 64;  // lane tiles per 32-column strip
+  p.b = g.b + ((nt32 * kt) << 10) + lane * 16;
   p.ratio = g.ratio + nt32 * 32 + (lane & 31);
 }
 
@@ -230,15 +231,15 @@ __device__ __forceinline__ void store_a(uint8_t* buf, int lds_a, const v4i (&ra)
 // column tile; int4 weights: one tile holds two k steps, so part KS loads
 // tile (kp = KS >> 1, nt = KS & 1), and the per-group ratios come with part 0.
 template <BOp B, AOp A, int TM, int KS>
-__device__ __forceinline__ void load_b_part(const TilePtrs<B, A, TM>& p, int64_t tiles_n, int64_t N, int s,
+__device__ __forceinline__ void load_b_part(const TilePtrs<B, A, TM>& p, int64_t kt, int64_t N, int s,
                                             v4i (&rb)[Tile<B, A, TM>::kNB], v2h (&rr)[2]) {
   if constexpr (B == BOp::W8) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
-      rb[KS * 2 + nt] = *reinterpret_cast<const v4i*>(p.b + ((static_cast<int64_t>(4 * s + KS) * tiles_n + nt) << 10));
+      rb[KS * 2 + nt] = *reinterpret_cast<const v4i*>(p.b + ((static_cast<int64_t>(4 * s + KS) + nt * kt) << 10));
   } else {
     constexpr int kp = KS >> 1, nt = KS & 1;
-    rb[kp * 2 + nt] = *reinterpret_cast<const v4i*>(p.b + ((static_cast<int64_t>(2 * s + kp) * tiles_n + nt) << 10));
+    rb[kp * 2 + nt] = *reinterpret_cast<const v4i*>(p.b + ((static_cast<int64_t>(2 * s + kp) + nt * kt) << 10));
     if constexpr (B == BOp::W4Group && KS == 0) {
 #pragma unroll
       for (int n2 = 0; n2 < 2; ++n2) {
@@ -250,12 +251,12 @@ __device__ __forceinline__ void load_b_part(const TilePtrs<B, A, TM>& p, int64_t
 }
 
 template <BOp B, AOp A, int TM>
-__device__ __forceinline__ void load_b(const TilePtrs<B, A, TM>& p, int64_t tiles_n, int64_t N, int s,
+__device__ __forceinline__ void load_b(const TilePtrs<B, A, TM>& p, int64_t kt, int64_t N, int s,
                                        v4i (&rb)[Tile<B, A, TM>::kNB], v2h (&rr)[2]) {
-  load_b_part<B, A, TM, 0>(p, tiles_n, N, s, rb, rr);
-  load_b_part<B, A, TM, 1>(p, tiles_n, N, s, rb, rr);
-  load_b_part<B, A, TM, 2>(p, tiles_n, N, s, rb, rr);
-  load_b_part<B, A, TM, 3>(p, tiles_n, N, s, rb, rr);
+  load_b_part<B, A, TM, 0>(p, kt, N, s, rb, rr);
+  load_b_part<B, A, TM, 1>(p, kt, N, s, rb, rr);
+  load_b_part<B, A, TM, 2>(p, kt, N, s, rb, rr);
+  load_b_part<B, A, TM, 3>(p, kt, N, s, rb, rr);
 }
 
 // Chunks [P * n / 2, (P + 1) * n / 2) of this thread's A loads of stage s.
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
   int64_t wcol0 = n0 + 64 * wave;
   const bool live = wcol0 < g.N;
   const int64_t nt32 = (live ? wcol0 : g.N - 64) / 32;
-  const int64_t b_tiles = g.N / 32;
+  const int64_t b_tiles = (B == BOp::W8) ? g.K / 32 : g.K / 64;  // lane tiles per 32-column strip
 
   TilePtrs<B, A, TM> p;
   tile_ptrs<B, A, TM>(g, m0, nt32, p);
@@ -690,7 +691,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny(GemmArgs g) {
 #pragma unroll
         for (int h = 0; h < NBU; ++h) {
           const int64_t tile_k = (B == BOp::W8) ? (2 * static_cast<int64_t>(u) + h) : static_cast<int64_t>(u);
-          rb[uu][nt][h] = ok ? *reinterpret_cast<const uint4*>(g.b + ((tile_k * tiles_n + nt0 + nt) << 10) + lane * 16)
+          const int64_t tix = (nt0 + nt) * ((B == BOp::W8) ? g.K / 32 : g.K / 64) + tile_k;
+          rb[uu][nt][h] = ok ? *reinterpret_cast<const uint4*>(g.b + (tix << 10) + lane * 16)
                              : make_uint4(0, 0, 0, 0);
         }
         rr[uu][nt] = v2h{static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f)};

@@ -18,7 +18,10 @@
 //        both operands unpack to the same k order.
 //   WO  tile (s, nt), s < ldO/16: fp16 value i of lane l = WO[16 s + 8 (l>>5) + i][n]
 //        (rows beyond nO are zero).
-// Tile (s, nt) starts at byte ((s * (N/32)) + nt) * 1024.
+// W8, W4S, W4U: the tiles of a 32-column strip are contiguous along K, tile
+// (s, nt) starting at byte (nt * KT + s) * 1024 with KT = K/32 (W8) or K/64
+// (W4): a kernel that owns a strip streams one contiguous range of memory.
+// WO: tile (s, nt) starts at byte ((s * (N/32)) + nt) * 1024.
 #pragma once
 
 #include <stdint.h>

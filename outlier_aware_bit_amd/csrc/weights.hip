@@ -166,8 +166,8 @@ __global__ void pack_w8_kernel(const int8_t* __restrict__ codes, int64_t K, int6
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (q >= K * N / 16) return;
   const int lane = static_cast<int>(q & 63);
-  const int64_t nt = (q >> 6) % (N / 32);
-  const int64_t s = (q >> 6) / (N / 32);
+  const int64_t nt = (q >> 6) / (K / 32);
+  const int64_t s = (q >> 6) % (K / 32);
   const int64_t n = nt * 32 + (lane & 31);
   const int64_t kb = s * 32 + 16 * (lane >> 5);
   uint32_t word[4] = {0, 0, 0, 0};
@@ -182,8 +182,8 @@ __global__ void pack_w4_kernel(const uint8_t* __restrict__ codes, int64_t K, int
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (q >= K * N / 32) return;
   const int lane = static_cast<int>(q & 63);
-  const int64_t nt = (q >> 6) % (N / 32);
-  const int64_t p = (q >> 6) / (N / 32);
+  const int64_t nt = (q >> 6) / (K / 64);
+  const int64_t p = (q >> 6) % (K / 64);
   const int64_t n = nt * 32 + (lane & 31);
   uint32_t word[4] = {0, 0, 0, 0};
   for (int half = 0; half < 2; ++half) {

@@ -84,17 +84,17 @@ def qlin_quant_act(x, r=None, O=None, s=None, q=None, scale=None, qO=None, xO=No
     return q, scale, qO, xO
 
 
-def qlin_hadamard_offset(x, signs, block=128, want_t=False):
+def qlin_hadamard_offset(x, signs, block=128, want_t=False, q4=None, scale=None, zero=None, rowsum=None):
     """OffQ block Hadamard + per-token asymmetric int4.
     Returns (q4 uint8 [M, K/2], scale, zero, rowsum, t or None)."""
     lib = _lib.load()
     _req(x, "x", torch.float16)
     M, K = x.shape
     _req(signs, "signs", torch.int8, (K,))
-    q4 = _empty((M, K // 2), torch.uint8, x)
-    scale = _empty((M,), torch.float32, x)
-    zero = _empty((M,), torch.int32, x)
-    rowsum = _empty((M,), torch.int32, x)
+    q4 = _req(q4, "q4", torch.uint8, (M, K // 2)) if q4 is not None else _empty((M, K // 2), torch.uint8, x)
+    scale = _req(scale, "scale", torch.float32, (M,)) if scale is not None else _empty((M,), torch.float32, x)
+    zero = _req(zero, "zero", torch.int32, (M,)) if zero is not None else _empty((M,), torch.int32, x)
+    rowsum = _req(rowsum, "rowsum", torch.int32, (M,)) if rowsum is not None else _empty((M,), torch.int32, x)
     t = _empty((M, K), torch.float32, x) if want_t else None
     _lib.check("qlin_hadamard_offset", lib.qlin_hadamard_offset(
         x.data_ptr(), M, K, signs.data_ptr(), block, q4.data_ptr(), scale.data_ptr(), zero.data_ptr(),
