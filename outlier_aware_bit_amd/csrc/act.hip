@@ -216,8 +216,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
 // each.  Butterflies of span 1..16 stay in the lane; spans 32 and 64 pair the
 // lanes of a quad.
 // ---------------------------------------------------------------------------
-constexpr int kHadThreads = 128;
-constexpr int kHadRegChunks = 2;  // 32-channel chunks held in registers per thread
+constexpr int kHadRegChunks = 2;  // 32-channel chunks held in registers per lane
 
 // Value of lane ^ 1 (MASK == 1) or lane ^ 2 (MASK == 2) within each quad, by
 // DPP quad permutes of the two halves (no LDS round trip).
@@ -295,22 +294,30 @@ __device__ __forceinline__ uint4 pack_codes(const float (&t)[32], float inv, int
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__global__ __launch_bounds__(kHadThreads) void hadamard_offset_kernel(
-    const uint16_t* __restrict__ x, int64_t K, const int8_t* __restrict__ signs,
+// One wavefront per token (four tokens per workgroup): lane l holds the
+// 32-channel chunks c = l + 64 i, so the four chunks of a 128-channel group
+// sit in the four lanes of a quad at the same register index, and the
+// per-token min, max and code sum are wavefront reductions (no LDS, no
+// barrier).  Rows longer than 64 * kHadRegChunks chunks recompute the
+// transform of the tail for the coding pass.
+constexpr int kHadWaves = 4;
+
+__global__ __launch_bounds__(64 * kHadWaves) void hadamard_offset_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const int8_t* __restrict__ signs,
     uint8_t* __restrict__ q4, float* __restrict__ scale, int32_t* __restrict__ zero,
     int32_t* __restrict__ rowsum, float* __restrict__ tout) {
-  __shared__ float redf[kHadThreads / 64];
-  __shared__ int redi[kHadThreads / 64];
-  const int64_t m = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * kHadWaves + (threadIdx.x >> 6);
+  if (m >= M) return;  // uniform per wave
   const uint16_t* xr = x + m * K;
-  const int nchunks = static_cast<int>(K / 32);
+  const int nchunks = static_cast<int>(K / 32);  // a multiple of 4: whole quads
 
   float t[kHadRegChunks][32];
   float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kHadRegChunks; ++i) {
-    const int c = threadIdx.x + i * kHadThreads;
-    if (i * kHadThreads < nchunks) {  // uniform per wave group: all quads take part
+    const int c = lane + 64 * i;
+    if (64 * i < nchunks) {  // uniform: quads are whole
       const int cc = c < nchunks ? c : (c & 3);
       hadamard_chunk(xr, signs, cc, t[i]);
       if (c < nchunks) {
@@ -328,8 +335,8 @@ __global__ __launch_bounds__(kHadThreads) void hadamard_offset_kernel(
       }
     }
   }
-  for (int base = kHadRegChunks * kHadThreads; base < nchunks; base += kHadThreads) {
-    const int c = base + threadIdx.x;
+  for (int base = 64 * kHadRegChunks; base < nchunks; base += 64) {
+    const int c = base + lane;
     const int cc = c < nchunks ? c : (c & 3);
     float tt[32];
     hadamard_chunk(xr, signs, cc, tt);
@@ -347,8 +354,8 @@ __global__ __launch_bounds__(kHadThreads) void hadamard_offset_kernel(
       }
     }
   }
-  mn = block_min<kHadThreads / 64>(mn, redf);
-  mx = block_max<kHadThreads / 64>(mx, redf);
+  mn = wave_min(mn);
+  mx = wave_max(mx);
   const float rng = sub_rn(mx, mn);
   const float inv = (rng == 0.0f) ? 1.0f : div_rn(15.0f, rng);
   const float step = (rng == 0.0f) ? 1.0f : div_rn(rng, 15.0f);
@@ -358,18 +365,18 @@ __global__ __launch_bounds__(kHadThreads) void hadamard_offset_kernel(
   uint8_t* qr = q4 + m * (K / 2);
 #pragma unroll
   for (int i = 0; i < kHadRegChunks; ++i) {
-    const int c = threadIdx.x + i * kHadThreads;
+    const int c = lane + 64 * i;
     if (c < nchunks) *reinterpret_cast<uint4*>(qr + static_cast<int64_t>(c) * 16) = pack_codes(t[i], inv, z, sum);
   }
-  for (int base = kHadRegChunks * kHadThreads; base < nchunks; base += kHadThreads) {
-    const int c = base + threadIdx.x;
+  for (int base = 64 * kHadRegChunks; base < nchunks; base += 64) {
+    const int c = base + lane;
     const int cc = c < nchunks ? c : (c & 3);
     float tt[32];
     hadamard_chunk(xr, signs, cc, tt);
     if (c < nchunks) *reinterpret_cast<uint4*>(qr + static_cast<int64_t>(c) * 16) = pack_codes(tt, inv, z, sum);
   }
-  sum = block_sum<kHadThreads / 64>(sum, redi);
-  if (threadIdx.x == 0) {
+  sum = wave_sum(sum);
+  if (lane == 0) {
     scale[m] = step;
     zero[m] = z;
     rowsum[m] = sum;
@@ -451,9 +458,9 @@ extern "C" qlin_status qlin_hadamard_offset(const uint16_t* x, int64_t M, int64_
   QLIN_PTR(zero);
   QLIN_PTR(rowsum);
   QLIN_OPT_PTR(t);
-  QLIN_REQUIRE(M <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
-  hadamard_offset_kernel<<<dim3(static_cast<unsigned>(M)), kHadThreads, 0, as_stream(stream)>>>(
-      x, K, signs, q4, scale, zero, rowsum, t);
+  QLIN_REQUIRE(M / kHadWaves < 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
+  hadamard_offset_kernel<<<dim3(static_cast<unsigned>((M + kHadWaves - 1) / kHadWaves)), 64 * kHadWaves, 0,
+                           as_stream(stream)>>>(x, M, K, signs, q4, scale, zero, rowsum, t);
   QLIN_LAUNCH_CHECK("hadamard_offset_kernel");
   return QLIN_OK;
 }
