@@ -317,19 +317,37 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");
 }
 
-// Tile index -> (tile row, tile column): XCD-contiguous blocks, groups of 4 rows.
+// Tile index -> (tile row, tile column).  Workgroup b runs on XCD b % 8, so
+// the tiles of XCD x are taken from one block of the tile grid: with a
+// 2 x 4 split of the grid (tile rows in 2 blocks, tile columns in 4, which
+// keeps each XCD's A rows and B columns -- the operands its L2 must fetch --
+// about equal in bytes for tiles twice as wide as tall), else from a
+// contiguous run of the row-grouped order.  Inside a block, tiles go in
+// groups of 4 tile rows so that tiles running at the same time share rows.
+__device__ __forceinline__ void group_order(int64_t idx, int64_t rows, int64_t cols, int64_t& r_out,
+                                            int64_t& c_out) {
+  constexpr int64_t G = 4;
+  const int64_t per_group = G * cols;
+  const int64_t first = (idx / per_group) * G;
+  const int64_t gm = (rows - first) < G ? (rows - first) : G;
+  const int64_t r = idx % per_group;
+  r_out = first + r % gm;
+  c_out = r / gm;
+}
+
 __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm_idx, int64_t& tn_idx) {
   const int64_t T = tiles_m * tiles_n;
-  int64_t bid = blockIdx.x;
-  if (T % 8 == 0) bid = (bid % 8) * (T / 8) + bid / 8;
-  constexpr int64_t G = 4;
-  const int64_t per_group = G * tiles_n;
-  const int64_t group = bid / per_group;
-  const int64_t first_m = group * G;
-  const int64_t gm = (tiles_m - first_m) < G ? (tiles_m - first_m) : G;
-  const int64_t r = bid % per_group;
-  tm_idx = first_m + r % gm;
-  tn_idx = r / gm;
+  const int64_t bid = blockIdx.x;
+  if (tiles_m % 2 == 0 && tiles_n % 4 == 0) {
+    const int64_t x = bid % 8, l = bid / 8;  // XCD, index within it
+    const int64_t br = tiles_m / 2, bc = tiles_n / 4;
+    int64_t r, c;
+    group_order(l, br, bc, r, c);
+    tm_idx = (x % 2) * br + r;
+    tn_idx = (x / 2) * bc + c;
+    return;
+  }
+  group_order((T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid, tiles_m, tiles_n, tm_idx, tn_idx);
 }
 
 // COMP: 0 no compensation term; 1 compensation after the K loop with xO read
