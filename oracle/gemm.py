@@ -70,6 +70,42 @@ def w4a4(qa: np.ndarray, step_a: np.ndarray, za: np.ndarray,
     return acc.astype(np.int32), y
 
 
+def w4a4_group(qa: np.ndarray, step_a: np.ndarray, za: np.ndarray,
+               qw: np.ndarray, step_w: np.ndarray, zw: np.ndarray, group: int = 128,
+               return_acc: bool = False):
+    """W4A4 with per-token, per-group activation steps and zero points (OffQ,
+    methodology, "grouped implementation"): each group of ``group`` k has its
+    own activation step step_a[m, g] and zero za[m, g]; the weights keep one
+    step and zero per output channel.
+
+    acc_g[m, n] = sum_{k in g} (qa_mk - za_mg)(qw_kn - zw_n)   (exact integers)
+    y[m, n]     = step_w[n] * sum_g step_a[m, g] * acc_g[m, n]  (float64)
+    Returns y, or (y, acc int32 [G x M x N]) with ``return_acc``; raises if an
+    acc_g leaves the int32 range.
+    """
+    qa = np.asarray(qa)
+    M, K = qa.shape
+    N = np.asarray(qw).shape[1]
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    cw = np.asarray(qw, np.int64) - np.asarray(zw, np.int64)[None, :]
+    y = np.zeros((M, N), np.float64)
+    accs = []
+    for g in range(K // group):
+        ks = slice(g * group, (g + 1) * group)
+        ca = qa[:, ks].astype(np.int64) - np.asarray(za, np.int64)[:, g][:, None]
+        acc = exact_int_matmul(ca, cw[ks])
+        if acc.size and np.max(np.abs(acc)) >= 2 ** 31:
+            raise ValueError("W4A4 group accumulator exceeds int32")
+        if return_acc:
+            accs.append(acc.astype(np.int32))
+        y += acc.astype(np.float64) * np.asarray(step_a, np.float64)[:, g][:, None]
+    y = y * np.asarray(step_w, np.float64)[None, :]
+    if return_acc:
+        return y, np.stack(accs) if accs else np.zeros((0, M, N), np.int32)
+    return y
+
+
 def w4a4_raw(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
     """raw_mn = sum_k qa_mk * qw_kn on the unsigned codes (int64)."""
     return exact_int_matmul(qa, qw)

@@ -60,3 +60,13 @@ def offq_forward(x, w, signs, block=128):
     acc, y = gemm.w4a4(qa, sa, za, qw, sw, zw)
     return dict(qa=qa, sa=sa, za=za, rowsum=rowsum, t=t, qw=qw, sw=sw, zw=zw,
                 colsum=colsum, acc=acc, y=y)
+
+
+def offq_group_forward(x, w, signs, block=128):
+    """OffQ with group-wise offsets: per-token per-block activation steps and
+    zero points, per-channel asymmetric int4 weights."""
+    qa, sa, za, rowsum, t = quant.hadamard_offset_int4_group(x, signs, block)
+    qw, sw, zw, colsum = quant.offq_weight(w, signs, block)
+    y = gemm.w4a4_group(qa, sa, za, qw, sw, zw, block)
+    return dict(qa=qa, sa=sa, za=za, rowsum=rowsum, t=t, qw=qw, sw=sw, zw=zw,
+                colsum_g=quant.weight_colsum_group(qw, block), y=y)

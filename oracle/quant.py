@@ -102,6 +102,48 @@ def hadamard_offset_int4(x: np.ndarray, signs: np.ndarray, block: int = 128):
     return q, step, z, rowsum, t
 
 
+def quant_act_asym_int4_group(t: np.ndarray, group: int = 128):
+    """Per-token, per-group asymmetric int4: every group of ``group``
+    consecutive channels of a token gets its own step and zero point.
+
+    OffQ (methodology, "grouped implementation"; ablations: group size 128):
+    several outlier channels are handled by splitting the channels into groups,
+    each group's top outlier is turned into an offset of that group alone, and
+    each group's own scale and zero point absorb it.  Within a group the rule is
+    the per-token rule of ``quant_act_asym_int4`` (range of the group's own
+    values, not widened to 0).
+
+    t fp32 [M x K], K a multiple of ``group``; G = K / group.
+    Returns (q uint8 [M x K], step fp32 [M x G], z int32 [M x G],
+    rowsum int32 [M x G]) with rowsum[m, g] = sum of the codes of group g.
+    """
+    t = np.asarray(t, dtype=F32)
+    M, K = t.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    G = K // group
+    q = np.zeros((M, K), np.uint8)
+    step = np.zeros((M, G), F32)
+    z = np.zeros((M, G), np.int32)
+    rowsum = np.zeros((M, G), np.int32)
+    for g in range(G):
+        cols = slice(g * group, (g + 1) * group)
+        q[:, cols], step[:, g], z[:, g], rowsum[:, g] = quant_act_asym_int4(t[:, cols])
+    return q, step, z, rowsum
+
+
+def hadamard_offset_int4_group(x: np.ndarray, signs: np.ndarray, block: int = 128):
+    """OffQ's group-wise activation path: the block transform of
+    ``hadamard_offset_int4`` (groups = Hadamard blocks), then per-token
+    per-group asymmetric int4 (``quant_act_asym_int4_group``).
+
+    Returns (q, step [M x G], z [M x G], rowsum [M x G], t32).
+    """
+    t = hadamard.transform_blocks(x, signs, block).astype(F32)
+    q, step, z, rowsum = quant_act_asym_int4_group(t, block)
+    return q, step, z, rowsum, t
+
+
 # --------------------------------------------------------------------------
 # Weights (offline preparation; W is [K x N], channel = output column n)
 # --------------------------------------------------------------------------
@@ -190,3 +232,15 @@ def offq_weight(w: np.ndarray, signs: np.ndarray, block: int = 128):
     """OffQ weight side: W'' = blockdiag(H'^{-1}) W exactly, then asymmetric int4
     per output channel.  Returns (qw, step, zw, colsum)."""
     return quant_weight_asym(hadamard.inverse_transform_weight(w, signs, block).astype(F32))
+
+
+def weight_colsum_group(qw: np.ndarray, group: int = 128) -> np.ndarray:
+    """Column sums of the weight codes over each group of k:
+    colsum_g[g, n] = sum_{k in group g} qw[k, n] (int32 [K/group x N]).  The
+    group-wise zero-point correction needs them, since the activation zero
+    point changes from one group to the next."""
+    qw = np.asarray(qw)
+    K, N = qw.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    return qw.astype(np.int64).reshape(K // group, group, N).sum(axis=1).astype(np.int32)
