@@ -123,6 +123,22 @@ qlin_status qlin_hadamard_offset(const uint16_t* x, int64_t M, int64_t K, const 
                                  int32_t* rowsum, float* t, void* stream);
 
 /*
+ * qlin_hadamard_offset_group -- OffQ's group-wise offsets (OffQ, methodology,
+ * "grouped implementation": each group of channels gets its own scale and
+ * zero point, which absorb that group's outlier; the ablations settle on
+ * groups of 128).  The transform of qlin_hadamard_offset, then the same
+ * asymmetric rule applied to every group g of `block` channels of a token
+ * separately (range of the group's own values).  G = K / block.
+ *   x, signs, block, q4, t  as in qlin_hadamard_offset
+ *   scale   fp32 [M x G] out: step of group g of token m at m * G + g
+ *   zero    int32 [M x G] out: z
+ *   rowsum  int32 [M x G] out: sum of the group's codes
+ */
+qlin_status qlin_hadamard_offset_group(const uint16_t* x, int64_t M, int64_t K, const int8_t* signs,
+                                       int32_t block, uint8_t* q4, float* scale, int32_t* zero,
+                                       int32_t* rowsum, float* t, void* stream);
+
+/*
  * qlin_momentum_update -- Quaff targeted momentum scaling, one step
  * (Quaff notes, "key design"): for o in O, c = max_m |x[m,o]|,
  * beta = max(1, sqrt(c / wmax_O[o])) (beta = 1 if wmax_O[o] == 0 or M == 0),
@@ -190,6 +206,17 @@ qlin_status qlin_quant_weight_offq(const uint16_t* w, int64_t K, int64_t N, cons
  */
 qlin_status qlin_weight_row_absmax(const uint16_t* w_rows, int64_t R, int64_t N, float* out,
                                    void* stream);
+
+/*
+ * qlin_weight_colsum_group -- column sums of weight codes over each group of
+ * `group` k, for the group-wise W4A4 zero-point correction (OffQ, methodology,
+ * "grouped implementation": the activation zero point changes per group).
+ *   codes    uint8 [K x N] (one code per byte, as from qlin_quant_weight_offq)
+ *   group    128 (the only size provided)
+ *   colsum_g int32 [K/group x N] out: colsum_g[g, n] = sum_{k in group g} codes[k, n]
+ */
+qlin_status qlin_weight_colsum_group(const uint8_t* codes, int64_t K, int64_t N, int32_t group,
+                                     int32_t* colsum_g, void* stream);
 
 /* Bytes of a packed weight buffer for `layout` (0 for invalid arguments). Host only. */
 size_t qlin_packed_bytes(int32_t layout, int64_t K, int64_t N);
@@ -261,6 +288,27 @@ qlin_status qlin_gemm_w4a4(const uint8_t* qa4, const float* sa, const int32_t* z
                            const int32_t* rowsum, const void* w4, const float* sw,
                            const int32_t* zw, const int32_t* colsum, int64_t M, int64_t N,
                            int64_t K, uint16_t* y, int32_t* acc, void* stream);
+
+/*
+ * qlin_gemm_w4a4_group -- W4A4 with OffQ's group-wise activation offsets
+ * (OffQ, methodology, "grouped implementation"): a step sa, zero point za and
+ * code sum per token and group of 128 k (from qlin_hadamard_offset_group),
+ * per-channel asymmetric int4 weights.  With G = K / 128:
+ *   acc_g = sum_{k in g} (qa - za[m,g]) (qw - zw[n])
+ *         = raw_g - za[m,g] * colsum_g[g,n] - zw[n] * (rowsum[m,g] - 128 za[m,g])
+ *   y     = fp16(sw[n] * sum_g sa[m,g] * acc_g)
+ * evaluated as fp32 sums over g of sa * fp32(raw_g - za * colsum_g) and of
+ * sa * fp32(rowsum - 128 za), combined per element at the end (the integers
+ * are exact).  Precondition: |za| < 2^12 (not checked on the device).
+ *   qa4 uint8 [M x K/2] (low nibble = even k);  sa fp32 [M x G];
+ *   za int32 [M x G];  rowsum int32 [M x G];  w4 packed QLIN_LAYOUT_W4U;
+ *   sw fp32 [N];  zw int32 [N];  colsum_g int32 [G x N] (qlin_weight_colsum_group;
+ *   16-byte aligned);  y fp16 [M x N] out.
+ */
+qlin_status qlin_gemm_w4a4_group(const uint8_t* qa4, const float* sa, const int32_t* za,
+                                 const int32_t* rowsum, const void* w4, const float* sw,
+                                 const int32_t* zw, const int32_t* colsum_g, int64_t M, int64_t N,
+                                 int64_t K, uint16_t* y, void* stream);
 
 /*
  * qlin_outlier_comp -- the sparse compensation term on its own, added to an

@@ -24,16 +24,19 @@ SIGNATURES = {
     "qlin_outlier_ld": (i32, [i32]),
     "qlin_quant_act": (i32, [p, i64, i64, p, p, p, p, i32, p, p, p, p]),
     "qlin_hadamard_offset": (i32, [p, i64, i64, p, i32, p, p, p, p, p, p]),
+    "qlin_hadamard_offset_group": (i32, [p, i64, i64, p, i32, p, p, p, p, p, p]),
     "qlin_momentum_update": (i32, [p, i64, i64, p, i32, p, f32, p, p, p]),
     "qlin_quant_weight_sym": (i32, [p, i64, i64, i32, p, p, p]),
     "qlin_quant_weight_group": (i32, [p, i64, i64, i32, p, p, p, p, p]),
     "qlin_quant_weight_offq": (i32, [p, i64, i64, p, i32, p, p, p, p, p]),
     "qlin_weight_row_absmax": (i32, [p, i64, i64, p, p]),
+    "qlin_weight_colsum_group": (i32, [p, i64, i64, i32, p, p]),
     "qlin_packed_bytes": (C.c_size_t, [i32, i64, i64]),
     "qlin_pack_weight": (i32, [i32, p, i64, i64, p, p]),
     "qlin_gemm_w8a8": (i32, [p, p, p, p, i64, i64, i64, p, i32, p, p, p, p]),
     "qlin_gemm_w4a8": (i32, [p, p, p, p, p, i32, i64, i64, i64, p, p, p]),
     "qlin_gemm_w4a4": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p, p]),
+    "qlin_gemm_w4a4_group": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p]),
     "qlin_outlier_comp": (i32, [p, p, i32, p, i64, i64, p, p]),
 }
 

@@ -1,11 +1,13 @@
 // Activation-side kernels of libqlin (gfx950):
-//   qlin_quant_act        per-token symmetric int8 (optionally of X * r)
-//   qlin_hadamard_offset  OffQ block Hadamard (all-ones first row) + per-token
-//                         asymmetric int4 with the offset in the zero point
+//   qlin_quant_act              per-token symmetric int8 (optionally of X * r)
+//   qlin_hadamard_offset        OffQ block Hadamard (all-ones first row) + per-token
+//                               asymmetric int4 with the offset in the zero point
+//   qlin_hadamard_offset_group  the same transform with a step and zero point per
+//                               128-channel group
 //
-// Both are HBM-bound streaming kernels: one workgroup per token, 16-byte
-// loads of 8 fp16 values, the per-token reduction as a wavefront butterfly
-// plus one LDS exchange between waves, and packed stores.
+// All are HBM-bound streaming kernels: one wavefront per token, 16-byte
+// loads, reductions as wavefront or quad exchanges (no LDS barrier), and
+// packed stores.
 #include <type_traits>
 
 #include "common.hpp"
@@ -383,6 +385,83 @@ __global__ __launch_bounds__(64 * kHadWaves) void hadamard_offset_kernel(
   }
 }
 
+// Group-wise offsets (OffQ, methodology, grouped implementation): every
+// 128-channel group of a token has its own step, zero point and code sum.
+// The four chunks of a group sit in the four lanes of a quad, so the group's
+// min, max and code sum are two quad exchanges each, and one pass over the
+// row suffices: each group is coded as soon as it is transformed.
+template <int MASK>
+__device__ __forceinline__ int quad_xor_i32(int v) {
+  constexpr int ctrl = (MASK == 1) ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __builtin_amdgcn_update_dpp(0, v, ctrl, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float quad_min(float v) {
+  v = fminf(v, __builtin_bit_cast(float, quad_xor_i32<1>(__builtin_bit_cast(int, v))));
+  return fminf(v, __builtin_bit_cast(float, quad_xor_i32<2>(__builtin_bit_cast(int, v))));
+}
+
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, quad_xor_i32<1>(__builtin_bit_cast(int, v))));
+  return fmaxf(v, __builtin_bit_cast(float, quad_xor_i32<2>(__builtin_bit_cast(int, v))));
+}
+
+__device__ __forceinline__ int quad_sum(int v) {
+  v += quad_xor_i32<1>(v);
+  return v + quad_xor_i32<2>(v);
+}
+
+__global__ __launch_bounds__(64 * kHadWaves) void hadamard_offset_group_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const int8_t* __restrict__ signs,
+    uint8_t* __restrict__ q4, float* __restrict__ scale, int32_t* __restrict__ zero,
+    int32_t* __restrict__ rowsum, float* __restrict__ tout) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * kHadWaves + (threadIdx.x >> 6);
+  if (m >= M) return;  // uniform per wave
+  const uint16_t* xr = x + m * K;
+  const int nchunks = static_cast<int>(K / 32);  // a multiple of 4: whole quads
+  const int64_t G = K / 128;
+  uint8_t* qr = q4 + m * (K / 2);
+  for (int base = 0; base < nchunks; base += 64) {  // uniform
+    const int c = base + lane;
+    // A lane past the row transforms an in-range chunk of the same quarter,
+    // so that its quad takes part in the exchanges, and stores nothing.
+    const int cc = c < nchunks ? c : (c & 3);
+    float t[32];
+    hadamard_chunk(xr, signs, cc, t);
+    float mn = t[0], mx = t[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) {
+      mn = fminf(mn, t[e]);
+      mx = fmaxf(mx, t[e]);
+    }
+    mn = quad_min(mn);
+    mx = quad_max(mx);
+    const float rng = sub_rn(mx, mn);
+    const float inv = (rng == 0.0f) ? 1.0f : div_rn(15.0f, rng);
+    const float step = (rng == 0.0f) ? 1.0f : div_rn(rng, 15.0f);
+    const int z = static_cast<int>(rint_f(mul_rn(-mn, inv)));
+    int sum = 0;
+    const uint4 codes = pack_codes(t, inv, z, sum);
+    sum = quad_sum(sum);
+    if (c < nchunks) {
+      *reinterpret_cast<uint4*>(qr + static_cast<int64_t>(c) * 16) = codes;
+      if (tout != nullptr) {
+        float* dst = tout + m * K + static_cast<int64_t>(c) * 32;
+#pragma unroll
+        for (int e = 0; e < 32; e += 4)
+          *reinterpret_cast<float4*>(dst + e) = make_float4(t[e], t[e + 1], t[e + 2], t[e + 3]);
+      }
+      if ((c & 3) == 0) {
+        const int64_t gi = m * G + (c >> 2);
+        scale[gi] = step;
+        zero[gi] = z;
+        rowsum[gi] = sum;
+      }
+    }
+  }
+}
+
 }  // namespace
 }  // namespace qlin
 
@@ -462,5 +541,27 @@ extern "C" qlin_status qlin_hadamard_offset(const uint16_t* x, int64_t M, int64_
   hadamard_offset_kernel<<<dim3(static_cast<unsigned>((M + kHadWaves - 1) / kHadWaves)), 64 * kHadWaves, 0,
                            as_stream(stream)>>>(x, M, K, signs, q4, scale, zero, rowsum, t);
   QLIN_LAUNCH_CHECK("hadamard_offset_kernel");
+  return QLIN_OK;
+}
+
+extern "C" qlin_status qlin_hadamard_offset_group(const uint16_t* x, int64_t M, int64_t K,
+                                                  const int8_t* signs, int32_t block, uint8_t* q4,
+                                                  float* scale, int32_t* zero, int32_t* rowsum,
+                                                  float* t, void* stream) {
+  QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
+  QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_REQUIRE(block == 128, QLIN_ERR_UNSUPPORTED, "block=%d: only 128 is provided", block);
+  if (M == 0) return QLIN_OK;
+  QLIN_PTR(x);
+  QLIN_PTR(signs);
+  QLIN_PTR(q4);
+  QLIN_PTR(scale);
+  QLIN_PTR(zero);
+  QLIN_PTR(rowsum);
+  QLIN_OPT_PTR(t);
+  QLIN_REQUIRE(M / kHadWaves < 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
+  hadamard_offset_group_kernel<<<dim3(static_cast<unsigned>((M + kHadWaves - 1) / kHadWaves)), 64 * kHadWaves, 0,
+                                 as_stream(stream)>>>(x, M, K, signs, q4, scale, zero, rowsum, t);
+  QLIN_LAUNCH_CHECK("hadamard_offset_group_kernel");
   return QLIN_OK;
 }

@@ -4,6 +4,9 @@
 //                   128 (fused fp16 dequant-quant inside the K loop)
 //   qlin_gemm_w4a4  OffQ-style asymmetric int4 x int4 with the zero-point
 //                   correction in the epilogue
+//   qlin_gemm_w4a4_group  the same with a step and zero point per token and
+//                   128-k group: each group's int32 partial sum is corrected
+//                   and scaled into fp32 accumulators inside the K loop
 //
 // Two kernels serve all of them, specialised by an operand policy.
 //
@@ -39,7 +42,8 @@ namespace qlin {
 namespace {
 
 enum class BOp { W8, W4Shift, W4Group, W4U };
-enum class AOp { I8, U4 };
+// U4G: int4 activations with a step and zero point per (token, 128-k group).
+enum class AOp { I8, U4, U4G };
 
 struct GemmArgs {
   const void* a;          // int8 [M x K] or packed uint4 [M x K/2]
@@ -48,10 +52,10 @@ struct GemmArgs {
   const uint16_t* sw_h;   // fp16 [N] (W8A8, W4A8)
   const float* sw_f;      // fp32 [N] (W4A4)
   const uint16_t* ratio;  // fp16 [K/128 x N] (per group)
-  const int32_t* za;      // [M]  (W4A4)
+  const int32_t* za;      // [M]  (W4A4); group-wise: [M x K/128], as sa and rowsum
   const int32_t* rowsum;  // [M]
   const int32_t* zw;      // [N]
-  const int32_t* colsum;  // [N]
+  const int32_t* colsum;  // [N]; group-wise W4A4: [K/128 x N]
   const uint16_t* xO;     // fp16 [M x ldO] compensation operand (W8A8)
   const uint8_t* WOp;     // packed fp16 W_O
   int ldO;
@@ -269,6 +273,65 @@ __device__ __forceinline__ void load_a_half(const TilePtrs<B, A, TM>& p, int s, 
     ra[i] = *reinterpret_cast<const v4i*>(p.a[i] + static_cast<int64_t>(s) * stage_bytes);
 }
 
+// Group-wise W4A4: the constants of one 128-k group (one K stage) for this
+// lane -- step, zero point and code sum of its TM token rows, and the
+// group's weight column sums for its 32 columns, in the accumulators' runs
+// of four (register v of block nt holds column 32 nt + 8 (v >> 2) + 4 h +
+// (v & 3), h = lane >> 5).
+template <int TM>
+struct GroupC {
+  float sa[TM];
+  int32_t za[TM];
+  int32_t rs[TM];
+  v4i cs[2][4];
+};
+
+// rowoff[tm]: (token row) * (K/128) for row 32 tm + (lane & 31) of the tile,
+// clamped to the last row; csp: colsum + first column of the wave + 4 h.
+template <int TM>
+__device__ __forceinline__ void load_group(const GemmArgs& g, const int64_t (&rowoff)[TM], const int32_t* csp,
+                                           int s, GroupC<TM>& c) {
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    c.sa[tm] = g.sa[rowoff[tm] + s];
+    c.za[tm] = g.za[rowoff[tm] + s];
+    c.rs[tm] = g.rowsum[rowoff[tm] + s];
+  }
+  const int32_t* p = csp + static_cast<int64_t>(s) * g.N;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c.cs[nt][q] = *reinterpret_cast<const v4i*>(p + 32 * nt + 8 * q);
+}
+
+// Product of two integers known to fit 24 bits (one v_mad_i32_i24 with an add).
+__device__ __forceinline__ int32_t mul24(int32_t a, int32_t b) { return ((a << 8) >> 8) * ((b << 8) >> 8); }
+
+// End of group s: with raw = sum over the group of qa * qw (the int32
+// accumulators, restarted every group),
+//   cf += sa_g * fp32(raw - za_g * colsum_g)     per element
+//   P  += sa_g * fp32(rowsum_g - 128 * za_g)     per token row
+// so that after the last group y = sw * (cf - zw * P) is
+//   sw * sum_g sa_g * sum_{k in g} (qa - za_g)(qw - zw).
+// Both integers are exact: |raw| <= 128 * 225 and |za_g| < 2^12.
+template <int TM>
+__device__ __forceinline__ void group_rescale(const v16i (&acc)[TM][2], v16f (&cf)[TM][2], float (&P)[TM],
+                                              const GroupC<TM>& c) {
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int32_t nza = -c.za[tm];
+    const float sa = c.sa[tm];
+    P[tm] = fmaf(sa, static_cast<float>(c.rs[tm] + 128 * nza), P[tm]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int32_t t = acc[tm][nt][v] + mul24(nza, c.cs[nt][v >> 2][v & 3]);
+        cf[tm][nt][v] = fmaf(sa, static_cast<float>(t), cf[tm][nt][v]);
+      }
+  }
+}
+
 // A fragments of k step ks (32 k) of an LDS stage: rows 32*tm + (lane & 31),
 // 16-byte half (lane >> 5).
 template <int TM>
@@ -362,7 +425,8 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
   // Three activation stages, then the epilogue constants of the tile: the
   // token steps (and W4A4 zero points / row sums) of its BM rows and the
   // column steps (and W4A4 zero points / column sums) of its 256 columns.
-  constexpr int kRowC = (B == BOp::W4U) ? 3 : 1, kColC = (B == BOp::W4U) ? 3 : 1;
+  constexpr bool kGrp = (A == AOp::U4G);
+  constexpr int kRowC = (B == BOp::W4U && !kGrp) ? 3 : 1, kColC = (B == BOp::W4U) ? 3 : 1;
   // COMP == 2 stages the tile's xO rows (BM x ldO fp16, unpadded) in the
   // same space before the activation stages are first written.
   constexpr int kXO = (COMP == 2) ? T::BM * 2 * kXOMaxLd : 0;
@@ -422,20 +486,25 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
     mc = mc < g.M ? mc : g.M - 1;
     int64_t nc = n0 + t;
     nc = nc < g.N ? nc : g.N - 1;
-    k_sa = g.sa[mc];
-    if constexpr (B == BOp::W4U) {
+    if constexpr (kGrp) {
+      k_sw = g.sw_f[nc];
+      k_zw = g.zw[nc];
+    } else if constexpr (B == BOp::W4U) {
+      k_sa = g.sa[mc];
       k_za = g.za[mc];
       k_rs = g.rowsum[mc];
       k_sw = g.sw_f[nc];
       k_zw = g.zw[nc];
       k_cs = g.colsum[nc];
     } else {
+      k_sa = g.sa[mc];
       k_sw = h2f(g.sw_h[nc]);
     }
   }
   auto clamp_s = [S](int t) { return t < S ? t : S - 1; };
-  [[maybe_unused]] v16f cf[COMP ? TM : 1][2];
-  if constexpr (COMP != 0) {
+  // fp32 accumulators: the compensation term (COMP), or the scaled group sums.
+  [[maybe_unused]] v16f cf[(COMP || kGrp) ? TM : 1][2];
+  if constexpr (COMP != 0 || kGrp) {
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -459,6 +528,25 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
   load_a<B, A, TM>(p, clamp_s(1), ra[1]);
 #pragma unroll
   for (int j = 0; j < BD; ++j) load_b<B, A, TM>(p, b_tiles, g.N, clamp_s(j), rb[j], rr[j]);
+  // Group-wise: the constants of group t are loaded at the start of stage t,
+  // right after the stage's first weight prefetch and ahead of its
+  // activation prefetch, so that waiting for them at the end of the stage
+  // waits for nothing issued later.
+  [[maybe_unused]] GroupC<TM> gc;
+  [[maybe_unused]] float P[kGrp ? TM : 1];
+  [[maybe_unused]] int64_t rowoff[TM];
+  [[maybe_unused]] const int32_t* csp = nullptr;
+  if constexpr (kGrp) {
+    const int64_t G = g.K / kBK;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      int64_t m = m0 + 32 * tm + (lane & 31);
+      m = m < g.M ? m : g.M - 1;
+      rowoff[tm] = m * G;
+      P[tm] = 0.0f;
+    }
+    csp = g.colsum + nt32 * 32 + 4 * (lane >> 5);
+  }
   if constexpr (COMP == 2) {
     // Wait for the xO chunks only: the K loop's loads issued after them may
     // stay in flight while the compensation runs.
@@ -477,7 +565,7 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
     const int t = threadIdx.x;
     if (t < T::BM) {
       c_sa[t] = k_sa;
-      if constexpr (B == BOp::W4U) {
+      if constexpr (B == BOp::W4U && !kGrp) {  // group-wise: no per-row constants
         c_za[t] = k_za;
         c_rs[t] = k_rs;
       }
@@ -510,6 +598,7 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
       else
         read_frags<TM>(nxt, 0, af[0]);
       load_b_part<B, A, TM, KS>(p, b_tiles, g.N, sb, rbn, rrn);
+      if constexpr (kGrp && KS == 0) load_group<TM>(g, rowoff, csp, st, gc);
       if constexpr (KS == 0) load_a_half<B, A, TM, 0>(p, s3, ra[1 - JA]);
       if constexpr (KS == 1) load_a_half<B, A, TM, 1>(p, s3, ra[1 - JA]);
       if constexpr (KS == 2) store_a<B, A, TM>(fut, p.lds_a, ra[JA]);
@@ -523,11 +612,14 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
           bf[nt] = bq[nt][KS & 1];
         }
       }
+      // Group-wise: every group starts its int32 sums afresh.
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[tm][nt] = mfma_i8(bf[nt], af[KS & 1][tm], acc[tm][nt]);
-      constexpr int nvm = kVmB + ((KS < 2) ? kVmA : 0) + ((B == BOp::W4Group && KS == 0) ? 2 : 0);
+        for (int nt = 0; nt < 2; ++nt)
+          acc[tm][nt] = mfma_i8(bf[nt], af[KS & 1][tm], (kGrp && KS == 0) ? v16i{} : acc[tm][nt]);
+      constexpr int nvm = kVmB + ((KS < 2) ? kVmA : 0) + ((B == BOp::W4Group && KS == 0) ? 2 : 0) +
+                          ((kGrp && KS == 0) ? 3 * TM + 8 : 0);
       sched_kstep<TM, nvm, (KS == 2) ? kDsW : 0>(std::make_integer_sequence<int, TM>{});
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -535,6 +627,7 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
     kstep(std::integral_constant<int, 1>{});
     kstep(std::integral_constant<int, 2>{});
     kstep(std::integral_constant<int, 3>{});
+    if constexpr (kGrp) group_rescale<TM>(acc, cf, P, gc);
     stage_barrier<TM>();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -616,9 +709,9 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
     const int64_t m = m0 + 32 * tm + r;
     // W4A4 zero points: acc = raw - zw*(rowsum - K*za) - za*colsum, evaluated
     // in wrapping 32-bit arithmetic (exact: the true value fits int32).
-    const float sam = c_sa[32 * tm + r];
+    const float sam = kGrp ? 1.0f : c_sa[32 * tm + r];
     [[maybe_unused]] uint32_t za = 0, rkt = 0;
-    if constexpr (B == BOp::W4U) {
+    if constexpr (B == BOp::W4U && !kGrp) {
       za = static_cast<uint32_t>(c_za[32 * tm + r]);
       rkt = static_cast<uint32_t>(c_rs[32 * tm + r]) - static_cast<uint32_t>(g.K) * za;
     }
@@ -641,13 +734,15 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
           int32_t val = acc[tm][nt][4 * q + j];
           if constexpr (B == BOp::W4Shift) {
             val >>= 4;  // every product is 16 * q * q4: the division is exact
-          } else if constexpr (B == BOp::W4U) {
+          } else if constexpr (B == BOp::W4U && !kGrp) {
             val = static_cast<int32_t>(static_cast<uint32_t>(val) - static_cast<uint32_t>(zw[j]) * rkt -
                                        za * static_cast<uint32_t>(cs[j]));
           }
           iv[j] = val;
           float f;
-          if constexpr (COMP == 1)
+          if constexpr (kGrp)
+            f = (cf[tm][nt][4 * q + j] - static_cast<float>(zw[j]) * P[tm]) * sw[j];
+          else if constexpr (COMP == 1)
             f = cf[tm][nt][4 * q + j];  // acc * sw + compensation
           else if constexpr (COMP == 2)
             f = static_cast<float>(val) * sw[j] + cf[tm][nt][4 * q + j];
@@ -657,7 +752,7 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
         }
         *reinterpret_cast<uint2*>(out_lds + r * kOutPitch + (32 * nt + 8 * q + 4 * h) * 2) =
             make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
-        if (COMP != 1 && want_acc && m < g.M) *reinterpret_cast<v4i*>(g.acc + m * g.N + n) = iv;
+        if (COMP != 1 && !kGrp && want_acc && m < g.M) *reinterpret_cast<v4i*>(g.acc + m * g.N + n) = iv;
       }
     // The wave reads back only rows it wrote; LDS operations of one wave
     // complete in order, so no barrier is needed, only a compiler fence.
@@ -824,7 +919,8 @@ template <BOp B, AOp A, int TM, int COMP>
 qlin_status launch_tile(const GemmArgs& g, hipStream_t st) {
   // Weight prefetch depth: two stages, except at 256-row tiles with int8 or
   // per-group requantized weights, where register room leaves one.
-  constexpr int BD = ((B == BOp::W8 || B == BOp::W4Group) && TM == 8) ? 1 : 2;
+  // Group-wise W4A4 keeps one (its group constants and fp32 sums take the room).
+  constexpr int BD = (((B == BOp::W8 || B == BOp::W4Group) && TM == 8) || A == AOp::U4G) ? 1 : 2;
   const int64_t tiles = ((g.M + 32 * TM - 1) / (32 * TM)) * ((g.N + kBN - 1) / kBN);
   QLIN_REQUIRE(tiles <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M=%lld too large", (long long)g.M);
   gemm_tile<B, A, TM, BD, COMP><<<dim3(static_cast<unsigned>(tiles)), kTileThreads, 0, st>>>(g);
@@ -834,28 +930,31 @@ qlin_status launch_tile(const GemmArgs& g, hipStream_t st) {
 
 template <BOp B, AOp A>
 qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
-  if (!comp && g.M <= 64) {
-    if (g.M <= 32)
-      launch_skinny<B, A, 1, 1, 8, 8>(g, st);
-    else
-      launch_skinny<B, A, 2, 2, 8, 4>(g, st);
-    QLIN_LAUNCH_CHECK("gemm_skinny");
-    return QLIN_OK;
-  }
-  if (comp) {
-    if constexpr (B == BOp::W8 && A == AOp::I8) {
-      if (g.ldO <= kXOMaxLd) return launch_tile<B, A, 4, 2>(g, st);
-      return launch_tile<B, A, 4, 1>(g, st);
+  if constexpr (A == AOp::U4G) {
+    // Group-wise W4A4: 128-row tiles at every M (the int32 and fp32
+    // accumulators both live in registers).
+    return launch_tile<B, A, 4, 0>(g, st);
+  } else {
+    if (!comp && g.M <= 64) {
+      if (g.M <= 32)
+        launch_skinny<B, A, 1, 1, 8, 8>(g, st);
+      else
+        launch_skinny<B, A, 2, 2, 8, 4>(g, st);
+      QLIN_LAUNCH_CHECK("gemm_skinny");
+      return QLIN_OK;
     }
+    if (comp) {
+      if constexpr (B == BOp::W8 && A == AOp::I8) {
+        if (g.ldO <= kXOMaxLd) return launch_tile<B, A, 4, 2>(g, st);
+        return launch_tile<B, A, 4, 1>(g, st);
+      }
+    }
+    // 256-row tiles when they still give every CU a tile: per weight byte
+    // streamed (and unpacked) they do twice the matrix-core work.
+    const int64_t tiles_n = (g.N + kBN - 1) / kBN;
+    if (((g.M + 255) / 256) * tiles_n >= 256) return launch_tile<B, A, 8, 0>(g, st);
+    return launch_tile<B, A, 4, 0>(g, st);
   }
-  // 256-row tiles when they still give every CU a tile: per weight byte
-  // streamed (and unpacked) they do twice the matrix-core work.
-  const int64_t tiles_n = (g.N + kBN - 1) / kBN;
-#if EXP_FORCE_TM4
-  return launch_tile<B, A, 4, 0>(g, st);
-#endif
-  if (((g.M + 255) / 256) * tiles_n >= 256) return launch_tile<B, A, 8, 0>(g, st);
-  return launch_tile<B, A, 4, 0>(g, st);
 }
 
 GemmArgs base_args(int64_t M, int64_t N, int64_t K, uint16_t* y, int32_t* acc) {
@@ -959,4 +1058,32 @@ extern "C" qlin_status qlin_gemm_w4a4(const uint8_t* qa4, const float* sa, const
   g.zw = zw;
   g.colsum = colsum;
   return launch<BOp::W4U, AOp::U4>(g, false, as_stream(stream));
+}
+
+extern "C" qlin_status qlin_gemm_w4a4_group(const uint8_t* qa4, const float* sa, const int32_t* za,
+                                            const int32_t* rowsum, const void* w4, const float* sw,
+                                            const int32_t* zw, const int32_t* colsum_g, int64_t M, int64_t N,
+                                            int64_t K, uint16_t* y, void* stream) {
+  QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
+  QLIN_K_N(K, N);
+  if (M == 0) return QLIN_OK;
+  QLIN_PTR(qa4);
+  QLIN_PTR(sa);
+  QLIN_PTR(za);
+  QLIN_PTR(rowsum);
+  QLIN_PTR(w4);
+  QLIN_PTR(sw);
+  QLIN_PTR(zw);
+  QLIN_PTR(colsum_g);
+  QLIN_PTR(y);
+  GemmArgs g = base_args(M, N, K, y, nullptr);
+  g.a = qa4;
+  g.sa = sa;
+  g.b = static_cast<const uint8_t*>(w4);
+  g.sw_f = sw;
+  g.za = za;
+  g.rowsum = rowsum;
+  g.zw = zw;
+  g.colsum = colsum_g;
+  return launch<BOp::W4U, AOp::U4G>(g, false, as_stream(stream));
 }

@@ -159,6 +159,20 @@ __global__ __launch_bounds__(kColThreads) void quant_offq_kernel(
   }
 }
 
+// Column sums of the codes over each group of 128 k (the group-wise W4A4
+// zero-point correction): one thread per (group, column), rows read
+// coalesced across the columns.
+__global__ __launch_bounds__(kColThreads) void colsum_group_kernel(const uint8_t* __restrict__ codes, int64_t K,
+                                                                   int64_t N, int32_t* __restrict__ out) {
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * kColThreads + threadIdx.x;
+  const int64_t g = blockIdx.y;
+  if (n >= N) return;
+  const uint8_t* p = codes + g * 128 * N + n;
+  int sum = 0;
+  for (int i = 0; i < 128; ++i) sum += p[i * N];
+  out[g * N + n] = sum;
+}
+
 // ---------------------------------------------------------------- packing
 // One thread writes one 16-byte lane chunk of the packed layout (layout.hpp).
 __global__ void pack_w8_kernel(const int8_t* __restrict__ codes, int64_t K, int64_t N,
@@ -272,6 +286,19 @@ extern "C" qlin_status qlin_quant_weight_offq(const uint16_t* w, int64_t K, int6
   quant_offq_kernel<<<dim3(static_cast<unsigned>(N / kOffCols)), kColThreads, 0, as_stream(stream)>>>(
       w, K, N, signs, codes, scale, zero, colsum);
   QLIN_LAUNCH_CHECK("quant_offq_kernel");
+  return QLIN_OK;
+}
+
+extern "C" qlin_status qlin_weight_colsum_group(const uint8_t* codes, int64_t K, int64_t N, int32_t group,
+                                                int32_t* colsum_g, void* stream) {
+  QLIN_K_N(K, N);
+  QLIN_REQUIRE(group == 128, QLIN_ERR_UNSUPPORTED, "group=%d: only 128 is provided", group);
+  QLIN_PTR(codes);
+  QLIN_PTR(colsum_g);
+  QLIN_REQUIRE(K / 128 <= 65535, QLIN_ERR_SHAPE, "K=%lld too large", (long long)K);
+  const dim3 grid(static_cast<unsigned>((N + kColThreads - 1) / kColThreads), static_cast<unsigned>(K / 128));
+  colsum_group_kernel<<<grid, kColThreads, 0, as_stream(stream)>>>(codes, K, N, colsum_g);
+  QLIN_LAUNCH_CHECK("colsum_group_kernel");
   return QLIN_OK;
 }
 

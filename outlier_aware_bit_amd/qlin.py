@@ -102,6 +102,26 @@ def qlin_hadamard_offset(x, signs, block=128, want_t=False, q4=None, scale=None,
     return q4, scale, zero, rowsum, t
 
 
+def qlin_hadamard_offset_group(x, signs, block=128, want_t=False, q4=None, scale=None, zero=None, rowsum=None):
+    """OffQ block Hadamard + asymmetric int4 with a step and zero point per
+    token and group of ``block`` channels.
+    Returns (q4 uint8 [M, K/2], scale [M, G], zero [M, G], rowsum [M, G], t or None)."""
+    lib = _lib.load()
+    _req(x, "x", torch.float16)
+    M, K = x.shape
+    G = K // block if block else 0
+    _req(signs, "signs", torch.int8, (K,))
+    q4 = _req(q4, "q4", torch.uint8, (M, K // 2)) if q4 is not None else _empty((M, K // 2), torch.uint8, x)
+    scale = _req(scale, "scale", torch.float32, (M, G)) if scale is not None else _empty((M, G), torch.float32, x)
+    zero = _req(zero, "zero", torch.int32, (M, G)) if zero is not None else _empty((M, G), torch.int32, x)
+    rowsum = _req(rowsum, "rowsum", torch.int32, (M, G)) if rowsum is not None else _empty((M, G), torch.int32, x)
+    t = _empty((M, K), torch.float32, x) if want_t else None
+    _lib.check("qlin_hadamard_offset_group", lib.qlin_hadamard_offset_group(
+        x.data_ptr(), M, K, signs.data_ptr(), block, q4.data_ptr(), scale.data_ptr(), zero.data_ptr(),
+        rowsum.data_ptr(), _ptr(t), _stream()))
+    return q4, scale, zero, rowsum, t
+
+
 def qlin_momentum_update(x, O, wmax_O, gamma, s, r):
     """One step of Quaff's momentum scaling; updates s in place and writes r."""
     lib = _lib.load()
@@ -166,6 +186,17 @@ def qlin_quant_weight_offq(w, signs, block=128):
         w.data_ptr(), K, N, signs.data_ptr(), block, codes.data_ptr(), scale.data_ptr(), zero.data_ptr(),
         colsum.data_ptr(), _stream()))
     return codes, scale, zero, colsum
+
+
+def qlin_weight_colsum_group(codes, group=128):
+    """Column sums of uint8 weight codes [K, N] over each group of ``group`` k: int32 [K/group, N]."""
+    lib = _lib.load()
+    _req(codes, "codes", torch.uint8)
+    K, N = codes.shape
+    out = _empty((K // group if group else 0, N), torch.int32, codes)
+    _lib.check("qlin_weight_colsum_group", lib.qlin_weight_colsum_group(
+        codes.data_ptr(), K, N, group, out.data_ptr(), _stream()))
+    return out
 
 
 def qlin_packed_bytes(layout, K, N) -> int:
@@ -243,6 +274,27 @@ def qlin_gemm_w4a4(qa4, sa, za, rowsum, w4, sw, zw, colsum, N, want_acc=False, y
         qa4.data_ptr(), sa.data_ptr(), za.data_ptr(), rowsum.data_ptr(), w4.data_ptr(), sw.data_ptr(), zw.data_ptr(),
         colsum.data_ptr(), M, N, K, y.data_ptr(), _ptr(acc), _stream()))
     return y, acc
+
+
+def qlin_gemm_w4a4_group(qa4, sa, za, rowsum, w4, sw, zw, colsum_g, N, y=None):
+    """W4A4 with a step, zero point and code sum per token and 128-k group
+    (sa, za, rowsum [M, K/128]) and per-channel weights (colsum_g [K/128, N])."""
+    lib = _lib.load()
+    _req(qa4, "qa4", torch.uint8)
+    M, K2 = qa4.shape
+    K = 2 * K2
+    G = K // 128
+    for t, n, d, sh in [(sa, "sa", torch.float32, (M, G)), (za, "za", torch.int32, (M, G)),
+                        (rowsum, "rowsum", torch.int32, (M, G)), (sw, "sw", torch.float32, (N,)),
+                        (zw, "zw", torch.int32, (N,)), (colsum_g, "colsum_g", torch.int32, (G, N))]:
+        _req(t, n, d, sh)
+    _req(w4, "w4", torch.uint8)
+    y = y if y is not None else _empty((M, N), torch.float16, qa4)
+    _req(y, "y", torch.float16, (M, N))
+    _lib.check("qlin_gemm_w4a4_group", lib.qlin_gemm_w4a4_group(
+        qa4.data_ptr(), sa.data_ptr(), za.data_ptr(), rowsum.data_ptr(), w4.data_ptr(), sw.data_ptr(), zw.data_ptr(),
+        colsum_g.data_ptr(), M, N, K, y.data_ptr(), _stream()))
+    return y
 
 
 def qlin_outlier_comp(xO, sa, nO, WO, y):

@@ -119,17 +119,22 @@ def qqq_prefill(M: int = 4096, K: int = 11008, N: int = 4096, seed: int = 3) -> 
 
 
 def offq_inputs(M: int = 2048, K: int = 4096, N: int = 14336, seed: int = 4, block: int = 128,
-                offset_mean: float = 200.0, offset_std: float = 20.0) -> Linear:
+                offset_mean: float = 200.0, offset_std: float = 20.0, offset_spread: float = 0.0) -> Linear:
     """OffQ-style activations: channel ``block*b`` ~ N(200, 20^2), others N(0,1).
 
+    With ``offset_spread`` > 0 the mean of channel ``block*b`` is drawn per
+    block from U(-offset_spread, offset_spread) instead (one outlier level per
+    group, the case of group-wise offsets).
     ``extra['signs']`` holds the int8 +-1 row signs of the partially random
     Hadamard matrix (one per channel; the sign of each block's first row is +1).
     """
     rng = np.random.default_rng(seed)
     x = rng.standard_normal(size=(M, K), dtype=np.float32)
     heads = np.arange(0, K, block)
-    x[:, heads] = rng.standard_normal(size=(M, heads.size), dtype=np.float32) * np.float32(offset_std) \
-        + np.float32(offset_mean)
+    mean = np.float32(offset_mean)
+    if offset_spread > 0:
+        mean = rng.uniform(-offset_spread, offset_spread, size=heads.size).astype(np.float32)
+    x[:, heads] = rng.standard_normal(size=(M, heads.size), dtype=np.float32) * np.float32(offset_std) + mean
     signs = rng.choice(np.array([-1, 1], dtype=np.int8), size=K)
     signs[heads] = 1
     w = _normal16(rng, (K, N), W_STD)
