@@ -339,7 +339,22 @@ def rows_measurements(q, layer):
     ops = 2 * M5 * K5 * N5
     out["A8_gemm_w4a4"] = dict(workload=f"{M5}x{K5}x{N5}", ms=t, ops=ops, tops=ops / t / 1e9,
                                frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma")
-    del cw, w4u, y, xo
+
+    # OffQ group-wise offsets (a step and zero point per token and 128-channel
+    # group), same shape, one outlier level per group.
+    lin = synth.offq_inputs(M=M5, K=K5, N=N5, seed=4, offset_spread=400.0)
+    xo = dev(lin.x)
+    G5 = K5 // 128
+    qg4, sag, zag, rsg, _ = q.qlin_hadamard_offset_group(xo, signs)
+    t = time_launches(lambda i: q.qlin_hadamard_offset_group(xo, signs, q4=qg4, scale=sag, zero=zag, rowsum=rsg), 50)
+    b = 2 * M5 * K5 + M5 * K5 // 2 + 12 * M5 * G5 + K5
+    out["A3g_hadamard_offset_group"] = dict(workload=f"{M5}x{K5}, groups of 128", ms=t, bytes=b, gbs=b / t / 1e6,
+                                            frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm")
+    csg = q.qlin_weight_colsum_group(cw)
+    t = time_launches(lambda i: q.qlin_gemm_w4a4_group(qg4, sag, zag, rsg, w4u, swf, zw, csg, N5, y=y), 20)
+    out["A8g_gemm_w4a4_group"] = dict(workload=f"{M5}x{K5}x{N5}, groups of 128", ms=t, ops=ops, tops=ops / t / 1e9,
+                                      frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma")
+    del cw, w4u, y, xo, qg4, csg
 
     # Tiny W8A8 (latency only).
     lin = synth.tiny_w8a8(seed=0)

@@ -1,4 +1,4 @@
-"""GPU parity at the full sizes of the five layer workloads, in the launch
+"""GPU parity at the full sizes of the five layer workloads (and of the group-wise form of the OffQ one), in the launch
 configurations bench.py times.
 
 Integer stages (codes, zero points, sums, the momentum state s and r) are
@@ -151,4 +151,33 @@ def test_offq_w4a4_full(q):
     rows = _sample_rows(M, 32, 9)
     acc_ref, y_ref = gemm.w4a4(qa_ref[rows], sa_ref[rows], za_ref[rows], qw_ref, sw_ref, zw_ref)
     assert_equal(host(acc)[rows], acc_ref, "acc")
+    assert_close(host(y)[rows], y_ref, "y")
+
+
+def test_offq_w4a4_group_full(q):
+    # Group-wise offsets at the OffQ shape, one outlier level per group.
+    M, K, N = 2048, 4096, 14336
+    log(f"OffQ W4A4 group-wise {M}x{K}x{N}")
+    lin = synth.offq_inputs(M=M, K=K, N=N, seed=4, offset_spread=400.0)
+    signs = lin.extra["signs"]
+    qa_ref, sa_ref, za_ref, rs_ref, t_ref = quant.hadamard_offset_int4_group(lin.x, signs)
+    qw_ref, sw_ref, zw_ref, _ = quant.offq_weight(lin.w, signs)
+    sd = dev(signs)
+    qa4, sa, za, rs, t = q.qlin_hadamard_offset_group(dev(lin.x), sd, want_t=True)
+    assert_equal(host(t), t_ref, "transformed activations")
+    packed = host(qa4)
+    codes = np.empty((M, K), np.uint8)
+    codes[:, 0::2] = packed & 0xF
+    codes[:, 1::2] = packed >> 4
+    assert_equal(codes, qa_ref, "activation codes")
+    assert_equal(host(sa), sa_ref, "activation steps")
+    assert_equal(host(za), za_ref, "activation zero points")
+    assert_equal(host(rs), rs_ref, "group code sums")
+    cw, sw, zw, _ = q.qlin_quant_weight_offq(dev(lin.w), sd)
+    assert_equal(host(cw), qw_ref, "weight codes")
+    csg = q.qlin_weight_colsum_group(cw)
+    assert_equal(host(csg), quant.weight_colsum_group(qw_ref), "column sums per group")
+    y = q.qlin_gemm_w4a4_group(qa4, sa, za, rs, q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, cw), sw, zw, csg, N)
+    rows = _sample_rows(M, 32, 10)
+    y_ref = gemm.w4a4_group(qa_ref[rows], sa_ref[rows], za_ref[rows], qw_ref, sw_ref, zw_ref)
     assert_close(host(y)[rows], y_ref, "y")
