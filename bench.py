@@ -373,6 +373,70 @@ def rows_measurements(q, layer):
     return out
 
 
+SWEEP_MS = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096]
+
+
+def token_sweep(q):
+    """W8A8, W4A8 per channel and W4A8 per group of 128 over token counts
+    M = 1 .. 4096 at a LLaMA-7B up_proj shape (K = 4096, N = 11008), each
+    through the library's own M-dependent dispatch.  Weight copies rotate
+    through at least twice the Infinity Cache, so small-M runs stream weights
+    from HBM.  An fp16 torch GEMM of the same shape is timed beside them as
+    context (eager, so its small-M figures include launch cost)."""
+    import torch
+    import synth
+    K, N = 4096, 11008
+    lin = synth.qqq_decode(M=max(SWEEP_MS), K=K, N=N, seed=2)
+    w = dev(lin.w)
+    x16 = dev(lin.x)
+    qa, sa, _, _ = q.qlin_quant_act(x16)
+    c8, s8 = q.qlin_quant_weight_sym(w, 8)
+    c4, s4 = q.qlin_quant_weight_sym(w, 4)
+    cg, _, sc, ratio = q.qlin_quant_weight_group(w, 128)
+
+    def copies_of(t):
+        n = max(2, (2 * MALL_BYTES) // t.numel() + 1)
+        return [t.clone() for _ in range(n)]
+
+    w8s = copies_of(q.qlin_pack_weight(q.QLIN_LAYOUT_W8, c8))
+    w4s = copies_of(q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, c4))
+    wgs = copies_of(q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, cg))
+    w16s = copies_of(w)
+    del c8, c4, cg
+    y = torch.empty((max(SWEEP_MS), N), dtype=torch.float16, device="cuda")
+    res = {"workload": f"M x {K} x {N}", "M": SWEEP_MS, "w8a8_us": [], "w4a8_channel_us": [], "w4a8_group_us": [],
+           "fp16_torch_us": []}
+    for m in SWEEP_MS:
+        a, s_, yy = qa[:m], sa[:m], y[:m]
+        reps = 240 if m <= 64 else (48 if m <= 1024 else 24)
+        res["w8a8_us"].append(1e3 * time_launches(
+            lambda i: q.qlin_gemm_w8a8(a, s_, w8s[i % len(w8s)], s8, N, y=yy), reps))
+        res["w4a8_channel_us"].append(1e3 * time_launches(
+            lambda i: q.qlin_gemm_w4a8(a, s_, w4s[i % len(w4s)], s4, N, y=yy), reps))
+        res["w4a8_group_us"].append(1e3 * time_launches(
+            lambda i: q.qlin_gemm_w4a8(a, s_, wgs[i % len(wgs)], sc, N, ratio=ratio, group=128, y=yy), reps))
+        xm = x16[:m]
+        for i in range(3):
+            torch.matmul(xm, w16s[i % len(w16s)])
+        torch.cuda.synchronize()
+        n16 = 4 * len(w16s)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n16):
+            torch.matmul(xm, w16s[i % len(w16s)])
+        e1.record()
+        e1.synchronize()
+        res["fp16_torch_us"].append(1e3 * e0.elapsed_time(e1) / n16)
+    for k in ("w8a8_us", "w4a8_channel_us", "w4a8_group_us", "fp16_torch_us"):
+        res[k] = [round(v, 2) for v in res[k]]
+    res["w4a8_channel_speedup_vs_w8a8"] = [round(a / b, 3) for a, b in zip(res["w8a8_us"], res["w4a8_channel_us"])]
+    res["w4a8_group_speedup_vs_w8a8"] = [round(a / b, 3) for a, b in zip(res["w8a8_us"], res["w4a8_group_us"])]
+    del w8s, w4s, wgs, w16s
+    torch.cuda.synchronize()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -452,6 +516,7 @@ def main():
     }
     if not a.no_rows:
         rec["rows"] = rows_measurements(q, layer)
+        rec["token_sweep"] = token_sweep(q)
     if not a.no_cpu:
         log("timing the CPU oracle")
         rec["cpu_baseline"] = cpu_baseline(layer, budget_s=a.cpu_budget)

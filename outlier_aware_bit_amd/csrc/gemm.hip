@@ -10,9 +10,10 @@
 //
 // Two kernels serve all of them, specialised by an operand policy.
 //
-// gemm_tile (M > 64): a workgroup computes a (32*TM) x 256 tile with four
-// waves side by side, each owning 64 distinct output columns (32*TM x 64
-// per wave, 2*TM accumulator fragments of 32 x 32).
+// gemm_tile (M > 128, with a compensation term, or group-wise W4A4): a
+// workgroup computes a (32*TM) x 256 tile with four waves side by side, each
+// owning 64 distinct output columns (32*TM x 64 per wave, 2*TM accumulator
+// fragments of 32 x 32).
 //   * Weights never touch LDS: the packed layout is in MFMA fragment order, so
 //     each wave streams its own columns straight from memory into registers
 //     with one 16-byte load per lane per fragment (int4 weights at half the
@@ -27,7 +28,7 @@
 //   * Workgroups are mapped to tiles in groups of 4 tile rows, with each
 //     XCD (every 8th workgroup) given a contiguous block of tiles so the
 //     operands it streams stay in its own L2.
-// gemm_skinny (M <= 64, decode): bound by the weight stream.  A workgroup
+// gemm_skinny (M <= 128: decode and small batches): bound by the weight stream.  A workgroup
 // owns NT 32-column tiles, its waves split K, every weight byte is loaded
 // once straight into MFMA fragments with U units of 64 k in flight per lane,
 // and the waves' int32 partial sums meet in LDS.
@@ -935,11 +936,16 @@ qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
     // accumulators both live in registers).
     return launch_tile<B, A, 4, 0>(g, st);
   } else {
-    if (!comp && g.M <= 64) {
+    // Up to 128 tokens the K-split skinny kernels (one 64-k unit per wave in
+    // flight at 128 rows) beat 128-row tiles, of which there would be fewer
+    // than one per CU.
+    if (!comp && g.M <= 128) {
       if (g.M <= 32)
         launch_skinny<B, A, 1, 1, 8, 8>(g, st);
-      else
+      else if (g.M <= 64)
         launch_skinny<B, A, 2, 2, 8, 4>(g, st);
+      else
+        launch_skinny<B, A, 4, 2, 8, 1>(g, st);
       QLIN_LAUNCH_CHECK("gemm_skinny");
       return QLIN_OK;
     }

@@ -1,4 +1,5 @@
-"""GPU parity at the full sizes of the five layer workloads (and of the group-wise form of the OffQ one), in the launch
+"""GPU parity at the full sizes of the five layer workloads (plus the
+group-wise form of the OffQ one and the token-count sweep), in the launch
 configurations bench.py times.
 
 Integer stages (codes, zero points, sums, the momentum state s and r) are
@@ -181,3 +182,47 @@ def test_offq_w4a4_group_full(q):
     rows = _sample_rows(M, 32, 10)
     y_ref = gemm.w4a4_group(qa_ref[rows], sa_ref[rows], za_ref[rows], qw_ref, sw_ref, zw_ref)
     assert_close(host(y)[rows], y_ref, "y")
+
+
+SWEEP_MS = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096]
+
+
+def test_token_sweep_llama7b(q):
+    # The token-count sweep of the three W*A8 GEMMs at K = 4096, N = 11008:
+    # every M goes through the library's own dispatch (skinny kernels up to
+    # 64 tokens, 128- or 256-row tiles above), the accumulators are exact on
+    # sampled rows, the outputs within 1e-3.
+    K, N = 4096, 11008
+    Mx = max(SWEEP_MS)
+    lin = synth.qqq_decode(M=Mx, K=K, N=N, seed=2)
+    q_ref, sa_ref = quant.quant_act_sym_int8(lin.x)
+    w8_ref, s8_ref = quant.quant_weight_sym(lin.w, 8)
+    w4_ref, s4_ref = quant.quant_weight_sym(lin.w, 4)
+    wg_ref, _, sc_ref, rg_ref = quant.quant_weight_group(lin.w, 128)
+    w8g_ref = quant.requant_group(wg_ref, rg_ref)
+    wd = dev(lin.w)
+    qa, sa, _, _ = q.qlin_quant_act(dev(lin.x))
+    assert_equal(host(qa), q_ref, "activation codes")
+    c8, s8 = q.qlin_quant_weight_sym(wd, 8)
+    c4, s4 = q.qlin_quant_weight_sym(wd, 4)
+    cg, _, sc, ratio = q.qlin_quant_weight_group(wd, 128)
+    assert_equal(host(c8), w8_ref, "int8 weight codes")
+    assert_equal(host(c4), w4_ref, "int4 weight codes")
+    assert_equal(host(cg), wg_ref, "group weight codes")
+    p8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, c8)
+    p4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, c4)
+    pg = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, cg)
+    for M in SWEEP_MS:
+        log(f"token sweep M={M}")
+        rows = _sample_rows(M, 6, M)
+        a, s_ = qa[:M], sa[:M]
+        for name, (fn, wq, ws) in {
+            "w8a8": (lambda: q.qlin_gemm_w8a8(a, s_, p8, s8, N, want_acc=True), w8_ref, s8_ref),
+            "w4a8 channel": (lambda: q.qlin_gemm_w4a8(a, s_, p4, s4, N, want_acc=True), w4_ref, s4_ref),
+            "w4a8 group": (lambda: q.qlin_gemm_w4a8(a, s_, pg, sc, N, ratio=ratio, group=128, want_acc=True),
+                           w8g_ref, sc_ref),
+        }.items():
+            y, acc = fn()
+            acc_ref, y_ref = gemm.w8a8(q_ref[rows], sa_ref[rows], wq, ws.astype(np.float32))
+            assert_equal(host(acc)[rows], acc_ref, f"{name} acc M={M}")
+            assert_close(host(y)[rows], y_ref, f"{name} y M={M}")

@@ -154,7 +154,8 @@ def test_weight_quantizers(q, K, N):
 
 # ------------------------------------------------------------ GEMMs
 GEMM_SHAPES = [(1, 256, 128), (7, 384, 192), (16, 256, 128), (33, 512, 64), (64, 1024, 256),
-               (65, 256, 192), (200, 384, 320), (256, 512, 128), (1000, 512, 1024)]
+               (65, 256, 192), (100, 384, 320), (128, 512, 128), (129, 256, 64), (200, 384, 320),
+               (256, 512, 128), (1000, 512, 1024)]
 
 
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
