@@ -264,11 +264,11 @@ __device__ __forceinline__ void load_b(const TilePtrs<B, A, TM>& p, int64_t kt, 
   load_b_part<B, A, TM, 3>(p, kt, N, s, rb, rr);
 }
 
-// Chunks [P * n / 2, (P + 1) * n / 2) of this thread's A loads of stage s.
+// Chunks [P * n / 2, (P + 1) * n / 2) of this thread's A loads of stage s
+// (with a single chunk, all of it in part 1).
 template <BOp B, AOp A, int TM, int P>
 __device__ __forceinline__ void load_a_half(const TilePtrs<B, A, TM>& p, int s, v4i (&ra)[Tile<B, A, TM>::kAChunks]) {
   constexpr int n = Tile<B, A, TM>::kAChunks, stage_bytes = (A == AOp::I8) ? kBK : kBK / 2;
-  static_assert(n % 2 == 0, "A chunks are loaded in two halves");
 #pragma unroll
   for (int i = P * n / 2; i < (P + 1) * n / 2; ++i)
     ra[i] = *reinterpret_cast<const v4i*>(p.a[i] + static_cast<int64_t>(s) * stage_bytes);
@@ -374,8 +374,10 @@ __device__ __forceinline__ void sched_kstep(std::integer_sequence<int, Ps...>) {
 // operations of a wave complete in order.
 template <int TM>
 __device__ __forceinline__ void stage_barrier() {
-  static_assert(TM == 4 || TM == 8, "lgkmcnt immediate");
-  if constexpr (TM == 4)
+  static_assert(TM == 2 || TM == 4 || TM == 8, "lgkmcnt immediate");
+  if constexpr (TM == 2)
+    asm volatile("s_waitcnt lgkmcnt(2)\n\ts_barrier" ::: "memory");
+  else if constexpr (TM == 4)
     asm volatile("s_waitcnt lgkmcnt(4)\n\ts_barrier" ::: "memory");
   else
     asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");
@@ -420,8 +422,11 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
 // (ldO <= kXOMaxLd).
 constexpr int kXOMaxLd = 384;
 
+// Group-wise W4A4 tiles are bound by the vector ALU (the per-group fold of
+// every accumulator): two workgroups per CU, so that one wave's fold runs
+// while the other's matrix-core work and loads proceed.
 template <BOp B, AOp A, int TM, int BD, int COMP>
-__global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
+__global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_tile(GemmArgs g) {
   using T = Tile<B, A, TM>;
   // Three activation stages, then the epilogue constants of the tile: the
   // token steps (and W4A4 zero points / row sums) of its BM rows and the
@@ -580,7 +585,6 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
   lds_barrier();
   read_frags<TM>(lds, 0, af[0]);
 
-  constexpr int kVmA = T::kAChunks / 2;                                  // A loads in k steps 0 and 1
   constexpr int kVmB = (B == BOp::W8) ? 2 : 1;                           // B loads per k step
   constexpr int kDsW = (A == AOp::I8) ? T::kAChunks : 2 * T::kAChunks;   // LDS stores in k step 2
   auto stage = [&](auto jb, auto ja, auto jl, int st) __attribute__((always_inline)) {
@@ -619,7 +623,8 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile(GemmArgs g) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           acc[tm][nt] = mfma_i8(bf[nt], af[KS & 1][tm], (kGrp && KS == 0) ? v16i{} : acc[tm][nt]);
-      constexpr int nvm = kVmB + ((KS < 2) ? kVmA : 0) + ((B == BOp::W4Group && KS == 0) ? 2 : 0) +
+      constexpr int kVmAKS = (KS == 0) ? T::kAChunks / 2 : (KS == 1) ? T::kAChunks - T::kAChunks / 2 : 0;
+      constexpr int nvm = kVmB + kVmAKS + ((B == BOp::W4Group && KS == 0) ? 2 : 0) +
                           ((kGrp && KS == 0) ? 3 * TM + 8 : 0);
       sched_kstep<TM, nvm, (KS == 2) ? kDsW : 0>(std::make_integer_sequence<int, TM>{});
       __builtin_amdgcn_sched_barrier(0);
@@ -932,9 +937,9 @@ qlin_status launch_tile(const GemmArgs& g, hipStream_t st) {
 template <BOp B, AOp A>
 qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
   if constexpr (A == AOp::U4G) {
-    // Group-wise W4A4: 128-row tiles at every M (the int32 and fp32
-    // accumulators both live in registers).
-    return launch_tile<B, A, 4, 0>(g, st);
+    // Group-wise W4A4: 64-row tiles at every M, two workgroups per CU (the
+    // int32 and fp32 accumulators both live in registers).
+    return launch_tile<B, A, 2, 0>(g, st);
   } else {
     // Up to 128 tokens the K-split skinny kernels (one 64-k unit per wave in
     // flight at 128 rows) beat 128-row tiles, of which there would be fewer
