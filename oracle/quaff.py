@@ -8,6 +8,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import gemm, quant
+
 F32 = np.float32
 
 
@@ -65,3 +67,50 @@ def compensation(q_o: np.ndarray, step_a: np.ndarray, s_o: np.ndarray, w_o: np.n
     xo = np.asarray(q_o, np.float64) * np.asarray(step_a, np.float64)[:, None]
     so = np.asarray(s_o, np.float64) - 1.0
     return xo @ (so[:, None] * np.asarray(w_o, np.float64))
+
+
+def ste_backward_exact(dy: np.ndarray, qw: np.ndarray, sw: np.ndarray, s: np.ndarray, r: np.ndarray,
+                       outliers: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """Input gradient of the layer under the straight-through estimator, in
+    float64 (Quaff notes, "loss function / training strategy": standard STE
+    for backpropagation; the forward is the decoupled form of "key design").
+
+    The forward is Y = X-hat W-hat + X-hat_{:,O} (s_O - 1) W_O with
+    X-hat = Q(X * r), W-hat = W_int * sw (per output channel n).  STE passes the
+    gradient through Q unchanged, so dX-hat/dX = diag(r) and
+      dX = (dY W-hat^T + scatter_O(dY W_O^T * (s_O - 1))) * r.
+    dy [M x N], qw int8 [K x N], sw fp16 [N], s, r fp32 [K], w_o fp16 [nO x N].
+    """
+    d = np.asarray(dy, np.float64)
+    what = np.asarray(qw, np.float64) * np.asarray(sw, np.float64)[None, :]
+    g = d @ what.T
+    o = np.asarray(outliers, np.int64)
+    if o.size:
+        g[:, o] += (d @ np.asarray(w_o, np.float64).T) * (np.asarray(s, np.float64)[o] - 1.0)[None, :]
+    return g * np.asarray(r, np.float64)[None, :]
+
+
+def ste_backward(dy: np.ndarray, qw: np.ndarray, sw: np.ndarray, s: np.ndarray, r: np.ndarray,
+                 outliers: np.ndarray, w_o: np.ndarray):
+    """The STE input gradient with the main product on int8 codes.
+
+    The weight step sw[n] lies along the reduction of dY W-hat^T, so it moves
+    to the gradient: G = dY * sw (fp32, one rounding), quantized per token by
+    the rule of the forward activations (symmetric int8, step gs[m]).  Then
+      acc[m, k] = sum_n gq[m, n] * W_int[k, n]                (exact int32)
+      cb[m, j]  = sum_n dY[m, n] * W_O[j, n]                   (float64)
+      dX[m, k]  = r_k * (gs[m] * acc[m, k] + [k = O_j] (s_k - 1) * cb[m, j])
+    Returns dict(gq, gs, acc, cb, dx) with dx in float64.
+    """
+    gq, gs = quant.quant_act_sym_int8(dy, np.asarray(sw).astype(F32))
+    acc = gemm.exact_int_matmul(gq, np.asarray(qw).T)
+    if acc.size and np.max(np.abs(acc)) >= 2 ** 31:
+        raise ValueError("backward accumulator exceeds int32")
+    o = np.asarray(outliers, np.int64)
+    d = np.asarray(dy, np.float64)
+    cb = d @ np.asarray(w_o, np.float64).T if o.size else np.zeros((d.shape[0], 0))
+    main = acc.astype(np.float64) * np.asarray(gs, np.float64)[:, None]
+    if o.size:
+        main[:, o] += cb * (np.asarray(s, np.float64)[o] - 1.0)[None, :]
+    dx = main * np.asarray(r, np.float64)[None, :]
+    return dict(gq=gq, gs=gs, acc=acc.astype(np.int32), cb=cb, dx=dx)
