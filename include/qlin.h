@@ -64,6 +64,9 @@ typedef int32_t qlin_status;
 #define QLIN_LAYOUT_W4S 2 /* signed int4 codes [-8,7] for qlin_gemm_w4a8            */
 #define QLIN_LAYOUT_W4U 3 /* unsigned int4 codes [0,15] for qlin_gemm_w4a4          */
 #define QLIN_LAYOUT_WO 4  /* fp16 rows W_O [nO x N] for the compensation term       */
+#define QLIN_LAYOUT_W8T 5 /* int8 codes [K x N] packed as their transpose [N x K]   */
+                          /* (reduction over N) for qlin_quaff_backward; needs      */
+                          /* N % 128 == 0 and K % 64 == 0                          */
 
 /* Version of this ABI (QLIN_ABI_VERSION). Host only. */
 int32_t qlin_abi_version(void);
@@ -309,6 +312,34 @@ qlin_status qlin_gemm_w4a4_group(const uint8_t* qa4, const float* sa, const int3
                                  const int32_t* rowsum, const void* w4, const float* sw,
                                  const int32_t* zw, const int32_t* colsum_g, int64_t M, int64_t N,
                                  int64_t K, uint16_t* y, void* stream);
+
+/*
+ * qlin_quaff_backward -- input gradient of the Quaff layer under the
+ * straight-through estimator (Quaff notes, "loss function / training
+ * strategy": standard STE; the forward is the decoupled form of "key design").
+ * STE passes the gradient through the quantizer, so with W-hat = W_int * sw:
+ *   dX = (dY W-hat^T + scatter_O(dY W_O^T * (s_O - 1))) * r
+ * The main product runs on int8 matrix cores: the weight step sw[n] lies along
+ * its reduction, so it moves to the gradient, G = dY * sw (fp32), which is
+ * quantized per token like the forward activations (gq, gs: the rule of
+ * qlin_quant_act).  Then
+ *   acc[m,k] = sum_n gq[m,n] * W_int[k,n]                     (int32)
+ *   cb[m,j]  = sum_n dY[m,n] * W_O[j,n]                        (fp32, fp16 products)
+ *   dX[m,k]  = fp16(r[k] * (gs[m] * acc[m,k] + [k = O[j]] (s[k] - 1) * cb[m,j]))
+ * Three launches on `stream`.  The caller provides the intermediates.
+ *   dy   fp16 [M x N];  sw fp16 [N] (the forward weight steps)
+ *   w8t  W_int packed with QLIN_LAYOUT_W8T (K x N codes; N % 128 == 0)
+ *   s, r fp32 [K]: the momentum state of the forward step (r = 1 / s)
+ *   O, nO  int32 [nO], strictly increasing;  w_o fp16 [nO x N] row-major: the
+ *          rows W_O (not packed).  With nO == 0, O, w_o and cb must be NULL.
+ *   gq int8 [M x N], gs fp32 [M], cb fp32 [M x qlin_outlier_ld(nO)]: scratch
+ *          written here (gq, gs: the quantized gradient; cb as above)
+ *   dx fp16 [M x K] out;  acc int32 [M x K] out or NULL
+ */
+qlin_status qlin_quaff_backward(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint16_t* sw,
+                                const void* w8t, const float* s, const float* r, const int32_t* O, int32_t nO,
+                                const uint16_t* w_o, int8_t* gq, float* gs, float* cb, uint16_t* dx,
+                                int32_t* acc, void* stream);
 
 /*
  * qlin_outlier_comp -- the sparse compensation term on its own, added to an

@@ -38,6 +38,7 @@ SIGNATURES = {
     "qlin_gemm_w4a4": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p, p]),
     "qlin_gemm_w4a4_group": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p]),
     "qlin_outlier_comp": (i32, [p, p, i32, p, i64, i64, p, p]),
+    "qlin_quaff_backward": (i32, [p, i64, i64, i64, p, p, p, p, p, i32, p, p, p, p, p, p, p]),
 }
 
 QLIN_OK = 0
@@ -50,6 +51,7 @@ QLIN_LAYOUT_W8 = 1
 QLIN_LAYOUT_W4S = 2
 QLIN_LAYOUT_W4U = 3
 QLIN_LAYOUT_WO = 4
+QLIN_LAYOUT_W8T = 5
 
 _lib = None
 

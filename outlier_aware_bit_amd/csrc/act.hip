@@ -11,6 +11,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "internal.hpp"
 #include "layout.hpp"
 
 namespace qlin {
@@ -32,15 +33,31 @@ __device__ __forceinline__ void load8_f16(const uint16_t* p, float (&v)[8]) {
   unpack8_f16(*reinterpret_cast<const v4i*>(p), v);
 }
 
-template <bool HAS_R>
-__device__ __forceinline__ void scale_chunk(const float* r, int c, float (&v)[8]) {
+// v *= r for the 8 channels of chunk c; r is fp32, or fp16 (RT = uint16_t,
+// widened exactly to fp32).
+template <bool HAS_R, typename RT>
+__device__ __forceinline__ void scale_chunk(const RT* r, int c, float (&v)[8]) {
   if constexpr (HAS_R) {
-    const float4 r0 = *reinterpret_cast<const float4*>(r + c * 8);
-    const float4 r1 = *reinterpret_cast<const float4*>(r + c * 8 + 4);
-    const float rr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    float rr[8];
+    if constexpr (std::is_same_v<RT, float>) {
+      const float4 r0 = *reinterpret_cast<const float4*>(r + c * 8);
+      const float4 r1 = *reinterpret_cast<const float4*>(r + c * 8 + 4);
+      rr[0] = r0.x; rr[1] = r0.y; rr[2] = r0.z; rr[3] = r0.w;
+      rr[4] = r1.x; rr[5] = r1.y; rr[6] = r1.z; rr[7] = r1.w;
+    } else {
+      load8_f16(r + c * 8, rr);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = mul_rn(v[i], rr[i]);
   }
+}
+
+template <typename RT>
+__device__ __forceinline__ float load_r(const RT* r, int i) {
+  if constexpr (std::is_same_v<RT, float>)
+    return r[i];
+  else
+    return h2f(r[i]);
 }
 
 __device__ __forceinline__ int sym_code(float v, float inv) {
@@ -73,9 +90,9 @@ __device__ __forceinline__ uint2 sym_codes8(const float (&v)[8], float inv) {
 // outlier values are read from there; otherwise they are re-read from memory.
 constexpr int kOutlierLdMax = 256;
 
-template <bool HAS_R, bool OL, int CH>
+template <bool HAS_R, bool OL, int CH, typename RT = float>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ r, int8_t* __restrict__ q,
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const RT* __restrict__ r, int8_t* __restrict__ q,
     float* __restrict__ scale, const int32_t* __restrict__ O, int nO, int ldO,
     const float* __restrict__ s, int8_t* __restrict__ qO, uint16_t* __restrict__ xO) {
   extern __shared__ __attribute__((aligned(16))) uint8_t qlds[];
@@ -107,7 +124,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
 #pragma unroll
     for (int i = 0; i < kOutlierLdMax / 64; ++i) {
       const int o = oj[i] >= 0 ? oj[i] : 0;
-      rj[i] = HAS_R ? r[o] : 1.0f;
+      rj[i] = HAS_R ? load_r(r, o) : 1.0f;
       sm1j[i] = (xO != nullptr && oj[i] >= 0) ? sub_rn(s[o], 1.0f) : 0.0f;
     }
     // The raw row goes to this wave's LDS for the outlier columns.
@@ -199,7 +216,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
       float sm1 = 0.0f;
       if (o >= 0 && o < K) {
         float vv = h2f(xr[o]);
-        if constexpr (HAS_R) vv = mul_rn(vv, r[o]);
+        if constexpr (HAS_R) vv = mul_rn(vv, load_r(r, o));
         code = sym_code(vv, inv);
         if (xO != nullptr) sm1 = sub_rn(s[o], 1.0f);
       }
@@ -463,6 +480,21 @@ __global__ __launch_bounds__(64 * kHadWaves) void hadamard_offset_group_kernel(
 }
 
 }  // namespace
+
+qlin_status launch_quant_grad(const uint16_t* dy, int64_t M, int64_t N, const uint16_t* sw, int8_t* gq, float* gs,
+                              hipStream_t st) {
+  constexpr int rows_per_block = kQuantThreads / 64;
+  const dim3 grid(static_cast<unsigned>((M + rows_per_block - 1) / rows_per_block));
+  if (N <= 4096)
+    quant_act_kernel<true, false, 8, uint16_t><<<grid, kQuantThreads, 0, st>>>(dy, M, N, sw, gq, gs, nullptr, 0, 0,
+                                                                                 nullptr, nullptr, nullptr);
+  else
+    quant_act_kernel<true, false, 16, uint16_t><<<grid, kQuantThreads, 0, st>>>(dy, M, N, sw, gq, gs, nullptr, 0, 0,
+                                                                                  nullptr, nullptr, nullptr);
+  QLIN_LAUNCH_CHECK("quant_act_kernel (gradient)");
+  return QLIN_OK;
+}
+
 }  // namespace qlin
 
 using namespace qlin;

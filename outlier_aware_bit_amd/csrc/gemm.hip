@@ -37,6 +37,7 @@
 
 #include "common.hpp"
 #include "comp.hpp"
+#include "internal.hpp"
 #include "layout.hpp"
 
 namespace qlin {
@@ -60,6 +61,12 @@ struct GemmArgs {
   const uint16_t* xO;     // fp16 [M x ldO] compensation operand (W8A8)
   const uint8_t* WOp;     // packed fp16 W_O
   int ldO;
+  // STE backward (COMP == 3): s [N], outlier indices O [nO] (increasing),
+  // cb fp32 [M x ldO]; sa holds the gradient steps, sw_f the column factors r.
+  const float* s;
+  const int32_t* O;
+  int nO;
+  const float* cb;
   uint16_t* y;
   int32_t* acc;
   int64_t M, N, K;
@@ -419,7 +426,9 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
 // COMP: 0 no compensation term; 1 compensation after the K loop with xO read
 // from memory; 2 compensation before the K loop, while the loop's first
 // operands are in flight, with the tile's xO rows staged in LDS
-// (ldO <= kXOMaxLd).
+// (ldO <= kXOMaxLd); 3 the STE backward epilogue, where output column k is
+// scaled by r[k] and, for an outlier column k = O[j], receives
+// (s[k] - 1) * cb[m, j] first.
 constexpr int kXOMaxLd = 384;
 
 // Group-wise W4A4 tiles are bound by the vector ALU (the per-group fold of
@@ -432,10 +441,12 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
   // token steps (and W4A4 zero points / row sums) of its BM rows and the
   // column steps (and W4A4 zero points / column sums) of its 256 columns.
   constexpr bool kGrp = (A == AOp::U4G);
-  constexpr int kRowC = (B == BOp::W4U && !kGrp) ? 3 : 1, kColC = (B == BOp::W4U) ? 3 : 1;
+  constexpr bool kBwd = (COMP == 3);
+  constexpr int kRowC = (B == BOp::W4U && !kGrp) ? 3 : 1, kColC = (B == BOp::W4U || kBwd) ? 3 : 1;
   // COMP == 2 stages the tile's xO rows (BM x ldO fp16, unpadded) in the
   // same space before the activation stages are first written.
   constexpr int kXO = (COMP == 2) ? T::BM * 2 * kXOMaxLd : 0;
+  static_assert(!kBwd || (B == BOp::W8 && A == AOp::I8), "the backward epilogue is int8 x int8");
   constexpr int kMainBytes = (kXO > 3 * T::kStage) ? kXO : 3 * T::kStage;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kMainBytes + 4 * (kRowC * T::BM + kColC * kBN)];
   [[maybe_unused]] uint8_t* const xlds = lds;
@@ -485,7 +496,7 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
   // arrive during the prologue instead of costing a round trip at the end.
   // Thread t takes column n0 + t and, if t < BM, row m0 + t (both clamped).
   float k_sa = 0.0f, k_sw;
-  [[maybe_unused]] int32_t k_za = 0, k_rs = 0, k_zw = 0, k_cs = 0;
+  [[maybe_unused]] int32_t k_za = 0, k_rs = 0, k_zw = 0, k_cs = 0, k_o = -1;
   {
     const int t = threadIdx.x;
     int64_t mc = m0 + (t < T::BM ? t : 0);
@@ -502,6 +513,13 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
       k_sw = g.sw_f[nc];
       k_zw = g.zw[nc];
       k_cs = g.colsum[nc];
+    } else if constexpr (kBwd) {
+      // Gradient step, r[k], s[k] - 1 and the first outlier index this
+      // thread checks against the tile's columns.
+      k_sa = g.sa[mc];
+      k_sw = g.sw_f[nc];
+      k_cs = __builtin_bit_cast(int32_t, sub_rn(g.s[nc], 1.0f));
+      k_o = t < g.nO ? g.O[t] : -1;
     } else {
       k_sa = g.sa[mc];
       k_sw = h2f(g.sw_h[nc]);
@@ -509,8 +527,9 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
   }
   auto clamp_s = [S](int t) { return t < S ? t : S - 1; };
   // fp32 accumulators: the compensation term (COMP), or the scaled group sums.
-  [[maybe_unused]] v16f cf[(COMP || kGrp) ? TM : 1][2];
-  if constexpr (COMP != 0 || kGrp) {
+  constexpr bool kCF = COMP == 1 || COMP == 2 || kGrp;
+  [[maybe_unused]] v16f cf[kCF ? TM : 1][2];
+  if constexpr (kCF) {
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -581,8 +600,22 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
       c_zw[t] = k_zw;
       c_cs[t] = k_cs;
     }
+    if constexpr (kBwd) {
+      c_zw[t] = -1;  // outlier index of the column, marked below
+      c_cs[t] = k_cs;
+    }
   }
   lds_barrier();
+  if constexpr (kBwd) {
+    // Mark the tile's outlier columns: c_zw[O[j] - n0] = j.  The marks are
+    // read only after the K loop's barriers.
+    const int t = threadIdx.x;
+    if (k_o >= n0 && k_o < n0 + kBN) c_zw[k_o - n0] = t;
+    for (int j = t + kTileThreads; j < g.nO; j += kTileThreads) {
+      const int o = g.O[j];
+      if (o >= n0 && o < n0 + kBN) c_zw[o - n0] = j;
+    }
+  }
   read_frags<TM>(lds, 0, af[0]);
 
   constexpr int kVmB = (B == BOp::W8) ? 2 : 1;                           // B loads per k step
@@ -733,6 +766,7 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
           zw = *reinterpret_cast<const v4i*>(c_zw + cb);
           cs = *reinterpret_cast<const v4i*>(c_cs + cb);
         }
+        if constexpr (kBwd) zw = *reinterpret_cast<const v4i*>(c_zw + cb);
         v4i iv;
         uint16_t hv[4];
 #pragma unroll
@@ -746,7 +780,17 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
           }
           iv[j] = val;
           float f;
-          if constexpr (kGrp)
+          if constexpr (kBwd) {
+            // r[k] * (gs[m] * acc + (s[k] - 1) * cb[m, o]) for outlier column k = O[o].
+            f = static_cast<float>(val) * sam;
+            const int o = zw[j];
+            if (o >= 0) {
+              const int64_t mcl = m < g.M ? m : g.M - 1;
+              const float sm1 = __builtin_bit_cast(float, c_cs[cb + j]);
+              f = fmaf(sm1, g.cb[mcl * g.ldO + o], f);
+            }
+            f = f * sw[j];
+          } else if constexpr (kGrp)
             f = (cf[tm][nt][4 * q + j] - static_cast<float>(zw[j]) * P[tm]) * sw[j];
           else if constexpr (COMP == 1)
             f = cf[tm][nt][4 * q + j];  // acc * sw + compensation
@@ -754,7 +798,7 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
             f = static_cast<float>(val) * sw[j] + cf[tm][nt][4 * q + j];
           else
             f = static_cast<float>(val) * sw[j];
-          hv[j] = f2h(f * sam);
+          hv[j] = f2h(kBwd ? f : f * sam);
         }
         *reinterpret_cast<uint2*>(out_lds + r * kOutPitch + (32 * nt + 8 * q + 4 * h) * 2) =
             make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
@@ -979,6 +1023,27 @@ GemmArgs base_args(int64_t M, int64_t N, int64_t K, uint16_t* y, int32_t* acc) {
 }
 
 }  // namespace
+
+qlin_status launch_gemm_bwd(const int8_t* gq, const float* gs, const void* w8t, const float* r, const float* s,
+                            const int32_t* O, int32_t nO, const float* cb, int64_t M, int64_t N, int64_t K,
+                            uint16_t* dx, int32_t* acc, hipStream_t st) {
+  // The product's reduction runs over N (the forward's output channels) and
+  // its columns are the forward's K input channels.
+  GemmArgs g = base_args(M, K, N, dx, acc);
+  g.a = gq;
+  g.sa = gs;
+  g.b = static_cast<const uint8_t*>(w8t);
+  g.sw_f = r;
+  g.s = s;
+  g.O = O;
+  g.nO = nO;
+  g.cb = cb;
+  g.ldO = static_cast<int>(outlier_ld(nO));
+  const int64_t tiles_n = (g.N + kBN - 1) / kBN;
+  if (((g.M + 255) / 256) * tiles_n >= 256) return launch_tile<BOp::W8, AOp::I8, 8, 3>(g, st);
+  return launch_tile<BOp::W8, AOp::I8, 4, 3>(g, st);
+}
+
 }  // namespace qlin
 
 using namespace qlin;

@@ -7,6 +7,7 @@
 // Spatial Stability Hypothesis" (paper notes), "key design".
 #include "common.hpp"
 #include "comp.hpp"
+#include "internal.hpp"
 #include "layout.hpp"
 
 namespace qlin {
@@ -158,6 +159,65 @@ __global__ __launch_bounds__(kCompThreads) void outlier_comp_kernel(
   }
 }
 
+// STE backward, compensation part: cb[m, j] = sum_n dy[m, n] * w_o[j, n] in
+// fp32 (fp16 products on the matrix cores), j < ldO, zero for j >= nO.  A
+// workgroup takes 32 rows and kGradCB column blocks of 32; its four waves take
+// interleaved 16-wide steps of n, and their partial sums are added in a
+// fixed order through LDS (the result does not depend on timing).  Both operands are
+// row-major with n contiguous, which is the fragment order of
+// v_mfma_f32_32x32x16_f16 (8 consecutive n per lane).
+constexpr int kGradCB = 4, kGradThreads = 256;
+
+__global__ __launch_bounds__(kGradThreads) void outlier_grad_kernel(const uint16_t* __restrict__ dy,
+                                                                   const uint16_t* __restrict__ w_o, int64_t M,
+                                                                   int64_t N, int nO, int ldO,
+                                                                   float* __restrict__ cb) {
+  __shared__ float red[kGradThreads / 64][kGradCB][16][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 32;
+  const int jb0 = blockIdx.y * kGradCB;
+  int64_t m = m0 + (lane & 31);
+  m = m < M ? m : M - 1;
+  const uint16_t* arow = dy + m * N + 8 * (lane >> 5);
+  const uint16_t* brow[kGradCB];
+  bool bok[kGradCB];
+#pragma unroll
+  for (int b = 0; b < kGradCB; ++b) {
+    const int j = 32 * (jb0 + b) + (lane & 31);
+    bok[b] = j < nO;
+    brow[b] = w_o + static_cast<int64_t>(bok[b] ? j : 0) * N + 8 * (lane >> 5);
+  }
+  v16f acc[kGradCB];
+#pragma unroll
+  for (int b = 0; b < kGradCB; ++b) acc[b] = v16f{};
+  const int steps = static_cast<int>(N / 16);
+#pragma unroll 4
+  for (int ks = wave; ks < steps; ks += kGradThreads / 64) {
+    const v8h a = *reinterpret_cast<const v8h*>(arow + 16 * static_cast<int64_t>(ks));
+#pragma unroll
+    for (int b = 0; b < kGradCB; ++b) {
+      v8h bb = *reinterpret_cast<const v8h*>(brow[b] + 16 * static_cast<int64_t>(ks));
+      if (!bok[b]) bb = v8h{};
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bb, acc[b], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < kGradCB; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red[wave][b][v][lane] = acc[b][v];
+  __syncthreads();
+  // Wave w stores block w: lane l holds column (l & 31) and rows frag_row(v, l).
+  static_assert(kGradCB == kGradThreads / 64, "one column block per wave");
+  const int j = 32 * (jb0 + wave) + (lane & 31);
+  if (j >= ldO) return;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t row = m0 + frag_row(v, lane);
+    const float sum = ((red[0][wave][v][lane] + red[1][wave][v][lane]) + red[2][wave][v][lane]) + red[3][wave][v][lane];
+    if (row < M) cb[row * ldO + j] = sum;
+  }
+}
+
 }  // namespace
 }  // namespace qlin
 
@@ -215,4 +275,44 @@ extern "C" qlin_status qlin_outlier_comp(const uint16_t* xO, const float* sa, in
       xO, static_cast<int>(outlier_ld(nO)), sa, static_cast<const uint8_t*>(WO), M, N, y);
   QLIN_LAUNCH_CHECK("outlier_comp_kernel");
   return QLIN_OK;
+}
+
+extern "C" qlin_status qlin_quaff_backward(const uint16_t* dy, int64_t M, int64_t N, int64_t K,
+                                           const uint16_t* sw, const void* w8t, const float* s, const float* r,
+                                           const int32_t* O, int32_t nO, const uint16_t* w_o, int8_t* gq,
+                                           float* gs, float* cb, uint16_t* dx, int32_t* acc, void* stream) {
+  QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
+  QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_REQUIRE(N > 0 && N % 128 == 0, QLIN_ERR_SHAPE, "N=%lld must be a positive multiple of 128", (long long)N);
+  QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
+  if (M == 0) return QLIN_OK;
+  QLIN_PTR(dy);
+  QLIN_PTR(sw);
+  QLIN_PTR(w8t);
+  QLIN_PTR(s);
+  QLIN_PTR(r);
+  QLIN_PTR(gq);
+  QLIN_PTR(gs);
+  QLIN_PTR(dx);
+  QLIN_OPT_PTR(acc);
+  if (nO > 0) {
+    QLIN_PTR(O);
+    QLIN_PTR(w_o);
+    QLIN_PTR(cb);
+  } else {
+    QLIN_REQUIRE(O == nullptr && w_o == nullptr && cb == nullptr, QLIN_ERR_INVALID_ARG,
+                 "O, w_o and cb must be NULL when nO == 0");
+  }
+  const int64_t gx = (M + 31) / 32;
+  QLIN_REQUIRE(gx <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
+  hipStream_t st = as_stream(stream);
+  qlin_status rc = launch_quant_grad(dy, M, N, sw, gq, gs, st);
+  if (rc != QLIN_OK) return rc;
+  if (nO > 0) {
+    const int ldO = static_cast<int>(outlier_ld(nO));
+    const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>((ldO + 32 * kGradCB - 1) / (32 * kGradCB)));
+    outlier_grad_kernel<<<grid, kGradThreads, 0, st>>>(dy, w_o, M, N, nO, ldO, cb);
+    QLIN_LAUNCH_CHECK("outlier_grad_kernel");
+  }
+  return launch_gemm_bwd(gq, gs, w8t, r, s, O, nO, cb, M, N, K, dx, acc, st);
 }

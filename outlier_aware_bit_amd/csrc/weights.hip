@@ -175,6 +175,9 @@ __global__ __launch_bounds__(kColThreads) void colsum_group_kernel(const uint8_t
 
 // ---------------------------------------------------------------- packing
 // One thread writes one 16-byte lane chunk of the packed layout (layout.hpp).
+// K and N are those of the packed matrix; TRANSPOSED packs the transpose of
+// codes [N x K] (row-major), so that element (k, n) is codes[n * K + k].
+template <bool TRANSPOSED>
 __global__ void pack_w8_kernel(const int8_t* __restrict__ codes, int64_t K, int64_t N,
                                uint8_t* __restrict__ out) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -185,8 +188,10 @@ __global__ void pack_w8_kernel(const int8_t* __restrict__ codes, int64_t K, int6
   const int64_t n = nt * 32 + (lane & 31);
   const int64_t kb = s * 32 + 16 * (lane >> 5);
   uint32_t word[4] = {0, 0, 0, 0};
-  for (int j = 0; j < 16; ++j)
-    word[j >> 2] |= static_cast<uint32_t>(static_cast<uint8_t>(codes[(kb + j) * N + n])) << (8 * (j & 3));
+  for (int j = 0; j < 16; ++j) {
+    const int8_t c = TRANSPOSED ? codes[n * K + kb + j] : codes[(kb + j) * N + n];
+    word[j >> 2] |= static_cast<uint32_t>(static_cast<uint8_t>(c)) << (8 * (j & 3));
+  }
   *reinterpret_cast<uint4*>(out + q * 16) = make_uint4(word[0], word[1], word[2], word[3]);
 }
 
@@ -307,11 +312,14 @@ extern "C" int32_t qlin_outlier_ld(int32_t nO) {
 }
 
 extern "C" size_t qlin_packed_bytes(int32_t layout, int64_t K, int64_t N) {
+  // The transposed layout packs the [N x K] matrix: N is its reduction length.
+  if (layout == QLIN_LAYOUT_W8T) return (K <= 0 || K % 64 || N <= 0 || N % 128) ? 0 : static_cast<size_t>(K * N);
   if (N <= 0 || N % 64) return 0;
   if (layout == QLIN_LAYOUT_WO) return K <= 0 ? 0 : static_cast<size_t>(outlier_ld(K) * N * 2);
   if (K <= 0 || K % 128) return 0;
   switch (layout) {
     case QLIN_LAYOUT_W8: return static_cast<size_t>(K * N);
+    case QLIN_LAYOUT_W8T: return static_cast<size_t>(K * N);
     case QLIN_LAYOUT_W4S:
     case QLIN_LAYOUT_W4U: return static_cast<size_t>(K * N / 2);
     default: return 0;
@@ -321,9 +329,11 @@ extern "C" size_t qlin_packed_bytes(int32_t layout, int64_t K, int64_t N) {
 extern "C" qlin_status qlin_pack_weight(int32_t layout, const void* codes, int64_t K, int64_t N,
                                         void* packed, void* stream) {
   QLIN_REQUIRE(layout == QLIN_LAYOUT_W8 || layout == QLIN_LAYOUT_W4S || layout == QLIN_LAYOUT_W4U ||
-                   layout == QLIN_LAYOUT_WO,
+                   layout == QLIN_LAYOUT_WO || layout == QLIN_LAYOUT_W8T,
                QLIN_ERR_INVALID_ARG, "layout=%d is not a QLIN_LAYOUT_* value", layout);
-  if (layout == QLIN_LAYOUT_WO) {
+  if (layout == QLIN_LAYOUT_W8T) {
+    QLIN_K_N(N, K);  // the packed matrix is [N x K]
+  } else if (layout == QLIN_LAYOUT_WO) {
     QLIN_REQUIRE(K > 0, QLIN_ERR_SHAPE, "nO=%lld must be positive", (long long)K);
     QLIN_REQUIRE(N > 0 && N % 64 == 0, QLIN_ERR_SHAPE, "N=%lld must be a positive multiple of 64", (long long)N);
   } else {
@@ -335,8 +345,12 @@ extern "C" qlin_status qlin_pack_weight(int32_t layout, const void* codes, int64
   hipStream_t st = as_stream(stream);
   if (layout == QLIN_LAYOUT_W8) {
     const int64_t total = K * N / 16;
-    pack_w8_kernel<<<dim3(static_cast<unsigned>((total + T - 1) / T)), T, 0, st>>>(
+    pack_w8_kernel<false><<<dim3(static_cast<unsigned>((total + T - 1) / T)), T, 0, st>>>(
         static_cast<const int8_t*>(codes), K, N, static_cast<uint8_t*>(packed));
+  } else if (layout == QLIN_LAYOUT_W8T) {
+    const int64_t total = K * N / 16;
+    pack_w8_kernel<true><<<dim3(static_cast<unsigned>((total + T - 1) / T)), T, 0, st>>>(
+        static_cast<const int8_t*>(codes), N, K, static_cast<uint8_t*>(packed));
   } else if (layout == QLIN_LAYOUT_WO) {
     const int64_t ldO = outlier_ld(K);
     const int64_t total = ldO * N / 8;

@@ -10,7 +10,7 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import QLIN_LAYOUT_W4S, QLIN_LAYOUT_W4U, QLIN_LAYOUT_W8, QLIN_LAYOUT_WO, QlinError  # noqa: F401
+from ._lib import QLIN_LAYOUT_W4S, QLIN_LAYOUT_W4U, QLIN_LAYOUT_W8, QLIN_LAYOUT_W8T, QLIN_LAYOUT_WO, QlinError  # noqa: F401
 
 
 def _stream():
@@ -204,7 +204,7 @@ def qlin_packed_bytes(layout, K, N) -> int:
 
 
 def qlin_pack_weight(layout, codes, out=None):
-    """Pack weights (int8 codes for W8/W4S, uint8 for W4U, fp16 rows for WO)."""
+    """Pack weights (int8 codes for W8/W4S/W8T, uint8 for W4U, fp16 rows for WO)."""
     lib = _lib.load()
     dt = {QLIN_LAYOUT_W4U: torch.uint8, QLIN_LAYOUT_WO: torch.float16}.get(layout, torch.int8)
     _req(codes, "codes", dt)
@@ -295,6 +295,35 @@ def qlin_gemm_w4a4_group(qa4, sa, za, rowsum, w4, sw, zw, colsum_g, N, y=None):
         qa4.data_ptr(), sa.data_ptr(), za.data_ptr(), rowsum.data_ptr(), w4.data_ptr(), sw.data_ptr(), zw.data_ptr(),
         colsum_g.data_ptr(), M, N, K, y.data_ptr(), _stream()))
     return y
+
+
+def qlin_quaff_backward(dy, sw, w8t, s, r, K, O=None, w_o=None, want_acc=False, dx=None, gq=None, gs=None, cb=None):
+    """STE input gradient of the Quaff layer: dX [M, K] (fp16).  w8t is the
+    int8 weight packed with QLIN_LAYOUT_W8T, w_o the fp16 rows W[O].
+    Returns (dx, gq, gs, cb or None, acc or None)."""
+    lib = _lib.load()
+    _req(dy, "dy", torch.float16)
+    M, N = dy.shape
+    _req(sw, "sw", torch.float16, (N,))
+    _req(w8t, "w8t", torch.uint8, (qlin_packed_bytes(QLIN_LAYOUT_W8T, K, N),))
+    _req(s, "s", torch.float32, (K,))
+    _req(r, "r", torch.float32, (K,))
+    nO = 0 if O is None else O.numel()
+    if nO:
+        _req(O, "O", torch.int32, (nO,))
+        _req(w_o, "w_o", torch.float16, (nO, N))
+        ld = qlin_outlier_ld(nO)
+        cb = _req(cb, "cb", torch.float32, (M, ld)) if cb is not None else _empty((M, ld), torch.float32, dy)
+    else:
+        O = w_o = cb = None
+    gq = _req(gq, "gq", torch.int8, (M, N)) if gq is not None else _empty((M, N), torch.int8, dy)
+    gs = _req(gs, "gs", torch.float32, (M,)) if gs is not None else _empty((M,), torch.float32, dy)
+    dx = _req(dx, "dx", torch.float16, (M, K)) if dx is not None else _empty((M, K), torch.float16, dy)
+    acc = _empty((M, K), torch.int32, dy) if want_acc else None
+    _lib.check("qlin_quaff_backward", lib.qlin_quaff_backward(
+        dy.data_ptr(), M, N, K, sw.data_ptr(), w8t.data_ptr(), s.data_ptr(), r.data_ptr(), _ptr(O), nO, _ptr(w_o),
+        gq.data_ptr(), gs.data_ptr(), _ptr(cb), dx.data_ptr(), _ptr(acc), _stream()))
+    return dx, gq, gs, cb, acc
 
 
 def qlin_outlier_comp(xO, sa, nO, WO, y):

@@ -108,6 +108,12 @@ def quaff_steps(M: int = 2048, K: int = 4096, N: int = 4096, n_outliers: int = 2
     return QuaffSteps(xs, w, o, mags, seed)
 
 
+def grad_output(M: int, N: int, seed: int, std: float = 1.0) -> np.ndarray:
+    """Upstream gradient dL/dY for a backward pass: N(0, std^2), fp16 [M x N]."""
+    rng = np.random.default_rng(seed)
+    return _normal16(rng, (M, N), std)
+
+
 def qqq_decode(M: int, K: int = 4096, N: int = 11008, seed: int = 2) -> Linear:
     """Decode / small-batch tokens: N(0,1) with 1% outlier channels x100."""
     return plain_linear(M, K, N, seed, n_outliers=max(1, round(0.01 * K)))

@@ -66,6 +66,11 @@ def test_packed_bytes():
     assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8, 4096, 100) == 0
     assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_WO, 205, 4096) == 208 * 4096 * 2
     assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_WO, 0, 4096) == 0
+    # the transposed int8 layout packs [N x K]: N % 128, K % 64
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8T, 4096, 4096) == 4096 * 4096
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8T, 64, 128) == 64 * 128
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8T, 4096, 64) == 0
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8T, 100, 4096) == 0
     assert [lib.qlin_outlier_ld(n) for n in (0, 1, 16, 17, 205)] == [0, 16, 16, 32, 208]
 
 
@@ -151,6 +156,30 @@ def test_gemm_validation():
     _err(lib.qlin_outlier_comp(A, A, 4, MIS, 16, 128, A, None), _lib.QLIN_ERR_ALIGN)
     _err(lib.qlin_outlier_comp(A, A, 0, A, 16, 128, A, None), _lib.QLIN_OK)
     _err(lib.qlin_pack_weight(_lib.QLIN_LAYOUT_WO, A, 0, 128, B, None), _lib.QLIN_ERR_SHAPE)
+
+
+def test_group_and_backward_validation():
+    lib = _lib.load()
+    _err(lib.qlin_hadamard_offset_group(A, 4, 256, B, 64, A, A, A, A, None, None), _lib.QLIN_ERR_UNSUPPORTED)
+    _err(lib.qlin_hadamard_offset_group(A, 4, 192, B, 128, A, A, A, A, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_hadamard_offset_group(A, 4, 256, B, 128, A, None, A, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_hadamard_offset_group(A, 0, 256, B, 128, A, A, A, A, None, None), _lib.QLIN_OK)
+    _err(lib.qlin_weight_colsum_group(A, 256, 128, 64, A, None), _lib.QLIN_ERR_UNSUPPORTED)
+    _err(lib.qlin_weight_colsum_group(A, 200, 128, 128, A, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_weight_colsum_group(A, 256, 128, 128, MIS, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_gemm_w4a4_group(A, A, A, A, B, A, A, None, 16, 128, 256, A, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w4a4_group(A, A, A, A, B, A, A, A, 16, 100, 256, A, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_gemm_w4a4_group(A, A, A, A, B, A, A, A, 0, 128, 256, A, None), _lib.QLIN_OK)
+    bw = [A, 8, 256, 128, A, B, A, A, A, 3, A, A, A, A, A, None, None]
+    _err(lib.qlin_quaff_backward(A, 8, 192, 128, *bw[4:]), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_quaff_backward(A, 8, 256, 192, *bw[4:]), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_quaff_backward(A, 8, 256, 128, *bw[4:9], 200, *bw[10:]), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_quaff_backward(A, 8, 256, 128, *bw[4:10], None, *bw[11:]), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_quaff_backward(A, 8, 256, 128, *bw[4:8], None, 0, None, A, A, A, A, None, None),
+         _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_quaff_backward(A, 8, 256, 128, *bw[4:14], MIS, None, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_quaff_backward(A, 0, 256, 128, *bw[4:]), _lib.QLIN_OK)
+    _err(lib.qlin_pack_weight(_lib.QLIN_LAYOUT_W8T, A, 128, 200, B, None), _lib.QLIN_ERR_SHAPE)
 
 
 def test_binding_refuses_cpu_tensors():
