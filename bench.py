@@ -149,7 +149,8 @@ class QuaffLayer:
         w = dev(d.w)
         codes, self.sw = q.qlin_quant_weight_sym(w, 8)
         self.w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
-        WO = dev(np.ascontiguousarray(d.w[d.outliers]))
+        self.w8t = q.qlin_pack_weight(q.QLIN_LAYOUT_W8T, codes)  # for the STE backward
+        WO = self.WO = dev(np.ascontiguousarray(d.w[d.outliers]))
         self.WOp = q.qlin_pack_weight(q.QLIN_LAYOUT_WO, WO)
         self.wmax = q.qlin_weight_row_absmax(WO)
         self.s = torch.ones(K, dtype=torch.float32, device="cuda")
@@ -283,6 +284,21 @@ def rows_measurements(q, layer):
     out["A5_outlier_comp_standalone"] = dict(workload=f"{M}x{nO}x{N}", ms=t, flops=fl, tflops=fl / t / 1e9,
                                              frac=fl / t / 1e9 / PEAK_FP16_TFLOPS, bound="mfma")
     del y2
+
+    # Quaff STE backward at the same shape: quantized gradient, the outlier
+    # product dY W_O^T and the int8 product against the transposed weights.
+    w8t = layer.w8t
+    import synth as _synth
+    dy = dev(_synth.grad_output(M, N, seed=5))
+    dx, gq, gs, cbuf, _ = q.qlin_quaff_backward(dy, layer.sw, w8t, layer.s, layer.r, K, O=layer.O, w_o=layer.WO)
+    t = time_launches(lambda i: q.qlin_quaff_backward(dy, layer.sw, w8t, layer.s, layer.r, K, O=layer.O,
+                                                      w_o=layer.WO, dx=dx, gq=gq, gs=gs, cb=cbuf), 100)
+    ops = 2 * M * N * K + 2 * (2 * M * nO * N)
+    out["NEXT3_quaff_ste_backward"] = dict(workload=f"dX {M}x{K} from dY {M}x{N}, |O|={nO}", ms=t,
+                                           int8_equiv_ops=ops, tops=ops / t / 1e9,
+                                           frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma",
+                                           launches="quantize dY*sw, dY W_O^T, int8 GEMM with the fix-up epilogue")
+    del dy, dx, gq, gs, cbuf
 
     # QQQ W4A8 per-channel decode, weights rotated through >= 2x the MALL.
     import synth

@@ -333,7 +333,8 @@ qlin_status qlin_gemm_w4a4_group(const uint8_t* qa4, const float* sa, const int3
  *   O, nO  int32 [nO], strictly increasing;  w_o fp16 [nO x N] row-major: the
  *          rows W_O (not packed).  With nO == 0, O, w_o and cb must be NULL.
  *   gq int8 [M x N], gs fp32 [M], cb fp32 [M x qlin_outlier_ld(nO)]: scratch
- *          written here (gq, gs: the quantized gradient; cb as above)
+ *          written here (gq, gs: the quantized gradient; cb as above, zero in
+ *          the columns nO..ldO-1)
  *   dx fp16 [M x K] out;  acc int32 [M x K] out or NULL
  */
 qlin_status qlin_quaff_backward(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint16_t* sw,

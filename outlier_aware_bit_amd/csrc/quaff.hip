@@ -160,45 +160,62 @@ __global__ __launch_bounds__(kCompThreads) void outlier_comp_kernel(
 }
 
 // STE backward, compensation part: cb[m, j] = sum_n dy[m, n] * w_o[j, n] in
-// fp32 (fp16 products on the matrix cores), j < ldO, zero for j >= nO.  A
-// workgroup takes 32 rows and kGradCB column blocks of 32; its four waves take
-// interleaved 16-wide steps of n, and their partial sums are added in a
-// fixed order through LDS (the result does not depend on timing).  Both operands are
-// row-major with n contiguous, which is the fragment order of
-// v_mfma_f32_32x32x16_f16 (8 consecutive n per lane).
-constexpr int kGradCB = 4, kGradThreads = 256;
+// fp32 (fp16 products on the matrix cores) for j < ldO, zero for j >= nO.
+// A small, latency-bound product (N long, ldO narrow): a workgroup takes 32
+// rows and kGradCB column blocks of 32, and its kGradWaves waves each take
+// one contiguous slice of n, with all loads of kGradU steps in flight before
+// their products.  The slices' sums are added in a fixed order through LDS,
+// so the result does not depend on timing.  Both operands are row-major with
+// n contiguous: the fragment order of v_mfma_f32_32x32x16_f16 (8 consecutive
+// n per lane).
+constexpr int kGradCB = 2, kGradWaves = 8, kGradThreads = 64 * kGradWaves, kGradU = 8;
 
 __global__ __launch_bounds__(kGradThreads) void outlier_grad_kernel(const uint16_t* __restrict__ dy,
                                                                    const uint16_t* __restrict__ w_o, int64_t M,
                                                                    int64_t N, int nO, int ldO,
                                                                    float* __restrict__ cb) {
-  __shared__ float red[kGradThreads / 64][kGradCB][16][64];
+  __shared__ float red[kGradWaves][kGradCB][16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 32;
   const int jb0 = blockIdx.y * kGradCB;
+  const int64_t slice = N / kGradWaves;  // a multiple of 16 (N % 128 == 0)
+  const int64_t nw = slice * wave;
   int64_t m = m0 + (lane & 31);
   m = m < M ? m : M - 1;
-  const uint16_t* arow = dy + m * N + 8 * (lane >> 5);
+  const uint16_t* arow = dy + m * N + nw + 8 * (lane >> 5);
   const uint16_t* brow[kGradCB];
   bool bok[kGradCB];
 #pragma unroll
   for (int b = 0; b < kGradCB; ++b) {
     const int j = 32 * (jb0 + b) + (lane & 31);
     bok[b] = j < nO;
-    brow[b] = w_o + static_cast<int64_t>(bok[b] ? j : 0) * N + 8 * (lane >> 5);
+    brow[b] = w_o + static_cast<int64_t>(bok[b] ? j : 0) * N + nw + 8 * (lane >> 5);
   }
   v16f acc[kGradCB];
 #pragma unroll
   for (int b = 0; b < kGradCB; ++b) acc[b] = v16f{};
-  const int steps = static_cast<int>(N / 16);
-#pragma unroll 4
-  for (int ks = wave; ks < steps; ks += kGradThreads / 64) {
+  const int steps = static_cast<int>(slice / 16);
+  int ks = 0;
+  for (; ks + kGradU <= steps; ks += kGradU) {
+    v8h a[kGradU], bb[kGradU][kGradCB];
+#pragma unroll
+    for (int u = 0; u < kGradU; ++u) {
+      a[u] = *reinterpret_cast<const v8h*>(arow + 16 * static_cast<int64_t>(ks + u));
+#pragma unroll
+      for (int b = 0; b < kGradCB; ++b) bb[u][b] = *reinterpret_cast<const v8h*>(brow[b] + 16 * static_cast<int64_t>(ks + u));
+    }
+#pragma unroll
+    for (int u = 0; u < kGradU; ++u)
+#pragma unroll
+      for (int b = 0; b < kGradCB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[u], bok[b] ? bb[u][b] : v8h{}, acc[b], 0, 0, 0);
+  }
+  for (; ks < steps; ++ks) {
     const v8h a = *reinterpret_cast<const v8h*>(arow + 16 * static_cast<int64_t>(ks));
 #pragma unroll
     for (int b = 0; b < kGradCB; ++b) {
-      v8h bb = *reinterpret_cast<const v8h*>(brow[b] + 16 * static_cast<int64_t>(ks));
-      if (!bok[b]) bb = v8h{};
-      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bb, acc[b], 0, 0, 0);
+      const v8h bv = *reinterpret_cast<const v8h*>(brow[b] + 16 * static_cast<int64_t>(ks));
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bok[b] ? bv : v8h{}, acc[b], 0, 0, 0);
     }
   }
 #pragma unroll
@@ -206,15 +223,16 @@ __global__ __launch_bounds__(kGradThreads) void outlier_grad_kernel(const uint16
 #pragma unroll
     for (int v = 0; v < 16; ++v) red[wave][b][v][lane] = acc[b][v];
   __syncthreads();
-  // Wave w stores block w: lane l holds column (l & 31) and rows frag_row(v, l).
-  static_assert(kGradCB == kGradThreads / 64, "one column block per wave");
-  const int j = 32 * (jb0 + wave) + (lane & 31);
-  if (j >= ldO) return;
+  // Thread t adds up elements e = t, t + kGradThreads, ... of the tile
+  // (block b, register v, lane l), the slices in order.
+  for (int e = threadIdx.x; e < kGradCB * 16 * 64; e += kGradThreads) {
+    const int b = e / (16 * 64), v = (e / 64) % 16, l = e % 64;
+    const int j = 32 * (jb0 + b) + (l & 31);
+    const int64_t row = m0 + frag_row(v, l);
+    float sum = red[0][b][v][l];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t row = m0 + frag_row(v, lane);
-    const float sum = ((red[0][wave][v][lane] + red[1][wave][v][lane]) + red[2][wave][v][lane]) + red[3][wave][v][lane];
-    if (row < M) cb[row * ldO + j] = sum;
+    for (int w = 1; w < kGradWaves; ++w) sum += red[w][b][v][l];
+    if (j < ldO && row < M) cb[row * ldO + j] = sum;
   }
 }
 

@@ -300,7 +300,7 @@ def qlin_gemm_w4a4_group(qa4, sa, za, rowsum, w4, sw, zw, colsum_g, N, y=None):
 def qlin_quaff_backward(dy, sw, w8t, s, r, K, O=None, w_o=None, want_acc=False, dx=None, gq=None, gs=None, cb=None):
     """STE input gradient of the Quaff layer: dX [M, K] (fp16).  w8t is the
     int8 weight packed with QLIN_LAYOUT_W8T, w_o the fp16 rows W[O].
-    Returns (dx, gq, gs, cb or None, acc or None)."""
+    Returns (dx, gq, gs, cb or None, acc or None); cb = dY W_O^T [M, qlin_outlier_ld(nO)]."""
     lib = _lib.load()
     _req(dy, "dy", torch.float16)
     M, N = dy.shape

@@ -226,3 +226,27 @@ def test_token_sweep_llama7b(q):
             acc_ref, y_ref = gemm.w8a8(q_ref[rows], sa_ref[rows], wq, ws.astype(np.float32))
             assert_equal(host(acc)[rows], acc_ref, f"{name} acc M={M}")
             assert_close(host(y)[rows], y_ref, f"{name} y M={M}")
+
+
+def test_quaff_q_proj_backward(q):
+    # The STE backward at the q_proj shape with the momentum state of one
+    # forward step: gradient codes and steps in full, acc and dX on sampled rows.
+    M, K, N, nO = 2048, 4096, 4096, 205
+    log(f"Quaff q_proj backward {M}x{N}x{K} |O|={nO}")
+    d = synth.quaff_steps(M=M, K=K, N=N, n_outliers=nO, steps=1, seed=1)
+    prep = layer.quaff_prepare(d.w, d.outliers)
+    o = d.outliers.astype(np.int64)
+    s_ref, r_ref = quaff.momentum_update(d.xs[0], o, prep["wmax"], 0.9, np.ones(K, np.float32))
+    dy = synth.grad_output(M, N, seed=5)
+    codes, sw = q.qlin_quant_weight_sym(dev(d.w), 8)
+    w8t = q.qlin_pack_weight(q.QLIN_LAYOUT_W8T, codes)
+    dx, gq, gs, cb, acc = q.qlin_quaff_backward(dev(dy), sw, w8t, dev(s_ref), dev(r_ref), K, O=dev(d.outliers),
+                                                w_o=dev(np.ascontiguousarray(prep["w_o"])), want_acc=True)
+    gq_ref, gs_ref = quant.quant_act_sym_int8(dy, prep["sw"].astype(np.float32))
+    assert_equal(host(gq), gq_ref, "gradient codes")
+    assert_equal(host(gs), gs_ref, "gradient steps")
+    rows = _sample_rows(M, 32, 11)
+    ref = quaff.ste_backward(dy[rows], prep["qw"], prep["sw"], s_ref, r_ref, o, prep["w_o"])
+    assert_equal(host(acc)[rows], ref["acc"], "acc")
+    assert_close(host(cb)[rows][:, :nO], ref["cb"], "cb", tol=1e-5)
+    assert_close(host(dx)[rows], ref["dx"], "dx")
