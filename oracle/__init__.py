@@ -23,9 +23,11 @@ Modules:
   gemm      -- integer accumulators and dequantized outputs of W8A8, W4A8, W4A4
   quaff     -- sparse outlier compensation and the momentum scale update
   layer     -- whole-layer forward passes composed from the above
+  pca       -- OffQ's Top-1 PCA concentration (extreme tokens, covariance,
+               leading eigenvector, Householder rotation of acts and weights)
 
 Parity pins: every public function is pinned in ``tests/test_oracle_*.py``
 against closed forms, brute force in exact Python integers / fractions,
 library routines, or hand-worked examples in ``tests/golden/``.
 """
-from . import hadamard, quant, gemm, quaff, layer  # noqa: F401
+from . import hadamard, quant, gemm, quaff, layer, pca  # noqa: F401

@@ -114,6 +114,23 @@ def grad_output(M: int, N: int, seed: int, std: float = 1.0) -> np.ndarray:
     return _normal16(rng, (M, N), std)
 
 
+def pca_calibration(S: int = 128, T: int = 512, K: int = 4096, seed: int = 6, planted: int = 2,
+                    amp_lo: float = 500.0, amp_hi: float = 1500.0):
+    """Calibration sequences with a planted outlier direction: tokens N(0,1)
+    fp16 [S x T x K]; in every sequence ``planted`` random tokens get a * u
+    added, u one dense random unit direction shared by all sequences and
+    a ~ U(amp_lo, amp_hi) per token.  Returns (x, u float64 [K])."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(K)
+    u /= np.linalg.norm(u)
+    x = rng.standard_normal(size=(S, T, K), dtype=np.float32)
+    for s_ in range(S):
+        ts = rng.choice(T, planted, replace=False)
+        amps = rng.uniform(amp_lo, amp_hi, planted)
+        x[s_, ts, :] += (amps[:, None] * u[None, :]).astype(np.float32)
+    return x.astype(np.float16), u
+
+
 def qqq_decode(M: int, K: int = 4096, N: int = 11008, seed: int = 2) -> Linear:
     """Decode / small-batch tokens: N(0,1) with 1% outlier channels x100."""
     return plain_linear(M, K, N, seed, n_outliers=max(1, round(0.01 * K)))
