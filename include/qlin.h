@@ -221,6 +221,52 @@ qlin_status qlin_weight_row_absmax(const uint16_t* w_rows, int64_t R, int64_t N,
 qlin_status qlin_weight_colsum_group(const uint8_t* codes, int64_t K, int64_t N, int32_t group,
                                      int32_t* colsum_g, void* stream);
 
+/* ------------------------------------------------------------------------
+ * OffQ concentration, Top-1 PCA (offline calibration; OffQ, methodology,
+ * "concentration via Top-1 PCA": only the most extreme token of each
+ * calibration sequence enters the covariance; its leading eigenvector is
+ * rotated into the first channel, and the weights take the inverse rotation)
+ * --------------------------------------------------------------------- */
+
+/*
+ * qlin_pca_select -- per sequence s, the token t = argmax_t max_k |x[s,t,k]|
+ * (fp32 of the fp16 values; the first such t on ties) and a copy of it.
+ *   x    fp16 [S x T x K], K % 8 == 0;  idx int32 [S] out;  z fp16 [S x K] out
+ */
+qlin_status qlin_pca_select(const uint16_t* x, int64_t S, int64_t T, int64_t K, int32_t* idx, uint16_t* z,
+                            void* stream);
+
+/*
+ * qlin_pca_leading_eigvec -- leading eigenvector v (unit, v[0] <= 0) and its
+ * eigenvalue of the sample covariance C = Zc^T Zc / (S - 1) of the rows of z,
+ * centred on their mean, by power iteration in float64 without forming C.
+ * The start vector is the centred row of largest norm; the iteration stops
+ * when successive vectors differ by less than tol (2-norm) or after max_iter.
+ *   z fp16 [S x K] (S >= 2);  v float64 [K] out;  lambda float64 [1] out;
+ *   iters int32 [1] out (iterations run);  ws float64 scratch [2K + S]
+ * One workgroup: a calibration step, not a per-token one.
+ */
+qlin_status qlin_pca_leading_eigvec(const uint16_t* z, int64_t S, int64_t K, int32_t max_iter, double tol,
+                                    double* v, double* lambda, int32_t* iters, double* ws, void* stream);
+
+/*
+ * qlin_pca_fold_weight -- w_out = fp16(H W) with the Householder reflection
+ * H = I - beta u u^T, u = v - e_0, beta = 2 / (u^T u), so H v = e_0 and
+ * (x H)(H W) = x W (H is its own inverse).  float64 arithmetic, one rounding.
+ *   w fp16 [K x N] (K <= 65535);  v float64 [K] (unit, v[0] <= 0);
+ *   w_out fp16 [K x N] out (may not alias w);  ws float64 scratch [N]
+ */
+qlin_status qlin_pca_fold_weight(const uint16_t* w, int64_t K, int64_t N, const double* v, uint16_t* w_out,
+                                 double* ws, void* stream);
+
+/*
+ * qlin_pca_rotate -- x_out = fp16(x H) for tokens x [M x K] (the activation
+ * side of the same rotation: x - beta (x . u) u^T in float64, one rounding).
+ * Where a preceding layer can absorb H offline, this kernel is not needed.
+ */
+qlin_status qlin_pca_rotate(const uint16_t* x, int64_t M, int64_t K, const double* v, uint16_t* x_out,
+                            void* stream);
+
 /* Bytes of a packed weight buffer for `layout` (0 for invalid arguments). Host only. */
 size_t qlin_packed_bytes(int32_t layout, int64_t K, int64_t N);
 

@@ -38,6 +38,10 @@ SIGNATURES = {
     "qlin_gemm_w4a4": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p, p]),
     "qlin_gemm_w4a4_group": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p]),
     "qlin_outlier_comp": (i32, [p, p, i32, p, i64, i64, p, p]),
+    "qlin_pca_select": (i32, [p, i64, i64, i64, p, p, p]),
+    "qlin_pca_leading_eigvec": (i32, [p, i64, i64, i32, C.c_double, p, p, p, p, p]),
+    "qlin_pca_fold_weight": (i32, [p, i64, i64, p, p, p, p]),
+    "qlin_pca_rotate": (i32, [p, i64, i64, p, p, p]),
     "qlin_quaff_backward": (i32, [p, i64, i64, i64, p, p, p, p, p, i32, p, p, p, p, p, p, p]),
 }
 
@@ -62,7 +66,7 @@ def load() -> C.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(
-                f"{LIB_PATH} is missing: build it with `python -m outlier_aware_bit_amd.build` "
+                f"{LIB_PATH} is missing: build it with `python outlier_aware_bit_amd/build.py` "
                 "(hipcc --offload-arch=gfx950); there is no fallback implementation")
         # One HIP runtime per process: torch ships its own libamdhip64 (same
         # SONAME as ROCm's).  Loading torch first makes libqlin bind to the

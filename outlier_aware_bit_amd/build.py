@@ -1,6 +1,7 @@
 """Builds libqlin.so for gfx950 in-tree with hipcc.
 
-Usage: python -m outlier_aware_bit_amd.build [--jobs N] [--quiet]
+Usage: python outlier_aware_bit_amd/build.py [--jobs N] [--quiet]
+(run by path: importing the package first would load the library being rebuilt)
 """
 from __future__ import annotations
 

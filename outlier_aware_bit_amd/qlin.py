@@ -339,3 +339,54 @@ def qlin_outlier_comp(xO, sa, nO, WO, y):
         _ptr(xO) if nO else None, _ptr(sa) if nO else None, nO, _ptr(WO) if nO else None, M, N,
         y.data_ptr(), _stream()))
     return y
+
+
+# ---------------------------------------------------------------- OffQ Top-1 PCA (offline)
+def qlin_pca_select(x):
+    """x fp16 [S, T, K] -> (idx int32 [S], z fp16 [S, K]): each sequence's most extreme token."""
+    lib = _lib.load()
+    _req(x, "x", torch.float16)
+    S, T, K = x.shape
+    idx = _empty((S,), torch.int32, x)
+    z = _empty((S, K), torch.float16, x)
+    _lib.check("qlin_pca_select", lib.qlin_pca_select(x.data_ptr(), S, T, K, idx.data_ptr(), z.data_ptr(),
+                                                      _stream()))
+    return idx, z
+
+
+def qlin_pca_leading_eigvec(z, max_iter=200, tol=1e-12):
+    """Leading eigenvector of the extreme tokens' covariance: (v float64 [K], lambda, iterations)."""
+    lib = _lib.load()
+    _req(z, "z", torch.float16)
+    S, K = z.shape
+    v = _empty((K,), torch.float64, z)
+    lam = _empty((1,), torch.float64, z)
+    its = _empty((1,), torch.int32, z)
+    ws = _empty((2 * K + S,), torch.float64, z)
+    _lib.check("qlin_pca_leading_eigvec", lib.qlin_pca_leading_eigvec(
+        z.data_ptr(), S, K, max_iter, tol, v.data_ptr(), lam.data_ptr(), its.data_ptr(), ws.data_ptr(), _stream()))
+    return v, lam, its
+
+
+def qlin_pca_fold_weight(w, v):
+    """fp16(H W) for the Householder reflection with H v = e_0."""
+    lib = _lib.load()
+    _req(w, "w", torch.float16)
+    K, N = w.shape
+    _req(v, "v", torch.float64, (K,))
+    out = _empty((K, N), torch.float16, w)
+    ws = _empty((N,), torch.float64, w)
+    _lib.check("qlin_pca_fold_weight", lib.qlin_pca_fold_weight(w.data_ptr(), K, N, v.data_ptr(), out.data_ptr(),
+                                                                ws.data_ptr(), _stream()))
+    return out
+
+
+def qlin_pca_rotate(x, v):
+    """fp16(x H) for tokens x [M, K]."""
+    lib = _lib.load()
+    _req(x, "x", torch.float16)
+    M, K = x.shape
+    _req(v, "v", torch.float64, (K,))
+    out = _empty((M, K), torch.float16, x)
+    _lib.check("qlin_pca_rotate", lib.qlin_pca_rotate(x.data_ptr(), M, K, v.data_ptr(), out.data_ptr(), _stream()))
+    return out

@@ -182,6 +182,22 @@ def test_group_and_backward_validation():
     _err(lib.qlin_pack_weight(_lib.QLIN_LAYOUT_W8T, A, 128, 200, B, None), _lib.QLIN_ERR_SHAPE)
 
 
+def test_pca_validation():
+    lib = _lib.load()
+    _err(lib.qlin_pca_select(A, 4, 16, 100, A, B, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_pca_select(A, 4, 0, 128, A, B, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_pca_select(A, 4, 16, 128, None, B, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_pca_select(A, 0, 16, 128, A, B, None), _lib.QLIN_OK)
+    _err(lib.qlin_pca_leading_eigvec(A, 1, 128, 10, 1e-9, A, A, A, A, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_pca_leading_eigvec(A, 8, 128, 0, 1e-9, A, A, A, A, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_pca_leading_eigvec(A, 8, 128, 10, -1.0, A, A, A, A, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_pca_leading_eigvec(A, 8, 128, 10, 1e-9, A, A, A, MIS, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_pca_fold_weight(A, 70000, 64, A, B, A, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_pca_fold_weight(A, 128, 64, None, B, A, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_pca_rotate(A, 0, 128, A, B, None), _lib.QLIN_OK)
+    _err(lib.qlin_pca_rotate(A, 4, 0, A, B, None), _lib.QLIN_ERR_SHAPE)
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     from outlier_aware_bit_amd import qlin
