@@ -372,6 +372,34 @@ def rows_measurements(q, layer):
                                       frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma")
     del cw, w4u, y, xo, qg4, csg
 
+    # OffQ Top-1 PCA calibration (offline, once per layer): 128 sequences of
+    # 512 tokens at K = 4096, then the fold of a 4096 x 4096 weight and the
+    # rotation of 2048 tokens.
+    S6, T6, K6 = 128, 512, 4096
+    xc, _ = _synth.pca_calibration(S=S6, T=T6, K=K6, seed=6)
+    xcd = dev(xc)
+    del xc
+    t_sel = time_launches(lambda i: q.qlin_pca_select(xcd), 10, graph_len=4)
+    _, zc = q.qlin_pca_select(xcd)
+    t_eig = time_launches(lambda i: q.qlin_pca_leading_eigvec(zc), 4, graph_len=2)
+    v6, _, its6 = q.qlin_pca_leading_eigvec(zc)
+    wf16 = (torch.randn(K6, K6, device="cuda") * 0.02).half()
+    t_fold = time_launches(lambda i: q.qlin_pca_fold_weight(wf16, v6), 4, graph_len=2)
+    xt = layer.xs[0]
+    t_rot = time_launches(lambda i: q.qlin_pca_rotate(xt, v6), 50)
+    b = S6 * T6 * K6 * 2
+    out["NEXT4_pca_select"] = dict(workload=f"{S6} sequences x {T6} tokens x {K6}", ms=t_sel, bytes=b,
+                                   gbs=b / t_sel / 1e6, frac=b / t_sel / 1e6 / PEAK_HBM_GBS, bound="hbm")
+    out["NEXT4_pca_leading_eigvec"] = dict(workload=f"{S6} extreme tokens x {K6}", ms=t_eig,
+                                           iterations=int(its6.item()), bound="latency (one workgroup)")
+    b = 2 * 2 * K6 * K6
+    out["NEXT4_pca_fold_weight"] = dict(workload=f"{K6}x{K6}", ms=t_fold, bytes=b, gbs=b / t_fold / 1e6,
+                                        frac=b / t_fold / 1e6 / PEAK_HBM_GBS, bound="hbm")
+    b = 2 * 2 * M * K6
+    out["NEXT4_pca_rotate"] = dict(workload=f"{M}x{K6}", ms=t_rot, bytes=b, gbs=b / t_rot / 1e6,
+                                   frac=b / t_rot / 1e6 / PEAK_HBM_GBS, bound="hbm")
+    del xcd, zc, wf16
+
     # Tiny W8A8 (latency only).
     lin = synth.tiny_w8a8(seed=0)
     codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 8)
