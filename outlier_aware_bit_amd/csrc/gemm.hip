@@ -990,7 +990,7 @@ qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
     // than one per CU.
     if (!comp && g.M <= 128) {
       if (g.M <= 32)
-        launch_skinny<B, A, 1, 1, 8, 8>(g, st);
+        launch_skinny<B, A, 1, 2, 8, 4>(g, st);
       else if (g.M <= 64)
         launch_skinny<B, A, 2, 2, 8, 4>(g, st);
       else
