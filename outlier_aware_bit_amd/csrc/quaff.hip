@@ -160,79 +160,156 @@ __global__ __launch_bounds__(kCompThreads) void outlier_comp_kernel(
 }
 
 // STE backward, compensation part: cb[m, j] = sum_n dy[m, n] * w_o[j, n] in
-// fp32 (fp16 products on the matrix cores) for j < ldO, zero for j >= nO.
-// A small, latency-bound product (N long, ldO narrow): a workgroup takes 32
-// rows and kGradCB column blocks of 32, and its kGradWaves waves each take
-// one contiguous slice of n, with all loads of kGradU steps in flight before
-// their products.  The slices' sums are added in a fixed order through LDS,
-// so the result does not depend on timing.  Both operands are row-major with
-// n contiguous: the fragment order of v_mfma_f32_32x32x16_f16 (8 consecutive
-// n per lane).
-constexpr int kGradCB = 2, kGradWaves = 8, kGradThreads = 64 * kGradWaves, kGradU = 8;
+// fp32 (fp16 products on the matrix cores) for j < nO, zero for
+// nO <= j < ldO.  A small product (N long, ldO narrow) bound by moving the
+// operands from L2 into the compute units: a workgroup takes 32 rows and
+// kGradCB column blocks of 32, its kGradWaves waves take the 64-wide blocks
+// of n in turn (wave w: blocks w, w + kGradWaves, ...).  A wave moves each
+// block through its own LDS region: coalesced 16-byte loads (eight lanes per
+// 128-byte row piece, kGradD blocks in flight), then reads in the fragment
+// order of v_mfma_f32_32x32x16_f16 (lane: row l & 31, 8 consecutive n from
+// 8 (l >> 5) on).  Each row's eight 16-byte chunks sit permuted by the xor
+// with grad_swz(row), so that 16 lanes reading one chunk of 16 consecutive
+// rows touch all 64 banks once (8 lanes of an aligned half: 32 distinct
+// banks).  The waves' sums meet in LDS in a fixed pairing order (w and
+// w + 4, then w and w + 2, then 0 and 1): the result does not depend on
+// timing.
+constexpr int kGradCB = 2, kGradWaves = 8, kGradThreads = 64 * kGradWaves, kGradD = 2;
+constexpr int kGradBW = 64;                      // n per block
+constexpr int kGradCPR = kGradBW / 8;            // 16-byte chunks per row
+constexpr int kGradRPL = 64 / kGradCPR;          // rows per load
+constexpr int kGradRows = 32 * (1 + kGradCB);    // staged rows per block: dy, then w_o
+constexpr int kGradLoads = kGradRows / kGradRPL;
+
+__device__ __forceinline__ int grad_swz(int row) { return ((row >> 1) & 3) | (((row ^ (row >> 3)) & 1) << 2); }
+__device__ __forceinline__ int grad_slot(int row, int chunk) { return kGradCPR * row + (chunk ^ grad_swz(row)); }
+
+// One wave's sweep over its blocks k = 0 .. cnt - 1 (block wave + kGradWaves k
+// of n) with the first NB column blocks live.  The loop body stores block k
+// from registers into LDS, refills those registers with block k + kGradD and
+// multiplies block k; the steady-state loop has no branch, so that the
+// compiler's load counting waits only for the block being stored.
+template <int NB>
+__device__ __forceinline__ void grad_sweep(const uint16_t* const* src, const int* dst, v4i* lds, int wave,
+                                           int cnt, int nblk, int lane, v16f* acc) {
+  constexpr int L = (32 / kGradRPL) * (1 + NB);  // loads per block: dy rows, then the live w_o rows
+  v4i reg[kGradD][L];
+  auto issue = [&](int k, v4i* r) {
+    int blk = wave + kGradWaves * k;
+    blk = blk < nblk ? blk : nblk - 1;  // the first kGradD loads of a short sweep
+    const int64_t off = kGradBW * static_cast<int64_t>(blk);
+#pragma unroll
+    for (int t = 0; t < L; ++t) r[t] = *reinterpret_cast<const v4i*>(src[t] + off);
+  };
+  const int rrow = lane & 31, rchunk = lane >> 5;
+  auto step = [&](v4i* r, bool refill, int next) {
+#pragma unroll
+    for (int t = 0; t < L; ++t) lds[dst[t]] = r[t];
+    if (refill) issue(next, r);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int st = 0; st < kGradBW / 16; ++st) {
+      const v8h a = __builtin_bit_cast(v8h, lds[grad_slot(rrow, 2 * st + rchunk)]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const v8h bv = __builtin_bit_cast(v8h, lds[grad_slot(32 + 32 * b + rrow, 2 * st + rchunk)]);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bv, acc[b], 0, 0, 0);
+      }
+    }
+    // The next block's stores to this region come after these reads.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // Unconditional, so that the loop's load counting starts from one state.
+#pragma unroll
+  for (int d = 0; d < kGradD; ++d) issue(d, reg[d]);
+  int k0 = 0;
+  for (; k0 + 2 * kGradD <= cnt; k0 += kGradD) {
+#pragma unroll
+    for (int d = 0; d < kGradD; ++d) step(reg[d], true, k0 + d + kGradD);
+  }
+  // Fewer than 2 kGradD blocks remain.
+#pragma unroll
+  for (int d = 0; d < kGradD; ++d) {
+    if (k0 + d < cnt) {
+      if (k0 + d + kGradD < cnt) step(reg[d], true, k0 + d + kGradD);
+      else step(reg[d], false, 0);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < kGradD; ++d)
+    if (k0 + kGradD + d < cnt) step(reg[d], false, 0);
+}
 
 __global__ __launch_bounds__(kGradThreads) void outlier_grad_kernel(const uint16_t* __restrict__ dy,
                                                                    const uint16_t* __restrict__ w_o, int64_t M,
                                                                    int64_t N, int nO, int ldO,
                                                                    float* __restrict__ cb) {
-  __shared__ float red[kGradWaves][kGradCB][16][64];
+  static_assert(kGradCB == 2, "the sweep is instantiated for one or two live column blocks");
+  __shared__ v4i stage[kGradWaves][kGradCPR * kGradRows];
+  __shared__ float red[kGradWaves / 2][kGradCB][16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 32;
   const int jb0 = blockIdx.y * kGradCB;
-  const int64_t slice = N / kGradWaves;  // a multiple of 16 (N % 128 == 0)
-  const int64_t nw = slice * wave;
-  int64_t m = m0 + (lane & 31);
-  m = m < M ? m : M - 1;
-  const uint16_t* arow = dy + m * N + nw + 8 * (lane >> 5);
-  const uint16_t* brow[kGradCB];
-  bool bok[kGradCB];
+  // Load t brings rows kGradRPL t .. kGradRPL (t + 1) - 1 of the block: lane l
+  // takes row kGradRPL t + l / kGradCPR, chunk l % kGradCPR.  Rows past M
+  // repeat row M - 1, columns past nO repeat row nO - 1 (their sums are
+  // dropped at the store); a column block wholly past nO is neither loaded
+  // nor multiplied.
+  const uint16_t* src[kGradLoads];
+  int dst[kGradLoads];
 #pragma unroll
-  for (int b = 0; b < kGradCB; ++b) {
-    const int j = 32 * (jb0 + b) + (lane & 31);
-    bok[b] = j < nO;
-    brow[b] = w_o + static_cast<int64_t>(bok[b] ? j : 0) * N + nw + 8 * (lane >> 5);
+  for (int t = 0; t < kGradLoads; ++t) {
+    const int row = kGradRPL * t + lane / kGradCPR, chunk = lane % kGradCPR;
+    if (row < 32) {
+      int64_t m = m0 + row;
+      m = m < M ? m : M - 1;
+      src[t] = dy + m * N + 8 * chunk;
+    } else {
+      int j = 32 * jb0 + row - 32;
+      j = j < nO ? j : nO - 1;
+      src[t] = w_o + static_cast<int64_t>(j) * N + 8 * chunk;
+    }
+    dst[t] = grad_slot(row, chunk);
   }
+  const int nblk = static_cast<int>(N / kGradBW);
+  const int cnt = nblk > wave ? (nblk - wave + kGradWaves - 1) / kGradWaves : 0;
   v16f acc[kGradCB];
 #pragma unroll
   for (int b = 0; b < kGradCB; ++b) acc[b] = v16f{};
-  const int steps = static_cast<int>(slice / 16);
-  int ks = 0;
-  for (; ks + kGradU <= steps; ks += kGradU) {
-    v8h a[kGradU], bb[kGradU][kGradCB];
+  if (32 * (jb0 + 1) < nO) grad_sweep<2>(src, dst, stage[wave], wave, cnt, nblk, lane, acc);
+  else grad_sweep<1>(src, dst, stage[wave], wave, cnt, nblk, lane, acc);
+  // Pairwise reduction over the waves in a fixed order.
 #pragma unroll
-    for (int u = 0; u < kGradU; ++u) {
-      a[u] = *reinterpret_cast<const v8h*>(arow + 16 * static_cast<int64_t>(ks + u));
-#pragma unroll
-      for (int b = 0; b < kGradCB; ++b) bb[u][b] = *reinterpret_cast<const v8h*>(brow[b] + 16 * static_cast<int64_t>(ks + u));
-    }
-#pragma unroll
-    for (int u = 0; u < kGradU; ++u)
+  for (int span = kGradWaves / 2; span >= 1; span /= 2) {
+    if (wave >= span && wave < 2 * span) {
 #pragma unroll
       for (int b = 0; b < kGradCB; ++b)
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[u], bok[b] ? bb[u][b] : v8h{}, acc[b], 0, 0, 0);
-  }
-  for (; ks < steps; ++ks) {
-    const v8h a = *reinterpret_cast<const v8h*>(arow + 16 * static_cast<int64_t>(ks));
 #pragma unroll
-    for (int b = 0; b < kGradCB; ++b) {
-      const v8h bv = *reinterpret_cast<const v8h*>(brow[b] + 16 * static_cast<int64_t>(ks));
-      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bok[b] ? bv : v8h{}, acc[b], 0, 0, 0);
+        for (int v = 0; v < 16; ++v) red[wave - span][b][v][lane] = acc[b][v];
     }
+    __syncthreads();
+    if (wave < span) {
+#pragma unroll
+      for (int b = 0; b < kGradCB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][v] += red[wave][b][v][lane];
+    }
+    __syncthreads();
   }
+  if (wave != 0) return;
+  // Lane l holds column (l & 31) and rows frag_row(v, l) of each block.
 #pragma unroll
-  for (int b = 0; b < kGradCB; ++b)
+  for (int b = 0; b < kGradCB; ++b) {
+    const int j = 32 * (jb0 + b) + (lane & 31);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) red[wave][b][v][lane] = acc[b][v];
-  __syncthreads();
-  // Thread t adds up elements e = t, t + kGradThreads, ... of the tile
-  // (block b, register v, lane l), the slices in order.
-  for (int e = threadIdx.x; e < kGradCB * 16 * 64; e += kGradThreads) {
-    const int b = e / (16 * 64), v = (e / 64) % 16, l = e % 64;
-    const int j = 32 * (jb0 + b) + (l & 31);
-    const int64_t row = m0 + frag_row(v, l);
-    float sum = red[0][b][v][l];
-#pragma unroll
-    for (int w = 1; w < kGradWaves; ++w) sum += red[w][b][v][l];
-    if (j < ldO && row < M) cb[row * ldO + j] = sum;
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = m0 + frag_row(v, lane);
+      if (j < ldO && row < M) cb[row * ldO + j] = j < nO ? acc[b][v] : 0.0f;
+    }
   }
 }
 
