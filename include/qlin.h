@@ -253,8 +253,9 @@ qlin_status qlin_pca_leading_eigvec(const uint16_t* z, int64_t S, int64_t K, int
  * qlin_pca_fold_weight -- w_out = fp16(H W) with the Householder reflection
  * H = I - beta u u^T, u = v - e_0, beta = 2 / (u^T u), so H v = e_0 and
  * (x H)(H W) = x W (H is its own inverse).  float64 arithmetic, one rounding.
- *   w fp16 [K x N] (K <= 65535);  v float64 [K] (unit, v[0] <= 0);
- *   w_out fp16 [K x N] out (may not alias w);  ws float64 scratch [N]
+ *   w fp16 [K x N] (K <= 65535, N % 8 == 0);  v float64 [K] (unit, v[0] <= 0);
+ *   w_out fp16 [K x N] out (may not alias w; also holds partial sums until
+ *   the last pass);  ws float64 scratch [N]
  */
 qlin_status qlin_pca_fold_weight(const uint16_t* w, int64_t K, int64_t N, const double* v, uint16_t* w_out,
                                  double* ws, void* stream);
@@ -262,7 +263,8 @@ qlin_status qlin_pca_fold_weight(const uint16_t* w, int64_t K, int64_t N, const 
 /*
  * qlin_pca_rotate -- x_out = fp16(x H) for tokens x [M x K] (the activation
  * side of the same rotation: x - beta (x . u) u^T in float64, one rounding).
- * Where a preceding layer can absorb H offline, this kernel is not needed.
+ * K % 8 == 0 and K <= 8192.  Where a preceding layer can absorb H offline,
+ * this kernel is not needed.
  */
 qlin_status qlin_pca_rotate(const uint16_t* x, int64_t M, int64_t K, const double* v, uint16_t* x_out,
                             void* stream);

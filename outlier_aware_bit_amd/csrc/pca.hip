@@ -13,7 +13,7 @@
 namespace qlin {
 namespace {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 512, kSelWaves = kSelThreads / 64, kSelParts = 4, kSelCH = 8;
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -21,29 +21,45 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-// One workgroup per sequence: wave w scans tokens w, w + 4, ...; the largest
-// max|x| wins, the first token on ties.  Then the winner is copied to z.
-__global__ __launch_bounds__(kSelThreads) void pca_select_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t K,
-                                                                 int32_t* __restrict__ idx, uint16_t* __restrict__ z) {
-  __shared__ float best_v[kSelThreads / 64];
-  __shared__ int64_t best_t[kSelThreads / 64];
+__device__ __forceinline__ float absmax8(v4i raw, float m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = static_cast<uint32_t>(raw[i]);
+    m = fmaxf(m, fabsf(h2f(static_cast<uint16_t>(w & 0xffffu))));
+    m = fmaxf(m, fabsf(h2f(static_cast<uint16_t>(w >> 16))));
+  }
+  return m;
+}
+
+// The extreme token in two passes.  Pass 1: workgroup (p, s) takes the p-th
+// of P contiguous runs of sequence s's tokens; wave w scans tokens w,
+// w + kSelWaves, ... of the run, all of a token's loads in flight at once;
+// the largest max|x| wins, the first token on ties.  Its candidate (value,
+// token) goes to slot p of z's row s, which pass 2 reads and then overwrites
+// with the winning token.
+__global__ __launch_bounds__(kSelThreads) void pca_select_part_kernel(const uint16_t* __restrict__ x, int64_t T,
+                                                                      int64_t K, int P, uint16_t* __restrict__ z) {
+  __shared__ float best_v[kSelWaves];
+  __shared__ int64_t best_t[kSelWaves];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t s = blockIdx.x;
+  const int64_t s = blockIdx.y, run = (T + P - 1) / P;
+  const int64_t t0 = blockIdx.x * run, t1 = t0 + run < T ? t0 + run : T;
   const uint16_t* xs = x + s * T * K;
+  const int nch = static_cast<int>(K / 8);
   float bv = -1.0f;
   int64_t bt = -1;
-  for (int64_t t = wave; t < T; t += kSelThreads / 64) {
+  for (int64_t t = t0 + wave; t < t1; t += kSelWaves) {
     const uint16_t* row = xs + t * K;
-    float m = 0.0f;
-    for (int64_t k = lane * 8; k < K; k += 64 * 8) {
-      const v4i raw = *reinterpret_cast<const v4i*>(row + k);
+    v4i raw[kSelCH];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = static_cast<uint32_t>(raw[i]);
-        m = fmaxf(m, fabsf(h2f(static_cast<uint16_t>(w & 0xffffu))));
-        m = fmaxf(m, fabsf(h2f(static_cast<uint16_t>(w >> 16))));
-      }
+    for (int i = 0; i < kSelCH; ++i) {
+      const int c = lane + 64 * i;
+      raw[i] = *reinterpret_cast<const v4i*>(row + 8 * (c < nch ? c : nch - 1));
     }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kSelCH; ++i) m = absmax8(raw[i], m);  // clamped repeats change no maximum
+    for (int c = lane + 64 * kSelCH; c < nch; c += 64) m = absmax8(*reinterpret_cast<const v4i*>(row + 8 * c), m);
     m = wave_max(m);
     if (m > bv) {  // tokens arrive in increasing t: strict > keeps the first
       bv = m;
@@ -55,18 +71,46 @@ __global__ __launch_bounds__(kSelThreads) void pca_select_kernel(const uint16_t*
     best_t[wave] = bt;
   }
   __syncthreads();
-  float v = best_v[0];
-  int64_t t = best_t[0];
-#pragma unroll
-  for (int w = 1; w < kSelThreads / 64; ++w) {
-    if (best_v[w] > v || (best_v[w] == v && best_t[w] < t)) {
-      v = best_v[w];
-      t = best_t[w];
+  if (threadIdx.x == 0) {
+    float v = best_v[0];
+    int64_t t = best_t[0];
+    for (int w = 1; w < kSelWaves; ++w) {
+      if (best_t[w] >= 0 && (t < 0 || best_v[w] > v || (best_v[w] == v && best_t[w] < t))) {
+        v = best_v[w];
+        t = best_t[w];
+      }
     }
+    float* slot = reinterpret_cast<float*>(z + s * K) + 2 * blockIdx.x;
+    slot[0] = v;
+    reinterpret_cast<int32_t*>(slot)[1] = static_cast<int32_t>(t);
   }
-  if (threadIdx.x == 0) idx[s] = static_cast<int32_t>(t);
-  const uint16_t* src = xs + t * K;
+}
+
+// Pass 2: the best of the P candidates (runs in increasing t: the first run
+// wins ties), then the copy of the winner into z.
+__global__ __launch_bounds__(kSelThreads) void pca_select_final_kernel(const uint16_t* __restrict__ x, int64_t T,
+                                                                       int64_t K, int P, int32_t* __restrict__ idx,
+                                                                       uint16_t* __restrict__ z) {
+  __shared__ int64_t win;
+  const int64_t s = blockIdx.x;
   uint16_t* dst = z + s * K;
+  if (threadIdx.x == 0) {
+    const float* slot = reinterpret_cast<const float*>(dst);
+    float v = -1.0f;
+    int64_t t = -1;
+    for (int p = 0; p < P; ++p) {
+      const float pv = slot[2 * p];
+      const int32_t pt = reinterpret_cast<const int32_t*>(slot)[2 * p + 1];
+      if (pt >= 0 && (t < 0 || pv > v)) {
+        v = pv;
+        t = pt;
+      }
+    }
+    win = t;
+    idx[s] = static_cast<int32_t>(t);
+  }
+  __syncthreads();
+  const uint16_t* src = x + (s * T + win) * K;
   for (int64_t k = threadIdx.x * 8; k < K; k += kSelThreads * 8)
     *reinterpret_cast<v4i*>(dst + k) = *reinterpret_cast<const v4i*>(src + k);
 }
@@ -200,54 +244,175 @@ __device__ double householder_beta(const double* v, int64_t K, double* red) {
   return r > 0.0 ? 2.0 / r : 0.0;
 }
 
-constexpr int kFoldThreads = 256;
+// The weight fold in three passes, sums in a fixed order (not k in order):
+//   partial: block (column block of kFoldCols, row block of kFoldRows) adds
+//            u[k] W[k, n] over its rows (each wave over kFoldRows / 4
+//            consecutive rows, then the four waves in order);
+//   reduce:  q[n] = beta * sum over the row blocks, in order;
+//   apply:   W'[k, n] = fp16(W[k, n] - u[k] q[n]).
+// The row-block sums are kept in w_out (8 bytes per column and row block fit
+// in the 2 bytes per element of w_out), which the apply pass then overwrites.
+constexpr int kFoldThreads = 256, kFoldCols = 512, kFoldRows = 64;
 
-// p[n] = sum_k w[k] W[k, n] (float64, k in order): one thread per column.
-__global__ __launch_bounds__(kFoldThreads) void pca_fold_dot_kernel(const uint16_t* __restrict__ wt, int64_t K,
-                                                                    int64_t N, const double* __restrict__ v,
-                                                                    double* __restrict__ p) {
-  const int64_t n = static_cast<int64_t>(blockIdx.x) * kFoldThreads + threadIdx.x;
-  if (n >= N) return;
-  double acc = 0.0;
-  for (int64_t k = 0; k < K; ++k) acc += (v[k] - (k == 0 ? 1.0 : 0.0)) * static_cast<double>(h2f(wt[k * N + n]));
-  p[n] = acc;
-}
-
-// W'[k, n] = fp16(W[k, n] - beta w[k] p[n]).
-__global__ __launch_bounds__(kFoldThreads) void pca_fold_apply_kernel(const uint16_t* __restrict__ wt, int64_t K,
-                                                                      int64_t N, const double* __restrict__ v,
-                                                                      const double* __restrict__ p,
-                                                                      uint16_t* __restrict__ out) {
-  __shared__ double red[kFoldThreads / 64];
-  const double beta = householder_beta(v, K, red);
-  const int64_t k = blockIdx.y;
-  const double wk = v[k] - (k == 0 ? 1.0 : 0.0);
-  for (int64_t n = static_cast<int64_t>(blockIdx.x) * kFoldThreads + threadIdx.x; n < N;
-       n += static_cast<int64_t>(gridDim.x) * kFoldThreads) {
-    const double r = static_cast<double>(h2f(wt[k * N + n])) - beta * wk * p[n];
-    out[k * N + n] = f2h(static_cast<float>(r));
+__device__ __forceinline__ void unpack8_f64(v4i raw, double (&d)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = static_cast<uint32_t>(raw[i]);
+    d[2 * i] = static_cast<double>(h2f(static_cast<uint16_t>(w & 0xffffu)));
+    d[2 * i + 1] = static_cast<double>(h2f(static_cast<uint16_t>(w >> 16)));
   }
 }
 
-// x'[m, :] = fp16(x - beta (x . w) w^T): one wave per token.
-constexpr int kRotWaves = 4;
+__global__ __launch_bounds__(kFoldThreads) void pca_fold_partial_kernel(const uint16_t* __restrict__ wt, int64_t K,
+                                                                        int64_t N, const double* __restrict__ v,
+                                                                        double* __restrict__ part) {
+  __shared__ double red[kFoldThreads / 64][64][8];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * kFoldCols + 8 * lane;
+  const int64_t kb = static_cast<int64_t>(blockIdx.y) * kFoldRows;
+  constexpr int kPer = kFoldRows / (kFoldThreads / 64);
+  const int64_t k0 = kb + kPer * wave;
+  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  if (n < N) {
+    v4i raw[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t k = k0 + i < K ? k0 + i : K - 1;
+      raw[i] = *reinterpret_cast<const v4i*>(wt + k * N + n);
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (k0 + i < K) {
+        const double uk = v[k0 + i] - (k0 + i == 0 ? 1.0 : 0.0);
+        double d[8];
+        unpack8_f64(raw[i], d);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += uk * d[j];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[wave][lane][j] = acc[j];
+  __syncthreads();
+  if (wave == 0 && n < N) {
+    double* dst = part + static_cast<int64_t>(blockIdx.y) * N + n;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      double t = red[0][lane][j];
+#pragma unroll
+      for (int w = 1; w < kFoldThreads / 64; ++w) t += red[w][lane][j];
+      dst[j] = t;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kFoldThreads) void pca_fold_reduce_kernel(const double* __restrict__ part, int64_t nb,
+                                                                       int64_t K, int64_t N,
+                                                                       const double* __restrict__ v,
+                                                                       double* __restrict__ q) {
+  __shared__ double red[kFoldThreads / 64];
+  const double beta = householder_beta(v, K, red);
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * kFoldThreads + threadIdx.x;
+  if (n >= N) return;
+  double acc = 0.0;
+  for (int64_t b = 0; b < nb; ++b) acc += part[b * N + n];
+  q[n] = beta * acc;
+}
+
+// Thread: 8 columns of one row; a workgroup 8 * kFoldThreads columns.
+__global__ __launch_bounds__(kFoldThreads) void pca_fold_apply_kernel(const uint16_t* __restrict__ wt, int64_t K,
+                                                                      int64_t N, const double* __restrict__ v,
+                                                                      const double* __restrict__ q,
+                                                                      uint16_t* __restrict__ out) {
+  const int64_t k = blockIdx.y;
+  const int64_t n = (static_cast<int64_t>(blockIdx.x) * kFoldThreads + threadIdx.x) * 8;
+  if (n >= N) return;
+  const double uk = v[k] - (k == 0 ? 1.0 : 0.0);
+  double d[8];
+  unpack8_f64(*reinterpret_cast<const v4i*>(wt + k * N + n), d);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double r0 = d[2 * i] - uk * q[n + 2 * i];
+    const double r1 = d[2 * i + 1] - uk * q[n + 2 * i + 1];
+    o[i] = static_cast<uint32_t>(f2h(static_cast<float>(r0))) |
+           (static_cast<uint32_t>(f2h(static_cast<float>(r1))) << 16);
+  }
+  *reinterpret_cast<v4i*>(out + k * N + n) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+}
+
+// x'[m, :] = fp16(x - beta (x . u) u^T), u = v - e_0: u and beta once per
+// workgroup in LDS, one wave per token, each lane 8 consecutive channels per
+// 16-byte chunk (chunks lane + 64 i, the first kRotCH of them held in
+// registers between the dot and the update).
+constexpr int kRotWaves = 8, kRotCH = 8, kRotMaxK = 8192;
 
 __global__ __launch_bounds__(64 * kRotWaves) void pca_rotate_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                                     int64_t K, const double* __restrict__ v,
                                                                     uint16_t* __restrict__ out) {
+  __shared__ double u[kRotMaxK];
   __shared__ double red[kRotWaves];
-  const double beta = householder_beta(v, K, red);
   const int lane = threadIdx.x & 63;
   const int64_t m = static_cast<int64_t>(blockIdx.x) * kRotWaves + (threadIdx.x >> 6);
-  if (m >= M) return;  // after the block-wide reduction above
-  const uint16_t* row = x + m * K;
-  double acc = 0.0;
-  for (int64_t k = lane; k < K; k += 64) acc += static_cast<double>(h2f(row[k])) * (v[k] - (k == 0 ? 1.0 : 0.0));
-  const double c = beta * wave_sum_f64(acc);
-  for (int64_t k = lane; k < K; k += 64) {
-    const double r = static_cast<double>(h2f(row[k])) - c * (v[k] - (k == 0 ? 1.0 : 0.0));
-    out[m * K + k] = f2h(static_cast<float>(r));
+  const int64_t mc = m < M ? m : M - 1;
+  const uint16_t* row = x + mc * K;
+  const int nch = static_cast<int>(K / 8);
+  v4i raw[kRotCH];
+#pragma unroll
+  for (int i = 0; i < kRotCH; ++i) {
+    const int c = lane + 64 * i;
+    raw[i] = *reinterpret_cast<const v4i*>(row + 8 * (c < nch ? c : nch - 1));
   }
+  for (int64_t k = threadIdx.x; k < K; k += 64 * kRotWaves) u[k] = v[k] - (k == 0 ? 1.0 : 0.0);
+  __syncthreads();
+  double part = 0.0;
+  for (int64_t k = threadIdx.x; k < K; k += 64 * kRotWaves) part += u[k] * u[k];
+  part = wave_sum_f64(part);
+  if (lane == 0) red[threadIdx.x >> 6] = part;
+  __syncthreads();
+  double uu = 0.0;
+#pragma unroll
+  for (int w = 0; w < kRotWaves; ++w) uu += red[w];
+  const double beta = uu > 0.0 ? 2.0 / uu : 0.0;
+  if (m >= M) return;  // after the workgroup's barriers
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < kRotCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      double d[8];
+      unpack8_f64(raw[i], d);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += d[j] * u[8 * c + j];
+    }
+  }
+  for (int c = lane + 64 * kRotCH; c < nch; c += 64) {
+    double d[8];
+    unpack8_f64(*reinterpret_cast<const v4i*>(row + 8 * c), d);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += d[j] * u[8 * c + j];
+  }
+  const double cf = beta * wave_sum_f64(acc);
+  uint16_t* orow = out + m * K;
+  auto emit = [&](int c, v4i r) {
+    double d[8];
+    unpack8_f64(r, d);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double r0 = d[2 * i] - cf * u[8 * c + 2 * i];
+      const double r1 = d[2 * i + 1] - cf * u[8 * c + 2 * i + 1];
+      o[i] = static_cast<uint32_t>(f2h(static_cast<float>(r0))) |
+             (static_cast<uint32_t>(f2h(static_cast<float>(r1))) << 16);
+    }
+    *reinterpret_cast<v4i*>(orow + 8 * c) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+  };
+#pragma unroll
+  for (int i = 0; i < kRotCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) emit(c, raw[i]);
+  }
+  for (int c = lane + 64 * kRotCH; c < nch; c += 64) emit(c, *reinterpret_cast<const v4i*>(row + 8 * c));
 }
 
 }  // namespace
@@ -264,8 +429,14 @@ extern "C" qlin_status qlin_pca_select(const uint16_t* x, int64_t S, int64_t T, 
   QLIN_PTR(idx);
   QLIN_PTR(z);
   QLIN_REQUIRE(S <= 0x7fffffffLL && T <= 0x7fffffffLL, QLIN_ERR_SHAPE, "S or T too large");
-  pca_select_kernel<<<dim3(static_cast<unsigned>(S)), kSelThreads, 0, as_stream(stream)>>>(x, T, K, idx, z);
-  QLIN_LAUNCH_CHECK("pca_select_kernel");
+  // P candidate slots of 8 bytes fit in a row of z (2K >= 16 bytes).
+  const int P = static_cast<int>(K / 4 < kSelParts ? K / 4 : kSelParts);
+  hipStream_t st = as_stream(stream);
+  pca_select_part_kernel<<<dim3(static_cast<unsigned>(P), static_cast<unsigned>(S)), kSelThreads, 0, st>>>(x, T, K, P,
+                                                                                                        z);
+  QLIN_LAUNCH_CHECK("pca_select_part_kernel");
+  pca_select_final_kernel<<<dim3(static_cast<unsigned>(S)), kSelThreads, 0, st>>>(x, T, K, P, idx, z);
+  QLIN_LAUNCH_CHECK("pca_select_final_kernel");
   return QLIN_OK;
 }
 
@@ -289,17 +460,27 @@ extern "C" qlin_status qlin_pca_leading_eigvec(const uint16_t* z, int64_t S, int
 
 extern "C" qlin_status qlin_pca_fold_weight(const uint16_t* w, int64_t K, int64_t N, const double* v,
                                             uint16_t* w_out, double* ws, void* stream) {
-  QLIN_REQUIRE(K > 0 && N > 0, QLIN_ERR_SHAPE, "K=%lld, N=%lld must be positive", (long long)K, (long long)N);
+  QLIN_REQUIRE(K > 0 && N > 0 && N % 8 == 0, QLIN_ERR_SHAPE, "K=%lld, N=%lld: both positive, N a multiple of 8",
+               (long long)K, (long long)N);
   QLIN_REQUIRE(K <= 65535, QLIN_ERR_SHAPE, "K=%lld too large", (long long)K);
   QLIN_PTR(w);
   QLIN_PTR(v);
   QLIN_PTR(w_out);
   QLIN_PTR(ws);
   hipStream_t st = as_stream(stream);
-  const unsigned gx = static_cast<unsigned>((N + kFoldThreads - 1) / kFoldThreads);
-  pca_fold_dot_kernel<<<dim3(gx), kFoldThreads, 0, st>>>(w, K, N, v, ws);
-  QLIN_LAUNCH_CHECK("pca_fold_dot_kernel");
-  pca_fold_apply_kernel<<<dim3(gx, static_cast<unsigned>(K)), kFoldThreads, 0, st>>>(w, K, N, v, ws, w_out);
+  const int64_t nb = (K + kFoldRows - 1) / kFoldRows;  // row blocks; with nb > 1, nb * N doubles fit in w_out
+  // One row block (K <= kFoldRows): its sums go straight to ws, where the
+  // reduce pass turns each into q in place.
+  double* const part = nb == 1 ? ws : reinterpret_cast<double*>(w_out);
+  pca_fold_partial_kernel<<<dim3(static_cast<unsigned>((N + kFoldCols - 1) / kFoldCols), static_cast<unsigned>(nb)),
+                            kFoldThreads, 0, st>>>(w, K, N, v, part);
+  QLIN_LAUNCH_CHECK("pca_fold_partial_kernel");
+  pca_fold_reduce_kernel<<<dim3(static_cast<unsigned>((N + kFoldThreads - 1) / kFoldThreads)), kFoldThreads, 0, st>>>(
+      part, nb, K, N, v, ws);
+  QLIN_LAUNCH_CHECK("pca_fold_reduce_kernel");
+  pca_fold_apply_kernel<<<dim3(static_cast<unsigned>((N / 8 + kFoldThreads - 1) / kFoldThreads),
+                               static_cast<unsigned>(K)),
+                          kFoldThreads, 0, st>>>(w, K, N, v, ws, w_out);
   QLIN_LAUNCH_CHECK("pca_fold_apply_kernel");
   return QLIN_OK;
 }
@@ -307,7 +488,8 @@ extern "C" qlin_status qlin_pca_fold_weight(const uint16_t* w, int64_t K, int64_
 extern "C" qlin_status qlin_pca_rotate(const uint16_t* x, int64_t M, int64_t K, const double* v, uint16_t* x_out,
                                        void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
-  QLIN_REQUIRE(K > 0, QLIN_ERR_SHAPE, "K=%lld must be positive", (long long)K);
+  QLIN_REQUIRE(K > 0 && K % 8 == 0 && K <= kRotMaxK, QLIN_ERR_SHAPE,
+               "K=%lld must be a positive multiple of 8, at most %d", (long long)K, kRotMaxK);
   if (M == 0) return QLIN_OK;
   QLIN_PTR(x);
   QLIN_PTR(v);

@@ -35,7 +35,7 @@ def _ulps(a, b):
     return np.abs(ai - bi)
 
 
-@pytest.mark.parametrize("S,T,K", [(3, 5, 8), (8, 64, 512), (17, 130, 1000), (64, 128, 4096)])
+@pytest.mark.parametrize("S,T,K", [(3, 5, 8), (2, 3, 64), (8, 64, 512), (17, 130, 1000), (64, 128, 4096)])
 def test_pca_select(q, S, T, K):
     log(f"pca select S={S} T={T} K={K}")
     x, _ = synth.pca_calibration(S=S, T=T, K=K, seed=S + T, planted=min(2, T))
@@ -64,7 +64,7 @@ def test_pca_leading_eigvec(q, S, K):
     assert float(host(lam)[0]) == pytest.approx(lam_ref, rel=1e-9)
 
 
-@pytest.mark.parametrize("K,N", [(128, 64), (1000, 192), (4096, 4096)])
+@pytest.mark.parametrize("K,N", [(8, 64), (40, 64), (128, 64), (1000, 192), (4096, 4096), (8192, 128)])
 def test_pca_fold_and_rotate(q, K, N):
     log(f"pca fold/rotate K={K} N={N}")
     rng = np.random.default_rng(K + N)
