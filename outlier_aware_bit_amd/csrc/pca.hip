@@ -21,6 +21,15 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+__device__ __forceinline__ void unpack8_f64(v4i raw, double (&d)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = static_cast<uint32_t>(raw[i]);
+    d[2 * i] = static_cast<double>(h2f(static_cast<uint16_t>(w & 0xffffu)));
+    d[2 * i + 1] = static_cast<double>(h2f(static_cast<uint16_t>(w >> 16)));
+  }
+}
+
 __device__ __forceinline__ float absmax8(v4i raw, float m) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -122,7 +131,17 @@ __global__ __launch_bounds__(kSelThreads) void pca_select_final_kernel(const uin
 // centred extreme token of largest norm (it holds the dominant direction
 // whenever one token carries it).  Stops when successive vectors differ by
 // less than tol in 2-norm, or after max_iter iterations; then v_0 <= 0.
-constexpr int kPowThreads = 1024, kPowWaves = kPowThreads / 64;
+//
+// Thread t owns the 8 channels of each 16-byte chunk t + kPowThreads q
+// (q < kPowCPT, K <= 8 * kPowThreads * kPowCPT): its passes over the tokens
+// keep kPowU tokens' loads in flight and its new vector entries in
+// registers.  The token pass (y = Zc v) is one wave per token, with a row's
+// loads in flight kPowB at a time and mu and v read from LDS, stored as
+// [j][chunk] (channel 8 chunk + j) so that the lanes of a wave read
+// consecutive doubles.
+constexpr int kPowThreads = 512, kPowWaves = kPowThreads / 64, kPowCPT = 2, kPowU = 8, kPowB = 8;
+constexpr int kPowCH = kPowThreads * kPowCPT / 64;  // chunks per lane in the token pass, at most
+constexpr int64_t kPowMaxK = 8 * kPowThreads * kPowCPT, kPowMaxS = 2048;
 
 __device__ double block_sum_f64(double v, double* red) {
   v = wave_sum_f64(v);
@@ -138,89 +157,183 @@ __device__ double block_sum_f64(double v, double* red) {
 __global__ __launch_bounds__(kPowThreads) void pca_power_kernel(const uint16_t* __restrict__ z, int64_t S, int64_t K,
                                                                 int max_iter, double tol, double* __restrict__ v,
                                                                 double* __restrict__ lambda_out,
-                                                                int32_t* __restrict__ iters_out,
-                                                                double* __restrict__ mu, double* __restrict__ vn,
-                                                                double* __restrict__ y) {
+                                                                int32_t* __restrict__ iters_out) {
+  extern __shared__ __attribute__((aligned(16))) double pl[];  // mu [K], v [K], y [S]
   __shared__ double red[kPowWaves];
-  __shared__ double sh_s[2];
+  __shared__ int64_t sh_s0;
+  double* const mu_l = pl;
+  double* const v_l = pl + K;
+  double* const y_l = pl + 2 * K;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nch = static_cast<int>(K / 8);
+  // Sum over the tokens of f(token s's chunk c), kPowU tokens in flight.
+  auto token_pass = [&](int c, auto&& f) {
+    const uint16_t* zc = z + 8 * static_cast<int64_t>(c);
+    int64_t s = 0;
+    for (; s + kPowU <= S; s += kPowU) {
+      v4i raw[kPowU];
+#pragma unroll
+      for (int u = 0; u < kPowU; ++u) raw[u] = *reinterpret_cast<const v4i*>(zc + (s + u) * K);
+#pragma unroll
+      for (int u = 0; u < kPowU; ++u) f(s + u, raw[u]);
+    }
+    for (; s < S; ++s) f(s, *reinterpret_cast<const v4i*>(zc + s * K));
+  };
   // mean over the S tokens
-  for (int64_t k = threadIdx.x; k < K; k += kPowThreads) {
-    double acc = 0.0;
-    for (int64_t s = 0; s < S; ++s) acc += static_cast<double>(h2f(z[s * K + k]));
-    mu[k] = acc / static_cast<double>(S);
+#pragma unroll
+  for (int q = 0; q < kPowCPT; ++q) {
+    const int c = threadIdx.x + kPowThreads * q;
+    if (c < nch) {
+      double mu[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+      token_pass(c, [&](int64_t, v4i raw) {
+        double d[8];
+        unpack8_f64(raw, d);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mu[j] += d[j];
+      });
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mu_l[j * nch + c] = mu[j] / static_cast<double>(S);
+    }
   }
   __syncthreads();
-  // norms of the centred tokens (one wave per token), start from the largest
-  for (int64_t s = wave; s < S; s += kPowWaves) {
-    double acc = 0.0;
-    for (int64_t k = lane; k < K; k += 64) {
-      const double d = static_cast<double>(h2f(z[s * K + k])) - mu[k];
-      acc += d * d;
+  // y_s = Zc[s] . w (w = mu_l-centred, from LDS): one wave per token.
+  auto rows_dot = [&](const double* w, bool square) {
+    for (int64_t s = wave; s < S; s += kPowWaves) {
+      const uint16_t* row = z + s * K;
+      double acc = 0.0;
+      for (int i0 = 0; i0 < kPowCH; i0 += kPowB) {
+        if (lane + 64 * i0 >= nch) break;
+        v4i raw[kPowB];
+#pragma unroll
+        for (int i = 0; i < kPowB; ++i) {
+          const int cc = lane + 64 * (i0 + i);
+          if (cc < nch) raw[i] = *reinterpret_cast<const v4i*>(row + 8 * cc);
+        }
+#pragma unroll
+        for (int i = 0; i < kPowB; ++i) {
+          const int cc = lane + 64 * (i0 + i);
+          if (cc < nch) {
+            double d[8];
+            unpack8_f64(raw[i], d);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const double e = d[j] - mu_l[j * nch + cc];
+              acc += e * (square ? e : w[j * nch + cc]);
+            }
+          }
+        }
+      }
+      acc = wave_sum_f64(acc);
+      if (lane == 0) y_l[s] = acc;
     }
-    acc = wave_sum_f64(acc);
-    if (lane == 0) y[s] = acc;
-  }
+  };
+  // norms of the centred tokens, start from the largest
+  rows_dot(nullptr, true);
   __syncthreads();
   if (threadIdx.x == 0) {
     int64_t bs = 0;
     for (int64_t s = 1; s < S; ++s)
-      if (y[s] > y[bs]) bs = s;
-    sh_s[0] = static_cast<double>(bs);
+      if (y_l[s] > y_l[bs]) bs = s;
+    sh_s0 = bs;
   }
   __syncthreads();
-  const int64_t s0 = static_cast<int64_t>(sh_s[0]);
   double part = 0.0;
-  for (int64_t k = threadIdx.x; k < K; k += kPowThreads) {
-    const double d = static_cast<double>(h2f(z[s0 * K + k])) - mu[k];
-    v[k] = d;
-    part += d * d;
+#pragma unroll
+  for (int q = 0; q < kPowCPT; ++q) {
+    const int c = threadIdx.x + kPowThreads * q;
+    if (c < nch) {
+      double d[8];
+      unpack8_f64(*reinterpret_cast<const v4i*>(z + sh_s0 * K + 8 * c), d);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double e = d[j] - mu_l[j * nch + c];
+        v_l[j * nch + c] = e;
+        part += e * e;
+      }
+    }
   }
-  double nrm = sqrt(block_sum_f64(part, red));
+  const double nrm = sqrt(block_sum_f64(part, red));
   const double inv0 = nrm > 0.0 ? 1.0 / nrm : 0.0;
-  for (int64_t k = threadIdx.x; k < K; k += kPowThreads) v[k] = nrm > 0.0 ? v[k] * inv0 : (k == 0 ? 1.0 : 0.0);
+#pragma unroll
+  for (int q = 0; q < kPowCPT; ++q) {
+    const int c = threadIdx.x + kPowThreads * q;
+    if (c < nch) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v_l[j * nch + c] = nrm > 0.0 ? v_l[j * nch + c] * inv0 : (8 * c + j == 0 ? 1.0 : 0.0);
+    }
+  }
   __syncthreads();
   const double inv_s1 = 1.0 / static_cast<double>(S > 1 ? S - 1 : 1);
   double lam = 0.0;
   int it = 0;
   for (; it < max_iter; ++it) {
-    // y = Zc v: one wave per token
-    for (int64_t s = wave; s < S; s += kPowWaves) {
-      double acc = 0.0;
-      for (int64_t k = lane; k < K; k += 64) acc += (static_cast<double>(h2f(z[s * K + k])) - mu[k]) * v[k];
-      acc = wave_sum_f64(acc);
-      if (lane == 0) y[s] = acc;
-    }
+    rows_dot(v_l, false);  // y = Zc v
     __syncthreads();
-    // v' = Zc^T y / (S - 1): one thread per channel, tokens in order
+    // v' = Zc^T y / (S - 1) on this thread's channels, tokens in order
+    double vn[kPowCPT][8];
     part = 0.0;
-    for (int64_t k = threadIdx.x; k < K; k += kPowThreads) {
-      double acc = 0.0;
-      for (int64_t s = 0; s < S; ++s) acc += (static_cast<double>(h2f(z[s * K + k])) - mu[k]) * y[s];
-      acc *= inv_s1;
-      vn[k] = acc;
-      part += acc * acc;
+#pragma unroll
+    for (int q = 0; q < kPowCPT; ++q) {
+      const int c = threadIdx.x + kPowThreads * q;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vn[q][j] = 0.0;
+      if (c < nch) {
+        token_pass(c, [&](int64_t s, v4i raw) {
+          double d[8];
+          unpack8_f64(raw, d);
+          const double ys = y_l[s];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vn[q][j] += (d[j] - mu_l[j * nch + c]) * ys;
+        });
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          vn[q][j] *= inv_s1;
+          part += vn[q][j] * vn[q][j];
+        }
+      }
     }
     lam = sqrt(block_sum_f64(part, red));
     const double inv = lam > 0.0 ? 1.0 / lam : 0.0;
     part = 0.0;
-    for (int64_t k = threadIdx.x; k < K; k += kPowThreads) {
-      const double nv = vn[k] * inv;
-      const double d = nv - v[k];
-      part += d * d;
-      v[k] = nv;
+#pragma unroll
+    for (int q = 0; q < kPowCPT; ++q) {
+      const int c = threadIdx.x + kPowThreads * q;
+      if (c < nch) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          vn[q][j] *= inv;
+          const double dd = vn[q][j] - v_l[j * nch + c];
+          part += dd * dd;
+        }
+      }
     }
+    // block_sum's barriers order every read of v_l and y_l in this
+    // iteration before the writes below.
     const double diff = sqrt(block_sum_f64(part, red));
+#pragma unroll
+    for (int q = 0; q < kPowCPT; ++q) {
+      const int c = threadIdx.x + kPowThreads * q;
+      if (c < nch) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v_l[j * nch + c] = vn[q][j];
+      }
+    }
+    __syncthreads();
     if (lam == 0.0 || diff < tol) {
       ++it;
       break;
     }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) sh_s[1] = v[0] > 0.0 ? -1.0 : 1.0;
-  __syncthreads();
-  const double sg = sh_s[1];
-  for (int64_t k = threadIdx.x; k < K; k += kPowThreads) v[k] *= sg;
+  const double sg = v_l[0] > 0.0 ? -1.0 : 1.0;
+#pragma unroll
+  for (int q = 0; q < kPowCPT; ++q) {
+    const int c = threadIdx.x + kPowThreads * q;
+    if (c < nch) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[8 * c + j] = v_l[j * nch + c] * sg;
+    }
+  }
   if (threadIdx.x == 0) {
     *lambda_out = lam;
     *iters_out = it;
@@ -253,15 +366,6 @@ __device__ double householder_beta(const double* v, int64_t K, double* red) {
 // The row-block sums are kept in w_out (8 bytes per column and row block fit
 // in the 2 bytes per element of w_out), which the apply pass then overwrites.
 constexpr int kFoldThreads = 256, kFoldCols = 512, kFoldRows = 64;
-
-__device__ __forceinline__ void unpack8_f64(v4i raw, double (&d)[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = static_cast<uint32_t>(raw[i]);
-    d[2 * i] = static_cast<double>(h2f(static_cast<uint16_t>(w & 0xffffu)));
-    d[2 * i + 1] = static_cast<double>(h2f(static_cast<uint16_t>(w >> 16)));
-  }
-}
 
 __global__ __launch_bounds__(kFoldThreads) void pca_fold_partial_kernel(const uint16_t* __restrict__ wt, int64_t K,
                                                                         int64_t N, const double* __restrict__ v,
@@ -443,17 +547,19 @@ extern "C" qlin_status qlin_pca_select(const uint16_t* x, int64_t S, int64_t T, 
 extern "C" qlin_status qlin_pca_leading_eigvec(const uint16_t* z, int64_t S, int64_t K, int32_t max_iter,
                                                double tol, double* v, double* lambda, int32_t* iters, double* ws,
                                                void* stream) {
-  QLIN_REQUIRE(S >= 2, QLIN_ERR_SHAPE, "S=%lld: a covariance needs at least 2 tokens", (long long)S);
-  QLIN_REQUIRE(K > 0, QLIN_ERR_SHAPE, "K=%lld must be positive", (long long)K);
+  QLIN_REQUIRE(S >= 2 && S <= kPowMaxS, QLIN_ERR_SHAPE, "S=%lld: a covariance needs 2 to %lld tokens", (long long)S,
+               (long long)kPowMaxS);
+  QLIN_REQUIRE(K > 0 && K % 8 == 0 && K <= kPowMaxK, QLIN_ERR_SHAPE,
+               "K=%lld must be a positive multiple of 8, at most %lld", (long long)K, (long long)kPowMaxK);
   QLIN_REQUIRE(max_iter > 0, QLIN_ERR_INVALID_ARG, "max_iter=%d must be positive", max_iter);
   QLIN_REQUIRE(tol >= 0.0, QLIN_ERR_INVALID_ARG, "tol must be non-negative");
   QLIN_PTR(z);
   QLIN_PTR(v);
   QLIN_PTR(lambda);
   QLIN_PTR(iters);
-  QLIN_PTR(ws);
-  pca_power_kernel<<<dim3(1), kPowThreads, 0, as_stream(stream)>>>(z, S, K, max_iter, tol, v, lambda, iters, ws,
-                                                                   ws + K, ws + 2 * K);
+  QLIN_OPT_PTR(ws);  // no longer used: mu, v and y live in LDS
+  const size_t lds = static_cast<size_t>(2 * K + S) * sizeof(double);
+  pca_power_kernel<<<dim3(1), kPowThreads, lds, as_stream(stream)>>>(z, S, K, max_iter, tol, v, lambda, iters);
   QLIN_LAUNCH_CHECK("pca_power_kernel");
   return QLIN_OK;
 }

@@ -192,6 +192,9 @@ def test_pca_validation():
     _err(lib.qlin_pca_leading_eigvec(A, 8, 128, 0, 1e-9, A, A, A, A, None), _lib.QLIN_ERR_INVALID_ARG)
     _err(lib.qlin_pca_leading_eigvec(A, 8, 128, 10, -1.0, A, A, A, A, None), _lib.QLIN_ERR_INVALID_ARG)
     _err(lib.qlin_pca_leading_eigvec(A, 8, 128, 10, 1e-9, A, A, A, MIS, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_pca_leading_eigvec(A, 8, 100, 10, 1e-9, A, A, A, A, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_pca_leading_eigvec(A, 8, 16384, 10, 1e-9, A, A, A, A, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_pca_leading_eigvec(A, 4096, 128, 10, 1e-9, A, A, A, A, None), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_pca_fold_weight(A, 70000, 64, A, B, A, None), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_pca_fold_weight(A, 128, 60, A, B, A, None), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_pca_rotate(A, 4, 100, A, B, None), _lib.QLIN_ERR_SHAPE)
