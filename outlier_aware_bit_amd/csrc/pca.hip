@@ -343,6 +343,7 @@ __global__ __launch_bounds__(kPowThreads) void pca_power_kernel(const uint16_t* 
 // Householder reflection with H v = e_0: w = v - e_0, beta = 2 / (w^T w).
 __device__ double householder_beta(const double* v, int64_t K, double* red) {
   double part = 0.0;
+#pragma unroll 8
   for (int64_t k = threadIdx.x; k < K; k += blockDim.x) {
     const double wk = v[k] - (k == 0 ? 1.0 : 0.0);
     part += wk * wk;
@@ -410,15 +411,18 @@ __global__ __launch_bounds__(kFoldThreads) void pca_fold_partial_kernel(const ui
   }
 }
 
-__global__ __launch_bounds__(kFoldThreads) void pca_fold_reduce_kernel(const double* __restrict__ part, int64_t nb,
+constexpr int kFoldRedThreads = 64;
+
+__global__ __launch_bounds__(kFoldRedThreads) void pca_fold_reduce_kernel(const double* __restrict__ part, int64_t nb,
                                                                        int64_t K, int64_t N,
                                                                        const double* __restrict__ v,
                                                                        double* __restrict__ q) {
-  __shared__ double red[kFoldThreads / 64];
+  __shared__ double red[kFoldRedThreads / 64];
   const double beta = householder_beta(v, K, red);
-  const int64_t n = static_cast<int64_t>(blockIdx.x) * kFoldThreads + threadIdx.x;
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * kFoldRedThreads + threadIdx.x;
   if (n >= N) return;
   double acc = 0.0;
+#pragma unroll 16
   for (int64_t b = 0; b < nb; ++b) acc += part[b * N + n];
   q[n] = beta * acc;
 }
@@ -581,7 +585,8 @@ extern "C" qlin_status qlin_pca_fold_weight(const uint16_t* w, int64_t K, int64_
   pca_fold_partial_kernel<<<dim3(static_cast<unsigned>((N + kFoldCols - 1) / kFoldCols), static_cast<unsigned>(nb)),
                             kFoldThreads, 0, st>>>(w, K, N, v, part);
   QLIN_LAUNCH_CHECK("pca_fold_partial_kernel");
-  pca_fold_reduce_kernel<<<dim3(static_cast<unsigned>((N + kFoldThreads - 1) / kFoldThreads)), kFoldThreads, 0, st>>>(
+  pca_fold_reduce_kernel<<<dim3(static_cast<unsigned>((N + kFoldRedThreads - 1) / kFoldRedThreads)), kFoldRedThreads,
+                           0, st>>>(
       part, nb, K, N, v, ws);
   QLIN_LAUNCH_CHECK("pca_fold_reduce_kernel");
   pca_fold_apply_kernel<<<dim3(static_cast<unsigned>((N / 8 + kFoldThreads - 1) / kFoldThreads),
