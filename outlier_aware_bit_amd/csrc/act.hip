@@ -433,13 +433,17 @@ __global__ __launch_bounds__(64 * kHadWaves) void hadamard_offset_group_kernel(
     uint8_t* __restrict__ q4, float* __restrict__ scale, int32_t* __restrict__ zero,
     int32_t* __restrict__ rowsum, float* __restrict__ tout) {
   const int lane = threadIdx.x & 63;
-  const int64_t m = static_cast<int64_t>(blockIdx.x) * kHadWaves + (threadIdx.x >> 6);
+  // Two waves per token: wave half h takes the 64-chunk blocks h, h + 2, ...
+  // (a group's four chunks stay in one quad of one wave).
+  const int64_t wg = static_cast<int64_t>(blockIdx.x) * kHadWaves + (threadIdx.x >> 6);
+  const int64_t m = wg >> 1;
+  const int half = static_cast<int>(wg & 1);
   if (m >= M) return;  // uniform per wave
   const uint16_t* xr = x + m * K;
   const int nchunks = static_cast<int>(K / 32);  // a multiple of 4: whole quads
   const int64_t G = K / 128;
   uint8_t* qr = q4 + m * (K / 2);
-  for (int base = 0; base < nchunks; base += 64) {  // uniform
+  for (int base = 64 * half; base < nchunks; base += 128) {  // uniform
     const int c = base + lane;
     // A lane past the row transforms an in-range chunk of the same quarter,
     // so that its quad takes part in the exchanges, and stores nothing.
@@ -591,8 +595,8 @@ extern "C" qlin_status qlin_hadamard_offset_group(const uint16_t* x, int64_t M, 
   QLIN_PTR(zero);
   QLIN_PTR(rowsum);
   QLIN_OPT_PTR(t);
-  QLIN_REQUIRE(M / kHadWaves < 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
-  hadamard_offset_group_kernel<<<dim3(static_cast<unsigned>((M + kHadWaves - 1) / kHadWaves)), 64 * kHadWaves, 0,
+  QLIN_REQUIRE(2 * M / kHadWaves < 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
+  hadamard_offset_group_kernel<<<dim3(static_cast<unsigned>((2 * M + kHadWaves - 1) / kHadWaves)), 64 * kHadWaves, 0,
                                  as_stream(stream)>>>(x, M, K, signs, q4, scale, zero, rowsum, t);
   QLIN_LAUNCH_CHECK("hadamard_offset_group_kernel");
   return QLIN_OK;
