@@ -17,8 +17,7 @@
 namespace qlin {
 namespace {
 
-constexpr int kQuantThreads = 256;  // four wavefronts, one token each
-constexpr int kQuantRegChunks = 16;  // 8-value chunks per lane held in registers (K <= 8192)
+constexpr int kQuantThreads = 256;  // four wavefronts, two per token
 
 __device__ __forceinline__ void unpack8_f16(v4i raw, float (&v)[8]) {
 #pragma unroll
@@ -78,17 +77,21 @@ __device__ __forceinline__ uint2 sym_codes8(const float (&v)[8], float inv) {
 }
 
 // Per-token symmetric int8: a = max|v|, inv = 127/a, q = clamp(rint(v*inv)).
-// One wavefront per token: the row stays in registers as raw fp16 (CH chunks
-// of 8 per lane: 8 up to K = 4096, 16 up to 8192), the absmax is a wavefront
-// butterfly, and there is no block barrier.  Longer rows re-read the tail
-// from cache.
+// Two wavefronts per token: wave half h takes the 64-chunk blocks h, h + 2,
+// ... of the row (chunks of 8 values), the first CH of them held in
+// registers as raw fp16 between the absmax and the coding pass (CH = 4 up to
+// K = 4096, 8 up to 8192; longer rows re-read the tail from cache).  The two
+// halves' maxima meet in LDS across one workgroup barrier.
 //
 // Outlier columns (row stride ldO, zero padded): the code of x[m, O[j]], and
 // the compensation operand fp16(code * (s[O[j]] - 1)).  With OL (ldO <= 256
-// and 2K bytes of LDS per wave), O, r[O] and s[O] are fetched before the row
-// is needed, and the row is staged in the wave's own LDS so that its
-// outlier values are read from there; otherwise they are re-read from memory.
+// and 2K bytes of LDS per token), O, r[O] and s[O] are fetched before the
+// row is needed, and the row is staged in LDS (each wave its own blocks; the
+// barrier makes the whole row visible), so that the outlier values are read
+// from there; otherwise they are re-read from memory.  Each wave takes every
+// other block of 64 outlier slots.
 constexpr int kOutlierLdMax = 256;
+constexpr int kQuantTokens = kQuantThreads / 128;  // tokens per workgroup
 
 template <bool HAS_R, bool OL, int CH, typename RT = float>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
@@ -96,46 +99,53 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     float* __restrict__ scale, const int32_t* __restrict__ O, int nO, int ldO,
     const float* __restrict__ s, int8_t* __restrict__ qO, uint16_t* __restrict__ xO) {
   extern __shared__ __attribute__((aligned(16))) uint8_t qlds[];
-  const int lane = threadIdx.x & 63;
-  const int64_t m = static_cast<int64_t>(blockIdx.x) * (kQuantThreads / 64) + (threadIdx.x >> 6);
-  if (m >= M) return;
-  const uint16_t* xr = x + m * K;
+  __shared__ float red[kQuantThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = wave & 1, tok = wave >> 1;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * kQuantTokens + tok;
+  // A token past M still takes part in the workgroup barrier (on row M - 1's
+  // data) and stores nothing.
+  const bool valid = m < M;
+  const uint16_t* xr = x + (valid ? m : M - 1) * K;
   const int nchunks = static_cast<int>(K / 8);
+  auto chunk = [&](int i) { return 64 * (2 * i + half) + lane; };  // this lane's i-th chunk
 
-  // The row first: chunks c = lane + 64 i (clamped to the row, so that every
-  // load is in range and unconditional).
+  // The row first: chunks clamped to the row, so that every load is in range
+  // and unconditional.
   v4i raw[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int c = lane + 64 * i;
+    const int c = chunk(i);
     raw[i] = *reinterpret_cast<const v4i*>(xr + (c < nchunks ? c : nchunks - 1) * 8);
   }
-  // Outlier bookkeeping of this lane (columns j = lane + 64 i), in flight
-  // with the row.
-  [[maybe_unused]] int oj[kOutlierLdMax / 64];
-  [[maybe_unused]] float rj[kOutlierLdMax / 64], sm1j[kOutlierLdMax / 64];
+  // Outlier bookkeeping of this lane (slots j = lane + 64 (2 i + half)), in
+  // flight with the row.
+  constexpr int kSl = kOutlierLdMax / 128;
+  [[maybe_unused]] int oj[kSl];
+  [[maybe_unused]] float rj[kSl], sm1j[kSl];
+  [[maybe_unused]] uint16_t* const rowl = reinterpret_cast<uint16_t*>(qlds + tok * 2 * K);
   if constexpr (OL) {
 #pragma unroll
-    for (int i = 0; i < kOutlierLdMax / 64; ++i) {
-      const int j = lane + 64 * i;
+    for (int i = 0; i < kSl; ++i) {
+      const int j = lane + 64 * (2 * i + half);
       const int o = j < nO ? O[j] : -1;
       oj[i] = (o >= 0 && o < K) ? o : -1;
     }
 #pragma unroll
-    for (int i = 0; i < kOutlierLdMax / 64; ++i) {
+    for (int i = 0; i < kSl; ++i) {
       const int o = oj[i] >= 0 ? oj[i] : 0;
       rj[i] = HAS_R ? load_r(r, o) : 1.0f;
       sm1j[i] = (xO != nullptr && oj[i] >= 0) ? sub_rn(s[o], 1.0f) : 0.0f;
     }
-    // The raw row goes to this wave's LDS for the outlier columns.
-    uint16_t* const rowl = reinterpret_cast<uint16_t*>(qlds + (threadIdx.x >> 6) * 2 * K);
+    // This wave's blocks of the raw row go to the token's LDS row.
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = lane + 64 * i;
+      const int c = chunk(i);
       if (c < nchunks) *reinterpret_cast<v4i*>(rowl + c * 8) = raw[i];
     }
-    for (int c = lane + 64 * CH; c < nchunks; c += 64)
-      *reinterpret_cast<v4i*>(rowl + c * 8) = *reinterpret_cast<const v4i*>(xr + c * 8);
+    for (int i = CH; chunk(i) - lane < nchunks; ++i) {
+      const int c = chunk(i);
+      if (c < nchunks) *reinterpret_cast<v4i*>(rowl + c * 8) = *reinterpret_cast<const v4i*>(xr + c * 8);
+    }
   }
 
   // v = x * r (HAS_R: held in registers between the two passes), absmax.
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int c = lane + 64 * i;
+    const int c = chunk(i);
     if (c < nchunks) {
       float v[8];
       unpack8_f16(raw[i], v);
@@ -156,21 +166,28 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
       }
     }
   }
-  for (int c = lane + 64 * CH; c < nchunks; c += 64) {
-    float v[8];
-    load8_f16(xr + c * 8, v);
-    scale_chunk<HAS_R>(r, c, v);
+  for (int i = CH; chunk(i) - lane < nchunks; ++i) {
+    const int c = chunk(i);
+    if (c < nchunks) {
+      float v[8];
+      load8_f16(xr + c * 8, v);
+      scale_chunk<HAS_R>(r, c, v);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    }
   }
-  const float a = wave_max(amax);
+  amax = wave_max(amax);
+  if (lane == 0) red[wave] = amax;
+  __syncthreads();  // both halves' maxima, and (OL) the whole staged row
+  const float a = fmaxf(red[2 * tok], red[2 * tok + 1]);
+  if (!valid) return;
   const float inv = (a == 0.0f) ? 0.0f : div_rn(127.0f, a);
-  if (lane == 0) scale[m] = (a == 0.0f) ? 0.0f : div_rn(a, 127.0f);
+  if (lane == 0 && half == 0) scale[m] = (a == 0.0f) ? 0.0f : div_rn(a, 127.0f);
 
   int8_t* qr = q + m * K;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int c = lane + 64 * i;
+    const int c = chunk(i);
     if (c < nchunks) {
       float v[8];
       if constexpr (HAS_R) {
@@ -182,22 +199,21 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
       *reinterpret_cast<uint2*>(qr + c * 8) = sym_codes8<HAS_R>(v, inv);
     }
   }
-  for (int c = lane + 64 * CH; c < nchunks; c += 64) {
-    float v[8];
-    load8_f16(xr + c * 8, v);
-    scale_chunk<HAS_R>(r, c, v);
-    *reinterpret_cast<uint2*>(qr + c * 8) = sym_codes8<HAS_R>(v, inv);
+  for (int i = CH; chunk(i) - lane < nchunks; ++i) {
+    const int c = chunk(i);
+    if (c < nchunks) {
+      float v[8];
+      load8_f16(xr + c * 8, v);
+      scale_chunk<HAS_R>(r, c, v);
+      *reinterpret_cast<uint2*>(qr + c * 8) = sym_codes8<HAS_R>(v, inv);
+    }
   }
   if (ldO == 0) return;
 
   if constexpr (OL) {
-    // The wave reads back only what it wrote: LDS operations of one wave
-    // complete in order.
-    const uint16_t* const rowl = reinterpret_cast<const uint16_t*>(qlds + (threadIdx.x >> 6) * 2 * K);
-    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < kOutlierLdMax / 64; ++i) {
-      const int j = lane + 64 * i;
+    for (int i = 0; i < kSl; ++i) {
+      const int j = lane + 64 * (2 * i + half);
       if (j < ldO) {
         int code = 0;
         if (oj[i] >= 0) {
@@ -210,7 +226,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
       }
     }
   } else {
-    for (int j = lane; j < ldO; j += 64) {
+    for (int j = lane + 64 * half; j < ldO; j += 128) {
       const int o = j < nO ? O[j] : -1;
       int code = 0;
       float sm1 = 0.0f;
@@ -487,13 +503,12 @@ __global__ __launch_bounds__(64 * kHadWaves) void hadamard_offset_group_kernel(
 
 qlin_status launch_quant_grad(const uint16_t* dy, int64_t M, int64_t N, const uint16_t* sw, int8_t* gq, float* gs,
                               hipStream_t st) {
-  constexpr int rows_per_block = kQuantThreads / 64;
-  const dim3 grid(static_cast<unsigned>((M + rows_per_block - 1) / rows_per_block));
+  const dim3 grid(static_cast<unsigned>((M + kQuantTokens - 1) / kQuantTokens));
   if (N <= 4096)
-    quant_act_kernel<true, false, 8, uint16_t><<<grid, kQuantThreads, 0, st>>>(dy, M, N, sw, gq, gs, nullptr, 0, 0,
+    quant_act_kernel<true, false, 4, uint16_t><<<grid, kQuantThreads, 0, st>>>(dy, M, N, sw, gq, gs, nullptr, 0, 0,
                                                                                  nullptr, nullptr, nullptr);
   else
-    quant_act_kernel<true, false, 16, uint16_t><<<grid, kQuantThreads, 0, st>>>(dy, M, N, sw, gq, gs, nullptr, 0, 0,
+    quant_act_kernel<true, false, 8, uint16_t><<<grid, kQuantThreads, 0, st>>>(dy, M, N, sw, gq, gs, nullptr, 0, 0,
                                                                                   nullptr, nullptr, nullptr);
   QLIN_LAUNCH_CHECK("quant_act_kernel (gradient)");
   return QLIN_OK;
@@ -525,11 +540,10 @@ extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, c
                  "O, qO and xO must be NULL when nO == 0");
   }
   const int ldO = static_cast<int>(outlier_ld(nO));
-  constexpr int rows_per_block = kQuantThreads / 64;
-  QLIN_REQUIRE(M / rows_per_block < 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
-  const dim3 grid(static_cast<unsigned>((M + rows_per_block - 1) / rows_per_block));
-  // Outlier columns through LDS when they fit (2K bytes per wave).
-  const size_t ol_lds = static_cast<size_t>(rows_per_block) * 2 * static_cast<size_t>(K);
+  QLIN_REQUIRE(M / kQuantTokens < 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
+  const dim3 grid(static_cast<unsigned>((M + kQuantTokens - 1) / kQuantTokens));
+  // Outlier columns through LDS when they fit (2K bytes per token).
+  const size_t ol_lds = static_cast<size_t>(kQuantTokens) * 2 * static_cast<size_t>(K);
   const bool ol = nO > 0 && ldO <= kOutlierLdMax && ol_lds <= 160 * 1024;
   hipStream_t st = as_stream(stream);
   auto go = [&](auto has_r, auto ol_c, auto ch) {
@@ -540,9 +554,9 @@ extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, c
   };
   auto go_ch = [&](auto has_r, auto ol_c) {
     if (K <= 4096)
-      go(has_r, ol_c, std::integral_constant<int, 8>{});
+      go(has_r, ol_c, std::integral_constant<int, 4>{});
     else
-      go(has_r, ol_c, std::integral_constant<int, 16>{});
+      go(has_r, ol_c, std::integral_constant<int, 8>{});
   };
   auto go_ol = [&](auto has_r) {
     if (ol)
