@@ -239,13 +239,15 @@ qlin_status qlin_pca_select(const uint16_t* x, int64_t S, int64_t T, int64_t K, 
 /*
  * qlin_pca_leading_eigvec -- leading eigenvector v (unit, v[0] <= 0) and its
  * eigenvalue of the sample covariance C = Zc^T Zc / (S - 1) of the rows of z,
- * centred on their mean, by power iteration in float64 without forming C.
- * The start vector is the centred row of largest norm; the iteration stops
- * when successive vectors differ by less than tol (2-norm) or after max_iter.
+ * centred on their mean, by power iteration in float64 without forming C
+ * (the iterates are kept as token weights a, v = Zc^T a, through the S x S
+ * Gram matrix Zc Zc^T).  The start vector is the centred row of largest
+ * norm; the iteration stops when successive vectors differ by less than tol
+ * (2-norm) or after max_iter.
  *   z fp16 [S x K] (2 <= S <= 2048, K % 8 == 0, K <= 8192);  v float64 [K] out;
  *   lambda float64 [1] out;  iters int32 [1] out (iterations run);
- *   ws: unused (the mean, the vector and the projections live in LDS); may be NULL
- * One workgroup: a calibration step, not a per-token one.
+ *   ws float64 scratch [S*S + K + S + 1]
+ * A calibration step, not a per-token one.
  */
 qlin_status qlin_pca_leading_eigvec(const uint16_t* z, int64_t S, int64_t K, int32_t max_iter, double tol,
                                     double* v, double* lambda, int32_t* iters, double* ws, void* stream);

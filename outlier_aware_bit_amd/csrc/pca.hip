@@ -125,23 +125,153 @@ __global__ __launch_bounds__(kSelThreads) void pca_select_final_kernel(const uin
 }
 
 // Power iteration for the leading eigenvector of C = Zc^T Zc / (S - 1), with
-// Zc the extreme tokens centred on their mean, without forming C:
-// y = Zc v, v' = Zc^T y / (S - 1), lambda = |v'|, v = v' / lambda.  One
-// workgroup; every sum in a fixed order, in float64.  The start vector is the
-// centred extreme token of largest norm (it holds the dominant direction
-// whenever one token carries it).  Stops when successive vectors differ by
-// less than tol in 2-norm, or after max_iter iterations; then v_0 <= 0.
-//
-// Thread t owns the 8 channels of each 16-byte chunk t + kPowThreads q
-// (q < kPowCPT, K <= 8 * kPowThreads * kPowCPT): its passes over the tokens
-// keep kPowU tokens' loads in flight and its new vector entries in
-// registers.  The token pass (y = Zc v) is one wave per token, with a row's
-// loads in flight kPowB at a time and mu and v read from LDS, stored as
-// [j][chunk] (channel 8 chunk + j) so that the lanes of a wave read
-// consecutive doubles.
-constexpr int kPowThreads = 512, kPowWaves = kPowThreads / 64, kPowCPT = 2, kPowU = 8, kPowB = 8;
-constexpr int kPowCH = kPowThreads * kPowCPT / 64;  // chunks per lane in the token pass, at most
-constexpr int64_t kPowMaxK = 8 * kPowThreads * kPowCPT, kPowMaxS = 2048;
+// Zc the extreme tokens centred on their mean, without forming C, run in the
+// tokens' coordinates: every iterate is v = Zc^T a for a vector a of S
+// token weights, and with the Gram matrix G = Zc Zc^T (S x S)
+//   C v = Zc^T b,  b = G a / (S - 1),  |C v|^2 = b^T G b,  |Zc^T d|^2 = d^T G d,
+// so the iteration v' = C v / |C v| is a' = b / lambda with lambda = |C v|,
+// the distance of successive vectors is sqrt(da^T G da), and v = Zc^T a at
+// the end.  The start vector is the centred extreme token of largest norm
+// (a = e_s0 / |Zc[s0]|, the largest diagonal entry of G); the iteration
+// stops when successive vectors differ by less than tol, or after max_iter;
+// then v_0 <= 0.  float64 throughout, every sum in a fixed order.  Passes:
+// the mean, G on the fp64 matrix cores, the iteration (one workgroup, one
+// product by G per iteration), and the projection v = Zc^T a.
+constexpr int kPcaThreads = 256;
+constexpr int kPowThreads = 256, kPowWaves = kPowThreads / 64, kPowU = 8;
+constexpr int64_t kPowMaxK = 8192, kPowMaxS = 2048, kPowLdsS = 128;  // G in LDS up to S = 128
+
+// Column sums over the tokens, sum_s f(s) (z[s, k] - c_k) w_s: a workgroup
+// takes 64 channels (8 chunks of 8); thread (chunk t & 7, token group
+// t >> 3) adds the tokens s = group, group + 32, ... (8 in flight), then the
+// 32 groups' sums are added in order through LDS.  kMean: c = 0, w = 1.
+constexpr int kColGroups = kPcaThreads / 8;
+
+template <bool kMean>
+__device__ __forceinline__ void column_sums(const uint16_t* __restrict__ z, int64_t S, int64_t K,
+                                            const double* __restrict__ cen, const double* __restrict__ w,
+                                            double (&out)[8], double (*red)[8][8]) {
+  const int ch = threadIdx.x & 7, grp = threadIdx.x >> 3;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 8 + ch;
+  const bool ok = c < K / 8;
+  const uint16_t* zc = z + 8 * (ok ? c : 0);
+  double m[8], acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m[j] = (kMean || !ok) ? 0.0 : cen[8 * c + j];
+  int64_t s = grp;
+  for (; s + kColGroups * (kPowU - 1) < S; s += kColGroups * kPowU) {
+    v4i raw[kPowU];
+#pragma unroll
+    for (int u = 0; u < kPowU; ++u) raw[u] = *reinterpret_cast<const v4i*>(zc + (s + kColGroups * u) * K);
+#pragma unroll
+    for (int u = 0; u < kPowU; ++u) {
+      double d[8];
+      unpack8_f64(raw[u], d);
+      const double ws = kMean ? 1.0 : w[s + kColGroups * u];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += kMean ? d[j] : (d[j] - m[j]) * ws;
+    }
+  }
+  for (; s < S; s += kColGroups) {
+    double d[8];
+    unpack8_f64(*reinterpret_cast<const v4i*>(zc + s * K), d);
+    const double ws = kMean ? 1.0 : w[s];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += kMean ? d[j] : (d[j] - m[j]) * ws;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[grp][ch][j] = acc[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out[j] = 0.0;
+  if (grp == 0) {
+    for (int g = 0; g < kColGroups; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out[j] += red[g][ch][j];
+  }
+}
+
+// mu[k] = sum_s z[s, k] / S.
+__global__ __launch_bounds__(kPcaThreads) void pca_mean_kernel(const uint16_t* __restrict__ z, int64_t S, int64_t K,
+                                                               double* __restrict__ mu) {
+  __shared__ double red[kColGroups][8][8];
+  double sum[8];
+  column_sums<true>(z, S, K, nullptr, nullptr, sum, red);
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x & 7);
+  if ((threadIdx.x >> 3) == 0 && c < K / 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mu[8 * c + j] = sum[j] / static_cast<double>(S);
+  }
+}
+
+// G tile (16 tokens i) x (16 tokens j) on v_mfma_f64_16x16x4f64.  In a
+// product step lane l gives the centred value of token (l & 15) at one k and
+// the hardware pairs A's lane (i, g) with B's lane (j, g), g = l >> 4; a
+// lane's 16-byte chunk (8 consecutive k) feeds 8 steps, so 4 lane groups
+// cover 32 k per 8 steps.  The 16 waves take the 32-k blocks in turn; their
+// tiles are added in order through LDS.  Result layout: lane l, register r
+// holds row 4 r + (l >> 4), column l & 15.
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+constexpr int kGramThreads = 1024;
+
+__global__ __launch_bounds__(kGramThreads) void pca_gram_kernel(const uint16_t* __restrict__ z, int64_t S, int64_t K,
+                                                                const double* __restrict__ mu,
+                                                                double* __restrict__ G) {
+  __shared__ double red[kGramThreads / 64][64][4];
+  __shared__ double mul[kPowMaxK];
+  for (int64_t k = threadIdx.x; k < K; k += kGramThreads) mul[k] = mu[k];
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t ti = static_cast<int64_t>(blockIdx.y) * 16 + (lane & 15);
+  const int64_t tj = static_cast<int64_t>(blockIdx.x) * 16 + (lane & 15);
+  const bool oki = ti < S, okj = tj < S;
+  const uint16_t* zi = z + (oki ? ti : 0) * K;
+  const uint16_t* zj = z + (okj ? tj : 0) * K;
+  const int nch = static_cast<int>(K / 8), g = lane >> 4;
+  v4d acc = v4d{0.0, 0.0, 0.0, 0.0};
+  constexpr int kW = kGramThreads / 64;
+  // Blocks blk = wave + kW u; two blocks' loads in flight per step.
+  for (int blk = wave; 4 * blk < nch; blk += 2 * kW) {
+    v4i ra[2], rb[2];
+    bool okc[2];
+    int cc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = 4 * (blk + kW * u) + g;  // this lane's chunk
+      okc[u] = c < nch;
+      cc[u] = okc[u] ? c : 0;
+      ra[u] = *reinterpret_cast<const v4i*>(zi + 8 * cc[u]);
+      rb[u] = *reinterpret_cast<const v4i*>(zj + 8 * cc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      double a[8], b[8];
+      unpack8_f64(ra[u], a);
+      unpack8_f64(rb[u], b);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double m = mul[8 * cc[u] + j];
+        const double av = (oki && okc[u]) ? a[j] - m : 0.0;
+        const double bv = (okj && okc[u]) ? b[j] - m : 0.0;
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][lane][r] = acc[r];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    double t = red[0][lane][r];
+#pragma unroll
+    for (int w = 1; w < kGramThreads / 64; ++w) t += red[w][lane][r];
+    const int64_t row = static_cast<int64_t>(blockIdx.y) * 16 + 4 * r + (lane >> 4);
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * 16 + (lane & 15);
+    if (row < S && col < S) G[row * S + col] = t;
+  }
+}
 
 __device__ double block_sum_f64(double v, double* red) {
   v = wave_sum_f64(v);
@@ -154,190 +284,155 @@ __device__ double block_sum_f64(double v, double* red) {
   return r;
 }
 
-__global__ __launch_bounds__(kPowThreads) void pca_power_kernel(const uint16_t* __restrict__ z, int64_t S, int64_t K,
-                                                                int max_iter, double tol, double* __restrict__ v,
-                                                                double* __restrict__ lambda_out,
-                                                                int32_t* __restrict__ iters_out) {
-  extern __shared__ __attribute__((aligned(16))) double pl[];  // mu [K], v [K], y [S]
+// The iteration in token coordinates (one workgroup).  out: a [S], then
+// the sign to apply to v (out[S]), lambda and the iteration count.
+__global__ __launch_bounds__(kPowThreads) void pca_iter_kernel(const uint16_t* __restrict__ z, int64_t S, int64_t K,
+                                                               const double* __restrict__ G,
+                                                               const double* __restrict__ mu, int max_iter,
+                                                               double tol, double* __restrict__ out,
+                                                               double* __restrict__ lambda_out,
+                                                               int32_t* __restrict__ iters_out) {
+  // LDS: a, ga, b, gb (S each), then G itself when S <= kPowLdsS.
+  extern __shared__ __attribute__((aligned(16))) double il[];
   __shared__ double red[kPowWaves];
   __shared__ int64_t sh_s0;
-  double* const mu_l = pl;
-  double* const v_l = pl + K;
-  double* const y_l = pl + 2 * K;
+  double* const a = il;
+  double* const ga = il + S;
+  double* const b = il + 2 * S;
+  double* const gb = il + 3 * S;
+  const bool g_lds = S <= kPowLdsS;
+  double* const gl = il + 4 * S;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nch = static_cast<int>(K / 8);
-  // Sum over the tokens of f(token s's chunk c), kPowU tokens in flight.
-  auto token_pass = [&](int c, auto&& f) {
-    const uint16_t* zc = z + 8 * static_cast<int64_t>(c);
-    int64_t s = 0;
-    for (; s + kPowU <= S; s += kPowU) {
-      v4i raw[kPowU];
-#pragma unroll
-      for (int u = 0; u < kPowU; ++u) raw[u] = *reinterpret_cast<const v4i*>(zc + (s + u) * K);
-#pragma unroll
-      for (int u = 0; u < kPowU; ++u) f(s + u, raw[u]);
-    }
-    for (; s < S; ++s) f(s, *reinterpret_cast<const v4i*>(zc + s * K));
-  };
-  // mean over the S tokens
-#pragma unroll
-  for (int q = 0; q < kPowCPT; ++q) {
-    const int c = threadIdx.x + kPowThreads * q;
-    if (c < nch) {
-      double mu[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-      token_pass(c, [&](int64_t, v4i raw) {
-        double d[8];
-        unpack8_f64(raw, d);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mu[j] += d[j];
-      });
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mu_l[j * nch + c] = mu[j] / static_cast<double>(S);
-    }
+  if (g_lds) {
+#pragma unroll 16
+    for (int64_t e = threadIdx.x; e < S * S; e += kPowThreads) gl[e] = G[e];
+  } else {
+#pragma unroll 2
+    for (int64_t t = threadIdx.x; t < S; t += kPowThreads) gb[t] = G[t * S + t];
   }
   __syncthreads();
-  // y_s = Zc[s] . w (w = mu_l-centred, from LDS): one wave per token.
-  auto rows_dot = [&](const double* w, bool square) {
-    for (int64_t s = wave; s < S; s += kPowWaves) {
-      const uint16_t* row = z + s * K;
+  const double* const gm = g_lds ? gl : G;
+  // y = G x: thread t sums column t of G (G is symmetric), j in order, so
+  // that the lanes read consecutive entries.
+  auto matvec = [&](const double* x, double* y) {
+    for (int64_t t = threadIdx.x; t < S; t += kPowThreads) {
       double acc = 0.0;
-      for (int i0 = 0; i0 < kPowCH; i0 += kPowB) {
-        if (lane + 64 * i0 >= nch) break;
-        v4i raw[kPowB];
-#pragma unroll
-        for (int i = 0; i < kPowB; ++i) {
-          const int cc = lane + 64 * (i0 + i);
-          if (cc < nch) raw[i] = *reinterpret_cast<const v4i*>(row + 8 * cc);
-        }
-#pragma unroll
-        for (int i = 0; i < kPowB; ++i) {
-          const int cc = lane + 64 * (i0 + i);
-          if (cc < nch) {
-            double d[8];
-            unpack8_f64(raw[i], d);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const double e = d[j] - mu_l[j * nch + cc];
-              acc += e * (square ? e : w[j * nch + cc]);
-            }
-          }
-        }
-      }
-      acc = wave_sum_f64(acc);
-      if (lane == 0) y_l[s] = acc;
+#pragma unroll 8
+      for (int64_t j = 0; j < S; ++j) acc += gm[j * S + t] * x[j];
+      y[t] = acc;
     }
   };
-  // norms of the centred tokens, start from the largest
-  rows_dot(nullptr, true);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t bs = 0;
-    for (int64_t s = 1; s < S; ++s)
-      if (y_l[s] > y_l[bs]) bs = s;
-    sh_s0 = bs;
-  }
-  __syncthreads();
-  double part = 0.0;
-#pragma unroll
-  for (int q = 0; q < kPowCPT; ++q) {
-    const int c = threadIdx.x + kPowThreads * q;
-    if (c < nch) {
-      double d[8];
-      unpack8_f64(*reinterpret_cast<const v4i*>(z + sh_s0 * K + 8 * c), d);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double e = d[j] - mu_l[j * nch + c];
-        v_l[j * nch + c] = e;
-        part += e * e;
+  // s0 = the first token of largest diagonal entry: each wave its stride of
+  // tokens, then wave 0 over the waves' winners (both keep the first).
+  {
+    __shared__ double wv[kPowWaves];
+    __shared__ int64_t wt[kPowWaves];
+    double bv = -1.0;
+    int64_t bt = S;
+    for (int64_t t = threadIdx.x; t < S; t += kPowThreads) {
+      const double dv = g_lds ? gl[t * S + t] : gb[t];
+      if (dv > bv) {  // t increases: strict > keeps the first
+        bv = dv;
+        bt = t;
       }
     }
-  }
-  const double nrm = sqrt(block_sum_f64(part, red));
-  const double inv0 = nrm > 0.0 ? 1.0 / nrm : 0.0;
 #pragma unroll
-  for (int q = 0; q < kPowCPT; ++q) {
-    const int c = threadIdx.x + kPowThreads * q;
-    if (c < nch) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        v_l[j * nch + c] = nrm > 0.0 ? v_l[j * nch + c] * inv0 : (8 * c + j == 0 ? 1.0 : 0.0);
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ov = __shfl_xor(bv, o, 64);
+      const int64_t ot = __shfl_xor(bt, o, 64);
+      if (ov > bv || (ov == bv && ot < bt)) {
+        bv = ov;
+        bt = ot;
+      }
     }
+    if (lane == 0) {
+      wv[wave] = bv;
+      wt[wave] = bt;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double v = wv[0];
+      int64_t t = wt[0];
+      for (int w = 1; w < kPowWaves; ++w)
+        if (wv[w] > v || (wv[w] == v && wt[w] < t)) {
+          v = wv[w];
+          t = wt[w];
+        }
+      sh_s0 = t < S ? t : 0;
+    }
+    __syncthreads();
+  }
+  const int64_t s0 = sh_s0;
+  const double n0 = gm[s0 * S + s0];
+  const bool zero = !(n0 > 0.0);  // every centred token is zero: v = e_0
+  const double inv0 = zero ? 0.0 : 1.0 / sqrt(n0);
+  for (int64_t t = threadIdx.x; t < S; t += kPowThreads) {
+    a[t] = t == s0 ? inv0 : 0.0;
+    ga[t] = gm[t * S + s0] * inv0;
   }
   __syncthreads();
-  const double inv_s1 = 1.0 / static_cast<double>(S > 1 ? S - 1 : 1);
+  const double inv_s1 = 1.0 / static_cast<double>(S - 1);
   double lam = 0.0;
   int it = 0;
   for (; it < max_iter; ++it) {
-    rows_dot(v_l, false);  // y = Zc v
+    for (int64_t t = threadIdx.x; t < S; t += kPowThreads) b[t] = ga[t] * inv_s1;
     __syncthreads();
-    // v' = Zc^T y / (S - 1) on this thread's channels, tokens in order
-    double vn[kPowCPT][8];
-    part = 0.0;
-#pragma unroll
-    for (int q = 0; q < kPowCPT; ++q) {
-      const int c = threadIdx.x + kPowThreads * q;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vn[q][j] = 0.0;
-      if (c < nch) {
-        token_pass(c, [&](int64_t s, v4i raw) {
-          double d[8];
-          unpack8_f64(raw, d);
-          const double ys = y_l[s];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) vn[q][j] += (d[j] - mu_l[j * nch + c]) * ys;
-        });
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          vn[q][j] *= inv_s1;
-          part += vn[q][j] * vn[q][j];
-        }
-      }
+    matvec(b, gb);
+    __syncthreads();
+    double part = 0.0;
+    for (int64_t t = threadIdx.x; t < S; t += kPowThreads) part += b[t] * gb[t];
+    const double l2 = block_sum_f64(part, red);
+    lam = l2 > 0.0 ? sqrt(l2) : 0.0;
+    if (lam == 0.0) {
+      ++it;
+      break;
     }
-    lam = sqrt(block_sum_f64(part, red));
-    const double inv = lam > 0.0 ? 1.0 / lam : 0.0;
+    const double inv = 1.0 / lam;
     part = 0.0;
-#pragma unroll
-    for (int q = 0; q < kPowCPT; ++q) {
-      const int c = threadIdx.x + kPowThreads * q;
-      if (c < nch) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          vn[q][j] *= inv;
-          const double dd = vn[q][j] - v_l[j * nch + c];
-          part += dd * dd;
-        }
-      }
+    for (int64_t t = threadIdx.x; t < S; t += kPowThreads) {
+      const double an = b[t] * inv, gan = gb[t] * inv;
+      part += (an - a[t]) * (gan - ga[t]);
     }
-    // block_sum's barriers order every read of v_l and y_l in this
-    // iteration before the writes below.
-    const double diff = sqrt(block_sum_f64(part, red));
-#pragma unroll
-    for (int q = 0; q < kPowCPT; ++q) {
-      const int c = threadIdx.x + kPowThreads * q;
-      if (c < nch) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v_l[j * nch + c] = vn[q][j];
-      }
+    const double d2 = block_sum_f64(part, red);  // its barriers order the reads above before the writes below
+    for (int64_t t = threadIdx.x; t < S; t += kPowThreads) {
+      a[t] = b[t] * inv;
+      ga[t] = gb[t] * inv;
     }
     __syncthreads();
-    if (lam == 0.0 || diff < tol) {
+    if (sqrt(d2 > 0.0 ? d2 : 0.0) < tol) {
       ++it;
       break;
     }
   }
-  const double sg = v_l[0] > 0.0 ? -1.0 : 1.0;
-#pragma unroll
-  for (int q = 0; q < kPowCPT; ++q) {
-    const int c = threadIdx.x + kPowThreads * q;
-    if (c < nch) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[8 * c + j] = v_l[j * nch + c] * sg;
-    }
-  }
+  // v_0 = sum_s (z[s, 0] - mu_0) a_s decides the sign.
+  double part = 0.0;
+  const double m0 = mu[0];
+  for (int64_t t = threadIdx.x; t < S; t += kPowThreads)
+    part += (static_cast<double>(h2f(z[t * K])) - m0) * a[t];
+  const double v0 = block_sum_f64(part, red);
+  for (int64_t t = threadIdx.x; t < S; t += kPowThreads) out[t] = a[t];
   if (threadIdx.x == 0) {
+    // zero: v = e_0, so v_0 = 1 > 0 flips it.
+    out[S] = zero ? 2.0 : (v0 > 0.0 ? -1.0 : 1.0);
     *lambda_out = lam;
     *iters_out = it;
   }
+}
+
+// v[k] = sign * sum_s (z[s, k] - mu[k]) a_s.  sign == 2 marks the all-zero
+// case: v = -e_0.
+__global__ __launch_bounds__(kPcaThreads) void pca_project_kernel(const uint16_t* __restrict__ z, int64_t S,
+                                                                  int64_t K, const double* __restrict__ mu,
+                                                                  const double* __restrict__ av,
+                                                                  double* __restrict__ v) {
+  __shared__ double red[kColGroups][8][8];
+  double sum[8];
+  column_sums<false>(z, S, K, mu, av, sum, red);
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x & 7);
+  if ((threadIdx.x >> 3) != 0 || c >= K / 8) return;
+  const double sg = av[S];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[8 * c + j] = sg == 2.0 ? ((8 * c + j == 0) ? -1.0 : 0.0) : sum[j] * sg;
 }
 
 // Householder reflection with H v = e_0: w = v - e_0, beta = 2 / (w^T w).
@@ -561,10 +656,24 @@ extern "C" qlin_status qlin_pca_leading_eigvec(const uint16_t* z, int64_t S, int
   QLIN_PTR(v);
   QLIN_PTR(lambda);
   QLIN_PTR(iters);
-  QLIN_OPT_PTR(ws);  // no longer used: mu, v and y live in LDS
-  const size_t lds = static_cast<size_t>(2 * K + S) * sizeof(double);
-  pca_power_kernel<<<dim3(1), kPowThreads, lds, as_stream(stream)>>>(z, S, K, max_iter, tol, v, lambda, iters);
-  QLIN_LAUNCH_CHECK("pca_power_kernel");
+  QLIN_PTR(ws);
+  // ws: G [S x S], mu [K], a [S] and the sign.
+  double* const G = ws;
+  double* const mu = ws + S * S;
+  double* const av = mu + K;
+  hipStream_t st = as_stream(stream);
+  const unsigned gc = static_cast<unsigned>((K / 8 + 7) / 8);  // 64 channels per workgroup
+  const unsigned gt = static_cast<unsigned>((S + 15) / 16);
+  pca_mean_kernel<<<dim3(gc), kPcaThreads, 0, st>>>(z, S, K, mu);
+  QLIN_LAUNCH_CHECK("pca_mean_kernel");
+  pca_gram_kernel<<<dim3(gt, gt), kGramThreads, 0, st>>>(z, S, K, mu, G);
+  QLIN_LAUNCH_CHECK("pca_gram_kernel");
+  const size_t ilds = static_cast<size_t>(4 * S + (S <= kPowLdsS ? S * S : 0)) * sizeof(double);
+  pca_iter_kernel<<<dim3(1), kPowThreads, ilds, st>>>(z, S, K, G, mu, max_iter,
+                                                                                           tol, av, lambda, iters);
+  QLIN_LAUNCH_CHECK("pca_iter_kernel");
+  pca_project_kernel<<<dim3(gc), kPcaThreads, 0, st>>>(z, S, K, mu, av, v);
+  QLIN_LAUNCH_CHECK("pca_project_kernel");
   return QLIN_OK;
 }
 

@@ -362,7 +362,7 @@ def qlin_pca_leading_eigvec(z, max_iter=200, tol=1e-12):
     v = _empty((K,), torch.float64, z)
     lam = _empty((1,), torch.float64, z)
     its = _empty((1,), torch.int32, z)
-    ws = _empty((2 * K + S,), torch.float64, z)
+    ws = _empty((S * S + K + S + 1,), torch.float64, z)
     _lib.check("qlin_pca_leading_eigvec", lib.qlin_pca_leading_eigvec(
         z.data_ptr(), S, K, max_iter, tol, v.data_ptr(), lam.data_ptr(), its.data_ptr(), ws.data_ptr(), _stream()))
     return v, lam, its
