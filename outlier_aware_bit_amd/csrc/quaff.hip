@@ -19,7 +19,10 @@ constexpr int kMomThreads = 256;
 // line per token row).  The outliers of a strip share its lines, so reading
 // the whole strip once per row fetches every line of X that holds an outlier
 // exactly once, with no reduction across workgroups.  Strips without an
-// outlier read nothing from X.
+// outlier read nothing from X.  (Splitting a strip's rows over several
+// workgroups needs either a second launch to fold their maxima or
+// device-scope fences, which write back and invalidate the per-XCD L2
+// caches; both cost more than the extra workgroups save at 2048 tokens.)
 //   c_k   = max_m |x[m, k]| for the 64 channels k of the strip
 //   o in O in the strip:  beta = max(1, sqrt(c_o / wmax)) (1 if wmax == 0),
 //                         s_o = gamma*s_o + (1-gamma)*beta, r_o = 1/s_o

@@ -42,7 +42,7 @@ class _Step:
 def test_quaff_step_graph_replays_match_eager():
     import torch
     from outlier_aware_bit_amd import qlin as q
-    M, K, N, nO = 256, 1024, 512, 51
+    M, K, N, nO = 1024, 1024, 512, 51
     log(f"graph replay of the Quaff step M={M} K={K} N={N} |O|={nO}")
     d = synth.quaff_steps(M=M, K=K, N=N, n_outliers=nO, steps=2, seed=11)
     codes, sw = q.qlin_quant_weight_sym(dev(d.w), 8)

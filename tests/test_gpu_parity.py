@@ -96,7 +96,8 @@ def test_hadamard_offset_constant_tokens(q):
 
 
 # ------------------------------------------------------------ Quaff
-@pytest.mark.parametrize("M,nO", [(300, 51), (1, 1), (0, 4), (64, 0)])
+# Up to 8300 tokens: one and several passes of a strip's 2048-row loads.
+@pytest.mark.parametrize("M,nO", [(300, 51), (1, 1), (0, 4), (64, 0), (513, 7), (2048, 51), (8300, 60)])
 def test_momentum_ten_steps(q, M, nO):
     import torch
     log(f"momentum M={M} nO={nO}")
