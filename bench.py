@@ -391,7 +391,7 @@ def rows_measurements(q, layer):
     out["NEXT4_pca_select"] = dict(workload=f"{S6} sequences x {T6} tokens x {K6}", ms=t_sel, bytes=b,
                                    gbs=b / t_sel / 1e6, frac=b / t_sel / 1e6 / PEAK_HBM_GBS, bound="hbm")
     out["NEXT4_pca_leading_eigvec"] = dict(workload=f"{S6} extreme tokens x {K6}", ms=t_eig,
-                                           iterations=int(its6.item()), bound="latency (one workgroup)")
+                                           iterations=int(its6.item()), bound="latency (mean, fp64-MFMA Gram matrix, one-workgroup iteration, projection)")
     b = 2 * 2 * K6 * K6
     out["NEXT4_pca_fold_weight"] = dict(workload=f"{K6}x{K6}", ms=t_fold, bytes=b, gbs=b / t_fold / 1e6,
                                         frac=b / t_fold / 1e6 / PEAK_HBM_GBS, bound="hbm")
