@@ -282,66 +282,166 @@ __device__ __forceinline__ void load_a_half(const TilePtrs<B, A, TM>& p, int s, 
 }
 
 // Group-wise W4A4: the constants of one 128-k group (one K stage) for this
-// lane -- step, zero point and code sum of its TM token rows, and the
-// group's weight column sums for its 32 columns, in the accumulators' runs
-// of four (register v of block nt holds column 32 nt + 8 (v >> 2) + 4 h +
-// (v & 3), h = lane >> 5).
+// lane -- step, zero point and code sum of its TM token rows.
 template <int TM>
 struct GroupC {
   float sa[TM];
   int32_t za[TM];
   int32_t rs[TM];
-  v4i cs[2][4];
 };
 
 // rowoff[tm]: (token row) * (K/128) for row 32 tm + (lane & 31) of the tile,
-// clamped to the last row; csp: colsum + first column of the wave + 4 h.
+// clamped to the last row.
 template <int TM>
-__device__ __forceinline__ void load_group(const GemmArgs& g, const int64_t (&rowoff)[TM], const int32_t* csp,
-                                           int s, GroupC<TM>& c) {
+__device__ __forceinline__ void load_group(const GemmArgs& g, const int64_t (&rowoff)[TM], int s, GroupC<TM>& c) {
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     c.sa[tm] = g.sa[rowoff[tm] + s];
     c.za[tm] = g.za[rowoff[tm] + s];
     c.rs[tm] = g.rowsum[rowoff[tm] + s];
   }
-  const int32_t* p = csp + static_cast<int64_t>(s) * g.N;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) c.cs[nt][q] = *reinterpret_cast<const v4i*>(p + 32 * nt + 8 * q);
 }
 
-// Product of two integers known to fit 24 bits (one v_mad_i32_i24 with an add).
-__device__ __forceinline__ int32_t mul24(int32_t a, int32_t b) { return ((a << 8) >> 8) * ((b << 8) >> 8); }
-
 // End of group s: with raw = sum over the group of qa * qw (the int32
-// accumulators, restarted every group),
-//   cf += sa_g * fp32(raw - za_g * colsum_g)     per element
-//   P  += sa_g * fp32(rowsum_g - 128 * za_g)     per token row
-// so that after the last group y = sw * (cf - zw * P) is
-//   sw * sum_g sa_g * sum_{k in g} (qa - za_g)(qw - zw).
-// Both integers are exact: |raw| <= 128 * 225 and |za_g| < 2^12.
+// accumulators, restarted every group; 0 <= raw <= 128 * 225),
+//   cf += sa_g * fp32(raw)                        per element
+//   P  += sa_g * fp32(rowsum_g - 128 * za_g)      per token row
+// and after the last group group_zero_corr adds
+//   sum_g (-sa_g za_g) * colsum_g                 per element
+// so that y = sw * (cf - zw * P) is sw * sum_g sa_g * sum_{k in g} (qa - za_g)(qw - zw).
 template <int TM>
 __device__ __forceinline__ void group_rescale(const v16i (&acc)[TM][2], v16f (&cf)[TM][2], float (&P)[TM],
                                               const GroupC<TM>& c) {
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
-    const int32_t nza = -c.za[tm];
     const float sa = c.sa[tm];
-    P[tm] = fmaf(sa, static_cast<float>(c.rs[tm] + 128 * nza), P[tm]);
+    P[tm] = fmaf(sa, static_cast<float>(c.rs[tm] - 128 * c.za[tm]), P[tm]);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int32_t t = acc[tm][nt][v] + mul24(nza, c.cs[nt][v >> 2][v & 3]);
-        cf[tm][nt][v] = fmaf(sa, static_cast<float>(t), cf[tm][nt][v]);
-      }
+      for (int v = 0; v < 16; ++v) cf[tm][nt][v] = fmaf(sa, static_cast<float>(acc[tm][nt][v]), cf[tm][nt][v]);
   }
 }
 
-// A fragments of k step ks (32 k) of an LDS stage: rows 32*tm + (lane & 31),
-// 16-byte half (lane >> 5).
+// The activation zero points' term of the group-wise W4A4 product,
+// cf[tm][nt] += sum_g w_g[m] * colsum_g[n] with w_g = -(sa_g * za_g), on fp16
+// matrix cores, the groups being the k dimension (16 per
+// v_mfma_f32_32x32x16_f16).  colsum (the first operand, rows n) is an integer
+// of at most 128 * 15, exact in fp16.  The workgroup forms w for its 32 * TM
+// token rows, kCorrG groups at a time, from coalesced row segments of sa and
+// za into LDS; per chunk each token's w (the second operand, columns m) is
+// scaled by the power of two 2^e that puts its largest magnitude in
+// [2^14, 2^15) and split into hi + lo fp16 halves, which carry it to within
+// 2^-21 of that magnitude (e then only decreases over later chunks); the
+// fp32 sums are scaled back by 2^-e exactly.  Lane half h takes groups 16 c + 8 h + [0, 8), as the operand
+// layout assigns k.  It runs before the K loop, between the first operand
+// prefetch and its LDS stores: the first chunk's sa and za are loaded ahead
+// of that prefetch (CorrIn) and the colsum loads behind it, so that their
+// latencies overlap.  Called by every wave (it has barriers); waves past N
+// read the last 64 columns and discard the result.
+constexpr int kCorrG = 32;
+
+template <int TM>
+struct CorrIn {
+  static constexpr int kPer = 32 * TM * kCorrG / kTileThreads;  // entries per thread
+  float sa[kPer];
+  int32_t za[kPer];
+};
+
+// Entry k of thread t: token row i = (t + 256 k) / kCorrG, group c0 + (t % kCorrG);
+// consecutive threads read consecutive groups of one token.
+template <int TM>
+__device__ __forceinline__ void corr_load(const GemmArgs& g, int64_t m0, int64_t c0, CorrIn<TM>& ci) {
+  const int t = threadIdx.x;
+  const int64_t G = g.K / kBK, gg = c0 + t % kCorrG;
+#pragma unroll
+  for (int k = 0; k < CorrIn<TM>::kPer; ++k) {
+    int64_t m = m0 + (t + kTileThreads * k) / kCorrG;
+    m = m < g.M ? m : g.M - 1;
+    const bool ok = gg < G;
+    ci.sa[k] = ok ? g.sa[m * G + gg] : 0.0f;
+    ci.za[k] = ok ? g.za[m * G + gg] : 0;
+  }
+}
+
+template <int TM>
+__device__ __forceinline__ void group_zero_corr(v16f (&cf)[TM][2], const GemmArgs& g, int64_t m0, int64_t wcol0,
+                                                bool live, uint8_t* lds, CorrIn<TM>& ci) {
+  constexpr int kPitch = kCorrG + 1;  // the odd pitch spreads token rows over the banks
+  const int t = threadIdx.x, lane = t & 63, h = lane >> 5, r = lane & 31;
+  const int64_t G = g.K / kBK;
+  float* const wl = reinterpret_cast<float*>(lds);
+  const int32_t* csn = g.colsum + (live ? wcol0 : g.N - 64) + r;
+  // cf (zero on entry) accumulates in units of 2^-e[tm]; e only decreases
+  // from chunk to chunk, so rescaling cf is an exact power-of-two step down.
+  int e[TM];
+  for (int64_t c0 = 0; c0 < G; c0 += kCorrG) {
+    if (c0 > 0) corr_load<TM>(g, m0, c0, ci);
+#pragma unroll
+    for (int k = 0; k < CorrIn<TM>::kPer; ++k)
+      wl[((t + kTileThreads * k) / kCorrG) * kPitch + t % kCorrG] = -(ci.sa[k] * static_cast<float>(ci.za[k]));
+    lds_barrier();
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const float* wr = wl + (32 * tm + r) * kPitch + 8 * h;
+      float mx = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kCorrG / 16; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(wr[16 * c + j]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      int x;
+      frexpf(mx, &x);  // mx in [2^(x-1), 2^x); x = 0 for mx = 0
+      const int ec = 15 - x;
+      if (c0 == 0) {
+        e[tm] = ec;
+      } else if (ec < e[tm]) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) cf[tm][nt][v] = ldexpf(cf[tm][nt][v], ec - e[tm]);
+        e[tm] = ec;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kCorrG / 16; ++c) {
+      v8h ca[2], wh[TM], wo[TM];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t gg = c0 + 16 * c + 8 * h + j;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          ca[nt][j] = static_cast<_Float16>(gg < G ? static_cast<float>(csn[gg * g.N + 32 * nt]) : 0.0f);
+      }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float sc = ldexpf(wl[(32 * tm + r) * kPitch + 16 * c + 8 * h + j], e[tm]);
+          const _Float16 hi = static_cast<_Float16>(sc);
+          wh[tm][j] = hi;
+          wo[tm][j] = static_cast<_Float16>(sc - static_cast<float>(hi));
+        }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          cf[tm][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ca[nt], wh[tm], cf[tm][nt], 0, 0, 0);
+          cf[tm][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ca[nt], wo[tm], cf[tm][nt], 0, 0, 0);
+        }
+    }
+    lds_barrier();  // the chunk's LDS rows are read before they are refilled
+  }
+  if (G > 0) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) cf[tm][nt][v] = ldexpf(cf[tm][nt][v], -e[tm]);
+  }
+}
+
 template <int TM>
 __device__ __forceinline__ void read_frags(const uint8_t* buf, int ks, v4i (&af)[TM]) {
   const int lane = threadIdx.x & 63;
@@ -549,6 +649,8 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
           (__attribute__((address_space(3))) void*)(xlds + (256 * j + 64 * wave) * 16), 16, 0, 0);
     }
   }
+  [[maybe_unused]] CorrIn<TM> ci;
+  if constexpr (kGrp) corr_load<TM>(g, m0, 0, ci);
   load_a<B, A, TM>(p, 0, ra[0]);
   load_a<B, A, TM>(p, clamp_s(1), ra[1]);
 #pragma unroll
@@ -560,7 +662,6 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
   [[maybe_unused]] GroupC<TM> gc;
   [[maybe_unused]] float P[kGrp ? TM : 1];
   [[maybe_unused]] int64_t rowoff[TM];
-  [[maybe_unused]] const int32_t* csp = nullptr;
   if constexpr (kGrp) {
     const int64_t G = g.K / kBK;
 #pragma unroll
@@ -570,7 +671,6 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
       rowoff[tm] = m * G;
       P[tm] = 0.0f;
     }
-    csp = g.colsum + nt32 * 32 + 4 * (lane >> 5);
   }
   if constexpr (COMP == 2) {
     // Wait for the xO chunks only: the K loop's loads issued after them may
@@ -582,6 +682,10 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
     lds_barrier();
     comp_accumulate_lds<TM, 2>(cf, xlds, 2 * g.ldO, g.ldO / 16, g.WOp, g.N, nt32);
     lds_barrier();  // every wave has read the staged xO rows
+  }
+  if constexpr (kGrp) {
+    static_assert(32 * TM * (kCorrG + 1) * 4 <= kMainBytes, "the w chunk exceeds the LDS buffers");
+    group_zero_corr<TM>(cf, g, m0, wcol0, live, lds, ci);
   }
   store_a<B, A, TM>(lds, p.lds_a, ra[0]);
   store_a<B, A, TM>(lds + T::kStage, p.lds_a, ra[1]);
@@ -636,7 +740,7 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
       else
         read_frags<TM>(nxt, 0, af[0]);
       load_b_part<B, A, TM, KS>(p, b_tiles, g.N, sb, rbn, rrn);
-      if constexpr (kGrp && KS == 0) load_group<TM>(g, rowoff, csp, st, gc);
+      if constexpr (kGrp && KS == 0) load_group<TM>(g, rowoff, st, gc);
       if constexpr (KS == 0) load_a_half<B, A, TM, 0>(p, s3, ra[1 - JA]);
       if constexpr (KS == 1) load_a_half<B, A, TM, 1>(p, s3, ra[1 - JA]);
       if constexpr (KS == 2) store_a<B, A, TM>(fut, p.lds_a, ra[JA]);
@@ -658,7 +762,7 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
           acc[tm][nt] = mfma_i8(bf[nt], af[KS & 1][tm], (kGrp && KS == 0) ? v16i{} : acc[tm][nt]);
       constexpr int kVmAKS = (KS == 0) ? T::kAChunks / 2 : (KS == 1) ? T::kAChunks - T::kAChunks / 2 : 0;
       constexpr int nvm = kVmB + kVmAKS + ((B == BOp::W4Group && KS == 0) ? 2 : 0) +
-                          ((kGrp && KS == 0) ? 3 * TM + 8 : 0);
+                          ((kGrp && KS == 0) ? 3 * TM : 0);
       sched_kstep<TM, nvm, (KS == 2) ? kDsW : 0>(std::make_integer_sequence<int, TM>{});
       __builtin_amdgcn_sched_barrier(0);
     };

@@ -115,6 +115,32 @@ def test_gemm_w4a4_group(q, M, K, N):
     assert_close(host(y2), ref["y"], "y end to end")
 
 
+def test_gemm_w4a4_group_many_groups_and_scales(q):
+    # 65 groups (three chunks of the zero-point term, the last with one
+    # group), zero points up to 2000 in magnitude and activation steps that
+    # jump by 10^3 from one 32-group chunk to the next and fall again, from
+    # codes drawn directly, against the oracle's group-wise product.
+    M, K, N = 70, 8320, 128
+    G = K // 128
+    log(f"w4a4 group from codes M={M} K={K} N={N}")
+    rng = np.random.default_rng(2024)
+    qa = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    qw = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    chunk_scale = np.array([1.0, 1e3, 1e-2])[np.arange(G) // 32]
+    sa = (rng.uniform(0.5, 2.0, (M, G)) * chunk_scale[None, :]).astype(np.float32)
+    za = rng.integers(-2000, 2001, (M, G)).astype(np.int32)
+    zw = rng.integers(0, 16, N).astype(np.int32)
+    rowsum = qa.reshape(M, G, 128).astype(np.int32).sum(axis=2).astype(np.int32)
+    colsum = quant.weight_colsum_group(qw)
+    y1 = gemm.w4a4_group(qa, sa, za, qw, np.ones(N), zw)
+    sw = (1000.0 / np.maximum(np.abs(y1).max(axis=0), 1e-30)).astype(np.float32)
+    ref = gemm.w4a4_group(qa, sa, za, qw, sw, zw)
+    packed = (qa[:, 0::2] | (qa[:, 1::2] << 4)).astype(np.uint8)
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, dev(qw))
+    y = q.qlin_gemm_w4a4_group(dev(packed), dev(sa), dev(za), dev(rowsum), w4, dev(sw), dev(zw), dev(colsum), N)
+    assert_close(host(y), ref, "y")
+
+
 def test_gemm_w4a4_group_one_group_matches_per_token(q):
     # K = 128: one group, so the group-wise GEMM must give the per-token
     # GEMM's output for the same codes (both against the oracle).
