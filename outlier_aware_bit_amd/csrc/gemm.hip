@@ -352,15 +352,20 @@ struct CorrIn {
 // consecutive threads read consecutive groups of one token.
 template <int TM>
 __device__ __forceinline__ void corr_load(const GemmArgs& g, int64_t m0, int64_t c0, CorrIn<TM>& ci) {
+  // Loads from clamped indices are unconditional (a guarded load would be a
+  // branch that waits for it); entries past the last group are zeroed after.
   const int t = threadIdx.x;
-  const int64_t G = g.K / kBK, gg = c0 + t % kCorrG;
+  const int64_t G = g.K / kBK, gg = c0 + t % kCorrG, gc = gg < G ? gg : G - 1;
 #pragma unroll
   for (int k = 0; k < CorrIn<TM>::kPer; ++k) {
     int64_t m = m0 + (t + kTileThreads * k) / kCorrG;
     m = m < g.M ? m : g.M - 1;
-    const bool ok = gg < G;
-    ci.sa[k] = ok ? g.sa[m * G + gg] : 0.0f;
-    ci.za[k] = ok ? g.za[m * G + gg] : 0;
+    ci.sa[k] = g.sa[m * G + gc];
+    ci.za[k] = g.za[m * G + gc];
+  }
+  if (gg >= G) {
+#pragma unroll
+    for (int k = 0; k < CorrIn<TM>::kPer; ++k) ci.za[k] = 0;
   }
 }
 
@@ -408,10 +413,12 @@ __device__ __forceinline__ void group_zero_corr(v16f (&cf)[TM][2], const GemmArg
       v8h ca[2], wh[TM], wo[TM];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int64_t gg = c0 + 16 * c + 8 * h + j;
+        const int64_t gg = c0 + 16 * c + 8 * h + j, gc = gg < G ? gg : G - 1;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          ca[nt][j] = static_cast<_Float16>(gg < G ? static_cast<float>(csn[gg * g.N + 32 * nt]) : 0.0f);
+        for (int nt = 0; nt < 2; ++nt) {
+          const int32_t v = csn[gc * g.N + 32 * nt];  // unconditional, from a clamped row
+          ca[nt][j] = static_cast<_Float16>(static_cast<float>(gg < G ? v : 0));
+        }
       }
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
