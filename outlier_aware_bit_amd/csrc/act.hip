@@ -32,12 +32,11 @@ __device__ __forceinline__ void load8_f16(const uint16_t* p, float (&v)[8]) {
   unpack8_f16(*reinterpret_cast<const v4i*>(p), v);
 }
 
-// v *= r for the 8 channels of chunk c; r is fp32, or fp16 (RT = uint16_t,
+// r for the 8 channels of chunk c; r is fp32, or fp16 (RT = uint16_t,
 // widened exactly to fp32).
 template <bool HAS_R, typename RT>
-__device__ __forceinline__ void scale_chunk(const RT* r, int c, float (&v)[8]) {
+__device__ __forceinline__ void load_r8(const RT* r, int c, float (&rr)[8]) {
   if constexpr (HAS_R) {
-    float rr[8];
     if constexpr (std::is_same_v<RT, float>) {
       const float4 r0 = *reinterpret_cast<const float4*>(r + c * 8);
       const float4 r1 = *reinterpret_cast<const float4*>(r + c * 8 + 4);
@@ -46,6 +45,15 @@ __device__ __forceinline__ void scale_chunk(const RT* r, int c, float (&v)[8]) {
     } else {
       load8_f16(r + c * 8, rr);
     }
+  }
+}
+
+// v *= r for the 8 channels of chunk c.
+template <bool HAS_R, typename RT>
+__device__ __forceinline__ void scale_chunk(const RT* r, int c, float (&v)[8]) {
+  if constexpr (HAS_R) {
+    float rr[8];
+    load_r8<HAS_R>(r, c, rr);
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = mul_rn(v[i], rr[i]);
   }
@@ -117,6 +125,16 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     const int c = chunk(i);
     raw[i] = *reinterpret_cast<const v4i*>(xr + (c < nchunks ? c : nchunks - 1) * 8);
   }
+  // The factors r of the same chunks, also clamped and unconditional (a load
+  // under "c < nchunks" is a branch that waits for it).
+  [[maybe_unused]] float rch[HAS_R ? CH : 1][8];
+  if constexpr (HAS_R) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = chunk(i);
+      load_r8<HAS_R>(r, c < nchunks ? c : nchunks - 1, rch[i]);
+    }
+  }
   // Outlier bookkeeping of this lane (slots j = lane + 64 (2 i + half)), in
   // flight with the row.
   constexpr int kSl = kOutlierLdMax / 128;
@@ -153,17 +171,20 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int c = chunk(i);
-    if (c < nchunks) {
-      float v[8];
-      unpack8_f16(raw[i], v);
-      scale_chunk<HAS_R>(r, c, v);
+    // Branch-free: a chunk past the row (a clamped repeat) is scaled too and
+    // left out of the maximum by the select.
+    const bool in = chunk(i) < nchunks;
+    float v[8];
+    unpack8_f16(raw[i], v);
+    if constexpr (HAS_R) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-      if constexpr (HAS_R) {
+      for (int j = 0; j < 8; ++j) v[j] = mul_rn(v[j], rch[i][j]);
+    }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) vr[i][j] = v[j];
-      }
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, in ? fabsf(v[j]) : 0.0f);
+    if constexpr (HAS_R) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vr[i][j] = v[j];
     }
   }
   for (int i = CH; chunk(i) - lane < nchunks; ++i) {
