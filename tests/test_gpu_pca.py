@@ -49,7 +49,9 @@ def test_pca_select(q, S, T, K):
     assert int(host(idx)[0]) == 0
 
 
-@pytest.mark.parametrize("S,K", [(16, 128), (64, 1000), (128, 4096)])
+# S <= 128 keeps the Gram matrix in LDS; 200 (ragged 16-row tiles) and 2048
+# (the largest S) read it from memory; S = 2 is the smallest.
+@pytest.mark.parametrize("S,K", [(2, 64), (16, 128), (64, 1000), (128, 4096), (200, 512), (2048, 256)])
 def test_pca_leading_eigvec(q, S, K):
     log(f"pca eigvec S={S} K={K}")
     x, u = synth.pca_calibration(S=S, T=8, K=K, seed=K + S)
