@@ -170,3 +170,40 @@ def test_w8a8_dequant_and_error_bound():
     bound = (np.abs(xf) @ np.ones_like(wf)) * dw / 2 + (np.ones_like(xf) @ np.abs(wf)) * da / 2 + 256 * da * dw / 4
     assert np.all(np.abs(y - xf @ wf) <= bound * 1.001)
     assert gemm.max_abs_rel(y, y) == 0.0
+
+
+def test_max_abs_rel_worked_examples():
+    # The parity measure itself, against hand-worked values: the denominator
+    # is max|y_ref| (not max|y|), the numerator the largest signed difference.
+    for c in GOLD["max_abs_rel_cases"]["cases"]:
+        y = np.asarray(c["y"], np.float64)
+        y_ref = np.asarray(c["y_ref"], np.float64)
+        got = gemm.max_abs_rel(y, y_ref)
+        if c.get("inf"):
+            assert got == float("inf"), c["derivation"]
+        else:
+            assert Fraction(got).limit_denominator(1000) == Fraction(c["num"], c["den"]), c["derivation"]
+
+
+def test_max_abs_rel_flags_a_planted_error():
+    # One element off by 2e-3 of the reference's largest magnitude must fail
+    # the 1e-3 bar, whatever the other elements hold.
+    rng = np.random.default_rng(3)
+    y_ref = rng.standard_normal((64, 64))
+    y = y_ref.copy()
+    y[17, 5] += 2e-3 * np.max(np.abs(y_ref))
+    assert 1.99e-3 < gemm.max_abs_rel(y, y_ref) < 2.01e-3
+
+
+def test_offq_weight_worked_example():
+    g = GOLD["offq_weight_block4"]
+    w = np.asarray(g["w"], np.float16)
+    signs = np.asarray(g["signs"], np.int64)
+    wt = hadamard.inverse_transform_weight(w, signs, g["block"])
+    assert np.array_equal(wt, np.asarray(g["w_transformed"], np.float64))
+    qw, step, zw, colsum = quant.offq_weight(w, signs, g["block"])
+    assert np.array_equal(qw, np.asarray(g["q"], np.uint8))
+    want_step = [np.float32(n) / np.float32(d) for n, d in zip(g["step_num"], g["step_den"])]
+    assert np.array_equal(step, np.asarray(want_step, np.float32))
+    assert np.array_equal(zw, np.asarray(g["z"], np.int32))
+    assert np.array_equal(colsum, np.asarray(g["colsum"], np.int32))

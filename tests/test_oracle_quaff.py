@@ -145,3 +145,10 @@ def test_quaff_error_bound_and_gain_over_plain_w8a8():
     assert np.all(np.abs(out["y"] - truth) <= bound)
     plain = layer.w8a8_forward(x, d.w)
     assert np.abs(out["y"] - truth).max() < 0.5 * np.abs(plain["y"] - truth).max()
+
+
+def test_weight_row_absmax_worked_example():
+    g = GOLD["weight_row_absmax_rows"]
+    got = quaff.weight_row_absmax(np.asarray(g["w_rows"], np.float16))
+    assert got.dtype == np.float32
+    assert np.array_equal(got, np.asarray(g["absmax"], np.float32))
