@@ -57,7 +57,7 @@ typedef int32_t qlin_status;
 #define QLIN_ERR_UNSUPPORTED 4 /* a group size / bit width / block not provided     */
 #define QLIN_ERR_HIP 5         /* the HIP runtime reported an error at launch       */
 
-#define QLIN_ABI_VERSION 1
+#define QLIN_ABI_VERSION 2
 
 /* Weight layouts accepted by qlin_pack_weight / qlin_packed_bytes. */
 #define QLIN_LAYOUT_W8 1  /* int8 codes for qlin_gemm_w8a8                         */
@@ -332,8 +332,11 @@ qlin_status qlin_gemm_w4a8(const int8_t* qa, const float* sa, const void* w4, co
  *   acc = raw - zw[n]*rowsum[m] - za[m]*colsum[n] + K*za[m]*zw[n]
  *       = sum_k (qa - za[m]) (qw - zw[n])           (int32)
  *   y   = fp16(acc * sa[m] * sw[n])
- * Precondition: every term above fits int32 (true whenever |za|,|zw| < 2^12
- * at K <= 2^14); not checked on the device.
+ * Precondition: the true sum fits int32, |sum_k (qa - za)(qw - zw)| < 2^31;
+ * K * (|za| + 15) * (|zw| + 15) < 2^31 is sufficient.  The expansion is
+ * evaluated in wrapping 32-bit arithmetic, so its intermediate terms may
+ * exceed int32 without harm; a true sum outside int32 wraps silently (not
+ * checked on the device).
  *   qa4 uint8 [M x K/2] (low nibble = even k), sa fp32 [M], za int32 [M],
  *   rowsum int32 [M];  w4 packed QLIN_LAYOUT_W4U;  sw fp32 [N], zw int32 [N],
  *   colsum int32 [N];  y fp16 [M x N] out;  acc int32 [M x N] out or NULL
@@ -348,21 +351,35 @@ qlin_status qlin_gemm_w4a4(const uint8_t* qa4, const float* sa, const int32_t* z
  * (OffQ, methodology, "grouped implementation"): a step sa, zero point za and
  * code sum per token and group of 128 k (from qlin_hadamard_offset_group),
  * per-channel asymmetric int4 weights.  With G = K / 128:
+ *   raw_g = sum_{k in g} qa * qw                                  (int32, exact)
  *   acc_g = sum_{k in g} (qa - za[m,g]) (qw - zw[n])
  *         = raw_g - za[m,g] * colsum_g[g,n] - zw[n] * (rowsum[m,g] - 128 za[m,g])
  *   y     = fp16(sw[n] * sum_g sa[m,g] * acc_g)
- * evaluated as fp32 sums over g of sa * fp32(raw_g - za * colsum_g) and of
- * sa * fp32(rowsum - 128 za), combined per element at the end (the integers
- * are exact).  Precondition: |za| < 2^12 (not checked on the device).
+ * Evaluation in fp32, per element:
+ *   Z = sum_g w_g[m] * colsum_g[g,n],  w_g = -fp32(sa[m,g] * za[m,g]),
+ *   then F = Z and, group by group in g order, F = fma(sa[m,g], fp32(raw_g), F);
+ *   per token P = sum_g fma(sa[m,g], fp32(rowsum[m,g] - 128 za[m,g]), .);
+ *   y = fp16((F - zw[n] * P) * sw[n]).
+ * Z runs on fp16 matrix cores with fp32 accumulation: colsum_g <= 1920 is
+ * exact in fp16; per token and chunk of 32 groups, w is scaled by the power of
+ * two that puts the chunk's largest |w| in [2^14, 2^15) and split into fp16
+ * hi + lo halves, which carry each w to within 2^-21 of that largest |w|
+ * (relative to max|sa * za| of the chunk), before the fp32 sums are scaled
+ * back exactly.  The fp16 output therefore lies within the normwise 1e-3 of
+ * the exact value whenever the terms do not cancel far below
+ * max|sa * za| * colsum; precondition |za| < 2^12 (not checked on the device).
  *   qa4 uint8 [M x K/2] (low nibble = even k);  sa fp32 [M x G];
  *   za int32 [M x G];  rowsum int32 [M x G];  w4 packed QLIN_LAYOUT_W4U;
  *   sw fp32 [N];  zw int32 [N];  colsum_g int32 [G x N] (qlin_weight_colsum_group;
- *   16-byte aligned);  y fp16 [M x N] out.
+ *   16-byte aligned);  y fp16 [M x N] out;
+ *   acc int32 [G x M x N] out or NULL: raw_g[g, m, n] at (g * M + m) * N + n,
+ *   the exact integer sums the fp32 evaluation starts from (for checking;
+ *   writing them makes the call slower).
  */
 qlin_status qlin_gemm_w4a4_group(const uint8_t* qa4, const float* sa, const int32_t* za,
                                  const int32_t* rowsum, const void* w4, const float* sw,
                                  const int32_t* zw, const int32_t* colsum_g, int64_t M, int64_t N,
-                                 int64_t K, uint16_t* y, void* stream);
+                                 int64_t K, uint16_t* y, int32_t* acc, void* stream);
 
 /*
  * qlin_quaff_backward -- input gradient of the Quaff layer under the

@@ -36,7 +36,7 @@ SIGNATURES = {
     "qlin_gemm_w8a8": (i32, [p, p, p, p, i64, i64, i64, p, i32, p, p, p, p]),
     "qlin_gemm_w4a8": (i32, [p, p, p, p, p, i32, i64, i64, i64, p, p, p]),
     "qlin_gemm_w4a4": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p, p]),
-    "qlin_gemm_w4a4_group": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p]),
+    "qlin_gemm_w4a4_group": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p, p]),
     "qlin_outlier_comp": (i32, [p, p, i32, p, i64, i64, p, p]),
     "qlin_pca_select": (i32, [p, i64, i64, i64, p, p, p]),
     "qlin_pca_leading_eigvec": (i32, [p, i64, i64, i32, C.c_double, p, p, p, p, p]),

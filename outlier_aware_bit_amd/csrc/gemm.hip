@@ -323,6 +323,29 @@ __device__ __forceinline__ void group_rescale(const v16i (&acc)[TM][2], v16f (&c
   }
 }
 
+// Group-wise W4A4, parity output: the raw int32 sums of group s for this
+// wave's fragments, raw[s, m, n] at ((s * M) + m) * N + n.  Lane l holds token
+// row m0 + 32 tm + (l & 31) and, in registers 4q..4q+3 of fragment nt, the
+// four adjacent columns wcol0 + 32 nt + 8 q + 4 (l >> 5) + [0, 4).
+template <int TM>
+__device__ __forceinline__ void store_group_sums(const GemmArgs& g, const v16i (&acc)[TM][2], int s, int64_t m0,
+                                                 int64_t wcol0, bool live) {
+  const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+  if (!live) return;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int64_t m = m0 + 32 * tm + r;
+    if (m >= g.M) continue;
+    int32_t* row = g.acc + (static_cast<int64_t>(s) * g.M + m) * g.N + wcol0 + 4 * h;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<v4i*>(row + 32 * nt + 8 * q) =
+            v4i{acc[tm][nt][4 * q], acc[tm][nt][4 * q + 1], acc[tm][nt][4 * q + 2], acc[tm][nt][4 * q + 3]};
+  }
+}
+
 // The activation zero points' term of the group-wise W4A4 product,
 // cf[tm][nt] += sum_g w_g[m] * colsum_g[n] with w_g = -(sa_g * za_g), on fp16
 // matrix cores, the groups being the k dimension (16 per
@@ -535,7 +558,9 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
 // operands are in flight, with the tile's xO rows staged in LDS
 // (ldO <= kXOMaxLd); 3 the STE backward epilogue, where output column k is
 // scaled by r[k] and, for an outlier column k = O[j], receives
-// (s[k] - 1) * cb[m, j] first.
+// (s[k] - 1) * cb[m, j] first; 4 (group-wise W4A4 only) the int32 sums of
+// every 128-k group are also written out, raw_g[g, m, n] = sum over the
+// group of qa * qw, for parity checks.
 constexpr int kXOMaxLd = 384;
 
 // Group-wise W4A4 tiles are bound by the vector ALU (the per-group fold of
@@ -549,6 +574,8 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
   // column steps (and W4A4 zero points / column sums) of its 256 columns.
   constexpr bool kGrp = (A == AOp::U4G);
   constexpr bool kBwd = (COMP == 3);
+  constexpr bool kGrpAcc = kGrp && COMP == 4;
+  static_assert(COMP != 4 || kGrp, "per-group sums exist only in the group-wise product");
   constexpr int kRowC = (B == BOp::W4U && !kGrp) ? 3 : 1, kColC = (B == BOp::W4U || kBwd) ? 3 : 1;
   // COMP == 2 stages the tile's xO rows (BM x ldO fp16, unpadded) in the
   // same space before the activation stages are first written.
@@ -777,6 +804,7 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
     kstep(std::integral_constant<int, 1>{});
     kstep(std::integral_constant<int, 2>{});
     kstep(std::integral_constant<int, 3>{});
+    if constexpr (kGrpAcc) store_group_sums<TM>(g, acc, st, m0, wcol0, live);
     if constexpr (kGrp) group_rescale<TM>(acc, cf, P, gc);
     stage_barrier<TM>();
     __builtin_amdgcn_sched_barrier(0);
@@ -1093,7 +1121,9 @@ template <BOp B, AOp A>
 qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
   if constexpr (A == AOp::U4G) {
     // Group-wise W4A4: 64-row tiles at every M, two workgroups per CU (the
-    // int32 and fp32 accumulators both live in registers).
+    // int32 and fp32 accumulators both live in registers).  With an acc
+    // buffer, the variant that also writes every group's int32 sums.
+    if (g.acc != nullptr) return launch_tile<B, A, 2, 4>(g, st);
     return launch_tile<B, A, 2, 0>(g, st);
   } else {
     // Up to 128 tokens the K-split skinny kernels (one 64-k unit per wave in
@@ -1250,7 +1280,7 @@ extern "C" qlin_status qlin_gemm_w4a4(const uint8_t* qa4, const float* sa, const
 extern "C" qlin_status qlin_gemm_w4a4_group(const uint8_t* qa4, const float* sa, const int32_t* za,
                                             const int32_t* rowsum, const void* w4, const float* sw,
                                             const int32_t* zw, const int32_t* colsum_g, int64_t M, int64_t N,
-                                            int64_t K, uint16_t* y, void* stream) {
+                                            int64_t K, uint16_t* y, int32_t* acc, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_K_N(K, N);
   if (M == 0) return QLIN_OK;
@@ -1263,7 +1293,8 @@ extern "C" qlin_status qlin_gemm_w4a4_group(const uint8_t* qa4, const float* sa,
   QLIN_PTR(zw);
   QLIN_PTR(colsum_g);
   QLIN_PTR(y);
-  GemmArgs g = base_args(M, N, K, y, nullptr);
+  QLIN_OPT_PTR(acc);
+  GemmArgs g = base_args(M, N, K, y, acc);
   g.a = qa4;
   g.sa = sa;
   g.b = static_cast<const uint8_t*>(w4);

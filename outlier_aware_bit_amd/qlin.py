@@ -276,9 +276,11 @@ def qlin_gemm_w4a4(qa4, sa, za, rowsum, w4, sw, zw, colsum, N, want_acc=False, y
     return y, acc
 
 
-def qlin_gemm_w4a4_group(qa4, sa, za, rowsum, w4, sw, zw, colsum_g, N, y=None):
+def qlin_gemm_w4a4_group(qa4, sa, za, rowsum, w4, sw, zw, colsum_g, N, want_acc=False, y=None):
     """W4A4 with a step, zero point and code sum per token and 128-k group
-    (sa, za, rowsum [M, K/128]) and per-channel weights (colsum_g [K/128, N])."""
+    (sa, za, rowsum [M, K/128]) and per-channel weights (colsum_g [K/128, N]).
+    Returns (y, acc); acc is the int32 raw sums of every group [K/128, M, N]
+    when want_acc, else None."""
     lib = _lib.load()
     _req(qa4, "qa4", torch.uint8)
     M, K2 = qa4.shape
@@ -291,10 +293,11 @@ def qlin_gemm_w4a4_group(qa4, sa, za, rowsum, w4, sw, zw, colsum_g, N, y=None):
     _req(w4, "w4", torch.uint8)
     y = y if y is not None else _empty((M, N), torch.float16, qa4)
     _req(y, "y", torch.float16, (M, N))
+    acc = _empty((G, M, N), torch.int32, qa4) if want_acc else None
     _lib.check("qlin_gemm_w4a4_group", lib.qlin_gemm_w4a4_group(
         qa4.data_ptr(), sa.data_ptr(), za.data_ptr(), rowsum.data_ptr(), w4.data_ptr(), sw.data_ptr(), zw.data_ptr(),
-        colsum_g.data_ptr(), M, N, K, y.data_ptr(), _stream()))
-    return y
+        colsum_g.data_ptr(), M, N, K, y.data_ptr(), _ptr(acc), _stream()))
+    return y, acc
 
 
 def qlin_quaff_backward(dy, sw, w8t, s, r, K, O=None, w_o=None, want_acc=False, dx=None, gq=None, gs=None, cb=None):

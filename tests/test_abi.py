@@ -49,7 +49,7 @@ def test_exported_symbols_via_nm_style_lookup():
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    assert lib.qlin_abi_version() == 1
+    assert lib.qlin_abi_version() == 2
     names = [lib.qlin_status_string(i).decode() for i in range(6)]
     assert names == ["QLIN_OK", "QLIN_ERR_INVALID_ARG", "QLIN_ERR_SHAPE", "QLIN_ERR_ALIGN",
                      "QLIN_ERR_UNSUPPORTED", "QLIN_ERR_HIP"]
@@ -167,9 +167,10 @@ def test_group_and_backward_validation():
     _err(lib.qlin_weight_colsum_group(A, 256, 128, 64, A, None), _lib.QLIN_ERR_UNSUPPORTED)
     _err(lib.qlin_weight_colsum_group(A, 200, 128, 128, A, None), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_weight_colsum_group(A, 256, 128, 128, MIS, None), _lib.QLIN_ERR_ALIGN)
-    _err(lib.qlin_gemm_w4a4_group(A, A, A, A, B, A, A, None, 16, 128, 256, A, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_gemm_w4a4_group(A, A, A, A, B, A, A, A, 16, 100, 256, A, None), _lib.QLIN_ERR_SHAPE)
-    _err(lib.qlin_gemm_w4a4_group(A, A, A, A, B, A, A, A, 0, 128, 256, A, None), _lib.QLIN_OK)
+    _err(lib.qlin_gemm_w4a4_group(A, A, A, A, B, A, A, None, 16, 128, 256, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w4a4_group(A, A, A, A, B, A, A, A, 16, 100, 256, A, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_gemm_w4a4_group(A, A, A, A, B, A, A, A, 16, 128, 256, A, A + 4, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_gemm_w4a4_group(A, A, A, A, B, A, A, A, 0, 128, 256, A, None, None), _lib.QLIN_OK)
     bw = [A, 8, 256, 128, A, B, A, A, A, 3, A, A, A, A, A, None, None]
     _err(lib.qlin_quaff_backward(A, 8, 192, 128, *bw[4:]), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_quaff_backward(A, 8, 256, 192, *bw[4:]), _lib.QLIN_ERR_SHAPE)

@@ -2,11 +2,11 @@
 group-wise form of the OffQ one and the token-count sweep), in the launch
 configurations bench.py times.
 
-Integer stages (codes, zero points, sums, the momentum state s and r) are
-compared in full, bit for bit.  GEMM accumulators and fp16 outputs are
-compared on sampled rows (the oracle's float64 product of the full matrices
-would take minutes): integer accumulators bit for bit, outputs within the
-normwise relative tolerance 1e-3 over the sample.
+Everything is compared in full, on every row: integer stages (codes, zero
+points, sums, the momentum state s and r, int32 accumulators) bit for bit,
+fp16 outputs within the normwise relative tolerance 1e-3.  The oracle's exact
+integer products run as float64 BLAS (a few seconds per full-size product on
+a 16-core host).
 """
 import numpy as np
 import pytest
@@ -14,6 +14,7 @@ import pytest
 import synth
 from oracle import gemm, layer, quant, quaff
 from tests.gpu_helpers import assert_close, assert_equal, dev, host, log
+from tests.test_gpu_offq_group import check_group_sums
 
 pytestmark = pytest.mark.gpu
 
@@ -24,12 +25,6 @@ def q():
     assert torch.cuda.is_available()
     from outlier_aware_bit_amd import qlin
     return qlin
-
-
-def _sample_rows(M, n, seed):
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(n, M), replace=False)]))
-    return rows.astype(np.int64)
 
 
 def test_tiny_w8a8_full(q):
@@ -64,7 +59,6 @@ def test_quaff_q_proj_ten_steps(q):
     s = torch.ones(K, dtype=torch.float32, device="cuda")
     r = torch.empty_like(s)
     s_ref = np.ones(K, np.float32)
-    rows = _sample_rows(M, 48, 7)
     o = d.outliers.astype(np.int64)
     for t, x in enumerate(d.xs):
         log(f"  step {t}")
@@ -78,10 +72,10 @@ def test_quaff_q_proj_ten_steps(q):
         q_ref, sa_ref = quant.quant_act_sym_int8(x, r_ref)
         assert_equal(host(qa), q_ref, f"codes step {t}")
         assert_equal(host(sa), sa_ref, f"steps step {t}")
-        acc_ref, y_main = gemm.w8a8(q_ref[rows], sa_ref[rows], prep["qw"], prep["sw"].astype(np.float32))
-        y_ref = y_main + quaff.compensation(q_ref[rows][:, o], sa_ref[rows], s_ref[o], prep["w_o"])
-        assert_equal(host(acc)[rows], acc_ref, f"acc step {t}")
-        assert_close(host(y)[rows], y_ref, f"y step {t}")
+        acc_ref, y_main = gemm.w8a8(q_ref, sa_ref, prep["qw"], prep["sw"].astype(np.float32))
+        y_ref = y_main + quaff.compensation(q_ref[:, o], sa_ref, s_ref[o], prep["w_o"])
+        assert_equal(host(acc), acc_ref, f"acc step {t}")
+        assert_close(host(y), y_ref, f"y step {t}")
 
 
 @pytest.mark.parametrize("M", [1, 16, 64])
@@ -118,10 +112,10 @@ def test_qqq_prefill_w4a8_group_full(q):
     assert_equal(host(qa), q_ref, "activation codes")
     assert_equal(host(sa), sa_ref, "activation steps")
     y, acc = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128, want_acc=True)
-    rows = _sample_rows(M, 40, 8)
-    acc_ref, y_ref = gemm.w4a8_group(q_ref[rows], sa_ref[rows], w8, sc.astype(np.float32))
-    assert_equal(host(acc)[rows], acc_ref, "acc")
-    assert_close(host(y)[rows], y_ref, "y")
+    log("  oracle product")
+    acc_ref, y_ref = gemm.w4a8_group(q_ref, sa_ref, w8, sc.astype(np.float32))
+    assert_equal(host(acc), acc_ref, "acc")
+    assert_close(host(y), y_ref, "y")
 
 
 def test_offq_w4a4_full(q):
@@ -149,10 +143,10 @@ def test_offq_w4a4_full(q):
     assert_equal(host(cs), cs_ref, "column sums")
     w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, cw)
     y, acc = q.qlin_gemm_w4a4(qa4, sa, za, rs, w4, sw, zw, cs, N, want_acc=True)
-    rows = _sample_rows(M, 32, 9)
-    acc_ref, y_ref = gemm.w4a4(qa_ref[rows], sa_ref[rows], za_ref[rows], qw_ref, sw_ref, zw_ref)
-    assert_equal(host(acc)[rows], acc_ref, "acc")
-    assert_close(host(y)[rows], y_ref, "y")
+    log("  oracle product")
+    acc_ref, y_ref = gemm.w4a4(qa_ref, sa_ref, za_ref, qw_ref, sw_ref, zw_ref)
+    assert_equal(host(acc), acc_ref, "acc")
+    assert_close(host(y), y_ref, "y")
 
 
 def test_offq_w4a4_group_full(q):
@@ -178,10 +172,20 @@ def test_offq_w4a4_group_full(q):
     assert_equal(host(cw), qw_ref, "weight codes")
     csg = q.qlin_weight_colsum_group(cw)
     assert_equal(host(csg), quant.weight_colsum_group(qw_ref), "column sums per group")
-    y = q.qlin_gemm_w4a4_group(qa4, sa, za, rs, q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, cw), sw, zw, csg, N)
-    rows = _sample_rows(M, 32, 10)
-    y_ref = gemm.w4a4_group(qa_ref[rows], sa_ref[rows], za_ref[rows], qw_ref, sw_ref, zw_ref)
-    assert_close(host(y)[rows], y_ref, "y")
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, cw)
+    y, _ = q.qlin_gemm_w4a4_group(qa4, sa, za, rs, w4, sw, zw, csg, N)
+    log("  oracle product")
+    y_ref = gemm.w4a4_group(qa_ref, sa_ref, za_ref, qw_ref, sw_ref, zw_ref)
+    assert_close(host(y), y_ref, "y")
+    del y_ref
+    # Every group's int32 sums (G x M x N), from the variant that writes them.
+    y2, acc = q.qlin_gemm_w4a4_group(qa4, sa, za, rs, w4, sw, zw, csg, N, want_acc=True)
+    assert_equal(host(y2).view(np.uint16), host(y).view(np.uint16), "y with and without the group sums")
+    log("  group sums")
+    got = host(acc)
+    del acc, y2
+    check_group_sums(got, dict(qa=qa_ref, qw=qw_ref, sa=sa_ref, za=za_ref, sw=sw_ref, zw=zw_ref, rowsum=rs_ref,
+                               colsum_g=quant.weight_colsum_group(qw_ref)))
 
 
 SWEEP_MS = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096]
@@ -190,8 +194,9 @@ SWEEP_MS = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096]
 def test_token_sweep_llama7b(q):
     # The token-count sweep of the three W*A8 GEMMs at K = 4096, N = 11008:
     # every M goes through the library's own dispatch (skinny kernels up to
-    # 64 tokens, 128- or 256-row tiles above), the accumulators are exact on
-    # sampled rows, the outputs within 1e-3.
+    # 128 tokens, 128- or 256-row tiles above).  Output rows do not depend on
+    # M, so the oracle runs once at the largest M and every M is compared on
+    # all of its rows: accumulators exact, outputs within 1e-3.
     K, N = 4096, 11008
     Mx = max(SWEEP_MS)
     lin = synth.qqq_decode(M=Mx, K=K, N=N, seed=2)
@@ -212,25 +217,26 @@ def test_token_sweep_llama7b(q):
     p8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, c8)
     p4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, c4)
     pg = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, cg)
-    for M in SWEEP_MS:
-        log(f"token sweep M={M}")
-        rows = _sample_rows(M, 6, M)
-        a, s_ = qa[:M], sa[:M]
-        for name, (fn, wq, ws) in {
-            "w8a8": (lambda: q.qlin_gemm_w8a8(a, s_, p8, s8, N, want_acc=True), w8_ref, s8_ref),
-            "w4a8 channel": (lambda: q.qlin_gemm_w4a8(a, s_, p4, s4, N, want_acc=True), w4_ref, s4_ref),
-            "w4a8 group": (lambda: q.qlin_gemm_w4a8(a, s_, pg, sc, N, ratio=ratio, group=128, want_acc=True),
-                           w8g_ref, sc_ref),
-        }.items():
-            y, acc = fn()
-            acc_ref, y_ref = gemm.w8a8(q_ref[rows], sa_ref[rows], wq, ws.astype(np.float32))
-            assert_equal(host(acc)[rows], acc_ref, f"{name} acc M={M}")
-            assert_close(host(y)[rows], y_ref, f"{name} y M={M}")
+    cases = {
+        "w8a8": (lambda a, s_: q.qlin_gemm_w8a8(a, s_, p8, s8, N, want_acc=True), w8_ref, s8_ref),
+        "w4a8 channel": (lambda a, s_: q.qlin_gemm_w4a8(a, s_, p4, s4, N, want_acc=True), w4_ref, s4_ref),
+        "w4a8 group": (lambda a, s_: q.qlin_gemm_w4a8(a, s_, pg, sc, N, ratio=ratio, group=128, want_acc=True),
+                       w8g_ref, sc_ref),
+    }
+    for name, (fn, wq, ws) in cases.items():
+        log(f"token sweep {name}: oracle product at M={Mx}")
+        acc_ref, y_ref = gemm.w8a8(q_ref, sa_ref, wq, ws.astype(np.float32))
+        for M in SWEEP_MS:
+            log(f"token sweep {name} M={M}")
+            y, acc = fn(qa[:M], sa[:M])
+            assert_equal(host(acc), acc_ref[:M], f"{name} acc M={M}")
+            assert_close(host(y), y_ref[:M], f"{name} y M={M}")
+        del acc_ref, y_ref
 
 
 def test_quaff_q_proj_backward(q):
     # The STE backward at the q_proj shape with the momentum state of one
-    # forward step: gradient codes and steps in full, acc and dX on sampled rows.
+    # forward step: every row of the gradient codes and steps, acc, cb and dX.
     M, K, N, nO = 2048, 4096, 4096, 205
     log(f"Quaff q_proj backward {M}x{N}x{K} |O|={nO}")
     d = synth.quaff_steps(M=M, K=K, N=N, n_outliers=nO, steps=1, seed=1)
@@ -245,8 +251,8 @@ def test_quaff_q_proj_backward(q):
     gq_ref, gs_ref = quant.quant_act_sym_int8(dy, prep["sw"].astype(np.float32))
     assert_equal(host(gq), gq_ref, "gradient codes")
     assert_equal(host(gs), gs_ref, "gradient steps")
-    rows = _sample_rows(M, 32, 11)
-    ref = quaff.ste_backward(dy[rows], prep["qw"], prep["sw"], s_ref, r_ref, o, prep["w_o"])
-    assert_equal(host(acc)[rows], ref["acc"], "acc")
-    assert_close(host(cb)[rows][:, :nO], ref["cb"], "cb", tol=1e-5)
-    assert_close(host(dx)[rows], ref["dx"], "dx")
+    log("  oracle product")
+    ref = quaff.ste_backward(dy, prep["qw"], prep["sw"], s_ref, r_ref, o, prep["w_o"])
+    assert_equal(host(acc), ref["acc"], "acc")
+    assert_close(host(cb)[:, :nO], ref["cb"], "cb", tol=1e-5)
+    assert_close(host(dx), ref["dx"], "dx")

@@ -90,6 +90,24 @@ def test_weight_colsum_group(q, K, N):
     assert_equal(host(got), quant.weight_colsum_group(codes), "colsum_g")
 
 
+def check_group_sums(got, ref, group=128):
+    """The GEMM's int32 sums of every group, got [G, M, N], bit for bit against
+    the oracle's raw sums of each group, and -- expanded with the documented
+    zero-point terms -- against the oracle's centred sums of each group."""
+    qa, qw = ref["qa"], ref["qw"]
+    G = qa.shape[1] // group
+    assert got.shape == (G, qa.shape[0], qw.shape[1]), got.shape
+    _, want_c = gemm.w4a4_group(qa, ref["sa"], ref["za"], qw, ref["sw"], ref["zw"], group, return_acc=True)
+    za = ref["za"].astype(np.int64)
+    zw = np.asarray(ref["zw"], np.int64)
+    for g in range(G):
+        ks = slice(g * group, (g + 1) * group)
+        assert_equal(got[g], gemm.w4a4_raw(qa[:, ks], qw[ks]).astype(np.int32), f"raw sums of group {g}")
+        centred = (got[g].astype(np.int64) - za[:, g][:, None] * ref["colsum_g"][g].astype(np.int64)[None, :]
+                   - zw[None, :] * (ref["rowsum"][:, g].astype(np.int64) - group * za[:, g])[:, None])
+        assert_equal(centred, want_c[g].astype(np.int64), f"centred sums of group {g}")
+
+
 GROUP_SHAPES = [(1, 128, 64), (7, 384, 192), (33, 512, 64), (65, 256, 320), (130, 1664, 320),
                 (200, 1024, 256), (300, 768, 128), (1000, 512, 1024)]
 
@@ -105,13 +123,17 @@ def test_gemm_w4a4_group(q, M, K, N):
     ref = layer.offq_group_forward(x, lin.w, signs)
     w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, dev(ref["qw"]))
     packed = (ref["qa"][:, 0::2] | (ref["qa"][:, 1::2] << 4)).astype(np.uint8)
-    y = q.qlin_gemm_w4a4_group(dev(packed), dev(ref["sa"]), dev(ref["za"]), dev(ref["rowsum"]), w4, dev(ref["sw"]),
-                               dev(ref["zw"]), dev(ref["colsum_g"]), N)
+    y, acc = q.qlin_gemm_w4a4_group(dev(packed), dev(ref["sa"]), dev(ref["za"]), dev(ref["rowsum"]), w4,
+                                    dev(ref["sw"]), dev(ref["zw"]), dev(ref["colsum_g"]), N, want_acc=True)
     assert_close(host(y), ref["y"], "y from oracle codes")
+    check_group_sums(host(acc), ref)
+    y0, _ = q.qlin_gemm_w4a4_group(dev(packed), dev(ref["sa"]), dev(ref["za"]), dev(ref["rowsum"]), w4,
+                                   dev(ref["sw"]), dev(ref["zw"]), dev(ref["colsum_g"]), N)
+    assert_equal(host(y0).view(np.uint16), host(y).view(np.uint16), "y with and without the group sums")
     qa4, sa, za, rs, _ = q.qlin_hadamard_offset_group(dev(x), dev(signs))
     cw, sw, zw, _ = q.qlin_quant_weight_offq(dev(lin.w), dev(signs))
     csg = q.qlin_weight_colsum_group(cw)
-    y2 = q.qlin_gemm_w4a4_group(qa4, sa, za, rs, q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, cw), sw, zw, csg, N)
+    y2, _ = q.qlin_gemm_w4a4_group(qa4, sa, za, rs, q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, cw), sw, zw, csg, N)
     assert_close(host(y2), ref["y"], "y end to end")
 
 
@@ -137,8 +159,13 @@ def test_gemm_w4a4_group_many_groups_and_scales(q):
     ref = gemm.w4a4_group(qa, sa, za, qw, sw, zw)
     packed = (qa[:, 0::2] | (qa[:, 1::2] << 4)).astype(np.uint8)
     w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, dev(qw))
-    y = q.qlin_gemm_w4a4_group(dev(packed), dev(sa), dev(za), dev(rowsum), w4, dev(sw), dev(zw), dev(colsum), N)
+    y, acc = q.qlin_gemm_w4a4_group(dev(packed), dev(sa), dev(za), dev(rowsum), w4, dev(sw), dev(zw), dev(colsum), N,
+                                    want_acc=True)
     assert_close(host(y), ref, "y")
+    got = host(acc)
+    for g in range(G):
+        ks = slice(g * 128, (g + 1) * 128)
+        assert_equal(got[g], gemm.w4a4_raw(qa[:, ks], qw[ks]).astype(np.int32), f"raw sums of group {g}")
 
 
 def test_gemm_w4a4_group_one_group_matches_per_token(q):
@@ -151,8 +178,8 @@ def test_gemm_w4a4_group_one_group_matches_per_token(q):
     qa4, sa, za, rs, _ = q.qlin_hadamard_offset(dev(lin.x), dev(signs))
     cw, sw, zw, cs = q.qlin_quant_weight_offq(dev(lin.w), dev(signs))
     w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, cw)
-    y = q.qlin_gemm_w4a4_group(qa4, sa.reshape(M, 1).contiguous(), za.reshape(M, 1).contiguous(),
-                               rs.reshape(M, 1).contiguous(), w4, sw, zw, cs.reshape(1, N).contiguous(), N)
+    y, _ = q.qlin_gemm_w4a4_group(qa4, sa.reshape(M, 1).contiguous(), za.reshape(M, 1).contiguous(),
+                                  rs.reshape(M, 1).contiguous(), w4, sw, zw, cs.reshape(1, N).contiguous(), N)
     assert_close(host(y), ref["y"], "y")
 
 
@@ -164,9 +191,11 @@ def test_gemm_w4a4_group_errors(q):
     buf = torch.zeros(1024, dtype=torch.int32, device="cuda")
     st = _lib.load().qlin_gemm_w4a4_group(buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
                                           buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr() + 4,
-                                          1, 64, 128, buf.data_ptr(), None)
+                                          1, 64, 128, buf.data_ptr(), None, None)
     assert st == _lib.QLIN_ERR_ALIGN
     st = lib.qlin_gemm_w4a4_group(buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(),
-                                  buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), 1, 64, 100, buf.data_ptr(), None)
+                                  buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), 1, 64, 100, buf.data_ptr(), None,
+                                  None)
     assert st == _lib.QLIN_ERR_SHAPE
-    assert lib.qlin_gemm_w4a4_group(None, None, None, None, None, None, None, None, 0, 64, 128, None, None) == 0
+    assert lib.qlin_gemm_w4a4_group(None, None, None, None, None, None, None, None, 0, 64, 128, None, None,
+                                    None) == 0

@@ -216,6 +216,37 @@ def test_gemm_w4a8_group_requant_edge_ratios(q):
     assert_equal(host(acc), want_w8.astype(np.int32), "requantized weights")
 
 
+@pytest.mark.parametrize("sign", [1, -1])
+@pytest.mark.parametrize("M", [128, 256])
+def test_gemm_w4a8_group_requant_exhaustive(q, sign, M):
+    # QQQ's fused dequant-quant on the device, exhaustively: one column per
+    # finite fp16 ratio of the given sign (31,744 of each, bit patterns
+    # 0x0000..0x7bff or 0x8000..0xfbff, N = 496 * 64), every int4 code -8..7
+    # down K = 128, one-hot int8 activations, unit scales, so that
+    # acc[m, n] = w8[m mod 128, n] = clamp(rint(fp16(q4 * r)), -127, 127).
+    # M = 128 runs the skinny kernel, M = 256 the 128-row tiles.
+    import torch
+    K = 128
+    bits = np.arange(0x7C00, dtype=np.uint32)
+    if sign < 0:
+        bits |= 0x8000
+    rg = bits.astype(np.uint16).view(np.float16)[None, :]
+    N = rg.shape[1]
+    assert N % 64 == 0
+    log(f"requant exhaustive sign={sign} M={M} N={N}")
+    codes = np.tile(np.arange(-8, 8, dtype=np.int8), K // 16)[:, None].repeat(N, 1)
+    want_w8 = quant.requant_group(codes, rg, 128).astype(np.int32)
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, dev(codes))
+    qa = np.tile(np.eye(K, dtype=np.int8), (M // K, 1))
+    y, acc = q.qlin_gemm_w4a8(dev(qa), dev(np.ones(M, np.float32)), w4, dev(np.ones(N, np.float16)), N,
+                              ratio=dev(rg), group=128, want_acc=True)
+    torch.cuda.synchronize()
+    got = host(acc)
+    for r0 in range(0, M, K):
+        assert_equal(got[r0:r0 + K], want_w8, f"requantized weights, rows {r0}..{r0 + K - 1}")
+    assert_equal(host(y).astype(np.float64), np.tile(want_w8, (M // K, 1)).astype(np.float64), "y = w8")
+
+
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
 def test_gemm_w4a4(q, M, K, N):
     log(f"w4a4 M={M} K={K} N={N}")
