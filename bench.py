@@ -50,6 +50,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_comp_q_proj_traffic.md"
 # Sources that make up the fused W8A8 GEMM kernel.
 GEMM_SOURCES = ["gemm.hip", "comp.hpp", "layout.hpp", "common.hpp"]
 COPY_CALIB_BYTES = 256 << 20
+GEMM_KERNEL = "gemm_tile<W8,I8,comp>"
 
 
 def gemm_sources_sha256():
@@ -155,6 +156,8 @@ class QuaffLayer:
         self.wmax = q.qlin_weight_row_absmax(WO)
         self.s = torch.ones(K, dtype=torch.float32, device="cuda")
         self.r = torch.empty_like(self.s)
+        self.work = torch.empty((max(1, q.qlin_momentum_work_bytes(M, self.nO) // 4),), dtype=torch.float32,
+                                device="cuda")
         self.qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
         self.sa = torch.empty((M,), dtype=torch.float32, device="cuda")
         self.xO = torch.empty((M, q.qlin_outlier_ld(self.nO)), dtype=torch.float16, device="cuda")
@@ -223,10 +226,23 @@ class QuaffLayer:
         return M * K + K * N + 4 * M + 2 * N + 2 * M * ldO + 2 * ldO * N + 2 * M * N
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(layer, budget_s=12.0, rows=128):
     """The oracle as it stands, on the host: the momentum update over the full
     batch, then quantization, the exact int8 GEMM (float64 BLAS) and the
-    compensation term on a sample of `rows` tokens; repeated until `budget_s`."""
+    compensation term on a sample of `rows` tokens; repeated until `budget_s`.
+    Each stage is also timed on its own (median of 3)."""
     from oracle import layer as ol
     from threadpoolctl import threadpool_info
     d = layer.data
@@ -234,14 +250,34 @@ def cpu_baseline(layer, budget_s=12.0, rows=128):
     s = np.ones(layer.K, np.float32)
     x_full = d.xs[0]
     from oracle import quaff, quant, gemm
+    sw32 = prep["sw"].astype(np.float32)
+    o = d.outliers
+
+    def med3(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    x = x_full[:rows]
+    s1, r1 = quaff.momentum_update(x_full, o, prep["wmax"], layer.gamma, s)
+    qa1, sa1 = quant.quant_act_sym_int8(x, r1)
+    stages = {
+        "momentum_ms": med3(lambda: quaff.momentum_update(x_full, o, prep["wmax"], layer.gamma, s)),
+        "quant_ms": med3(lambda: quant.quant_act_sym_int8(x, r1)),
+        "gemm_ms": med3(lambda: gemm.w8a8(qa1, sa1, prep["qw"], sw32)),
+        "compensation_ms": med3(lambda: quaff.compensation(qa1[:, o], sa1, s1[o], prep["w_o"])),
+    }
+    stages = {k: round(v * 1e3, 3) for k, v in stages.items()}
     t0 = time.perf_counter()
     n = 0
     while True:
-        s, r = quaff.momentum_update(x_full, d.outliers, prep["wmax"], layer.gamma, s)
-        x = x_full[:rows]
+        s, r = quaff.momentum_update(x_full, o, prep["wmax"], layer.gamma, s)
         qa, sa = quant.quant_act_sym_int8(x, r)
-        acc, y = gemm.w8a8(qa, sa, prep["qw"], prep["sw"].astype(np.float32))
-        y = y + quaff.compensation(qa[:, d.outliers], sa, s[d.outliers], prep["w_o"])
+        acc, y = gemm.w8a8(qa, sa, prep["qw"], sw32)
+        y = y + quaff.compensation(qa[:, o], sa, s[o], prep["w_o"])
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -252,6 +288,8 @@ def cpu_baseline(layer, budget_s=12.0, rows=128):
         "value": ops / el / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
         "sample": f"{n} oracle layer steps on {rows} of {layer.M} tokens (momentum over all {layer.M}); "
                   f"{el:.1f} s; ops counted for the sampled rows only",
+        "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+        "stages": dict(stages, sample_rows=rows, momentum_rows=layer.M),
     }
 
 
@@ -492,8 +530,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--graphs", action="store_true",
                     help="launch the step as HIP graphs (slower than eager launches on ROCm 7)")
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="record the GEMM's timing events on every n-th timed step (event records cost host time)")
+    ap.add_argument("--event-every", type=int, default=1,
+                    help="record the GEMM's timing events on every n-th timed step (default: every step)")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -527,7 +565,8 @@ def main():
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_step = el * 1e3 / a.steps
-    gemm_ms = statistics.mean(e0.elapsed_time(e1) for e0, e1 in evs)
+    gemm_samples = [e0.elapsed_time(e1) for e0, e1 in evs]
+    gemm_ms = statistics.mean(gemm_samples)
     ops_step = layer.int8_ops() + layer.fp16_flops()
     eq_ops = layer.int8_ops() + 2 * layer.fp16_flops()
     achieved = eq_ops / (gemm_ms * 1e-3) / 1e12
@@ -551,15 +590,21 @@ def main():
                    "N": layer.N, "n_outliers": layer.nO, "gamma": layer.gamma, "activation_batches": 10,
                    "step": "momentum_update + quant_act + gemm_w8a8(fused compensation)",
                    "launch": "hip_graphs" if a.graphs else "eager"},
-        "roofline": {"bound": "mfma", "kernel": "gemm_tile<W8,I8,comp>", "achieved": round(achieved, 2),
-                     "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": GEMM_KERNEL, "achieved": round(achieved, 2),
+                     "peak": PEAK_INT8_TOPS, "unit": "TOPS", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                      "traffic": (tr["read"] + tr["write"]) if tr else None,
                      "traffic_read_write": [tr["read"], tr["write"]] if tr else None,
                      "algorithmic_bytes": layer.gemm_bytes(), "launch_ms": round(gemm_ms, 5),
+                     "launch_ms_median": round(statistics.median(gemm_samples), 5),
+                     "event_samples": len(gemm_samples),
+                     "timing": "HIP events around the GEMM launch on its stream, every timed step",
                      "work": "int8 MACs x2 plus fp16 compensation flops x2 (fp16 peak is half the int8 peak)"},
     }
     if not a.no_rows:
         rec["rows"] = rows_measurements(q, layer)
+        # The same kernel replayed back to back from a HIP graph (no event
+        # packets beside each launch), for comparison with the live figure.
+        rec["roofline"]["launch_ms_graph"] = rec["rows"]["A4A5_gemm_w8a8_fused_comp"]["ms"]
         rec["token_sweep"] = token_sweep(q)
     if not a.no_cpu:
         log("timing the CPU oracle")

@@ -155,10 +155,21 @@ qlin_status qlin_hadamard_offset_group(const uint16_t* x, int64_t M, int64_t K, 
  *   wmax_O  fp32 [nO]: max_n |W[O[j], n]| (qlin_weight_row_absmax)
  *   gamma   momentum in [0, 1]
  *   s       fp32 [K] in/out;  r fp32 [K] out
+ *   work    device workspace of qlin_momentum_work_bytes(M, nO) bytes, or
+ *           NULL.  With a workspace and M >= 4096 the column maxima are taken
+ *           by up to 16 row blocks per 64-channel strip in one launch and
+ *           folded per outlier channel in a second (every CU reads part of
+ *           x); otherwise one launch with one workgroup per strip.  Same
+ *           result either way.  The workspace holds partial maxima until the
+ *           call's kernels end; calls that overlap must not share it.
  */
 qlin_status qlin_momentum_update(const uint16_t* x, int64_t M, int64_t K, const int32_t* O,
                                  int32_t nO, const float* wmax_O, float gamma, float* s, float* r,
-                                 void* stream);
+                                 float* work, void* stream);
+
+/* Bytes of the qlin_momentum_update workspace for M tokens and nO outliers
+ * (0 for negative arguments). Host only. */
+size_t qlin_momentum_work_bytes(int64_t M, int32_t nO);
 
 /* ------------------------------------------------------------------------
  * Weight preparation (offline; W is frozen)

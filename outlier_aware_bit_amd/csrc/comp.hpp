@@ -141,4 +141,39 @@ __device__ __forceinline__ void comp_accumulate_lds(v16f (&f)[TM][NT], const uin
     __builtin_amdgcn_sched_barrier(0);
   }
 }
+// As comp_accumulate_lds, with the W_O fragments staged in LDS too: step js,
+// column tile nt at wlds + (NT js + nt) * 1 KB + 16 lane (one lane tile each).
+// The fragments of step js + 1 are read before the products of step js.
+template <int TM, int NT>
+__device__ __forceinline__ void comp_accumulate_lds2(v16f (&f)[TM][NT], const uint8_t* xlds, int pitch, int nj,
+                                                     const uint8_t* wlds) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t* arow = xlds + (lane & 31) * pitch + 16 * (lane >> 5);
+  const uint8_t* bcol = wlds + lane * 16;
+  auto read = [&](int js, v8h (&ap)[TM], v8h (&bp)[NT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) ap[tm] = *reinterpret_cast<const v8h*>(arow + tm * 32 * pitch + 32 * js);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bp[nt] = *reinterpret_cast<const v8h*>(bcol + (NT * js + nt) * 1024);
+  };
+  auto mma = [&](const v8h (&ap)[TM], const v8h (&bp)[NT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        f[tm][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bp[nt], ap[tm], f[tm][nt], 0, 0, 0);
+  };
+  if (nj <= 0) return;
+  v8h a0[TM], b0[NT], a1[TM], b1[NT];
+  read(0, a0, b0);
+  int js = 0;
+  for (; js + 2 <= nj; js += 2) {
+    read(js + 1, a1, b1);
+    mma(a0, b0);
+    if (js + 2 < nj) read(js + 2, a0, b0);
+    mma(a1, b1);
+  }
+  if (js < nj) mma(a0, b0);
+}
+
 }  // namespace qlin

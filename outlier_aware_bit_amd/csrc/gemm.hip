@@ -560,8 +560,11 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
 // scaled by r[k] and, for an outlier column k = O[j], receives
 // (s[k] - 1) * cb[m, j] first; 4 (group-wise W4A4 only) the int32 sums of
 // every 128-k group are also written out, raw_g[g, m, n] = sum over the
-// group of qa * qw, for parity checks.
+// group of qa * qw, for parity checks; 5 as 2, with the tile's W_O fragments
+// also staged in LDS at the start (ldO <= kXOLdsLd): every operand of the
+// compensation arrives in one round trip, under the K loop's first loads.
 constexpr int kXOMaxLd = 384;
+constexpr int kXOLdsLd = 208;
 
 // Group-wise W4A4 tiles are bound by the vector ALU (the per-group fold of
 // every accumulator): two workgroups per CU, so that one wave's fold runs
@@ -579,8 +582,13 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
   constexpr int kRowC = (B == BOp::W4U && !kGrp) ? 3 : 1, kColC = (B == BOp::W4U || kBwd) ? 3 : 1;
   // COMP == 2 stages the tile's xO rows (BM x ldO fp16, unpadded) in the
   // same space before the activation stages are first written.
-  constexpr int kXO = (COMP == 2) ? T::BM * 2 * kXOMaxLd : 0;
+  constexpr bool kComp1st = (COMP == 2 || COMP == 5);
+  // COMP == 5: xO rows, then each wave's W_O lane tiles (2 column tiles per
+  // 16 rows of W_O, ldO / 16 of them).
+  constexpr int kXORows = (COMP == 5) ? T::BM * 2 * kXOLdsLd : T::BM * 2 * kXOMaxLd;
+  constexpr int kXO = (COMP == 2) ? kXORows : (COMP == 5) ? kXORows + 4 * (kXOLdsLd / 16) * 2 * 1024 : 0;
   static_assert(!kBwd || (B == BOp::W8 && A == AOp::I8), "the backward epilogue is int8 x int8");
+  static_assert(!kComp1st || (B == BOp::W8 && A == AOp::I8), "the compensation belongs to the W8A8 product");
   constexpr int kMainBytes = (kXO > 3 * T::kStage) ? kXO : 3 * T::kStage;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kMainBytes + 4 * (kRowC * T::BM + kColC * kBN)];
   [[maybe_unused]] uint8_t* const xlds = lds;
@@ -661,7 +669,7 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
   }
   auto clamp_s = [S](int t) { return t < S ? t : S - 1; };
   // fp32 accumulators: the compensation term (COMP), or the scaled group sums.
-  constexpr bool kCF = COMP == 1 || COMP == 2 || kGrp;
+  constexpr bool kCF = COMP == 1 || kComp1st || kGrp;
   [[maybe_unused]] v16f cf[kCF ? TM : 1][2];
   if constexpr (kCF) {
 #pragma unroll
@@ -669,7 +677,7 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
 #pragma unroll
       for (int b = 0; b < 2; ++b) cf[a][b] = v16f{};
   }
-  if constexpr (COMP == 2) {
+  if constexpr (kComp1st) {
     // The tile's xO rows go straight from memory into LDS (16 * ldO chunks
     // of 16 bytes in row-major order, 64 consecutive chunks per wave and
     // load), ahead of the K loop's first operands.
@@ -681,6 +689,20 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(g.xO + m * g.ldO + 8 * cc),
           (__attribute__((address_space(3))) void*)(xlds + (256 * j + 64 * wave) * 16), 16, 0, 0);
+    }
+    if constexpr (COMP == 5) {
+      // This wave's W_O lane tiles (js, nt32 + nt), js < ldO / 16, to
+      // consecutive 1 KB slots of its own region.
+      const int nj = g.ldO / 16;
+      const int64_t tiles32 = g.N / 32;
+      uint8_t* const wl = xlds + kXORows + wave * (kXOLdsLd / 16) * 2 * 1024;
+      for (int js = 0; js < nj; ++js)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)(g.WOp + ((static_cast<int64_t>(js) * tiles32 + nt32 + nt)
+                                                                       << 10) + lane * 16),
+              (__attribute__((address_space(3))) void*)(wl + (2 * js + nt) * 1024), 16, 0, 0);
     }
   }
   [[maybe_unused]] CorrIn<TM> ci;
@@ -706,16 +728,19 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
       P[tm] = 0.0f;
     }
   }
-  if constexpr (COMP == 2) {
-    // Wait for the xO chunks only: the K loop's loads issued after them may
-    // stay in flight while the compensation runs.
+  if constexpr (kComp1st) {
+    // Wait for the staged operands only: the K loop's loads issued after
+    // them may stay in flight while the compensation runs.
     constexpr int younger = 2 * T::kAChunks + BD * T::kNB;
     static_assert(younger < 64, "vmcnt immediate");
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(((younger >> 4) << 14) | (15 << 8) | (7 << 4) | (younger & 15));
     lds_barrier();
-    comp_accumulate_lds<TM, 2>(cf, xlds, 2 * g.ldO, g.ldO / 16, g.WOp, g.N, nt32);
-    lds_barrier();  // every wave has read the staged xO rows
+    if constexpr (COMP == 5)
+      comp_accumulate_lds2<TM, 2>(cf, xlds, 2 * g.ldO, g.ldO / 16, xlds + kXORows + wave * (kXOLdsLd / 16) * 2 * 1024);
+    else
+      comp_accumulate_lds<TM, 2>(cf, xlds, 2 * g.ldO, g.ldO / 16, g.WOp, g.N, nt32);
+    lds_barrier();  // every wave has read the staged operands
   }
   if constexpr (kGrp) {
     static_assert(32 * TM * (kCorrG + 1) * 4 <= kMainBytes, "the w chunk exceeds the LDS buffers");
@@ -933,7 +958,7 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
             f = (cf[tm][nt][4 * q + j] - static_cast<float>(zw[j]) * P[tm]) * sw[j];
           else if constexpr (COMP == 1)
             f = cf[tm][nt][4 * q + j];  // acc * sw + compensation
-          else if constexpr (COMP == 2)
+          else if constexpr (kComp1st)
             f = static_cast<float>(val) * sw[j] + cf[tm][nt][4 * q + j];
           else
             f = static_cast<float>(val) * sw[j];
@@ -1141,6 +1166,7 @@ qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
     }
     if (comp) {
       if constexpr (B == BOp::W8 && A == AOp::I8) {
+        if (g.ldO <= kXOLdsLd) return launch_tile<B, A, 4, 5>(g, st);
         if (g.ldO <= kXOMaxLd) return launch_tile<B, A, 4, 2>(g, st);
         return launch_tile<B, A, 4, 1>(g, st);
       }

@@ -122,8 +122,14 @@ def qlin_hadamard_offset_group(x, signs, block=128, want_t=False, q4=None, scale
     return q4, scale, zero, rowsum, t
 
 
-def qlin_momentum_update(x, O, wmax_O, gamma, s, r):
-    """One step of Quaff's momentum scaling; updates s in place and writes r."""
+def qlin_momentum_work_bytes(M, nO) -> int:
+    return int(_lib.load().qlin_momentum_work_bytes(M, nO))
+
+
+def qlin_momentum_update(x, O, wmax_O, gamma, s, r, work=None):
+    """One step of Quaff's momentum scaling; updates s in place and writes r.
+    work: a device workspace (float32) of at least qlin_momentum_work_bytes(M, nO)
+    bytes for the two-launch form, or None for the single-launch form."""
     lib = _lib.load()
     _req(x, "x", torch.float16)
     M, K = x.shape
@@ -132,9 +138,14 @@ def qlin_momentum_update(x, O, wmax_O, gamma, s, r):
     _req(wmax_O, "wmax_O", torch.float32, (nO,))
     _req(s, "s", torch.float32, (K,))
     _req(r, "r", torch.float32, (K,))
+    if work is not None:
+        _req(work, "work", torch.float32)
+        need = qlin_momentum_work_bytes(M, nO)
+        if work.numel() * 4 < need:
+            raise ValueError(f"work holds {work.numel() * 4} bytes, {need} needed")
     _lib.check("qlin_momentum_update", lib.qlin_momentum_update(
         x.data_ptr(), M, K, O.data_ptr() if nO else None, nO, wmax_O.data_ptr() if nO else None,
-        float(gamma), s.data_ptr(), r.data_ptr(), _stream()))
+        float(gamma), s.data_ptr(), r.data_ptr(), _ptr(work), _stream()))
     return s, r
 
 

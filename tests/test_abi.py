@@ -115,11 +115,19 @@ def test_hadamard_validation():
 
 def test_momentum_validation():
     lib = _lib.load()
-    _err(lib.qlin_momentum_update(A, 8, 256, A, 4, A, 1.5, A, B, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_momentum_update(A, 8, 256, A, 400, A, 0.9, A, B, None), _lib.QLIN_ERR_SHAPE)
-    _err(lib.qlin_momentum_update(A, 8, 256, None, 4, A, 0.9, A, B, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_momentum_update(A, 8, 256, A, 4, A, 0.9, None, B, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_momentum_update(A, -2, 256, A, 4, A, 0.9, A, B, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_momentum_update(A, 8, 256, A, 4, A, 1.5, A, B, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_momentum_update(A, 8, 256, A, 400, A, 0.9, A, B, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_momentum_update(A, 8, 256, None, 4, A, 0.9, A, B, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_momentum_update(A, 8, 256, A, 4, A, 0.9, None, B, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_momentum_update(A, -2, 256, A, 4, A, 0.9, A, B, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_momentum_update(A, 8, 256, A, 4, A, 0.9, A, B, A + 4, None), _lib.QLIN_ERR_ALIGN)
+    # Workspace: up to 16 row blocks of 128 tokens, one float per outlier each.
+    assert lib.qlin_momentum_work_bytes(0, 205) == 205 * 4
+    assert lib.qlin_momentum_work_bytes(128, 205) == 205 * 4
+    assert lib.qlin_momentum_work_bytes(129, 205) == 2 * 205 * 4
+    assert lib.qlin_momentum_work_bytes(2048, 205) == 16 * 205 * 4
+    assert lib.qlin_momentum_work_bytes(100000, 7) == 16 * 7 * 4
+    assert lib.qlin_momentum_work_bytes(-1, 7) == 0
 
 
 def test_weight_prep_validation():

@@ -58,13 +58,14 @@ def test_quaff_q_proj_ten_steps(q):
     wmax = q.qlin_weight_row_absmax(WO)
     s = torch.ones(K, dtype=torch.float32, device="cuda")
     r = torch.empty_like(s)
+    work = torch.empty((q.qlin_momentum_work_bytes(M, nO) // 4,), dtype=torch.float32, device="cuda")
     s_ref = np.ones(K, np.float32)
     o = d.outliers.astype(np.int64)
     for t, x in enumerate(d.xs):
         log(f"  step {t}")
         s_ref, r_ref = quaff.momentum_update(x, o, prep["wmax"], 0.9, s_ref)
         xd = dev(x)
-        q.qlin_momentum_update(xd, O, wmax, 0.9, s, r)
+        q.qlin_momentum_update(xd, O, wmax, 0.9, s, r, work=work)
         qa, sa, _, xO = q.qlin_quant_act(xd, r, O, s=s, want_qO=False)
         y, acc = q.qlin_gemm_w8a8(qa, sa, w8, sw, N, xO=xO, nO=nO, WO=WOp, want_acc=True)
         assert_equal(host(s), s_ref, f"s step {t}")

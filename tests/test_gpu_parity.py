@@ -96,11 +96,16 @@ def test_hadamard_offset_constant_tokens(q):
 
 
 # ------------------------------------------------------------ Quaff
-# Up to 8300 tokens: one and several passes of a strip's 2048-row loads.
-@pytest.mark.parametrize("M,nO", [(300, 51), (1, 1), (0, 4), (64, 0), (513, 7), (2048, 51), (8300, 60)])
-def test_momentum_ten_steps(q, M, nO):
+# Up to 8300 tokens: one and several passes of a strip's 2048-row loads
+# (single launch); with a workspace, from 4096 tokens, the two-launch form:
+# 16 row blocks of 256 rows (4096), of ragged ones (5000) and of several
+# passes each (8300).  Below 4096 tokens a workspace is not used.
+@pytest.mark.parametrize("work", [False, True])
+@pytest.mark.parametrize("M,nO", [(300, 51), (1, 1), (0, 4), (64, 0), (513, 7), (2048, 51), (4096, 33),
+                                  (5000, 205), (8300, 60)])
+def test_momentum_ten_steps(q, M, nO, work):
     import torch
-    log(f"momentum M={M} nO={nO}")
+    log(f"momentum M={M} nO={nO} work={work}")
     K = 1024
     d = synth.quaff_steps(M=max(M, 1), K=K, N=64, n_outliers=max(nO, 1), steps=10, seed=3)
     O = d.outliers[:nO]
@@ -111,10 +116,15 @@ def test_momentum_ten_steps(q, M, nO):
     s = torch.ones(K, dtype=torch.float32, device="cuda")
     r = torch.empty(K, dtype=torch.float32, device="cuda")
     Od, wd = dev(O.astype(np.int32)), dev(wmax)
+    wk = None
+    if work:
+        nb = q.qlin_momentum_work_bytes(M, nO)
+        assert nb == min(16, max(1, -(-M // 128))) * nO * 4
+        wk = torch.full((max(nb // 4, 1),), float("nan"), dtype=torch.float32, device="cuda")
     for t in range(10):
         x = d.xs[t][:M]
         s_ref, r_ref = quaff.momentum_update(x, O, wmax, 0.9, s_ref)
-        q.qlin_momentum_update(dev(x), Od, wd, 0.9, s, r)
+        q.qlin_momentum_update(dev(x), Od, wd, 0.9, s, r, work=wk)
         assert_equal(host(s), s_ref, f"s step {t}")
         assert_equal(host(r), r_ref, f"r step {t}")
 
@@ -299,8 +309,12 @@ def test_gemm_tiled_k_depths(q, stages):
     assert_close(host(y), ref["y"], "w4a4 y")
 
 
+# The fused compensation has three forms by the padded outlier count ldO:
+# ldO <= 208, xO rows and W_O tiles both staged in LDS before the K loop;
+# ldO <= 384, xO rows staged, W_O read from memory; above, after the K loop.
 @pytest.mark.parametrize("M,K,N,nO", [(16, 256, 128, 13), (200, 512, 192, 64), (130, 384, 64, 33),
-                                       (300, 256, 320, 16)])
+                                       (300, 256, 320, 16), (257, 1024, 256, 205), (200, 1024, 192, 209),
+                                       (150, 1024, 128, 400)])
 def test_quaff_fused_and_standalone_compensation(q, M, K, N, nO):
     import torch
     log(f"quaff comp M={M} K={K} N={N} nO={nO}")
