@@ -171,6 +171,25 @@ qlin_status qlin_momentum_update(const uint16_t* x, int64_t M, int64_t K, const 
  * (0 for negative arguments). Host only. */
 size_t qlin_momentum_work_bytes(int64_t M, int32_t nO);
 
+/*
+ * qlin_momentum_update_noalloc -- qlin_momentum_update without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, result and rounding as
+ * qlin_momentum_update with a workspace; the partial maxima live in a static
+ * device array of the library, one per GPU, held until the process ends
+ * (16 row blocks x 8192 outlier channels of fp32, 512 KiB).
+ *   nO      at most 8192 (QLIN_ERR_SHAPE otherwise, before any HIP call)
+ * The first call on a device looks up the array's address on that device
+ * (the device of `stream`).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams, or from different
+ * host threads) race and give undefined s and r; calls in one stream are
+ * ordered and do not.  No part of the array needs to start at zero.
+ */
+qlin_status qlin_momentum_update_noalloc(const uint16_t* x, int64_t M, int64_t K, const int32_t* O,
+                                         int32_t nO, const float* wmax_O, float gamma, float* s,
+                                         float* r, void* stream);
+
 /* ------------------------------------------------------------------------
  * Weight preparation (offline; W is frozen)
  * --------------------------------------------------------------------- */

@@ -5,6 +5,8 @@
 //
 // Source: "Quaff: Quantized Parameter-Efficient Fine-Tuning under Outlier
 // Spatial Stability Hypothesis" (paper notes), "key design".
+#include <mutex>
+
 #include "common.hpp"
 #include "comp.hpp"
 #include "internal.hpp"
@@ -421,6 +423,46 @@ __global__ __launch_bounds__(kGradThreads) void outlier_grad_kernel(const uint16
   }
 }
 
+// Partial maxima of the allocation-free momentum update: a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code reaches
+// it only through the address hipGetSymbolAddress gives for each device.
+constexpr int kScratchOutliers = 8192;
+constexpr int64_t kScratchFloats = static_cast<int64_t>(kMaxRowBlocks) * kScratchOutliers;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+float* g_scratch[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// The device address of `scratch` on the device of `st` (looked up once per
+// device, with that device current).
+qlin_status scratch_on(hipStream_t st, float** out) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess) return fail(QLIN_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QLIN_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev, kMaxDevices - 1);
+  std::call_once(g_scratch_once[dev], [dev]() {
+    int cur = -1;
+    hipError_t err = hipGetDevice(&cur);
+    if (err == hipSuccess && cur != dev) err = hipSetDevice(dev);
+    void* p = nullptr;
+    if (err == hipSuccess) err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (err == hipSuccess) err = back;
+    }
+    g_scratch_err[dev] = err;
+    g_scratch[dev] = static_cast<float*>(p);
+  });
+  if (g_scratch_err[dev] != hipSuccess)
+    return fail(QLIN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                hipGetErrorString(g_scratch_err[dev]));
+  *out = g_scratch[dev];
+  return QLIN_OK;
+}
+
 qlin_status launch_momentum(const uint16_t* x, int64_t M, int64_t K, const int32_t* O, int32_t nO,
                             const float* wmax_O, float gamma, float* s, float* r, float* work, hipStream_t st) {
   if (work == nullptr || M < kWorkMinRows) {
@@ -467,6 +509,30 @@ extern "C" qlin_status qlin_momentum_update(const uint16_t* x, int64_t M, int64_
     if (M > 0) QLIN_PTR(x);
   }
   QLIN_REQUIRE(K / 64 <= 0x7fffffffLL, QLIN_ERR_SHAPE, "K too large");
+  return launch_momentum(x, M, K, O, nO, wmax_O, gamma, s, r, work, as_stream(stream));
+}
+
+extern "C" qlin_status qlin_momentum_update_noalloc(const uint16_t* x, int64_t M, int64_t K, const int32_t* O,
+                                                    int32_t nO, const float* wmax_O, float gamma, float* s,
+                                                    float* r, void* stream) {
+  QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
+  QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
+  QLIN_REQUIRE(nO <= kScratchOutliers, QLIN_ERR_SHAPE,
+               "nO=%d: the static scratch holds partial maxima for at most %d outlier channels", nO,
+               kScratchOutliers);
+  QLIN_REQUIRE(gamma >= 0.0f && gamma <= 1.0f, QLIN_ERR_INVALID_ARG, "gamma=%g must be in [0, 1]", (double)gamma);
+  QLIN_PTR(s);
+  QLIN_PTR(r);
+  if (nO > 0) {
+    QLIN_PTR(O);
+    QLIN_PTR(wmax_O);
+    if (M > 0) QLIN_PTR(x);
+  }
+  QLIN_REQUIRE(K / 64 <= 0x7fffffffLL, QLIN_ERR_SHAPE, "K too large");
+  float* work = nullptr;
+  const qlin_status st = scratch_on(as_stream(stream), &work);
+  if (st != QLIN_OK) return st;
   return launch_momentum(x, M, K, O, nO, wmax_O, gamma, s, r, work, as_stream(stream));
 }
 
