@@ -90,6 +90,67 @@ def copy_calibration():
     del src, dst
 
 
+class FenceFreeEvent:
+    """A HIP timing event created with hipEventDisableSystemFence, through the
+    HIP runtime torch has loaded.  Recording a default event releases and
+    acquires at system scope, which writes back and invalidates the caches:
+    about 2 us per record on the GPU timeline, and a cold L2 for the kernel
+    that follows.  These events only timestamp the stream; they are read
+    after a device synchronisation."""
+    _lib = None
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    @classmethod
+    def _hip(cls):
+        if cls._lib is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64.so" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded")
+            lib = ctypes.CDLL(path)
+            v, i = ctypes.c_void_p, ctypes.c_int
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(v), ctypes.c_uint]
+            lib.hipEventCreateWithFlags.restype = i
+            lib.hipEventRecord.argtypes = [v, v]
+            lib.hipEventRecord.restype = i
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), v, v]
+            lib.hipEventElapsedTime.restype = i
+            lib.hipEventDestroy.argtypes = [v]
+            lib.hipEventDestroy.restype = i
+            cls._lib = lib
+        return cls._lib
+
+    def __init__(self):
+        import ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self._hip().hipEventCreateWithFlags(ctypes.byref(self.ev), self.FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: {rc}")
+
+    def record(self):
+        import torch
+        rc = self._hip().hipEventRecord(self.ev, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord: {rc}")
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._hip().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime: {rc}")
+        return ms.value
+
+    def __del__(self):
+        if self._lib is not None and self.ev:
+            self._lib.hipEventDestroy(self.ev)
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -97,6 +158,9 @@ def log(msg):
 def dev(a):
     import torch
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+PROFILE_LAUNCHES = 0  # > 0: rows launch eagerly this many times each, untimed (counter runs)
 
 
 def time_launches(fn, reps, trials=5, warm=3, graph_len=24):
@@ -108,6 +172,11 @@ def time_launches(fn, reps, trials=5, warm=3, graph_len=24):
     of the Python argument checks of each call, which for a kernel of a few
     microseconds would otherwise set the pace."""
     import torch
+    if PROFILE_LAUNCHES:
+        for i in range(PROFILE_LAUNCHES):
+            fn(i)
+        torch.cuda.synchronize()
+        return float("nan")
     for _ in range(warm):
         fn(0)
     torch.cuda.synchronize()
@@ -528,10 +597,15 @@ def main():
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--profile", type=int, default=0, metavar="N",
+                    help="counter runs: after the headline steps, launch every row's kernels N times eagerly "
+                         "(untimed, no graphs, no token sweep)")
     ap.add_argument("--graphs", action="store_true",
                     help="launch the step as HIP graphs (slower than eager launches on ROCm 7)")
     ap.add_argument("--event-every", type=int, default=1,
                     help="record the GEMM's timing events on every n-th timed step (default: every step)")
+    ap.add_argument("--torch-events", action="store_true",
+                    help="time the GEMM with torch's default events (with a system-scope fence on each record)")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -556,8 +630,11 @@ def main():
         run(t)
     torch.cuda.synchronize()
     every = max(1, a.event_every)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range((a.steps + every - 1) // every)]
+    if a.torch_events:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range((a.steps + every - 1) // every)]
+    else:
+        evs = [(FenceFreeEvent(), FenceFreeEvent()) for _ in range((a.steps + every - 1) // every)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for t in range(a.steps):
@@ -597,9 +674,17 @@ def main():
                      "algorithmic_bytes": layer.gemm_bytes(), "launch_ms": round(gemm_ms, 5),
                      "launch_ms_median": round(statistics.median(gemm_samples), 5),
                      "event_samples": len(gemm_samples),
-                     "timing": "HIP events around the GEMM launch on its stream, every timed step",
+                     "timing": ("HIP events (hipEventDisableSystemFence unless --torch-events) around the GEMM "
+                                f"launch on its stream, every {every}. timed step"),
                      "work": "int8 MACs x2 plus fp16 compensation flops x2 (fp16 peak is half the int8 peak)"},
     }
+    if a.profile:
+        global PROFILE_LAUNCHES
+        PROFILE_LAUNCHES = a.profile
+        rows_measurements(q, layer)
+        log(f"profile run: every row launched {a.profile} times")
+        a.no_rows = True
+        a.no_cpu = True
     if not a.no_rows:
         rec["rows"] = rows_measurements(q, layer)
         # The same kernel replayed back to back from a HIP graph (no event
