@@ -27,14 +27,18 @@
  *   - Every pointer must be 16-byte aligned (QLIN_ERR_ALIGN otherwise).
  *   - Shapes: M >= 0 (M == 0 returns QLIN_OK after the shape checks, reads no
  *     pointer and launches nothing, except qlin_momentum_update);
- *     K > 0 and K % 128 == 0; N > 0 and N % 64 == 0 (QLIN_ERR_SHAPE otherwise).
+ *     K > 0 and K % 128 == 0; N > 0 and N % 64 == 0; every dimension below
+ *     2^31 and every operand (M*K, K*N, M*N elements) at most 2^40, so that no
+ *     size or index overflows 64 bits (QLIN_ERR_SHAPE otherwise).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream).  Nothing is synchronised; results are ready when the stream is.
  *   - Arguments are validated before any HIP call; a non-zero status means
  *     nothing was launched and no output was touched, except QLIN_ERR_HIP,
  *     which reports a failed launch.  qlin_last_error() gives a message.
- *   - No entry point allocates device memory or retains state between calls;
- *     calls on different streams touching disjoint outputs may overlap.
+ *   - No entry point allocates device memory or retains state between calls
+ *     (qlin_momentum_update_noalloc aside: it works in a static device array,
+ *     see there); calls on different streams touching disjoint outputs may
+ *     overlap.
  *   - Rounding: every float -> integer decision is round-half-to-even in IEEE
  *     float32 (float16 where stated), one rounding per operation, no fused
  *     multiply-add, correctly rounded division and square root.
@@ -52,7 +56,7 @@ extern "C" {
 typedef int32_t qlin_status;
 #define QLIN_OK 0
 #define QLIN_ERR_INVALID_ARG 1 /* null pointer, negative size, bad enum value      */
-#define QLIN_ERR_SHAPE 2       /* K % 128, N % 64, nO > K, block/group != 128       */
+#define QLIN_ERR_SHAPE 2       /* K % 128, N % 64, nO > K, sizes beyond the limits  */
 #define QLIN_ERR_ALIGN 3       /* a pointer is not 16-byte aligned                  */
 #define QLIN_ERR_UNSUPPORTED 4 /* a group size / bit width / block not provided     */
 #define QLIN_ERR_HIP 5         /* the HIP runtime reported an error at launch       */

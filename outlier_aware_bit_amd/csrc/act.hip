@@ -544,6 +544,7 @@ extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, c
                                       const float* s, int8_t* qO, uint16_t* xO, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_DIMS(M, K);
   QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
   if (M == 0) return QLIN_OK;
   QLIN_PTR(x);
@@ -599,6 +600,7 @@ extern "C" qlin_status qlin_hadamard_offset(const uint16_t* x, int64_t M, int64_
                                             float* t, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_DIMS(M, K);
   QLIN_REQUIRE(block == 128, QLIN_ERR_UNSUPPORTED, "block=%d: only 128 is provided", block);
   if (M == 0) return QLIN_OK;
   QLIN_PTR(x);
@@ -621,6 +623,7 @@ extern "C" qlin_status qlin_hadamard_offset_group(const uint16_t* x, int64_t M, 
                                                   float* t, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_DIMS(M, K);
   QLIN_REQUIRE(block == 128, QLIN_ERR_UNSUPPORTED, "block=%d: only 128 is provided", block);
   if (M == 0) return QLIN_OK;
   QLIN_PTR(x);

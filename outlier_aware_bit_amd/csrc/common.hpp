@@ -40,6 +40,21 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
     QLIN_REQUIRE((N) > 0 && (N) % 64 == 0, QLIN_ERR_SHAPE, "N=%lld must be a positive multiple of 64", (long long)(N));   \
   } while (0)
 
+// Size limits of every entry point: each dimension below 2^31 and each
+// matrix operand at most 2^40 elements (far beyond device memory), so that no
+// size, byte count, grid or index computed on the host or in a kernel
+// overflows 64 bits.
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+inline bool dims_ok(int64_t a, int64_t b) {
+  return a >= 0 && b >= 0 && a < kMaxDim && b < kMaxDim && a * b <= kMaxElems;
+}
+
+#define QLIN_DIMS(a, b)                                                                                  \
+  QLIN_REQUIRE(::qlin::dims_ok((a), (b)), QLIN_ERR_SHAPE,                                                \
+               "%s x %s = %lld x %lld: each dimension must be below 2^31 and their product at most 2^40", \
+               #a, #b, (long long)(a), (long long)(b))
+
 #define QLIN_LAUNCH_CHECK(what)                  \
   do {                                           \
     qlin_status st_ = ::qlin::launch_status(what); \

@@ -1221,6 +1221,9 @@ extern "C" qlin_status qlin_gemm_w8a8(const int8_t* qa, const float* sa, const v
                                       int32_t* acc, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_K_N(K, N);
+  QLIN_DIMS(M, K);
+  QLIN_DIMS(K, N);
+  QLIN_DIMS(M, N);
   QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
   if (M == 0) return QLIN_OK;
   QLIN_PTR(qa);
@@ -1252,6 +1255,9 @@ extern "C" qlin_status qlin_gemm_w4a8(const int8_t* qa, const float* sa, const v
                                       void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_K_N(K, N);
+  QLIN_DIMS(M, K);
+  QLIN_DIMS(K, N);
+  QLIN_DIMS(M, N);
   QLIN_REQUIRE(group == 0 || group == 128, QLIN_ERR_UNSUPPORTED, "group=%d: only 0 and 128 are provided", group);
   if (M == 0) return QLIN_OK;
   QLIN_PTR(qa);
@@ -1280,6 +1286,9 @@ extern "C" qlin_status qlin_gemm_w4a4(const uint8_t* qa4, const float* sa, const
                                       int64_t K, uint16_t* y, int32_t* acc, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_K_N(K, N);
+  QLIN_DIMS(M, K);
+  QLIN_DIMS(K, N);
+  QLIN_DIMS(M, N);
   if (M == 0) return QLIN_OK;
   QLIN_PTR(qa4);
   QLIN_PTR(sa);
@@ -1309,6 +1318,9 @@ extern "C" qlin_status qlin_gemm_w4a4_group(const uint8_t* qa4, const float* sa,
                                             int64_t K, uint16_t* y, int32_t* acc, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_K_N(K, N);
+  QLIN_DIMS(M, K);
+  QLIN_DIMS(K, N);
+  QLIN_DIMS(M, N);
   if (M == 0) return QLIN_OK;
   QLIN_PTR(qa4);
   QLIN_PTR(sa);

@@ -632,6 +632,8 @@ extern "C" qlin_status qlin_pca_select(const uint16_t* x, int64_t S, int64_t T, 
   QLIN_PTR(idx);
   QLIN_PTR(z);
   QLIN_REQUIRE(S <= 0x7fffffffLL && T <= 0x7fffffffLL, QLIN_ERR_SHAPE, "S or T too large");
+  QLIN_DIMS(S, T);
+  QLIN_DIMS(S * T, K);
   // P candidate slots of 8 bytes fit in a row of z (2K >= 16 bytes).
   const int P = static_cast<int>(K / 4 < kSelParts ? K / 4 : kSelParts);
   hipStream_t st = as_stream(stream);
@@ -682,6 +684,7 @@ extern "C" qlin_status qlin_pca_fold_weight(const uint16_t* w, int64_t K, int64_
   QLIN_REQUIRE(K > 0 && N > 0 && N % 8 == 0, QLIN_ERR_SHAPE, "K=%lld, N=%lld: both positive, N a multiple of 8",
                (long long)K, (long long)N);
   QLIN_REQUIRE(K <= 65535, QLIN_ERR_SHAPE, "K=%lld too large", (long long)K);
+  QLIN_DIMS(K, N);
   QLIN_PTR(w);
   QLIN_PTR(v);
   QLIN_PTR(w_out);
@@ -715,6 +718,7 @@ extern "C" qlin_status qlin_pca_rotate(const uint16_t* x, int64_t M, int64_t K, 
   QLIN_PTR(v);
   QLIN_PTR(x_out);
   QLIN_REQUIRE(M / kRotWaves < 0x7fffffffLL, QLIN_ERR_SHAPE, "M too large");
+  QLIN_DIMS(M, K);
   pca_rotate_kernel<<<dim3(static_cast<unsigned>((M + kRotWaves - 1) / kRotWaves)), 64 * kRotWaves, 0,
                       as_stream(stream)>>>(x, M, K, v, x_out);
   QLIN_LAUNCH_CHECK("pca_rotate_kernel");

@@ -498,6 +498,7 @@ extern "C" qlin_status qlin_momentum_update(const uint16_t* x, int64_t M, int64_
                                             float gamma, float* s, float* r, float* work, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_DIMS(M, K);
   QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
   QLIN_REQUIRE(gamma >= 0.0f && gamma <= 1.0f, QLIN_ERR_INVALID_ARG, "gamma=%g must be in [0, 1]", (double)gamma);
   QLIN_PTR(s);
@@ -517,6 +518,7 @@ extern "C" qlin_status qlin_momentum_update_noalloc(const uint16_t* x, int64_t M
                                                     float* r, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_DIMS(M, K);
   QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
   QLIN_REQUIRE(nO <= kScratchOutliers, QLIN_ERR_SHAPE,
                "nO=%d: the static scratch holds partial maxima for at most %d outlier channels", nO,
@@ -540,6 +542,7 @@ extern "C" qlin_status qlin_weight_row_absmax(const uint16_t* w_rows, int64_t R,
                                               float* out, void* stream) {
   QLIN_REQUIRE(R >= 0, QLIN_ERR_INVALID_ARG, "R=%lld is negative", (long long)R);
   QLIN_REQUIRE(N > 0 && N % 64 == 0, QLIN_ERR_SHAPE, "N=%lld must be a positive multiple of 64", (long long)N);
+  QLIN_DIMS(R, N);
   if (R == 0) return QLIN_OK;
   QLIN_PTR(w_rows);
   QLIN_PTR(out);
@@ -554,6 +557,7 @@ extern "C" qlin_status qlin_outlier_comp(const uint16_t* xO, const float* sa, in
                                          void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_REQUIRE(N > 0 && N % 64 == 0, QLIN_ERR_SHAPE, "N=%lld must be a positive multiple of 64", (long long)N);
+  QLIN_DIMS(M, N);
   QLIN_REQUIRE(nO >= 0, QLIN_ERR_INVALID_ARG, "nO=%d is negative", nO);
   if (M == 0 || nO == 0) return QLIN_OK;
   QLIN_PTR(xO);
@@ -575,7 +579,10 @@ extern "C" qlin_status qlin_quaff_backward(const uint16_t* dy, int64_t M, int64_
                                            float* gs, float* cb, uint16_t* dx, int32_t* acc, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_DIMS(M, K);
   QLIN_REQUIRE(N > 0 && N % 128 == 0, QLIN_ERR_SHAPE, "N=%lld must be a positive multiple of 128", (long long)N);
+  QLIN_DIMS(M, N);
+  QLIN_DIMS(K, N);
   QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
   if (M == 0) return QLIN_OK;
   QLIN_PTR(dy);

@@ -248,6 +248,7 @@ using namespace qlin;
 extern "C" qlin_status qlin_quant_weight_sym(const uint16_t* w, int64_t K, int64_t N, int32_t bits,
                                              int8_t* codes, uint16_t* scale, void* stream) {
   QLIN_K_N(K, N);
+  QLIN_DIMS(K, N);
   QLIN_REQUIRE(bits == 8 || bits == 4, QLIN_ERR_UNSUPPORTED, "bits=%d: only 8 and 4 are provided", bits);
   QLIN_PTR(w);
   QLIN_PTR(codes);
@@ -264,6 +265,7 @@ extern "C" qlin_status qlin_quant_weight_group(const uint16_t* w, int64_t K, int
                                                uint16_t* channel_scale, uint16_t* ratio,
                                                void* stream) {
   QLIN_K_N(K, N);
+  QLIN_DIMS(K, N);
   QLIN_REQUIRE(group == 128, QLIN_ERR_UNSUPPORTED, "group=%d: only 128 is provided", group);
   QLIN_PTR(w);
   QLIN_PTR(codes);
@@ -281,6 +283,7 @@ extern "C" qlin_status qlin_quant_weight_offq(const uint16_t* w, int64_t K, int6
                                               float* scale, int32_t* zero, int32_t* colsum,
                                               void* stream) {
   QLIN_K_N(K, N);
+  QLIN_DIMS(K, N);
   QLIN_REQUIRE(block == 128, QLIN_ERR_UNSUPPORTED, "block=%d: only 128 is provided", block);
   QLIN_PTR(w);
   QLIN_PTR(signs);
@@ -297,6 +300,7 @@ extern "C" qlin_status qlin_quant_weight_offq(const uint16_t* w, int64_t K, int6
 extern "C" qlin_status qlin_weight_colsum_group(const uint8_t* codes, int64_t K, int64_t N, int32_t group,
                                                 int32_t* colsum_g, void* stream) {
   QLIN_K_N(K, N);
+  QLIN_DIMS(K, N);
   QLIN_REQUIRE(group == 128, QLIN_ERR_UNSUPPORTED, "group=%d: only 128 is provided", group);
   QLIN_PTR(codes);
   QLIN_PTR(colsum_g);
@@ -312,6 +316,7 @@ extern "C" int32_t qlin_outlier_ld(int32_t nO) {
 }
 
 extern "C" size_t qlin_packed_bytes(int32_t layout, int64_t K, int64_t N) {
+  if (!dims_ok(K, N)) return 0;
   // The transposed layout packs the [N x K] matrix: N is its reduction length.
   if (layout == QLIN_LAYOUT_W8T) return (K <= 0 || K % 64 || N <= 0 || N % 128) ? 0 : static_cast<size_t>(K * N);
   if (N <= 0 || N % 64) return 0;
@@ -333,11 +338,14 @@ extern "C" qlin_status qlin_pack_weight(int32_t layout, const void* codes, int64
                QLIN_ERR_INVALID_ARG, "layout=%d is not a QLIN_LAYOUT_* value", layout);
   if (layout == QLIN_LAYOUT_W8T) {
     QLIN_K_N(N, K);  // the packed matrix is [N x K]
+    QLIN_DIMS(K, N);
   } else if (layout == QLIN_LAYOUT_WO) {
     QLIN_REQUIRE(K > 0, QLIN_ERR_SHAPE, "nO=%lld must be positive", (long long)K);
     QLIN_REQUIRE(N > 0 && N % 64 == 0, QLIN_ERR_SHAPE, "N=%lld must be a positive multiple of 64", (long long)N);
+    QLIN_DIMS(K, N);
   } else {
     QLIN_K_N(K, N);
+    QLIN_DIMS(K, N);
   }
   QLIN_PTR(codes);
   QLIN_PTR(packed);

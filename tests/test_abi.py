@@ -221,3 +221,20 @@ def test_binding_refuses_cpu_tensors():
         qlin.qlin_quant_act(torch.zeros((4, 256), dtype=torch.float16))
     with pytest.raises(TypeError):
         qlin.qlin_quant_act(torch.zeros((4, 256), dtype=torch.float32))
+
+
+def test_size_limits():
+    # Every dimension below 2^31 and every operand at most 2^40 elements:
+    # larger sizes are rejected before any size arithmetic can overflow.
+    lib = _lib.load()
+    big, bigger = 1 << 40, 1 << 62
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8, big, big) == 0
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_WO, bigger, 128) == 0
+    assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8, 1 << 20, 1 << 20) == 1 << 40
+    _err(lib.qlin_gemm_w8a8(A, A, B, A, bigger, 128, 256, None, 0, None, A, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_gemm_w8a8(A, A, B, A, 1 << 31, 128, 256, None, 0, None, A, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 0, big, big, big, A, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_quant_act(A, bigger, 256, None, B, A, None, 0, None, None, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_momentum_update(A, bigger, 256, A, 4, A, 0.9, A, B, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_pack_weight(_lib.QLIN_LAYOUT_W8, A, big, big, B, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_pca_fold_weight(A, 128, bigger, A, B, A, None), _lib.QLIN_ERR_SHAPE)
