@@ -439,11 +439,17 @@ def rows_measurements(q, layer):
     out["A2_quant_act_prefill"] = dict(workload=f"{M4}x{K4}", ms=t, bytes=b, gbs=b / t / 1e6,
                                        frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm")
     y = torch.empty((M4, N4), dtype=torch.float16, device="cuda")
-    t = time_launches(lambda i: q.qlin_gemm_w4a8(qa, sa, w4, cs, N4, ratio=ratio, group=128, y=y), 20)
+    work = torch.empty(q.qlin_gemm_w4a8_work_bytes(M4, N4, K4, 128), dtype=torch.uint8, device="cuda")
+    t = time_launches(lambda i: q.qlin_gemm_w4a8(qa, sa, w4, cs, N4, ratio=ratio, group=128, y=y, work=work), 20)
     ops = 2 * M4 * K4 * N4
     out["A7_gemm_w4a8_group128"] = dict(workload=f"{M4}x{K4}x{N4}", ms=t, ops=ops, tops=ops / t / 1e9,
-                                        frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma")
-    del codes, w4, xq, qa, y
+                                        frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma",
+                                        launches="requantization once per call into a workspace, then the int8 tile")
+    t = time_launches(lambda i: q.qlin_gemm_w4a8(qa, sa, w4, cs, N4, ratio=ratio, group=128, y=y), 20)
+    out["A7_gemm_w4a8_group128_in_loop"] = dict(workload=f"{M4}x{K4}x{N4}", ms=t, ops=ops, tops=ops / t / 1e9,
+                                                frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma",
+                                                launches="one tile kernel requantizing in its K loop (no workspace)")
+    del codes, w4, xq, qa, y, work
 
     # OffQ W4A4 at LLaMA-3-8B up_proj shape.
     M5, K5, N5 = 2048, 4096, 14336
@@ -555,8 +561,9 @@ def token_sweep(q):
     w16s = copies_of(w)
     del c8, c4, cg
     y = torch.empty((max(SWEEP_MS), N), dtype=torch.float16, device="cuda")
+    work = torch.empty(q.qlin_gemm_w4a8_work_bytes(max(SWEEP_MS), N, K, 128), dtype=torch.uint8, device="cuda")
     res = {"workload": f"M x {K} x {N}", "M": SWEEP_MS, "w8a8_us": [], "w4a8_channel_us": [], "w4a8_group_us": [],
-           "fp16_torch_us": []}
+           "w4a8_group_work_us": [], "fp16_torch_us": []}
     for m in SWEEP_MS:
         a, s_, yy = qa[:m], sa[:m], y[:m]
         reps = 240 if m <= 64 else (48 if m <= 1024 else 24)
@@ -566,6 +573,9 @@ def token_sweep(q):
             lambda i: q.qlin_gemm_w4a8(a, s_, w4s[i % len(w4s)], s4, N, y=yy), reps))
         res["w4a8_group_us"].append(1e3 * time_launches(
             lambda i: q.qlin_gemm_w4a8(a, s_, wgs[i % len(wgs)], sc, N, ratio=ratio, group=128, y=yy), reps))
+        res["w4a8_group_work_us"].append(1e3 * time_launches(
+            lambda i: q.qlin_gemm_w4a8(a, s_, wgs[i % len(wgs)], sc, N, ratio=ratio, group=128, y=yy, work=work),
+            reps))
         xm = x16[:m]
         for i in range(3):
             torch.matmul(xm, w16s[i % len(w16s)])
@@ -579,10 +589,12 @@ def token_sweep(q):
         e1.record()
         e1.synchronize()
         res["fp16_torch_us"].append(1e3 * e0.elapsed_time(e1) / n16)
-    for k in ("w8a8_us", "w4a8_channel_us", "w4a8_group_us", "fp16_torch_us"):
+    for k in ("w8a8_us", "w4a8_channel_us", "w4a8_group_us", "w4a8_group_work_us", "fp16_torch_us"):
         res[k] = [round(v, 2) for v in res[k]]
     res["w4a8_channel_speedup_vs_w8a8"] = [round(a / b, 3) for a, b in zip(res["w8a8_us"], res["w4a8_channel_us"])]
     res["w4a8_group_speedup_vs_w8a8"] = [round(a / b, 3) for a, b in zip(res["w8a8_us"], res["w4a8_group_us"])]
+    res["w4a8_group_work_speedup_vs_w8a8"] = [round(a / b, 3)
+                                              for a, b in zip(res["w8a8_us"], res["w4a8_group_work_us"])]
     del w8s, w4s, wgs, w16s
     torch.cuda.synchronize()
     return res

@@ -61,7 +61,7 @@ typedef int32_t qlin_status;
 #define QLIN_ERR_UNSUPPORTED 4 /* a group size / bit width / block not provided     */
 #define QLIN_ERR_HIP 5         /* the HIP runtime reported an error at launch       */
 
-#define QLIN_ABI_VERSION 2
+#define QLIN_ABI_VERSION 3
 
 /* Weight layouts accepted by qlin_pack_weight / qlin_packed_bytes. */
 #define QLIN_LAYOUT_W8 1  /* int8 codes for qlin_gemm_w8a8                         */
@@ -348,15 +348,28 @@ qlin_status qlin_gemm_w8a8(const int8_t* qa, const float* sa, const void* w8, co
  * byte (a left shift by 4, i.e. 16 * q4 as int8), multiplied in int8, and the
  * sum is divided by 16 exactly: acc = sum_k qa * q4;  y = fp16(acc * sa * sw).
  * group == 128, per group: w8 = clamp(rint(fp16(q4 * ratio[k/128, n])), -127, 127)
- * (one fp16 rounding of the exact product, then round half to even) inside
- * the K loop; acc = sum_k qa * w8;  y = fp16(acc * sa * sw) with sw = s_c.
+ * (one fp16 rounding of the exact product, then round half to even);
+ * acc = sum_k qa * w8;  y = fp16(acc * sa * sw) with sw = s_c.  The
+ * requantization runs inside the K loop of every tile, or, given a
+ * workspace and more than 128 tokens, once per call into `work` (the int8
+ * weights in QLIN_LAYOUT_W8 order), after which the int8 tile reads them from
+ * there: the same acc and y bit for bit, with the vector work done once
+ * instead of once per 128- or 256-row tile.
  *   qa int8 [M x K];  sa fp32 [M];  w4 packed QLIN_LAYOUT_W4S;  sw fp16 [N]
  *   ratio fp16 [K/128 x N] (group == 128) or NULL (group == 0)
  *   y fp16 [M x N] out;  acc int32 [M x N] out or NULL
+ *   work  device scratch of qlin_gemm_w4a8_work_bytes(M, N, K, group) bytes,
+ *         16-byte aligned, overlapping no other argument, or NULL; its
+ *         contents on entry do not matter and are left undefined.  Ignored
+ *         when that size is 0 (per channel, or M <= 128).  Calls that share
+ *         a workspace must be ordered (one stream).
  */
 qlin_status qlin_gemm_w4a8(const int8_t* qa, const float* sa, const void* w4, const uint16_t* sw,
                            const uint16_t* ratio, int32_t group, int64_t M, int64_t N, int64_t K,
-                           uint16_t* y, int32_t* acc, void* stream);
+                           uint16_t* y, int32_t* acc, void* work, void* stream);
+/* Workspace bytes qlin_gemm_w4a8 uses for these arguments: K * N for
+ * group == 128 with M > 128 and valid shapes, else 0. Host only. */
+size_t qlin_gemm_w4a8_work_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
 
 /*
  * qlin_gemm_w4a4 -- asymmetric int4 x int4 on int8 matrix cores with the

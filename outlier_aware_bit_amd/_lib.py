@@ -36,7 +36,8 @@ SIGNATURES = {
     "qlin_packed_bytes": (C.c_size_t, [i32, i64, i64]),
     "qlin_pack_weight": (i32, [i32, p, i64, i64, p, p]),
     "qlin_gemm_w8a8": (i32, [p, p, p, p, i64, i64, i64, p, i32, p, p, p, p]),
-    "qlin_gemm_w4a8": (i32, [p, p, p, p, p, i32, i64, i64, i64, p, p, p]),
+    "qlin_gemm_w4a8": (i32, [p, p, p, p, p, i32, i64, i64, i64, p, p, p, p]),
+    "qlin_gemm_w4a8_work_bytes": (C.c_size_t, [i64, i64, i64, i32]),
     "qlin_gemm_w4a4": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p, p]),
     "qlin_gemm_w4a4_group": (i32, [p, p, p, p, p, p, p, p, i64, i64, i64, p, p, p]),
     "qlin_outlier_comp": (i32, [p, p, i32, p, i64, i64, p, p]),

@@ -1122,6 +1122,35 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------------ per-group requant
+// The per-group requantization of a whole W4S-packed weight matrix into the
+// W8 layout, once per call (QQQ review, "technical architecture": the fused
+// dequant-quant of the per-group W4A8 kernel).  One thread per 16-byte lane
+// chunk of a 64-k tile t of strip nt; the chunk's two int8 fragments are W8
+// tiles 2t and 2t + 1 of the same strip, each value the same
+// requant_word result the tiled kernel computes in its K loop.
+__global__ __launch_bounds__(256) void requant_w4_group_kernel(const uint8_t* w4, const uint16_t* ratio, int64_t K,
+                                                               int64_t N, uint8_t* w8) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t kt4 = K / 64;
+  if (i >= kt4 * (N / 32) * 64) return;
+  const int lane = static_cast<int>(i & 63);
+  const int64_t nt = (i >> 6) / kt4, t = (i >> 6) % kt4;
+  const uint4 raw = *reinterpret_cast<const uint4*>(w4 + i * 16);
+  const _Float16 r = __builtin_bit_cast(_Float16, ratio[(t / 2) * N + nt * 32 + (lane & 31)]);
+  v4i c0, c1;
+  unpack_w4<BOp::W4Group>(raw, v2h{r, r}, c0, c1);
+  uint8_t* const out = w8 + ((nt * (K / 32) + 2 * t) << 10) + lane * 16;
+  *reinterpret_cast<v4i*>(out) = c0;
+  *reinterpret_cast<v4i*>(out + 1024) = c1;
+}
+
+// Tokens above which the per-group W4A8 product, given a workspace,
+// requantizes the weights once per call and runs the int8 tile on them.  At
+// and below it the skinny kernels stream the int4 weights once, which beats
+// reading them, writing twice the bytes and reading those again.
+constexpr int64_t kRequantMinRows = 128;
+
 // ------------------------------------------------------------ dispatch
 template <BOp B, AOp A, int MT, int NT, int WAVES, int U>
 void launch_skinny(const GemmArgs& g, hipStream_t st) {
@@ -1252,13 +1281,14 @@ extern "C" qlin_status qlin_gemm_w8a8(const int8_t* qa, const float* sa, const v
 extern "C" qlin_status qlin_gemm_w4a8(const int8_t* qa, const float* sa, const void* w4,
                                       const uint16_t* sw, const uint16_t* ratio, int32_t group,
                                       int64_t M, int64_t N, int64_t K, uint16_t* y, int32_t* acc,
-                                      void* stream) {
+                                      void* work, void* stream) {
   QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
   QLIN_K_N(K, N);
   QLIN_DIMS(M, K);
   QLIN_DIMS(K, N);
   QLIN_DIMS(M, N);
   QLIN_REQUIRE(group == 0 || group == 128, QLIN_ERR_UNSUPPORTED, "group=%d: only 0 and 128 are provided", group);
+  QLIN_OPT_PTR(work);
   if (M == 0) return QLIN_OK;
   QLIN_PTR(qa);
   QLIN_PTR(sa);
@@ -1276,8 +1306,25 @@ extern "C" qlin_status qlin_gemm_w4a8(const int8_t* qa, const float* sa, const v
   g.b = static_cast<const uint8_t*>(w4);
   g.sw_h = sw;
   g.ratio = ratio;
-  if (group == 128) return launch<BOp::W4Group, AOp::I8>(g, false, as_stream(stream));
-  return launch<BOp::W4Shift, AOp::I8>(g, false, as_stream(stream));
+  hipStream_t st = as_stream(stream);
+  if (group == 128 && work != nullptr && M > kRequantMinRows) {
+    const int64_t chunks = K * N / 32;
+    requant_w4_group_kernel<<<dim3(static_cast<unsigned>((chunks + 255) / 256)), 256, 0, st>>>(
+        static_cast<const uint8_t*>(w4), ratio, K, N, static_cast<uint8_t*>(work));
+    QLIN_LAUNCH_CHECK("requant_w4_group_kernel");
+    g.b = static_cast<const uint8_t*>(work);
+    g.ratio = nullptr;
+    return launch<BOp::W8, AOp::I8>(g, false, st);
+  }
+  if (group == 128) return launch<BOp::W4Group, AOp::I8>(g, false, st);
+  return launch<BOp::W4Shift, AOp::I8>(g, false, st);
+}
+
+extern "C" size_t qlin_gemm_w4a8_work_bytes(int64_t M, int64_t N, int64_t K, int32_t group) {
+  if (group != 128 || M <= qlin::kRequantMinRows || K <= 0 || K % 128 || N <= 0 || N % 64 ||
+      !qlin::dims_ok(M, K) || !qlin::dims_ok(K, N) || !qlin::dims_ok(M, N))
+    return 0;
+  return static_cast<size_t>(K * N);
 }
 
 extern "C" qlin_status qlin_gemm_w4a4(const uint8_t* qa4, const float* sa, const int32_t* za,

@@ -234,7 +234,7 @@ def qlin_gemm_w8a8(qa, sa, w8, sw, N, xO=None, nO=0, WO=None, want_acc=False, y=
     _req(qa, "qa", torch.int8)
     M, K = qa.shape
     _req(sa, "sa", torch.float32, (M,))
-    _req(w8, "w8", torch.uint8)
+    _req(w8, "w8", torch.uint8, (qlin_packed_bytes(QLIN_LAYOUT_W8, K, N),))
     _req(sw, "sw", torch.float16, (N,))
     if nO:
         _req(xO, "xO", torch.float16, (M, qlin_outlier_ld(nO)))
@@ -250,21 +250,36 @@ def qlin_gemm_w8a8(qa, sa, w8, sw, N, xO=None, nO=0, WO=None, want_acc=False, y=
     return y, acc
 
 
-def qlin_gemm_w4a8(qa, sa, w4, sw, N, ratio=None, group=0, want_acc=False, y=None):
+def qlin_gemm_w4a8_work_bytes(M, N, K, group) -> int:
+    return int(_lib.load().qlin_gemm_w4a8_work_bytes(M, N, K, group))
+
+
+def qlin_gemm_w4a8(qa, sa, w4, sw, N, ratio=None, group=0, want_acc=False, y=None, work=None):
+    """W4A8 per channel (group=0) or per group of 128 (group=128); returns (y, acc or None).
+    work: an optional device workspace (uint8) of at least
+    qlin_gemm_w4a8_work_bytes(M, N, K, group) bytes; with it, the per-group
+    form requantizes the weights once per call instead of in every tile."""
     lib = _lib.load()
     _req(qa, "qa", torch.int8)
     M, K = qa.shape
     _req(sa, "sa", torch.float32, (M,))
-    _req(w4, "w4", torch.uint8)
+    _req(w4, "w4", torch.uint8, (qlin_packed_bytes(QLIN_LAYOUT_W4S, K, N),))
     _req(sw, "sw", torch.float16, (N,))
     if group:
         _req(ratio, "ratio", torch.float16, (K // group, N))
     y = y if y is not None else _empty((M, N), torch.float16, qa)
     _req(y, "y", torch.float16, (M, N))
     acc = _empty((M, N), torch.int32, qa) if want_acc else None
+    need = qlin_gemm_w4a8_work_bytes(M, N, K, group)
+    if work is not None and need:
+        _req(work, "work", torch.uint8)
+        if work.numel() < need:
+            raise ValueError(f"work: {work.numel()} bytes, needs {need}")
+    else:
+        work = None
     _lib.check("qlin_gemm_w4a8", lib.qlin_gemm_w4a8(
         qa.data_ptr(), sa.data_ptr(), w4.data_ptr(), sw.data_ptr(), _ptr(ratio) if group else None, group, M, N, K,
-        y.data_ptr(), _ptr(acc), _stream()))
+        y.data_ptr(), _ptr(acc), _ptr(work), _stream()))
     return y, acc
 
 
@@ -277,7 +292,7 @@ def qlin_gemm_w4a4(qa4, sa, za, rowsum, w4, sw, zw, colsum, N, want_acc=False, y
                         (rowsum, "rowsum", torch.int32, (M,)), (sw, "sw", torch.float32, (N,)),
                         (zw, "zw", torch.int32, (N,)), (colsum, "colsum", torch.int32, (N,))]:
         _req(t, n, d, sh)
-    _req(w4, "w4", torch.uint8)
+    _req(w4, "w4", torch.uint8, (qlin_packed_bytes(QLIN_LAYOUT_W4U, K, N),))
     y = y if y is not None else _empty((M, N), torch.float16, qa4)
     _req(y, "y", torch.float16, (M, N))
     acc = _empty((M, N), torch.int32, qa4) if want_acc else None
@@ -301,7 +316,7 @@ def qlin_gemm_w4a4_group(qa4, sa, za, rowsum, w4, sw, zw, colsum_g, N, want_acc=
                         (rowsum, "rowsum", torch.int32, (M, G)), (sw, "sw", torch.float32, (N,)),
                         (zw, "zw", torch.int32, (N,)), (colsum_g, "colsum_g", torch.int32, (G, N))]:
         _req(t, n, d, sh)
-    _req(w4, "w4", torch.uint8)
+    _req(w4, "w4", torch.uint8, (qlin_packed_bytes(QLIN_LAYOUT_W4U, K, N),))
     y = y if y is not None else _empty((M, N), torch.float16, qa4)
     _req(y, "y", torch.float16, (M, N))
     acc = _empty((G, M, N), torch.int32, qa4) if want_acc else None

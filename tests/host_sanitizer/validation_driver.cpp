@@ -191,7 +191,7 @@ void gemms() {
   EXPECT(w8(0, 128, 256, nullptr, 0, nullptr, nullptr), QLIN_OK);
 
   auto w4 = [&](const uint16_t* ratio, int32_t group, int64_t M, int64_t N, int64_t K) {
-    return qlin_gemm_w4a8(qa, sa, w, sw, ratio, group, M, N, K, y, nullptr, nullptr);
+    return qlin_gemm_w4a8(qa, sa, w, sw, ratio, group, M, N, K, y, nullptr, nullptr, nullptr);
   };
   EXPECT(w4(nullptr, 64, 16, 128, 256), QLIN_ERR_UNSUPPORTED);
   EXPECT(w4(nullptr, 128, 16, 128, 256), QLIN_ERR_INVALID_ARG);
@@ -199,6 +199,14 @@ void gemms() {
   EXPECT(w4(nullptr, 0, kHuger, 128, 256), QLIN_ERR_SHAPE);
   EXPECT(w4(nullptr, 0, kHuge, kHuge, kHuge), QLIN_ERR_SHAPE);
   EXPECT(w4(nullptr, 0, 0, 128, 256), QLIN_OK);
+  EXPECT(qlin_gemm_w4a8(qa, sa, w, sw, at<uint16_t>(kA), 128, 256, 128, 256, y, nullptr, at<void>(kMis), nullptr),
+         QLIN_ERR_ALIGN);
+  if (qlin_gemm_w4a8_work_bytes(4096, 4096, 11008, 128) != size_t(4096) * 11008 ||
+      qlin_gemm_w4a8_work_bytes(128, 4096, 11008, 128) != 0 || qlin_gemm_w4a8_work_bytes(kHuger, 4096, 256, 128) != 0 ||
+      qlin_gemm_w4a8_work_bytes(kHuge, kHuge, kHuge, 128) != 0) {
+    ++g_failures;
+    printf("FAIL qlin_gemm_w4a8_work_bytes\n");
+  }
 
   for (int grouped = 0; grouped < 2; ++grouped) {
     auto f = grouped ? qlin_gemm_w4a4_group : qlin_gemm_w4a4;

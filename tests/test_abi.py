@@ -49,7 +49,7 @@ def test_exported_symbols_via_nm_style_lookup():
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    assert lib.qlin_abi_version() == 2
+    assert lib.qlin_abi_version() == 3
     names = [lib.qlin_status_string(i).decode() for i in range(6)]
     assert names == ["QLIN_OK", "QLIN_ERR_INVALID_ARG", "QLIN_ERR_SHAPE", "QLIN_ERR_ALIGN",
                      "QLIN_ERR_UNSUPPORTED", "QLIN_ERR_HIP"]
@@ -152,10 +152,17 @@ def test_gemm_validation():
     _err(lib.qlin_gemm_w8a8(*ok[:7], None, 300, None, A, None, None), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_gemm_w8a8(*ok[:10], A, MIS, None), _lib.QLIN_ERR_ALIGN)
     _err(lib.qlin_gemm_w8a8(*ok[:4], 0, *ok[5:]), _lib.QLIN_OK)
-    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 64, 16, 128, 256, A, None, None), _lib.QLIN_ERR_UNSUPPORTED)
-    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 128, 16, 128, 256, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_gemm_w4a8(A, A, B, A, A, 0, 16, 128, 256, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
-    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 0, 0, 128, 256, A, None, None), _lib.QLIN_OK)
+    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 64, 16, 128, 256, A, None, None, None), _lib.QLIN_ERR_UNSUPPORTED)
+    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 128, 16, 128, 256, A, None, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w4a8(A, A, B, A, A, 0, 16, 128, 256, A, None, None, None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(lib.qlin_gemm_w4a8(A, A, B, A, A, 128, 256, 128, 256, A, None, MIS, None), _lib.QLIN_ERR_ALIGN)
+    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 0, 0, 128, 256, A, None, None, None), _lib.QLIN_OK)
+    # Workspace of the once-per-call requantization: per group, above 128 tokens.
+    assert lib.qlin_gemm_w4a8_work_bytes(129, 4096, 11008, 128) == 11008 * 4096
+    assert lib.qlin_gemm_w4a8_work_bytes(128, 4096, 11008, 128) == 0
+    assert lib.qlin_gemm_w4a8_work_bytes(4096, 4096, 11008, 0) == 0
+    assert lib.qlin_gemm_w4a8_work_bytes(4096, 100, 11008, 128) == 0
+    assert lib.qlin_gemm_w4a8_work_bytes(1 << 40, 4096, 11008, 128) == 0
     _err(lib.qlin_gemm_w4a4(A, A, A, A, B, A, A, None, 16, 128, 256, A, None, None), _lib.QLIN_ERR_INVALID_ARG)
     _err(lib.qlin_gemm_w4a4(A, A, A, A, B, A, A, A, 16, 128, 384 + 64, A, None, None), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_gemm_w4a4(A, A, A, A, B, A, A, A, 0, 128, 256, A, None, None), _lib.QLIN_OK)
@@ -233,7 +240,7 @@ def test_size_limits():
     assert lib.qlin_packed_bytes(_lib.QLIN_LAYOUT_W8, 1 << 20, 1 << 20) == 1 << 40
     _err(lib.qlin_gemm_w8a8(A, A, B, A, bigger, 128, 256, None, 0, None, A, None, None), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_gemm_w8a8(A, A, B, A, 1 << 31, 128, 256, None, 0, None, A, None, None), _lib.QLIN_ERR_SHAPE)
-    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 0, big, big, big, A, None, None), _lib.QLIN_ERR_SHAPE)
+    _err(lib.qlin_gemm_w4a8(A, A, B, A, None, 0, big, big, big, A, None, None, None), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_quant_act(A, bigger, 256, None, B, A, None, 0, None, None, None, None), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_momentum_update(A, bigger, 256, A, 4, A, 0.9, A, B, None, None), _lib.QLIN_ERR_SHAPE)
     _err(lib.qlin_pack_weight(_lib.QLIN_LAYOUT_W8, A, big, big, B, None), _lib.QLIN_ERR_SHAPE)

@@ -112,7 +112,14 @@ def test_qqq_prefill_w4a8_group_full(q):
     q_ref, sa_ref = quant.quant_act_sym_int8(lin.x)
     assert_equal(host(qa), q_ref, "activation codes")
     assert_equal(host(sa), sa_ref, "activation steps")
-    y, acc = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128, want_acc=True)
+    # As timed: requantized once per call into a workspace, then the int8
+    # tile; the in-loop requantization must give the same bits.
+    import torch
+    work = torch.empty(q.qlin_gemm_w4a8_work_bytes(M, N, K, 128), dtype=torch.uint8, device="cuda")
+    y, acc = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128, want_acc=True, work=work)
+    y0, acc0 = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128, want_acc=True)
+    assert_equal(host(acc0), host(acc), "acc, requantized in the K loop vs once per call")
+    assert_equal(host(y0), host(y), "y, requantized in the K loop vs once per call")
     log("  oracle product")
     acc_ref, y_ref = gemm.w4a8_group(q_ref, sa_ref, w8, sc.astype(np.float32))
     assert_equal(host(acc), acc_ref, "acc")
@@ -218,11 +225,15 @@ def test_token_sweep_llama7b(q):
     p8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, c8)
     p4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, c4)
     pg = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, cg)
+    import torch
+    work = torch.empty(q.qlin_gemm_w4a8_work_bytes(Mx, N, K, 128), dtype=torch.uint8, device="cuda")
     cases = {
         "w8a8": (lambda a, s_: q.qlin_gemm_w8a8(a, s_, p8, s8, N, want_acc=True), w8_ref, s8_ref),
         "w4a8 channel": (lambda a, s_: q.qlin_gemm_w4a8(a, s_, p4, s4, N, want_acc=True), w4_ref, s4_ref),
         "w4a8 group": (lambda a, s_: q.qlin_gemm_w4a8(a, s_, pg, sc, N, ratio=ratio, group=128, want_acc=True),
                        w8g_ref, sc_ref),
+        "w4a8 group, workspace": (lambda a, s_: q.qlin_gemm_w4a8(a, s_, pg, sc, N, ratio=ratio, group=128,
+                                                                 want_acc=True, work=work), w8g_ref, sc_ref),
     }
     for name, (fn, wq, ws) in cases.items():
         log(f"token sweep {name}: oracle product at M={Mx}")

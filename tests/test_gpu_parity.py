@@ -195,17 +195,35 @@ def test_gemm_w4a8_channel(q, M, K, N):
     assert_close(host(y), ref["y"], "y")
 
 
+def _requant_work(q, M, N, K):
+    # A workspace of the size the library asks for, filled with a pattern:
+    # its contents on entry must not matter.
+    import torch
+    nbytes = q.qlin_gemm_w4a8_work_bytes(M, N, K, 128)
+    return torch.full((max(nbytes, 16),), 0xA5, dtype=torch.uint8, device="cuda"), nbytes
+
+
+@pytest.mark.parametrize("work", [False, True])
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
-def test_gemm_w4a8_group(q, M, K, N):
-    log(f"w4a8 group M={M} K={K} N={N}")
+def test_gemm_w4a8_group(q, M, K, N, work):
+    # With a workspace, above 128 tokens the weights are requantized once per
+    # call and the int8 tile runs on them; the result is the same to the bit.
+    log(f"w4a8 group M={M} K={K} N={N} work={work}")
     lin = synth.plain_linear(M, K, N, seed=M * 13 + K)
     ref = layer.w4a8_group_forward(lin.x, lin.w)
     codes, gs, cs, ratio = q.qlin_quant_weight_group(dev(lin.w), 128)
     w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes)
     qa, sa, _, _ = q.qlin_quant_act(dev(lin.x))
-    y, acc = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128, want_acc=True)
+    buf = None
+    if work:
+        buf, nbytes = _requant_work(q, M, N, K)
+        assert nbytes == (K * N if M > 128 else 0)
+    y, acc = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128, want_acc=True, work=buf)
     assert_equal(host(acc), ref["acc"], "acc")
     assert_close(host(y), ref["y"], "y")
+    if work:
+        y0, _ = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128)
+        assert_equal(host(y), host(y0), "y with and without the workspace")
 
 
 def test_gemm_w4a8_group_requant_edge_ratios(q):
@@ -227,14 +245,16 @@ def test_gemm_w4a8_group_requant_edge_ratios(q):
 
 
 @pytest.mark.parametrize("sign", [1, -1])
-@pytest.mark.parametrize("M", [128, 256])
-def test_gemm_w4a8_group_requant_exhaustive(q, sign, M):
+@pytest.mark.parametrize("M,work", [(128, False), (256, False), (256, True)])
+def test_gemm_w4a8_group_requant_exhaustive(q, sign, M, work):
     # QQQ's fused dequant-quant on the device, exhaustively: one column per
     # finite fp16 ratio of the given sign (31,744 of each, bit patterns
     # 0x0000..0x7bff or 0x8000..0xfbff, N = 496 * 64), every int4 code -8..7
     # down K = 128, one-hot int8 activations, unit scales, so that
     # acc[m, n] = w8[m mod 128, n] = clamp(rint(fp16(q4 * r)), -127, 127).
-    # M = 128 runs the skinny kernel, M = 256 the 128-row tiles.
+    # M = 128 runs the skinny kernel, M = 256 the 128-row tiles (requantizing
+    # in the K loop) or, with a workspace, the once-per-call requantization
+    # followed by the int8 tile.
     import torch
     K = 128
     bits = np.arange(0x7C00, dtype=np.uint32)
@@ -243,13 +263,14 @@ def test_gemm_w4a8_group_requant_exhaustive(q, sign, M):
     rg = bits.astype(np.uint16).view(np.float16)[None, :]
     N = rg.shape[1]
     assert N % 64 == 0
-    log(f"requant exhaustive sign={sign} M={M} N={N}")
+    log(f"requant exhaustive sign={sign} M={M} N={N} work={work}")
     codes = np.tile(np.arange(-8, 8, dtype=np.int8), K // 16)[:, None].repeat(N, 1)
     want_w8 = quant.requant_group(codes, rg, 128).astype(np.int32)
     w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, dev(codes))
     qa = np.tile(np.eye(K, dtype=np.int8), (M // K, 1))
+    buf = _requant_work(q, M, N, K)[0] if work else None
     y, acc = q.qlin_gemm_w4a8(dev(qa), dev(np.ones(M, np.float32)), w4, dev(np.ones(N, np.float16)), N,
-                              ratio=dev(rg), group=128, want_acc=True)
+                              ratio=dev(rg), group=128, want_acc=True, work=buf)
     torch.cuda.synchronize()
     got = host(acc)
     for r0 in range(0, M, K):
