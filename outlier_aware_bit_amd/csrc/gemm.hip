@@ -1122,6 +1122,181 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------------ skinny, LDS-staged
+// gemm_skinny_lds (32 < M <= 128, int8 activations): the skinny kernel with
+// its activations staged through LDS.  Loaded straight into fragments, a
+// 16-byte-per-lane activation load touches 32 token rows in 32-byte pieces;
+// here the workgroup loads each round's activation block (all 32 * MT rows,
+// 512 * U bytes of each) as whole row segments, 16 bytes per thread and a
+// row segment per 32 * U threads, stores it to LDS with the 16-byte chunks of
+// row m XOR-permuted by (m & 15) (16 rows reading one logical chunk hit 16
+// different bank groups), and every wave reads its fragments from there.
+// Round r covers units [8U r, 8U (r + 1)) of 64 k; wave w takes units
+// 8U r + w + 8j, j < U.  Activations are loaded two rounds ahead and stored
+// to the other of two LDS buffers one round ahead; weights are loaded two
+// rounds ahead into two register sets.  Units past K (a partial last round)
+// get zero weights, and their activation chunks are read from a clamped,
+// in-bounds address: they add exactly zero.  Rows past M are read from row
+// M - 1 and their outputs are not stored.
+template <BOp B, int MT, int U>
+__global__ __launch_bounds__(512) void gemm_skinny_lds(GemmArgs g) {
+  constexpr int NT = 2, WAVES = 8;
+  constexpr int kRows = 32 * MT;
+  constexpr int kRowB = 512 * U;         // bytes of a row per round
+  constexpr int kBuf = kRows * kRowB;    // bytes of a round's block
+  constexpr int kCh = kBuf / 16 / 512;   // 16-byte chunks per thread per round
+  constexpr int kCpr = kRowB / 16;       // chunks per row segment
+  constexpr int kRpi = 512 / kCpr;       // rows between a thread's chunks
+  constexpr int NBU = (B == BOp::W8) ? 2 : 1;
+  static_assert(MT * NT * 16 * 64 * 4 <= 2 * kBuf, "the reduction reuses the activation buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBuf];
+  int* const red = reinterpret_cast<int*>(lds);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int arow = lane & 31, ahalf = lane >> 5;
+  const int64_t nt0 = static_cast<int64_t>(blockIdx.x) * NT;  // N % 64 == 0: both strips exist
+  const int KU = static_cast<int>(g.K / 64);
+  const int R = (KU + 8 * U - 1) / (8 * U);
+  const int64_t KT = (B == BOp::W8) ? g.K / 32 : g.K / 64;
+
+  // Chunk i of this thread in a round: row i * kRpi + tid / kCpr, chunk cc.
+  const int cc = tid % kCpr, r0 = tid / kCpr;
+  const int8_t* const a0 = static_cast<const int8_t*>(g.a);
+  auto load_act = [&](int r, v4i (&ra)[kCh]) __attribute__((always_inline)) {
+    int64_t k = static_cast<int64_t>(r) * kRowB + cc * 16;
+    k = k < g.K ? k : g.K - 16;
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      int64_t m = i * kRpi + r0;
+      m = m < g.M ? m : g.M - 1;
+      ra[i] = *reinterpret_cast<const v4i*>(a0 + m * g.K + k);
+    }
+  };
+  auto store_act = [&](uint8_t* buf, const v4i (&ra)[kCh]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      const int row = i * kRpi + r0;
+      *reinterpret_cast<v4i*>(buf + row * kRowB + ((cc ^ (row & 15)) << 4)) = ra[i];
+    }
+  };
+  auto load_w = [&](int r, uint4 (&rb)[U][NT][NBU], v2h (&rr)[U][NT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int u = 8 * U * r + wave + 8 * j;
+      const bool ok = u < KU;
+      const int uc = ok ? u : KU - 1;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int h = 0; h < NBU; ++h) {
+          const int64_t tix = (nt0 + nt) * KT + ((B == BOp::W8) ? 2 * static_cast<int64_t>(uc) + h : uc);
+          const uint4 w = *reinterpret_cast<const uint4*>(g.b + (tix << 10) + lane * 16);
+          rb[j][nt][h] = ok ? w : make_uint4(0, 0, 0, 0);
+        }
+        if constexpr (B == BOp::W4Group) {
+          const _Float16 q = __builtin_bit_cast(
+              _Float16, g.ratio[static_cast<int64_t>(uc / 2) * g.N + (nt0 + nt) * 32 + arow]);
+          rr[j][nt] = v2h{q, q};
+        } else {
+          rr[j][nt] = v2h{};
+        }
+      }
+    }
+  };
+
+  v16i acc[MT][NT];
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = v16i{};
+
+  v4i ra[kCh];
+  uint4 rb[2][U][NT][NBU];
+  v2h rr[2][U][NT];
+  load_act(0, ra);
+  load_w(0, rb[0], rr[0]);
+  store_act(lds, ra);
+  if (R > 1) {
+    load_act(1, ra);
+    load_w(1, rb[1], rr[1]);
+  }
+  __syncthreads();
+
+  auto round = [&](auto par, int r) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    const uint8_t* const cur = lds + P * kBuf;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      v4i af[MT][2];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 32 * mt + arow, c = 4 * (wave + 8 * j) + 2 * h + ahalf;
+          af[mt][h] = *reinterpret_cast<const v4i*>(cur + row * kRowB + ((c ^ (row & 15)) << 4));
+        }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        v4i bf[2];
+        if constexpr (B == BOp::W8) {
+          const uint4 w0 = rb[P][j][nt][0], w1 = rb[P][j][nt][NBU - 1];
+          bf[0] = v4i{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w};
+          bf[1] = v4i{(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+        } else {
+          unpack_w4<B>(rb[P][j][nt][0], rr[P][j][nt], bf[0], bf[1]);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma_i8(af[mt][h], bf[h], acc[mt][nt]);
+      }
+    }
+    // The other buffer was last read in round r - 1, before its closing barrier.
+    if (r + 1 < R) store_act(lds + (1 - P) * kBuf, ra);
+    if (r + 2 < R) {
+      load_act(r + 2, ra);
+      load_w(r + 2, rb[P], rr[P]);
+    }
+    __syncthreads();
+  };
+  for (int r = 0; r < R; r += 2) {
+    round(std::integral_constant<int, 0>{}, r);
+    if (r + 1 < R) round(std::integral_constant<int, 1>{}, r + 1);
+  }
+
+  // The waves' int32 partial sums meet in the (now free) activation buffers.
+  for (int i = tid; i < MT * NT * 16 * 64; i += 512) red[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) atomicAdd(&red[((mt * NT + nt) * 16 + v) * 64 + lane], acc[mt][nt][v]);
+  __syncthreads();
+  for (int fi = wave; fi < MT * NT; fi += WAVES) {
+    const int mt = fi / NT, nt = fi % NT;
+    const int64_t n = (nt0 + nt) * 32 + arow;
+    const float sw = h2f(g.sw_h[n]);
+    float sam[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      int64_t m = mt * 32 + frag_row(v, lane);
+      m = m < g.M ? m : g.M - 1;
+      sam[v] = g.sa[m];
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t m = mt * 32 + frag_row(v, lane);
+      if (m >= g.M) continue;
+      int32_t val = red[(fi * 16 + v) * 64 + lane];
+      if constexpr (B == BOp::W4Shift) val >>= 4;  // every product is 16 * q * q4: the division is exact
+      if (g.acc != nullptr) g.acc[m * g.N + n] = val;
+      g.y[m * g.N + n] = f2h(static_cast<float>(val) * sw * sam[v]);
+    }
+  }
+}
+
 // ------------------------------------------------------ per-group requant
 // The per-group requantization of a whole W4S-packed weight matrix into the
 // W8 layout, once per call (QQQ review, "technical architecture": the fused
@@ -1184,6 +1359,24 @@ qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
     // flight at 128 rows) beat 128-row tiles, of which there would be fewer
     // than one per CU.
     if (!comp && g.M <= 128) {
+      // int8 activations from 33 tokens: staged through LDS (measured at
+      // 4096 x 11008: M = 64 per channel 16.8 -> 13.3 us, M = 128 26.4 ->
+      // 18.7 us), except where the direct form measured faster: the
+      // requantizing per-group weights at 128 rows, whose registers spill,
+      // and int8 weights at 128 rows up to 96 tokens.
+      const int64_t dgrid = g.N / 64;
+      if constexpr (A == AOp::I8) {
+        if (g.M > 32 && g.M <= 64) {
+          gemm_skinny_lds<B, 2, 2><<<dim3(static_cast<unsigned>(dgrid)), 512, 0, st>>>(g);
+          QLIN_LAUNCH_CHECK("gemm_skinny_lds");
+          return QLIN_OK;
+        }
+        if (g.M > 64 && (B == BOp::W4Shift || (B == BOp::W8 && g.M > 96))) {
+          gemm_skinny_lds<B, 4, 1><<<dim3(static_cast<unsigned>(dgrid)), 512, 0, st>>>(g);
+          QLIN_LAUNCH_CHECK("gemm_skinny_lds");
+          return QLIN_OK;
+        }
+      }
       if (g.M <= 32)
         launch_skinny<B, A, 1, 2, 8, 4>(g, st);
       else if (g.M <= 64)
