@@ -468,6 +468,25 @@ def rows_measurements(q, layer):
     ops = 2 * M5 * K5 * N5
     out["A8_gemm_w4a4"] = dict(workload=f"{M5}x{K5}x{N5}", ms=t, ops=ops, tops=ops / t / 1e9,
                                frac=ops / t / 1e9 / PEAK_INT8_TOPS, bound="mfma")
+    if PROFILE_LAUNCHES:
+        # Counter runs only: the W4A4 tile at K = 256 beside the row above, and
+        # the int8 tile of the same 256-row configuration at K = 256 and 4096,
+        # so that a counter's share per 128-deep stage can be told from its
+        # fixed share (prologue and epilogue).
+        Kd = 256
+        lin_d = synth.offq_inputs(M=M5, K=Kd, N=N5, seed=4)
+        signs_d = dev(lin_d.extra["signs"])
+        qd4, sad, zad, rsd, _ = q.qlin_hadamard_offset(dev(lin_d.x), signs_d)
+        cwd, swd, zwd, csd = q.qlin_quant_weight_offq(dev(lin_d.w), signs_d)
+        wd4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, cwd)
+        time_launches(lambda i: q.qlin_gemm_w4a4(qd4, sad, zad, rsd, wd4, swd, zwd, csd, N5, y=y), 0)
+        for Kw in (Kd, K5):
+            lin_w = synth.plain_linear(M5, Kw, N5, seed=8)
+            c8, s8 = q.qlin_quant_weight_sym(dev(lin_w.w), 8)
+            w8d = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, c8)
+            qa8, sa8, _, _ = q.qlin_quant_act(dev(lin_w.x))
+            time_launches(lambda i: q.qlin_gemm_w8a8(qa8, sa8, w8d, s8, N5, y=y), 0)
+        del lin_d, qd4, cwd, wd4, c8, w8d, qa8
 
     # OffQ group-wise offsets (a step and zero point per token and 128-channel
     # group), same shape, one outlier level per group.
