@@ -280,8 +280,10 @@ template <int MASK>
 __device__ __forceinline__ double quad_xor_f64(double v) {
   constexpr int ctrl = (MASK == 1) ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b & 0xffffffffu), ctrl, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), ctrl, 0xF, 0xF, false);
+  // Every lane of a quad permute has a source, so no "old" value is needed
+  // (mov_dpp, all rows and banks enabled).
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(b & 0xffffffffu), ctrl, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(b >> 32), ctrl, 0xF, 0xF, true);
   return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo));
 }
 
@@ -313,22 +315,19 @@ __device__ __forceinline__ void hadamard_chunk(const uint16_t* xr, const int8_t*
       }
     }
   }
+  // Spans 32 and 64 pair the lanes of a quad: the lower lane of a pair keeps
+  // u + other, the upper one other - u.  Both are fma(u, +-1, other): the
+  // product is exact, so the one rounding is that of the add or subtract.
   const int quarter = c & 3;
   {  // span 32: lanes xor 1
-    const bool upper = (quarter & 1) != 0;
+    const double sg = (quarter & 1) ? -1.0 : 1.0;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const double other = quad_xor_f64<1>(u[e]);
-      u[e] = upper ? (other - u[e]) : (u[e] + other);
-    }
+    for (int e = 0; e < 32; ++e) u[e] = __builtin_fma(u[e], sg, quad_xor_f64<1>(u[e]));
   }
   {  // span 64: lanes xor 2
-    const bool upper = (quarter & 2) != 0;
+    const double sg = (quarter & 2) ? -1.0 : 1.0;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const double other = quad_xor_f64<2>(u[e]);
-      u[e] = upper ? (other - u[e]) : (u[e] + other);
-    }
+    for (int e = 0; e < 32; ++e) u[e] = __builtin_fma(u[e], sg, quad_xor_f64<2>(u[e]));
   }
 #pragma unroll
   for (int e = 0; e < 32; ++e) t[e] = static_cast<float>(u[e]);
@@ -447,7 +446,7 @@ __global__ __launch_bounds__(64 * kHadWaves) void hadamard_offset_kernel(
 template <int MASK>
 __device__ __forceinline__ int quad_xor_i32(int v) {
   constexpr int ctrl = (MASK == 1) ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
-  return __builtin_amdgcn_update_dpp(0, v, ctrl, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(v, ctrl, 0xF, 0xF, true);
 }
 
 __device__ __forceinline__ float quad_min(float v) {
