@@ -293,16 +293,22 @@ __device__ __forceinline__ void hadamard_chunk(const uint16_t* xr, const int8_t*
   double u[32];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    float f[8];
-    load8_f16(xr + c * 32 + p * 8, f);
+    v4i raw = *reinterpret_cast<const v4i*>(xr + c * 32 + p * 8);
     const uint2 sraw = *reinterpret_cast<const uint2*>(signs + c * 32 + p * 8);
-    const uint32_t sw[2] = {sraw.x, sraw.y};
+    // x * d on the fp16 bits: the sign bit (bit 7) of d's bytes 2i and 2i+1
+    // is moved to bits 15 and 31 of the mask of fp16 pair i (a byte permute
+    // with zero bytes, then an AND) and XORed in.  Exact, as is the widening.
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int8_t d = static_cast<int8_t>((sw[j >> 2] >> (8 * (j & 3))) & 0xffu);
-      const double xv = static_cast<double>(f[j]);
-      u[p * 8 + j] = (d < 0) ? -xv : xv;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t sw = (i < 2) ? sraw.x : sraw.y;
+      const uint32_t sel = (i & 1) ? 0x030c020cu : 0x010c000cu;
+      const uint32_t mask = __builtin_amdgcn_perm(0u, sw, sel) & 0x80008000u;
+      raw[i] = static_cast<int>(static_cast<uint32_t>(raw[i]) ^ mask);
     }
+    float f[8];
+    unpack8_f16(raw, f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[p * 8 + j] = static_cast<double>(f[j]);
   }
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1) {
