@@ -388,8 +388,13 @@ def rows_measurements(q, layer):
     y2 = layer.y.clone()
     t = time_launches(lambda i: q.qlin_outlier_comp(layer.xO, layer.sa, nO, layer.WOp, y2), 100)
     fl = layer.fp16_flops()
-    out["A5_outlier_comp_standalone"] = dict(workload=f"{M}x{nO}x{N}", ms=t, flops=fl, tflops=fl / t / 1e9,
-                                             frac=fl / t / 1e9 / PEAK_FP16_TFLOPS, bound="mfma")
+    # Bound by the read-modify-write of y (the products are 3.4 GFLOP): bytes
+    # of xO, the packed W_O, sa and y read and written.
+    ldO = q.qlin_outlier_ld(nO)
+    b = 2 * M * ldO + 2 * ldO * N + 4 * M + 2 * 2 * M * N
+    out["A5_outlier_comp_standalone"] = dict(workload=f"{M}x{nO}x{N}", ms=t, bytes=b, gbs=b / t / 1e6,
+                                             frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm", flops=fl,
+                                             tflops=fl / t / 1e9)
     del y2
 
     # Quaff STE backward at the same shape: quantized gradient, the outlier

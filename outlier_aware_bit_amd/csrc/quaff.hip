@@ -229,13 +229,18 @@ __global__ __launch_bounds__(kMomThreads) void row_absmax_kernel(const uint16_t*
 }
 
 // Standalone compensation: y = fp16(y + sa * sum_j xO[m,j] * WO[j,n]) on
-// 128 x 256 tiles, four waves of 128 x 64 (no LDS: both operands arrive in
-// fragment order).
+// 128 x 256 tiles, four waves of 128 x 64 (both operands arrive in fragment
+// order).  The read-modify-write of y goes through the wave's own LDS rows,
+// 32 x 64 at a time: whole 128-byte row pieces are read and written (eight
+// lanes per row), and each lane works on its fragment's runs of four
+// adjacent columns in between.
 constexpr int kCompTM = 4, kCompThreads = 256;
+constexpr int kCompPitch = 144;  // bytes per staged row: 128 + 16 spreads rows over the banks
 
 __global__ __launch_bounds__(kCompThreads) void outlier_comp_kernel(
     const uint16_t* __restrict__ xO, int ldO, const float* __restrict__ sa,
     const uint8_t* __restrict__ WOp, int64_t M, int64_t N, uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint8_t ylds[kCompThreads / 64][32 * kCompPitch];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 32 * kCompTM;
   const int64_t wcol0 = static_cast<int64_t>(blockIdx.x) * 256 + 64 * wave;
@@ -246,18 +251,34 @@ __global__ __launch_bounds__(kCompThreads) void outlier_comp_kernel(
 #pragma unroll
     for (int b = 0; b < 2; ++b) f[a][b] = v16f{};
   comp_accumulate<kCompTM, 2>(f, xO, ldO, WOp, M, N, m0, wcol0 / 32);
-  // Lane l holds row (l & 31) and runs of four adjacent columns: 8-byte
-  // read-modify-write of y per run.
+  uint8_t* const yl = ylds[wave];
+  const int r = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int tm = 0; tm < kCompTM; ++tm) {
-    const int64_t m = m0 + 32 * tm + (lane & 31);
-    if (m >= M) continue;
-    const float sam = sa[m];
+    // Rows past M: the clamped row is read and nothing is written back.
+    v4i blk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 3) + 8 * i, chunk = lane & 7;
+      int64_t mr = m0 + 32 * tm + row;
+      mr = mr < M ? mr : M - 1;
+      blk[i] = *reinterpret_cast<const v4i*>(y + mr * N + wcol0 + 8 * chunk);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 3) + 8 * i, chunk = lane & 7;
+      *reinterpret_cast<v4i*>(yl + row * kCompPitch + chunk * 16) = blk[i];
+    }
+    // One wave's LDS operations complete in order: a compiler fence suffices.
+    asm volatile("" ::: "memory");
+    int64_t mc = m0 + 32 * tm + r;
+    mc = mc < M ? mc : M - 1;
+    const float sam = sa[mc];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint2* p = reinterpret_cast<uint2*>(y + m * N + wcol0 + 32 * nt + 8 * q + 4 * (lane >> 5));
+        uint2* p = reinterpret_cast<uint2*>(yl + r * kCompPitch + (32 * nt + 8 * q + 4 * h) * 2);
         const uint2 old = *p;
         const uint16_t in[4] = {static_cast<uint16_t>(old.x & 0xffffu), static_cast<uint16_t>(old.x >> 16),
                                 static_cast<uint16_t>(old.y & 0xffffu), static_cast<uint16_t>(old.y >> 16)};
@@ -266,6 +287,15 @@ __global__ __launch_bounds__(kCompThreads) void outlier_comp_kernel(
         for (int j = 0; j < 4; ++j) o[j] = f2h(h2f(in[j]) + sam * f[tm][nt][4 * q + j]);
         *p = make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
       }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 3) + 8 * i, chunk = lane & 7;
+      const int64_t mr = m0 + 32 * tm + row;
+      const v4i d = *reinterpret_cast<const v4i*>(yl + row * kCompPitch + chunk * 16);
+      if (mr < M) *reinterpret_cast<v4i*>(y + mr * N + wcol0 + 8 * chunk) = d;
+    }
+    asm volatile("" ::: "memory");
   }
 }
 
