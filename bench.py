@@ -638,8 +638,9 @@ def main():
                          "(untimed, no graphs, no token sweep)")
     ap.add_argument("--graphs", action="store_true",
                     help="launch the step as HIP graphs (slower than eager launches on ROCm 7)")
-    ap.add_argument("--event-every", type=int, default=1,
-                    help="record the GEMM's timing events on every n-th timed step (default: every step)")
+    ap.add_argument("--event-every", type=int, default=0,
+                    help="record the GEMM's timing events on every n-th timed step (default 0: every "
+                         "max(1, steps // 20)-th, so at least 20 samples, or every step below 40 steps)")
     ap.add_argument("--torch-events", action="store_true",
                     help="time the GEMM with torch's default events (with a system-scope fence on each record)")
     a = ap.parse_args()
@@ -665,7 +666,10 @@ def main():
     for t in range(a.warmup):
         run(t)
     torch.cuda.synchronize()
-    every = max(1, a.event_every)
+    # Each event record costs the GPU about a microsecond beside a 60-us step,
+    # so the events sample the GEMM (at least 20 samples) rather than
+    # bracket every launch.
+    every = a.event_every if a.event_every > 0 else max(1, a.steps // 20)
     if a.torch_events:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range((a.steps + every - 1) // every)]
