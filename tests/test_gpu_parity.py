@@ -226,6 +226,36 @@ def test_gemm_w4a8_group(q, M, K, N, work):
         assert_equal(host(y), host(y0), "y with and without the workspace")
 
 
+# The skinny kernels with LDS-staged activations (33..128 tokens) around their
+# dispatch edges: 32/33, 64/65, 96/97 and 128 tokens, with K from one
+# partial round (K = 128: 2 of a round's 8 or 16 units) to several rounds
+# with a partial last one (K = 640: 10 units).
+SKINNY_EDGE = [(M, K, N) for M in (32, 33, 64, 65, 96, 97, 128) for K, N in ((128, 64), (640, 192))]
+
+
+@pytest.mark.parametrize("M,K,N", SKINNY_EDGE)
+def test_skinny_dispatch_edges(q, M, K, N):
+    log(f"skinny edges M={M} K={K} N={N}")
+    lin = synth.plain_linear(M, K, N, seed=M * 19 + K, n_outliers=2)
+    qa, sa, _, _ = q.qlin_quant_act(dev(lin.x))
+    ref8 = layer.w8a8_forward(lin.x, lin.w)
+    codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 8)
+    y, acc = q.qlin_gemm_w8a8(qa, sa, q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes), sw, N, want_acc=True)
+    assert_equal(host(acc), ref8["acc"], "w8a8 acc")
+    assert_close(host(y), ref8["y"], "w8a8 y")
+    ref4 = layer.w4a8_channel_forward(lin.x, lin.w)
+    codes, sw = q.qlin_quant_weight_sym(dev(lin.w), 4)
+    y, acc = q.qlin_gemm_w4a8(qa, sa, q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes), sw, N, want_acc=True)
+    assert_equal(host(acc), ref4["acc"], "w4a8 channel acc")
+    assert_close(host(y), ref4["y"], "w4a8 channel y")
+    refg = layer.w4a8_group_forward(lin.x, lin.w)
+    codes, gs, cs, ratio = q.qlin_quant_weight_group(dev(lin.w), 128)
+    y, acc = q.qlin_gemm_w4a8(qa, sa, q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes), cs, N, ratio=ratio, group=128,
+                              want_acc=True)
+    assert_equal(host(acc), refg["acc"], "w4a8 group acc")
+    assert_close(host(y), refg["y"], "w4a8 group y")
+
+
 def test_gemm_w4a8_group_requant_edge_ratios(q):
     # Hand-picked ratios (ties, clamping, fp16 rounding that changes the integer)
     # and every int4 code, including -8, checked through the GEMM accumulator
