@@ -256,6 +256,27 @@ def test_skinny_dispatch_edges(q, M, K, N):
     assert_close(host(y), refg["y"], "w4a8 group y")
 
 
+@pytest.mark.parametrize("M,K,N", [(129, 128, 64), (300, 128, 192), (130, 1152, 64)])
+def test_gemm_w4a8_group_workspace_small_k(q, M, K, N):
+    # The once-per-call requantization at one group (K = 128) and at an odd
+    # number of groups, against the oracle and the in-loop form.
+    import torch
+    log(f"w4a8 group workspace M={M} K={K} N={N}")
+    lin = synth.plain_linear(M, K, N, seed=M * 23 + K)
+    ref = layer.w4a8_group_forward(lin.x, lin.w)
+    codes, gs, cs, ratio = q.qlin_quant_weight_group(dev(lin.w), 128)
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4S, codes)
+    qa, sa, _, _ = q.qlin_quant_act(dev(lin.x))
+    work = torch.full((q.qlin_gemm_w4a8_work_bytes(M, N, K, 128),), 0x5A, dtype=torch.uint8, device="cuda")
+    assert work.numel() == K * N
+    y, acc = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128, want_acc=True, work=work)
+    assert_equal(host(acc), ref["acc"], "acc")
+    assert_close(host(y), ref["y"], "y")
+    y0, acc0 = q.qlin_gemm_w4a8(qa, sa, w4, cs, N, ratio=ratio, group=128, want_acc=True)
+    assert_equal(host(acc0), host(acc), "acc in the K loop vs once per call")
+    assert_equal(host(y0), host(y), "y in the K loop vs once per call")
+
+
 def test_gemm_w4a8_group_requant_edge_ratios(q):
     # Hand-picked ratios (ties, clamping, fp16 rounding that changes the integer)
     # and every int4 code, including -8, checked through the GEMM accumulator
