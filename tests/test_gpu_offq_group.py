@@ -137,18 +137,21 @@ def test_gemm_w4a4_group(q, M, K, N):
     assert_close(host(y2), ref["y"], "y end to end")
 
 
-def test_gemm_w4a4_group_many_groups_and_scales(q):
-    # 65 groups (three chunks of the zero-point term, the last with one
-    # group), zero points up to 2000 in magnitude and activation steps that
-    # jump by 10^3 from one 32-group chunk to the next and fall again, from
-    # codes drawn directly, against the oracle's group-wise product.
-    M, K, N = 70, 8320, 128
+# 65 groups: three chunks of the zero-point term (the last with one group)
+# and two of the staged group constants.  100 groups: three chunks of the
+# group constants, the third loaded ahead of the K loop's last, partial
+# rotation of stages.
+@pytest.mark.parametrize("M,K,N", [(70, 8320, 128), (130, 12800, 192)])
+def test_gemm_w4a4_group_many_groups_and_scales(q, M, K, N):
+    # Zero points up to 2000 in magnitude and activation steps that jump by
+    # 10^3 from one 32-group chunk to the next and fall again, from codes
+    # drawn directly, against the oracle's group-wise product.
     G = K // 128
     log(f"w4a4 group from codes M={M} K={K} N={N}")
-    rng = np.random.default_rng(2024)
+    rng = np.random.default_rng(2024 + K)
     qa = rng.integers(0, 16, (M, K)).astype(np.uint8)
     qw = rng.integers(0, 16, (K, N)).astype(np.uint8)
-    chunk_scale = np.array([1.0, 1e3, 1e-2])[np.arange(G) // 32]
+    chunk_scale = np.array([1.0, 1e3, 1e-2])[(np.arange(G) // 32) % 3]
     sa = (rng.uniform(0.5, 2.0, (M, G)) * chunk_scale[None, :]).astype(np.float32)
     za = rng.integers(-2000, 2001, (M, G)).astype(np.int32)
     zw = rng.integers(0, 16, N).astype(np.int32)
@@ -162,6 +165,8 @@ def test_gemm_w4a4_group_many_groups_and_scales(q):
     y, acc = q.qlin_gemm_w4a4_group(dev(packed), dev(sa), dev(za), dev(rowsum), w4, dev(sw), dev(zw), dev(colsum), N,
                                     want_acc=True)
     assert_close(host(y), ref, "y")
+    y0, _ = q.qlin_gemm_w4a4_group(dev(packed), dev(sa), dev(za), dev(rowsum), w4, dev(sw), dev(zw), dev(colsum), N)
+    assert_close(host(y0), ref, "y without the group sums")
     got = host(acc)
     for g in range(G):
         ks = slice(g * 128, (g + 1) * 128)
