@@ -147,6 +147,20 @@ __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// Unsigned int4 codes (0..15, one per byte) on the fp8 matrix cores.  Read
+// as OCP e4m3, the byte c encodes c * 2^-9 (a subnormal for c < 8), so every
+// product is c * c' * 2^-18 and a 64-deep sum, at most 64 * 225 * 2^-18, is
+// exact in fp32: the int32 sum of the same bytes as int8, times 2^-18, with
+// the fp32 result the group-wise fold needs and no conversion.  Slot t of
+// lane half h of the first operand pairs with slot t of lane half h of the
+// second, as in two int8 products over the low and high register halves.
+// Zero scale operands select the unscaled instruction.
+__device__ __forceinline__ v16f mfma_c4(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- epilogue
 template <BOp B>
 __device__ __forceinline__ float col_scale(const GemmArgs& g, int64_t n) {
@@ -283,15 +297,16 @@ __device__ __forceinline__ void load_a_half(const TilePtrs<B, A, TM>& p, int s, 
 
 // Group-wise W4A4: the constants of one 128-k group (one K stage) for this
 // lane's TM token rows -- the step and d = rowsum - 128 za (code sum less
-// the zero point's share).
+// the zero point's share), as sa * 2^18 and d * 2^-18 (both exact): the
+// fp8 products carry a factor 2^-18 that the first cancels.
 template <int TM>
 struct GroupC {
   float sa[TM];
-  int32_t d[TM];
+  float d[TM];
 };
 
 // The tile's per-group token constants, staged in LDS kGcChunk groups at a
-// time: the step sa and d = rowsum - 128 za of every (row, group), row
+// time: sa * 2^18 and (rowsum - 128 za) * 2^-18 of every (row, group), row
 // pitch kGcChunk + 1 words so that the 32 rows a wave reads at one group
 // fall in 32 different banks.  A token's groups are contiguous in memory,
 // so these loads are coalesced; a per-stage load of one group for the
@@ -305,7 +320,7 @@ constexpr int kGcBatch = 6;  // entries per thread in flight when a later chunk 
 // at kernel start, a few at a time inside the K loop, where the prefetched
 // operands hold most registers.
 template <int TM, int kB>
-__device__ __forceinline__ void gc_stage_chunk(const GemmArgs& g, int64_t m0, int64_t c0, float* gsa, int32_t* gd) {
+__device__ __forceinline__ void gc_stage_chunk(const GemmArgs& g, int64_t m0, int64_t c0, float* gsa, float* gd) {
   constexpr int kPer = 32 * TM * kGcChunk / kTileThreads;
   static_assert(kPer % kB == 0, "batch must divide the per-thread share");
   // The empty asm keeps the address arithmetic here: hoisted out of the K
@@ -315,8 +330,7 @@ __device__ __forceinline__ void gc_stage_chunk(const GemmArgs& g, int64_t m0, in
   const int64_t G = g.K / kBK;
 #pragma unroll
   for (int k0 = 0; k0 < kPer; k0 += kB) {
-    float sv[kB];
-    int32_t dv[kB];
+    float sv[kB], dv[kB];
     // Clamped, unconditional loads (rows past M and groups past G repeat
     // the last ones; nothing reads them back).
 #pragma unroll
@@ -327,8 +341,8 @@ __device__ __forceinline__ void gc_stage_chunk(const GemmArgs& g, int64_t m0, in
       int64_t gi = c0 + gg;
       gi = gi < G ? gi : G - 1;
       const int64_t o = m * G + gi;
-      sv[k] = g.sa[o];
-      dv[k] = g.rowsum[o] - 128 * g.za[o];
+      sv[k] = g.sa[o] * 262144.0f;
+      dv[k] = static_cast<float>(g.rowsum[o] - 128 * g.za[o]) * 0x1p-18f;
     }
 #pragma unroll
     for (int k = 0; k < kB; ++k) {
@@ -342,7 +356,7 @@ __device__ __forceinline__ void gc_stage_chunk(const GemmArgs& g, int64_t m0, in
 // The constants of group s (s % kGcChunk within the staged chunk) for this
 // lane's TM token rows.
 template <int TM>
-__device__ __forceinline__ void load_group(const float* gsa, const int32_t* gd, int s, GroupC<TM>& c) {
+__device__ __forceinline__ void load_group(const float* gsa, const float* gd, int s, GroupC<TM>& c) {
   const int r = threadIdx.x & 31, gg = s % kGcChunk;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
@@ -351,33 +365,38 @@ __device__ __forceinline__ void load_group(const float* gsa, const int32_t* gd, 
   }
 }
 
-// End of group s: with raw = sum over the group of qa * qw (the int32
-// accumulators, restarted every group; 0 <= raw <= 128 * 225),
+// End of group s: with raw = sum over the group of qa * qw (exact; the fp8
+// products give f = raw * 2^-18, and 0 <= raw <= 128 * 225),
 //   cf += sa_g * fp32(raw)                        per element
 //   P  += sa_g * fp32(rowsum_g - 128 * za_g)      per token row
-// and after the last group group_zero_corr adds
+// each one fma of the scaled constants (the same rounding as of sa_g and
+// fp32(raw)), and after the last group group_zero_corr adds
 //   sum_g (-sa_g za_g) * colsum_g                 per element
 // so that y = sw * (cf - zw * P) is sw * sum_g sa_g * sum_{k in g} (qa - za_g)(qw - zw).
 template <int TM>
-__device__ __forceinline__ void group_rescale(const v16i (&acc)[TM][2], v16f (&cf)[TM][2], float (&P)[TM],
+__device__ __forceinline__ void group_rescale(const v16f (&accf)[TM][2], v16f (&cf)[TM][2], float (&P)[TM],
                                               const GroupC<TM>& c) {
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const float sa = c.sa[tm];
-    P[tm] = fmaf(sa, static_cast<float>(c.d[tm]), P[tm]);
+    P[tm] = fmaf(sa, c.d[tm], P[tm]);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) cf[tm][nt][v] = fmaf(sa, static_cast<float>(acc[tm][nt][v]), cf[tm][nt][v]);
+      for (int v = 0; v < 16; ++v) cf[tm][nt][v] = fmaf(sa, accf[tm][nt][v], cf[tm][nt][v]);
   }
 }
+
+// The integer sum behind an fp8 product of codes (exact: f * 2^18 is an
+// integer below 2^15).
+__device__ __forceinline__ int32_t raw_of(float f) { return static_cast<int32_t>(f * 262144.0f); }
 
 // Group-wise W4A4, parity output: the raw int32 sums of group s for this
 // wave's fragments, raw[s, m, n] at ((s * M) + m) * N + n.  Lane l holds token
 // row m0 + 32 tm + (l & 31) and, in registers 4q..4q+3 of fragment nt, the
 // four adjacent columns wcol0 + 32 nt + 8 q + 4 (l >> 5) + [0, 4).
 template <int TM>
-__device__ __forceinline__ void store_group_sums(const GemmArgs& g, const v16i (&acc)[TM][2], int s, int64_t m0,
+__device__ __forceinline__ void store_group_sums(const GemmArgs& g, const v16f (&accf)[TM][2], int s, int64_t m0,
                                                  int64_t wcol0, bool live) {
   const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
   if (!live) return;
@@ -391,7 +410,8 @@ __device__ __forceinline__ void store_group_sums(const GemmArgs& g, const v16i (
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<v4i*>(row + 32 * nt + 8 * q) =
-            v4i{acc[tm][nt][4 * q], acc[tm][nt][4 * q + 1], acc[tm][nt][4 * q + 2], acc[tm][nt][4 * q + 3]};
+            v4i{raw_of(accf[tm][nt][4 * q]), raw_of(accf[tm][nt][4 * q + 1]), raw_of(accf[tm][nt][4 * q + 2]),
+                raw_of(accf[tm][nt][4 * q + 3])};
   }
 }
 
@@ -530,6 +550,23 @@ __device__ __forceinline__ void read_frags(const uint8_t* buf, int ks, v4i (&af)
   for (int tm = 0; tm < TM; ++tm) af[tm] = *reinterpret_cast<const v4i*>(abuf + tm * 32 * kBK);
 }
 
+// The same fragments into the low (HI = 0) or high (HI = 1) halves of the
+// fp8 operands of the group-wise product.
+template <int TM, int HI>
+__device__ __forceinline__ void read_frags_half(const uint8_t* buf, int ks, v8i (&af)[TM]) {
+  const int lane = threadIdx.x & 63;
+  const int arow = lane & 31, ahalf = lane >> 5;
+  const uint8_t* abuf = buf + arow * kBK + (((2 * ks + ahalf) ^ swz_key(arow)) << 4);
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const v4i v = *reinterpret_cast<const v4i*>(abuf + tm * 32 * kBK);
+    if constexpr (HI)
+      af[tm].hi = v;
+    else
+      af[tm].lo = v;
+  }
+}
+
 template <int Mask, int N>
 __device__ __forceinline__ void sched_group() {
   if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(Mask, N, 0);
@@ -551,6 +588,23 @@ template <int TM, int NVM, int NDS, int... Ps>
 __device__ __forceinline__ void sched_kstep(std::integer_sequence<int, Ps...>) {
   sched_group<0x100, TM>();  // LDS fragment reads of the next k step
   (sched_kpair<TM, NVM, NDS, Ps>(), ...);
+}
+
+// The group-wise product's k steps: an even one has no matrix-core work
+// (fragment reads, then loads and stores); an odd one issues its 2*TM
+// products in pairs with its loads and stores, then the fragment reads that
+// overwrite the low operand halves.
+template <int TM, int NVM, int NDS>
+__device__ __forceinline__ void sched_kstep_c4_even() {
+  sched_group<0x100, TM>();
+  sched_group<0x020, NVM>();
+  sched_group<0x200, NDS>();
+}
+
+template <int TM, int NVM, int NDS, int... Ps>
+__device__ __forceinline__ void sched_kstep_c4_odd(std::integer_sequence<int, Ps...>) {
+  (sched_kpair<TM, NVM, NDS, Ps>(), ...);
+  sched_group<0x100, TM>();
 }
 
 // Stage barrier.  The last TM LDS operations of the wave are the fragment
@@ -649,7 +703,7 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
   [[maybe_unused]] int32_t* const c_zw = reinterpret_cast<int32_t*>(c_sw + kBN);
   [[maybe_unused]] int32_t* const c_cs = c_zw + kBN;
   [[maybe_unused]] float* const gsa = reinterpret_cast<float*>(lds + kMainBytes + 4 * (kRowC * T::BM + kColC * kBN));
-  [[maybe_unused]] int32_t* const gd = reinterpret_cast<int32_t*>(gsa + T::BM * (kGcChunk + 1));
+  [[maybe_unused]] float* const gd = gsa + T::BM * (kGcChunk + 1);
   const int64_t tiles_m = (g.M + T::BM - 1) / T::BM, tiles_n = (g.N + kBN - 1) / kBN;
   int64_t tmi, tni;
   tile_coords(tiles_m, tiles_n, tmi, tni);
@@ -671,6 +725,10 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
   for (int a = 0; a < TM; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = v16i{};
+  // Group-wise: fp32 sums of the fp8 products of one group, and the fp8
+  // operand fragments (low half: even k step, high half: odd k step).
+  [[maybe_unused]] v16f accf[TM][2];
+  [[maybe_unused]] v8i af8[TM];
 
   const int S = static_cast<int>(g.K / kBK);
   // Stage t of K: its weights live in B register set t % NBS (NBS = BD + 1),
@@ -826,7 +884,10 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
       if (o >= n0 && o < n0 + kBN) c_zw[o - n0] = j;
     }
   }
-  read_frags<TM>(lds, 0, af[0]);
+  if constexpr (kGrp)
+    read_frags_half<TM, 0>(lds, 0, af8);
+  else
+    read_frags<TM>(lds, 0, af[0]);
 
   constexpr int kVmB = (B == BOp::W8) ? 2 : 1;                           // B loads per k step
   constexpr int kDsW = (A == AOp::I8) ? T::kAChunks : 2 * T::kAChunks;   // LDS stores in k step 2
@@ -846,7 +907,6 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
       else
         read_frags<TM>(nxt, 0, af[0]);
       load_b_part<B, A, TM, KS>(p, b_tiles, g.N, sb, rbn, rrn);
-      if constexpr (kGrp && KS == 0) load_group<TM>(gsa, gd, st, gc);
       if constexpr (KS == 0) load_a_half<B, A, TM, 0>(p, s3, ra[1 - JA]);
       if constexpr (KS == 1) load_a_half<B, A, TM, 1>(p, s3, ra[1 - JA]);
       if constexpr (KS == 2) store_a<B, A, TM>(fut, p.lds_a, ra[JA]);
@@ -860,23 +920,67 @@ __global__ __launch_bounds__(kTileThreads, (A == AOp::U4G) ? 2 : 1) void gemm_ti
           bf[nt] = bq[nt][KS & 1];
         }
       }
-      // Group-wise: every group starts its int32 sums afresh.
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[tm][nt] = mfma_i8(bf[nt], af[KS & 1][tm], (kGrp && KS == 0) ? v16i{} : acc[tm][nt]);
+        for (int nt = 0; nt < 2; ++nt) acc[tm][nt] = mfma_i8(bf[nt], af[KS & 1][tm], acc[tm][nt]);
       constexpr int kVmAKS = (KS == 0) ? T::kAChunks / 2 : (KS == 1) ? T::kAChunks - T::kAChunks / 2 : 0;
       constexpr int nvm = kVmB + kVmAKS + ((B == BOp::W4Group && KS == 0) ? 2 : 0);
       sched_kstep<TM, nvm, (KS == 2) ? kDsW : 0>(std::make_integer_sequence<int, TM>{});
       __builtin_amdgcn_sched_barrier(0);
     };
-    kstep(std::integral_constant<int, 0>{});
-    kstep(std::integral_constant<int, 1>{});
-    kstep(std::integral_constant<int, 2>{});
-    kstep(std::integral_constant<int, 3>{});
-    if constexpr (kGrpAcc) store_group_sums<TM>(g, acc, st, m0, wcol0, live);
-    if constexpr (kGrp) group_rescale<TM>(acc, cf, P, gc);
+    // Group-wise: int4 codes on the fp8 matrix cores, two k steps per
+    // product.  An even k step reads the next k step's fragments into the
+    // high operand halves and unpacks the weights of both; an odd one issues
+    // the products, then reads the following k step's fragments into the low
+    // halves.  Every group starts its sums afresh.
+    [[maybe_unused]] v8i bq8[2];
+    auto kstep_c4 = [&](auto ksc) __attribute__((always_inline)) {
+      constexpr int KS = decltype(ksc)::value;
+      if constexpr ((KS & 1) == 0) read_frags_half<TM, 1>(cur, KS + 1, af8);
+      load_b_part<B, A, TM, KS>(p, b_tiles, g.N, sb, rbn, rrn);
+      if constexpr (KS == 0) load_group<TM>(gsa, gd, st, gc);
+      if constexpr (KS == 0) load_a_half<B, A, TM, 0>(p, s3, ra[1 - JA]);
+      if constexpr (KS == 1) load_a_half<B, A, TM, 1>(p, s3, ra[1 - JA]);
+      if constexpr (KS == 2) store_a<B, A, TM>(fut, p.lds_a, ra[JA]);
+      if constexpr ((KS & 1) == 0) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          v4i c0, c1;
+          unpack_w4v<B>(rb[JB][(KS >> 1) * 2 + nt], rr[JB][nt], c0, c1);
+          bq8[nt] = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      } else {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) accf[tm][nt] = mfma_c4(bq8[nt], af8[tm], KS == 1 ? v16f{} : accf[tm][nt]);
+        if constexpr (KS == 1)
+          read_frags_half<TM, 0>(cur, 2, af8);
+        else
+          read_frags_half<TM, 0>(nxt, 0, af8);
+      }
+      constexpr int kVmAKS = (KS == 0) ? T::kAChunks / 2 : (KS == 1) ? T::kAChunks - T::kAChunks / 2 : 0;
+      constexpr int nvm = kVmB + kVmAKS;
+      if constexpr ((KS & 1) == 0)
+        sched_kstep_c4_even<TM, nvm, (KS == 2) ? kDsW : 0>();
+      else
+        sched_kstep_c4_odd<TM, nvm, 0>(std::make_integer_sequence<int, TM>{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (kGrp) {
+      kstep_c4(std::integral_constant<int, 0>{});
+      kstep_c4(std::integral_constant<int, 1>{});
+      kstep_c4(std::integral_constant<int, 2>{});
+      kstep_c4(std::integral_constant<int, 3>{});
+    } else {
+      kstep(std::integral_constant<int, 0>{});
+      kstep(std::integral_constant<int, 1>{});
+      kstep(std::integral_constant<int, 2>{});
+      kstep(std::integral_constant<int, 3>{});
+    }
+    if constexpr (kGrpAcc) store_group_sums<TM>(g, accf, st, m0, wcol0, live);
+    if constexpr (kGrp) group_rescale<TM>(accf, cf, P, gc);
     stage_barrier<TM>();
     __builtin_amdgcn_sched_barrier(0);
   };
