@@ -1093,15 +1093,27 @@ __global__ __launch_bounds__(64 * WV, (A == AOp::U4G) ? 2 : 1) void gemm_tile(Ge
     comp_accumulate<TM, NTW>(cf, g.xO, g.ldO, g.WOp, g.M, g.N, m0, nt32);
   }
   lds_barrier();  // every wave has finished reading the activation stages
-  if (!live) return;
-  // Bytes per staged row: 64 NTW + 16 spreads the rows over the banks.
-  constexpr int kOutPitch = 64 * NTW + 16;
-  static_assert(WV * 32 * kOutPitch <= kMainBytes, "output staging exceeds the LDS buffers");
-  uint8_t* const out_lds = lds + wave * 32 * kOutPitch;
+  // Eight waves: the two waves of a pair (2i, 2i + 1) hold the two 64-byte
+  // halves of the same 128-byte row pieces.  Written by each wave on its
+  // own, every line of y would be written in two halves at different times,
+  // which the memory system turns into extra write traffic (23 MB instead
+  // of 16.8 at q_proj); so a pair stages its 32 x 64 block in one LDS region
+  // (two regions, alternating over tm) and, after a barrier, each wave
+  // writes 16 of its rows as whole lines.  Dead waves (whole pairs past N)
+  // stay for the barriers.
+  if (WV == 4 && !live) return;
+  // Bytes per staged row: 128 + 16 spreads the rows over the banks.
+  constexpr int kOutPitch = 144;
+  constexpr int kPairBytes = 32 * kOutPitch;
+  static_assert((WV == 4 ? 4 : 8) * kPairBytes <= kMainBytes, "output staging exceeds the LDS buffers");
   const bool want_acc = g.acc != nullptr;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const int64_t m = m0 + 32 * tm + r;
+    // This wave's staging rows and the byte offset of its columns in them.
+    uint8_t* const out_lds = (WV == 4) ? lds + wave * kPairBytes
+                                       : lds + (tm & 1) * 4 * kPairBytes + (wave >> 1) * kPairBytes;
+    const int out_col = (WV == 4) ? 0 : 64 * (wave & 1);
     // W4A4 zero points: acc = raw - zw*(rowsum - K*za) - za*colsum, evaluated
     // in wrapping 32-bit arithmetic (exact: the true value fits int32).
     const float sam = kGrp ? 1.0f : c_sa[32 * tm + r];
@@ -1156,21 +1168,30 @@ __global__ __launch_bounds__(64 * WV, (A == AOp::U4G) ? 2 : 1) void gemm_tile(Ge
             f = static_cast<float>(val) * sw[j];
           hv[j] = f2h(kBwd ? f : f * sam);
         }
-        *reinterpret_cast<uint2*>(out_lds + r * kOutPitch + (32 * nt + 8 * q + 4 * h) * 2) =
-            make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
-        if (COMP != 1 && !kGrp && want_acc && m < g.M) *reinterpret_cast<v4i*>(g.acc + m * g.N + n) = iv;
+        if (WV == 4 || live)
+          *reinterpret_cast<uint2*>(out_lds + r * kOutPitch + out_col + (32 * nt + 8 * q + 4 * h) * 2) =
+              make_uint2(hv[0] | (static_cast<uint32_t>(hv[1]) << 16), hv[2] | (static_cast<uint32_t>(hv[3]) << 16));
+        if (COMP != 1 && !kGrp && want_acc && live && m < g.M) *reinterpret_cast<v4i*>(g.acc + m * g.N + n) = iv;
       }
-    // The wave reads back only rows it wrote; LDS operations of one wave
-    // complete in order, so no barrier is needed, only a compiler fence.
-    asm volatile("" ::: "memory");
-    constexpr int kCh = 4 * NTW, kRowsPass = 64 / kCh;  // 16-byte chunks per row, rows per pass
+    // Four waves: each reads back only the rows it wrote; LDS operations of
+    // one wave complete in order, so a compiler fence suffices.  Eight: the
+    // pair's other half comes from the other wave, after a barrier.
+    if constexpr (WV == 4)
+      asm volatile("" ::: "memory");
+    else
+      lds_barrier();
+    // 128-byte rows, 8 lanes per row: all 32 rows (four waves), or this
+    // wave's 16 of the pair's 32 (eight waves).
+    constexpr int kRows = (WV == 4) ? 32 : 16;
+    const int row0 = (WV == 4) ? 0 : 16 * (wave & 1);
+    const int64_t col0 = (WV == 4) ? wcol0 : n0 + 64 * (wave >> 1);
 #pragma unroll
-    for (int i = 0; i < 32 / kRowsPass; ++i) {
-      const int row = lane / kCh + kRowsPass * i, chunk = lane % kCh;
+    for (int i = 0; i < kRows / 8; ++i) {
+      const int row = row0 + (lane >> 3) + 8 * i, chunk = lane & 7;
       const v4i d = *reinterpret_cast<const v4i*>(out_lds + row * kOutPitch + chunk * 16);
       const int64_t mr = m0 + 32 * tm + row;
       // Streaming store: the output is not read again by this kernel.
-      if (mr < g.M) __builtin_nontemporal_store(d, reinterpret_cast<v4i*>(g.y + mr * g.N + wcol0 + 8 * chunk));
+      if (live && mr < g.M) __builtin_nontemporal_store(d, reinterpret_cast<v4i*>(g.y + mr * g.N + col0 + 8 * chunk));
     }
     asm volatile("" ::: "memory");
   }
