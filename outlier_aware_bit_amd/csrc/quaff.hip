@@ -20,8 +20,10 @@ constexpr int kMomThreads = 256;
 // Momentum update, one workgroup per 64-channel strip of X (one 128-byte
 // line per token row).  The outliers of a strip share its lines, so reading
 // the whole strip once per row fetches every line of X that holds an outlier
-// exactly once, with no reduction across workgroups.  Strips without an
-// outlier read nothing from X.  (Splitting a strip's rows over several
+// exactly once, with no reduction across workgroups.  The rows of strips
+// without an outlier are read too (about 3 of 64 strips at 205 outliers in
+// 4096 channels), so that no load waits for the outlier bookkeeping.
+// (Splitting a strip's rows over several
 // workgroups needs either a second launch to fold their maxima or
 // device-scope fences, which write back and invalidate the per-XCD L2
 // caches; both cost more than the extra workgroups save at 2048 tokens.)
@@ -40,34 +42,64 @@ __global__ __launch_bounds__(kStripThreads) void momentum_kernel(
   __shared__ int owner[64];  // 1 + index into O of the outlier at this channel, or 0
   const int64_t strip = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Issue order: the first outlier index of this thread and s of its channel
+  // (threads below 64), then the strip's rows, so that the outlier
+  // bookkeeping below waits only for the former while the rows are in
+  // flight (a wait for a load also waits for every load issued before it).
+  // Every load is unconditional, from a clamped, in-range address: a load
+  // under a condition compiles to a branch, and after the join the compiler
+  // can only count the loads of the shortest path.  Without outliers or rows
+  // (x may then be NULL) the row loads read 16 bytes of s instead and are
+  // not folded in.
+  const bool rx = M > 0 && nO > 0;  // uniform
+  const int32_t* const Op = (nO > 0) ? O : reinterpret_cast<const int32_t*>(s);
+  const int o_raw = Op[(tid < nO) ? tid : 0];
+  const float s_k = s[strip * 64 + lane];
+  const uint16_t* const col = (rx ? x : reinterpret_cast<const uint16_t*>(s)) + strip * 64 + (tid & 7) * 8;
+  const int64_t ldx = rx ? K : 0;
+  const int64_t row0 = tid >> 3;
+  auto load_rows = [&](int64_t mb, v4i (&v)[kStripLoads]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kStripLoads; ++i) {
+      // Rows past M repeat row M - 1: the maximum is unchanged.
+      int64_t m = mb + row0 + static_cast<int64_t>(kStripThreads / 8) * i;
+      m = m < M ? m : M - 1;
+      v[i] = *reinterpret_cast<const v4i*>(col + m * ldx);
+    }
+  };
+  float cm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // channels 8*(tid&7) + [0, 8)
+  auto fold_rows = [&](const v4i (&v)[kStripLoads]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kStripLoads; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t u = static_cast<uint32_t>(v[i][w]);
+        cm[2 * w] = fmaxf(cm[2 * w], fabsf(h2f(static_cast<uint16_t>(u & 0xffffu))));
+        cm[2 * w + 1] = fmaxf(cm[2 * w + 1], fabsf(h2f(static_cast<uint16_t>(u >> 16))));
+      }
+  };
+  v4i v[kStripLoads];
+  load_rows(0, v);
   if (tid < 64) owner[tid] = 0;
   __syncthreads();
-  for (int j = tid; j < nO; j += kStripThreads) {
+  const int o0 = (tid < nO) ? o_raw : -1;
+  if (o0 >= 0 && o0 < K && o0 / 64 == strip) owner[o0 % 64] = tid + 1;
+  for (int j = tid + kStripThreads; j < nO; j += kStripThreads) {
     const int o = O[j];
     if (o >= 0 && o < K && o / 64 == strip) owner[o % 64] = j + 1;
   }
   __syncthreads();
-  const bool any = __syncthreads_or(tid < 64 && owner[tid] != 0);
-
-  float cm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // channels 8*(tid&7) + [0, 8)
-  if (any) {
-    const uint16_t* col = x + strip * 64 + (tid & 7) * 8;
-    const int64_t row0 = tid >> 3;
-    for (int64_t mb = 0; mb < M; mb += kStripRows) {
-      v4i v[kStripLoads];
-#pragma unroll
-      for (int i = 0; i < kStripLoads; ++i) {
-        const int64_t m = mb + row0 + static_cast<int64_t>(kStripThreads / 8) * i;
-        v[i] = (m < M) ? *reinterpret_cast<const v4i*>(col + m * K) : v4i{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int i = 0; i < kStripLoads; ++i)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t u = static_cast<uint32_t>(v[i][w]);
-          cm[2 * w] = fmaxf(cm[2 * w], fabsf(h2f(static_cast<uint16_t>(u & 0xffffu))));
-          cm[2 * w + 1] = fmaxf(cm[2 * w + 1], fabsf(h2f(static_cast<uint16_t>(u >> 16))));
-        }
+  // The outlier's weight-row maximum, also in flight with the rows.
+  const int own = (tid < 64) ? owner[tid] : 0;
+  const float* const wp = (nO > 0) ? wmax : s;
+  const float wm_raw = wp[(own != 0) ? own - 1 : 0];
+  const float wm = (own != 0) ? wm_raw : 0.0f;
+  if (rx) {
+    fold_rows(v);
+    for (int64_t mb = kStripRows; mb < M; mb += kStripRows) {
+      load_rows(mb, v);
+      __builtin_amdgcn_sched_barrier(0);  // all of a pass's loads before any use
+      fold_rows(v);
     }
   }
   // Lanes with equal (lane & 7) hold the same channels: combine over lane bits 3..5.
@@ -89,17 +121,15 @@ __global__ __launch_bounds__(kStripThreads) void momentum_kernel(
 #pragma unroll
     for (int w = 0; w < kStripThreads / 64; ++w) c = fmaxf(c, red[w][tid]);
     const int64_t k = strip * 64 + tid;
-    const int own = owner[tid];
     if (own != 0) {
-      const float wm = wmax[own - 1];
       float beta = 1.0f;
       if (wm != 0.0f) beta = fmaxf(1.0f, sqrt_rn(div_rn(c, wm)));
       const float g1 = sub_rn(1.0f, gamma);
-      const float sn = add_rn(mul_rn(gamma, s[k]), mul_rn(g1, beta));
+      const float sn = add_rn(mul_rn(gamma, s_k), mul_rn(g1, beta));
       s[k] = sn;
       r[k] = div_rn(1.0f, sn);
     } else {
-      r[k] = div_rn(1.0f, s[k]);
+      r[k] = div_rn(1.0f, s_k);
     }
   }
 }
