@@ -1,19 +1,21 @@
-// Integer GEMMs of libqlin on gfx950 matrix cores (v_mfma_i32_32x32x32_i8):
+// Integer GEMMs of libqlin on gfx950 matrix cores (v_mfma_i32_32x32x32_i8;
+// the group-wise W4A4 product on the fp8 form, v_mfma_f32_32x32x64_f8f6f4):
 //   qlin_gemm_w8a8  int8 x int8, fused dequant, optional fused Quaff compensation
 //   qlin_gemm_w4a8  QQQ W4A8: per channel (shift-by-4 unpack) or per group of
 //                   128 (fused fp16 dequant-quant inside the K loop)
 //   qlin_gemm_w4a4  OffQ-style asymmetric int4 x int4 with the zero-point
 //                   correction in the epilogue
 //   qlin_gemm_w4a4_group  the same with a step and zero point per token and
-//                   128-k group: each group's int32 partial sum is corrected
-//                   and scaled into fp32 accumulators inside the K loop
+//                   128-k group: each group's exact partial sum is scaled
+//                   into fp32 accumulators inside the K loop
 //
 // Two kernels serve all of them, specialised by an operand policy.
 //
 // gemm_tile (M > 128, with a compensation term, or group-wise W4A4): a
 // workgroup computes a (32*TM) x 256 tile with four waves side by side, each
 // owning 64 distinct output columns (32*TM x 64 per wave, 2*TM accumulator
-// fragments of 32 x 32).
+// fragments of 32 x 32), or, for 128-row int8 tiles, eight waves of 32
+// columns (two per SIMD).
 //   * Weights never touch LDS: the packed layout is in MFMA fragment order, so
 //     each wave streams its own columns straight from memory into registers
 //     with one 16-byte load per lane per fragment (int4 weights at half the
@@ -21,7 +23,7 @@
 //   * The K loop is unrolled over the period of the register rotation with no
 //     branches inside (prefetch indices are clamped to the last stage), so
 //     the accumulators stay in place in the accumulation registers.
-//   * Activations, shared by the four waves, go global -> registers -> LDS
+//   * Activations, shared by the waves, go global -> registers -> LDS
 //     (double buffered, loaded two stages of 128 k ahead), stored as 16-byte chunks
 //     XOR-swizzled by row so that fragment reads and row stores are free of
 //     bank conflicts.
@@ -583,9 +585,10 @@ __device__ __forceinline__ void sched_group() {
   if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(Mask, N, 0);
 }
 
-// Issue order of one k step (2*TM MFMAs).  A wave is alone on its SIMD and
-// issues in order, so a burst of memory instructions that fills a queue
-// stalls the matrix-core instructions behind it: the next k step's fragment
+// Issue order of one k step (2*TM MFMAs with four waves, TM with eight).  A
+// wave issues in order (alone on its SIMD with four waves), so a burst of
+// memory instructions that fills a queue stalls the matrix-core instructions
+// behind it: the next k step's fragment
 // reads go first (a full k step of cover), then pairs of MFMAs, each pair
 // followed by its share of the global loads and LDS stores of the k step.
 template <int NP, int NVM, int NDS, int P>
@@ -681,9 +684,9 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
 constexpr int kXOMaxLd = 384;
 constexpr int kXOLdsLd = 208;
 
-// Group-wise W4A4 tiles are bound by the vector ALU (the per-group fold of
-// every accumulator): two workgroups per CU, so that one wave's fold runs
-// while the other's matrix-core work and loads proceed.  WV = 8 (int8 x int8
+// Group-wise W4A4 tiles carry a per-group fold of every accumulator on the
+// vector ALU: two workgroups per CU, so that one wave's fold runs while the
+// other's matrix-core work and loads proceed.  WV = 8 (int8 x int8
 // without the compensation or with it staged in LDS): eight waves of 32
 // columns, two per SIMD, so that each CU has twice the operand loads in
 // flight.
