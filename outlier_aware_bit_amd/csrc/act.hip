@@ -117,8 +117,23 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
   const int nchunks = static_cast<int>(K / 8);
   auto chunk = [&](int i) { return 64 * (2 * i + half) + lane; };  // this lane's i-th chunk
 
-  // The row first: chunks clamped to the row, so that every load is in range
-  // and unconditional.
+  // Outlier slots of this lane (j = lane + 64 (2 i + half)): their channel
+  // indices are loaded first, so that the loads of r[O[j]] and s[O[j]] below
+  // wait only for them and not for the row issued after them (a wait for a
+  // load also waits for every load issued before it).  Unconditional, from
+  // a clamped index (a guarded load is a branch that waits for it).
+  constexpr int kSl = kOutlierLdMax / 128;
+  [[maybe_unused]] int oj[kSl];
+  if constexpr (OL) {
+#pragma unroll
+    for (int i = 0; i < kSl; ++i) {
+      const int j = lane + 64 * (2 * i + half);
+      const int o = O[j < nO ? j : nO - 1];
+      oj[i] = (j < nO && o >= 0 && o < K) ? o : -1;
+    }
+  }
+  // The row: chunks clamped to the row, so that every load is in range and
+  // unconditional.
   v4i raw[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
@@ -135,24 +150,21 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
       load_r8<HAS_R>(r, c < nchunks ? c : nchunks - 1, rch[i]);
     }
   }
-  // Outlier bookkeeping of this lane (slots j = lane + 64 (2 i + half)), in
-  // flight with the row.
-  constexpr int kSl = kOutlierLdMax / 128;
-  [[maybe_unused]] int oj[kSl];
+  // (Every row and factor load is issued before the wait for the indices.)
+  __builtin_amdgcn_sched_barrier(0);
+  // r and s of the lane's outlier slots, in flight with the row.  s may be
+  // NULL without xO: the load then reads O[0] instead and is not used.
   [[maybe_unused]] float rj[kSl], sm1j[kSl];
   [[maybe_unused]] uint16_t* const rowl = reinterpret_cast<uint16_t*>(qlds + tok * 2 * K);
   if constexpr (OL) {
-#pragma unroll
-    for (int i = 0; i < kSl; ++i) {
-      const int j = lane + 64 * (2 * i + half);
-      const int o = j < nO ? O[j] : -1;
-      oj[i] = (o >= 0 && o < K) ? o : -1;
-    }
+    const bool wx = xO != nullptr;
+    const float* const sp = wx ? s : reinterpret_cast<const float*>(O);
 #pragma unroll
     for (int i = 0; i < kSl; ++i) {
       const int o = oj[i] >= 0 ? oj[i] : 0;
       rj[i] = HAS_R ? load_r(r, o) : 1.0f;
-      sm1j[i] = (xO != nullptr && oj[i] >= 0) ? sub_rn(s[o], 1.0f) : 0.0f;
+      const float sv = sp[wx ? o : 0];
+      sm1j[i] = (wx && oj[i] >= 0) ? sub_rn(sv, 1.0f) : 0.0f;
     }
     // This wave's blocks of the raw row go to the token's LDS row.
 #pragma unroll
