@@ -767,15 +767,18 @@ __global__ __launch_bounds__(64 * WV, (A == AOp::U4G) ? 2 : 1) void gemm_tile(Ge
   v4i af[2][TM];
   // The epilogue constants are fetched first, with the first operands: they
   // arrive during the prologue instead of costing a round trip at the end.
-  // Thread t takes column n0 + t if t < 256 and row m0 + t if t < BM (both
-  // clamped).
+  // Thread t takes row m0 + t % BM and column n0 + t % 256 (both clamped),
+  // so that every thread loads and stores them unconditionally (threads with
+  // equal indices store equal values): a load used only under a condition is
+  // sunk into it, and the wait for it there would drain every operand load
+  // issued before it.
   float k_sa = 0.0f, k_sw;
   [[maybe_unused]] int32_t k_za = 0, k_rs = 0, k_zw = 0, k_cs = 0, k_o = -1;
   {
     const int t = threadIdx.x;
-    int64_t mc = m0 + (t < T::BM ? t : 0);
+    int64_t mc = m0 + t % T::BM;
     mc = mc < g.M ? mc : g.M - 1;
-    int64_t nc = n0 + t;
+    int64_t nc = n0 + t % kBN;
     nc = nc < g.N ? nc : g.N - 1;
     if constexpr (kGrp) {
       k_sw = g.sw_f[nc];
@@ -793,7 +796,9 @@ __global__ __launch_bounds__(64 * WV, (A == AOp::U4G) ? 2 : 1) void gemm_tile(Ge
       k_sa = g.sa[mc];
       k_sw = g.sw_f[nc];
       k_cs = __builtin_bit_cast(int32_t, sub_rn(g.s[nc], 1.0f));
-      k_o = t < g.nO ? g.O[t] : -1;
+      const int32_t* const Op = (g.nO > 0) ? g.O : reinterpret_cast<const int32_t*>(g.sa);  // sa: any valid word
+      const int32_t o = Op[(t < g.nO) ? t : 0];
+      k_o = (t < g.nO) ? o : -1;
     } else {
       k_sa = g.sa[mc];
       k_sw = h2f(g.sw_h[nc]);
@@ -879,24 +884,20 @@ __global__ __launch_bounds__(64 * WV, (A == AOp::U4G) ? 2 : 1) void gemm_tile(Ge
   store_a<B, A, TM, WV>(lds + T::kStage, p.lds_a, ra[1]);
   load_a<B, A, TM, WV>(p, clamp_s(2), ra[0]);
   {
-    const int t = threadIdx.x;
-    if (t < T::BM) {
-      c_sa[t] = k_sa;
-      if constexpr (B == BOp::W4U && !kGrp) {  // group-wise: no per-row constants
-        c_za[t] = k_za;
-        c_rs[t] = k_rs;
-      }
+    const int tr = threadIdx.x % T::BM, tc = threadIdx.x % kBN;
+    c_sa[tr] = k_sa;
+    if constexpr (B == BOp::W4U && !kGrp) {  // group-wise: no per-row constants
+      c_za[tr] = k_za;
+      c_rs[tr] = k_rs;
     }
-    if (T::kThreads == kBN || t < kBN) {
-      c_sw[t] = k_sw;
-      if constexpr (B == BOp::W4U) {
-        c_zw[t] = k_zw;
-        c_cs[t] = k_cs;
-      }
-      if constexpr (kBwd) {
-        c_zw[t] = -1;  // outlier index of the column, marked below
-        c_cs[t] = k_cs;
-      }
+    c_sw[tc] = k_sw;
+    if constexpr (B == BOp::W4U) {
+      c_zw[tc] = k_zw;
+      c_cs[tc] = k_cs;
+    }
+    if constexpr (kBwd) {
+      c_zw[tc] = -1;  // outlier index of the column, marked below
+      c_cs[tc] = k_cs;
     }
   }
   lds_barrier();
