@@ -188,6 +188,47 @@ def test_gemm_w4a4_group_one_group_matches_per_token(q):
     assert_close(host(y), ref["y"], "y")
 
 
+# Code patterns at the ends of the range: every group sum at its largest
+# (all codes 15: 128 * 225 = 28800), all zero, and alternating 0 / 15 rows
+# against 15 / 0 columns (sums of 0 and of 28800 / 2 side by side).  The
+# group-wise product forms each group sum on the fp8 matrix cores (codes read
+# as e4m3 values c * 2^-9), exact only if every such sum is; the per-group
+# sums are compared bit-exactly.
+@pytest.mark.parametrize("pattern", ["all15", "zeros", "alternate"])
+def test_gemm_w4a4_group_code_extremes(q, pattern):
+    M, K, N = 70, 384, 128
+    G = K // 128
+    log(f"w4a4 group code extremes {pattern} M={M} K={K} N={N}")
+    if pattern == "all15":
+        qa = np.full((M, K), 15, np.uint8)
+        qw = np.full((K, N), 15, np.uint8)
+    elif pattern == "zeros":
+        qa = np.zeros((M, K), np.uint8)
+        qw = np.zeros((K, N), np.uint8)
+    else:
+        qa = np.where((np.arange(M)[:, None] + np.arange(K)[None, :] // 128) % 2 == 0, 15, 0).astype(np.uint8)
+        qw = np.where((np.arange(N)[None, :] + np.arange(K)[:, None] // 128) % 2 == 0, 0, 15).astype(np.uint8)
+    rng = np.random.default_rng(77)
+    sa = (rng.uniform(0.5, 2.0, (M, G)) * 1e-3).astype(np.float32)  # |y| well inside fp16
+    za = rng.integers(-20, 21, (M, G)).astype(np.int32)
+    zw = rng.integers(0, 16, N).astype(np.int32)
+    sw = (rng.uniform(0.5, 2.0, N) * 1e-3).astype(np.float32)
+    rowsum = qa.reshape(M, G, 128).astype(np.int32).sum(axis=2).astype(np.int32)
+    colsum = quant.weight_colsum_group(qw)
+    ref = gemm.w4a4_group(qa, sa, za, qw, sw, zw)
+    packed = (qa[:, 0::2] | (qa[:, 1::2] << 4)).astype(np.uint8)
+    w4 = q.qlin_pack_weight(q.QLIN_LAYOUT_W4U, dev(qw))
+    y, acc = q.qlin_gemm_w4a4_group(dev(packed), dev(sa), dev(za), dev(rowsum), w4, dev(sw), dev(zw), dev(colsum), N,
+                                    want_acc=True)
+    got = host(acc)
+    for g in range(G):
+        ks = slice(g * 128, (g + 1) * 128)
+        assert_equal(got[g], gemm.w4a4_raw(qa[:, ks], qw[ks]).astype(np.int32), f"raw sums of group {g}")
+    y0, _ = q.qlin_gemm_w4a4_group(dev(packed), dev(sa), dev(za), dev(rowsum), w4, dev(sw), dev(zw), dev(colsum), N)
+    assert_equal(host(y0).view(np.uint16), host(y).view(np.uint16), "y with and without the group sums")
+    assert_close(host(y), ref, "y")
+
+
 def test_gemm_w4a4_group_errors(q):
     import torch
     from outlier_aware_bit_amd import _lib
