@@ -259,15 +259,17 @@ __global__ __launch_bounds__(kMomThreads) void row_absmax_kernel(const uint16_t*
 }
 
 // Standalone compensation: y = fp16(y + sa * sum_j xO[m,j] * WO[j,n]) on
-// 128 x 256 tiles, four waves of 128 x 64 (both operands arrive in fragment
-// order).  The read-modify-write of y goes through the wave's own LDS rows,
+// 64 x 256 tiles, four waves of 64 x 64 (both operands arrive in fragment
+// order), two workgroups per CU, so that one's products overlap the other's
+// read-modify-write of y (128-row tiles, one per CU: 13.1 us at 2048 x 208
+// x 4096; 64 rows: 12.1; 32 rows: 12.6).  The read-modify-write of y goes through the wave's own LDS rows,
 // 32 x 64 at a time: whole 128-byte row pieces are read and written (eight
 // lanes per row), and each lane works on its fragment's runs of four
 // adjacent columns in between.
-constexpr int kCompTM = 4, kCompThreads = 256;
+constexpr int kCompTM = 2, kCompThreads = 256;
 constexpr int kCompPitch = 144;  // bytes per staged row: 128 + 16 spreads rows over the banks
 
-__global__ __launch_bounds__(kCompThreads) void outlier_comp_kernel(
+__global__ __launch_bounds__(kCompThreads, 2) void outlier_comp_kernel(
     const uint16_t* __restrict__ xO, int ldO, const float* __restrict__ sa,
     const uint8_t* __restrict__ WOp, int64_t M, int64_t N, uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint8_t ylds[kCompThreads / 64][32 * kCompPitch];
