@@ -7,6 +7,9 @@ pre-quantized to int8 per output channel, fp16 rows W_O on the outlier set,
 momentum gamma = 0.9.  One step is one forward of the layer on one batch:
   momentum update of s on O  ->  per-token int8 quantization of X / s
   ->  W8A8 int8-MFMA GEMM with the fused compensation term  ->  Y fp16.
+The first two run as one qlin_quaff_momentum_quant call (the momentum
+maxima over row blocks, folded by the quantizer; bit-identical to the
+momentum update followed by the quantizer).
 
 Printed: one JSON line with the step throughput (TOPS of the layer's
 algorithmic work), the roofline of the dominant kernel (the fused GEMM) timed
@@ -225,6 +228,8 @@ class QuaffLayer:
         self.wmax = q.qlin_weight_row_absmax(WO)
         self.s = torch.ones(K, dtype=torch.float32, device="cuda")
         self.r = torch.empty_like(self.s)
+        self.mq_work = torch.empty((max(1, q.qlin_quaff_momentum_quant_work_bytes(M, self.nO) // 4),),
+                                   dtype=torch.float32, device="cuda")
         self.work = torch.empty((max(1, q.qlin_momentum_work_bytes(M, self.nO) // 4),), dtype=torch.float32,
                                 device="cuda")
         self.qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
@@ -237,6 +242,10 @@ class QuaffLayer:
     def momentum(self, x):
         self.q.qlin_momentum_update(x, self.O, self.wmax, self.gamma, self.s, self.r)
 
+    def momentum_quant(self, x):
+        self.q.qlin_quaff_momentum_quant(x, self.O, self.wmax, self.gamma, self.s, self.r, work=self.mq_work,
+                                         q=self.qa, scale=self.sa, xO=self.xO)
+
     def quant(self, x):
         self.q.qlin_quant_act(x, self.r, self.O, s=self.s, q=self.qa, scale=self.sa, xO=self.xO, want_qO=False)
 
@@ -246,8 +255,7 @@ class QuaffLayer:
 
     def step(self, t, ev=None):
         x = self.xs[t % len(self.xs)]
-        self.momentum(x)
-        self.quant(x)
+        self.momentum_quant(x)
         if ev is not None:
             ev[0].record()
         self.gemm()
@@ -264,8 +272,7 @@ class QuaffLayer:
         for x in self.xs:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                self.momentum(x)
-                self.quant(x)
+                self.momentum_quant(x)
             self.g_pre.append(g)
         self.g_gemm = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.g_gemm):
@@ -377,6 +384,12 @@ def rows_measurements(q, layer):
     b = 2 * M * K + M * K + 4 * M + 4 * K + 2 * M * nO
     out["A2_quant_act"] = dict(workload=f"quaff M={M} K={K} with r and xO", ms=t, bytes=b, gbs=b / t / 1e6,
                                frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm")
+    # The step's form of A1 + A2: the momentum maxima over row blocks, folded
+    # by the quantizer (two launches); the algorithmic bytes of the two rows.
+    t = time_launches(lambda i: layer.momentum_quant(layer.xs[i % len(layer.xs)]), 200)
+    b = (2 * M * nO + 4 * nO * 3 + 4 * K * 2) + (2 * M * K + M * K + 4 * M + 4 * K + 2 * M * nO)
+    out["A1A2_momentum_quant"] = dict(workload=f"quaff M={M} K={K} |O|={nO}, one call", ms=t, bytes=b,
+                                      gbs=b / t / 1e6, frac=b / t / 1e6 / PEAK_HBM_GBS, bound="hbm")
     t = time_launches(lambda i: layer.gemm(), 100)
     ops = layer.int8_ops() + 2 * layer.fp16_flops()
     out["A4A5_gemm_w8a8_fused_comp"] = dict(workload=f"{M}x{K}x{N} + |O|={nO}", ms=t, int8_equiv_ops=ops,
@@ -705,7 +718,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "quaff_w8a8_outlier_comp_q_proj", "M_tokens": layer.M, "K": layer.K,
                    "N": layer.N, "n_outliers": layer.nO, "gamma": layer.gamma, "activation_batches": 10,
-                   "step": "momentum_update + quant_act + gemm_w8a8(fused compensation)",
+                   "step": "quaff_momentum_quant (momentum update + quant_act) + gemm_w8a8(fused compensation)",
                    "launch": "hip_graphs" if a.graphs else "eager"},
         "roofline": {"bound": "mfma", "kernel": GEMM_KERNEL, "achieved": round(achieved, 2),
                      "peak": PEAK_INT8_TOPS, "unit": "TOPS", "frac": round(achieved / PEAK_INT8_TOPS, 4),

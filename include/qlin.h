@@ -176,6 +176,33 @@ qlin_status qlin_momentum_update(const uint16_t* x, int64_t M, int64_t K, const 
 size_t qlin_momentum_work_bytes(int64_t M, int32_t nO);
 
 /*
+ * qlin_quaff_momentum_quant -- one Quaff step's activation side in one call:
+ * the momentum update of qlin_momentum_update, then qlin_quant_act of x with
+ * the new r and the compensation operand xO with the new s (Quaff notes,
+ * "key design": targeted momentum scaling, then the INT8 quantization of the
+ * decoupled form).  Bit-identical to those two calls in that order.
+ *   x, M, K, O, nO, wmax_O, gamma, s, r   as in qlin_momentum_update
+ *   work    device workspace of qlin_quaff_momentum_quant_work_bytes(M, nO)
+ *           bytes, or NULL.  With it (and 1 <= nO <= 256, K <= 8192) the
+ *           maxima are taken by every CU over 4 row blocks per 64-channel
+ *           strip, and each quantizer wave folds them into the new s[O],
+ *           r[O] itself (two launches in all, no launch for the fold);
+ *           otherwise the two calls above are made.  Calls that overlap
+ *           must not share it.
+ *   q, scale, xO   as in qlin_quant_act (xO required when nO > 0, NULL
+ *           otherwise; the codes of the outlier columns are not written)
+ * M == 0 runs the momentum update alone.
+ */
+qlin_status qlin_quaff_momentum_quant(const uint16_t* x, int64_t M, int64_t K, const int32_t* O,
+                                      int32_t nO, const float* wmax_O, float gamma, float* s,
+                                      float* r, float* work, int8_t* q, float* scale, uint16_t* xO,
+                                      void* stream);
+
+/* Bytes of the qlin_quaff_momentum_quant workspace for M tokens and nO
+ * outliers (0 for negative arguments). */
+size_t qlin_quaff_momentum_quant_work_bytes(int64_t M, int32_t nO);
+
+/*
  * qlin_momentum_update_noalloc -- qlin_momentum_update without a workspace
  * argument and without any allocation, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses

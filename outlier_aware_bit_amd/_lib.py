@@ -28,6 +28,8 @@ SIGNATURES = {
     "qlin_momentum_update": (i32, [p, i64, i64, p, i32, p, f32, p, p, p, p]),
     "qlin_momentum_work_bytes": (C.c_size_t, [i64, i32]),
     "qlin_momentum_update_noalloc": (i32, [p, i64, i64, p, i32, p, f32, p, p, p]),
+    "qlin_quaff_momentum_quant": (i32, [p, i64, i64, p, i32, p, f32, p, p, p, p, p, p, p]),
+    "qlin_quaff_momentum_quant_work_bytes": (C.c_size_t, [i64, i32]),
     "qlin_quant_weight_sym": (i32, [p, i64, i64, i32, p, p, p]),
     "qlin_quant_weight_group": (i32, [p, i64, i64, i32, p, p, p, p, p]),
     "qlin_quant_weight_offq": (i32, [p, i64, i64, p, i32, p, p, p, p, p]),

@@ -98,14 +98,24 @@ __device__ __forceinline__ uint2 sym_codes8(const float (&v)[8], float inv) {
 // barrier makes the whole row visible), so that the outlier values are read
 // from there; otherwise they are re-read from memory.  Each wave takes every
 // other block of 64 outlier slots.
+//
+// MF (the momentum step folded in; HAS_R, OL, K <= 512 * CH): r[O[j]] and
+// s[O[j]] are not read but formed from the momentum step's row-block maxima
+// (mf.part), which each lane folds for its own slots; the first workgroup
+// writes them to mf.s and mf.r.  The maxima kernel leaves a marker in r at
+// each outlier channel, a NaN carrying the slot (mom_slot_marker); r read
+// for the row is replaced there by the new r of that slot, from an LDS
+// table (one barrier).  A lane that reads r[O[j]] after the first workgroup
+// has written it gets the same new r, which it keeps.
 constexpr int kOutlierLdMax = 256;
 constexpr int kQuantTokens = kQuantThreads / 128;  // tokens per workgroup
 
-template <bool HAS_R, bool OL, int CH, typename RT = float>
+template <bool HAS_R, bool OL, int CH, typename RT = float, bool MF = false>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const RT* __restrict__ r, int8_t* __restrict__ q,
     float* __restrict__ scale, const int32_t* __restrict__ O, int nO, int ldO,
-    const float* __restrict__ s, int8_t* __restrict__ qO, uint16_t* __restrict__ xO) {
+    const float* __restrict__ s, int8_t* __restrict__ qO, uint16_t* __restrict__ xO, MomFold mf) {
+  static_assert(!MF || (HAS_R && OL && std::is_same_v<RT, float>), "the momentum fold needs r and the LDS row");
   extern __shared__ __attribute__((aligned(16))) uint8_t qlds[];
   __shared__ float red[kQuantThreads / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = wave & 1, tok = wave >> 1;
@@ -132,6 +142,19 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
       oj[i] = (j < nO && o >= 0 && o < K) ? o : -1;
     }
   }
+  // MF: the slots' row-block maxima, w_max and old s, indexed by slot alone
+  // and issued ahead of the row.
+  [[maybe_unused]] float fpart[MF ? kSl : 1][kMomFoldBlocks], fw[MF ? kSl : 1], fs[MF ? kSl : 1];
+  if constexpr (MF) {
+#pragma unroll
+    for (int i = 0; i < kSl; ++i) {
+      const int j = lane + 64 * (2 * i + half), jc = j < nO ? j : nO - 1;
+#pragma unroll
+      for (int b = 0; b < kMomFoldBlocks; ++b) fpart[i][b] = mf.part[b * nO + jc];
+      fw[i] = mf.wmax[jc];
+      fs[i] = mf.part[kMomFoldBlocks * nO + jc];
+    }
+  }
   // The row: chunks clamped to the row, so that every load is in range and
   // unconditional.
   v4i raw[CH];
@@ -156,15 +179,47 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
   // NULL without xO: the load then reads O[0] instead and is not used.
   [[maybe_unused]] float rj[kSl], sm1j[kSl];
   [[maybe_unused]] uint16_t* const rowl = reinterpret_cast<uint16_t*>(qlds + tok * 2 * K);
-  if constexpr (OL) {
-    const bool wx = xO != nullptr;
-    const float* const sp = wx ? s : reinterpret_cast<const float*>(O);
+  if constexpr (MF) {
+    // The momentum step of the lane's slots and the new r by slot in LDS
+    // (the first token's lanes write it), then the lane's chunks take the
+    // new r at their outlier channels.
+    float* const rn_of = reinterpret_cast<float*>(qlds + kQuantTokens * 2 * K);
 #pragma unroll
     for (int i = 0; i < kSl; ++i) {
-      const int o = oj[i] >= 0 ? oj[i] : 0;
-      rj[i] = HAS_R ? load_r(r, o) : 1.0f;
-      const float sv = sp[wx ? o : 0];
-      sm1j[i] = (wx && oj[i] >= 0) ? sub_rn(sv, 1.0f) : 0.0f;
+      const int j = lane + 64 * (2 * i + half);
+      float c = fpart[i][0];
+#pragma unroll
+      for (int b = 1; b < kMomFoldBlocks; ++b) c = fmaxf(c, fpart[i][b]);
+      float sn, rn;
+      momentum_step(c, fw[i], mf.gamma, fs[i], sn, rn);
+      rj[i] = rn;
+      sm1j[i] = (oj[i] >= 0) ? sub_rn(sn, 1.0f) : 0.0f;
+      if (tok == 0) rn_of[j] = rn;
+      if (blockIdx.x == 0 && tok == 0 && oj[i] >= 0) {
+        mf.s[oj[i]] = sn;
+        mf.r[oj[i]] = rn;
+      }
+    }
+    lds_barrier();  // (not __syncthreads(), which would wait for the row first)
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, rch[i][w]);
+        if ((u & ~kMomSlotMask) == kMomSlotTag) rch[i][w] = rn_of[u & kMomSlotMask];
+      }
+  }
+  if constexpr (OL) {
+    const bool wx = xO != nullptr;
+    [[maybe_unused]] const float* const sp = wx ? s : reinterpret_cast<const float*>(O);
+    if constexpr (!MF) {
+#pragma unroll
+      for (int i = 0; i < kSl; ++i) {
+        const int o = oj[i] >= 0 ? oj[i] : 0;
+        rj[i] = HAS_R ? load_r(r, o) : 1.0f;
+        const float sv = sp[wx ? o : 0];
+        sm1j[i] = (wx && oj[i] >= 0) ? sub_rn(sv, 1.0f) : 0.0f;
+      }
     }
     // This wave's blocks of the raw row go to the token's LDS row.
 #pragma unroll
@@ -255,7 +310,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
           code = sym_code(vv, inv);
         }
         if (qO != nullptr) qO[m * ldO + j] = static_cast<int8_t>(code);
-        if (xO != nullptr) xO[m * ldO + j] = f2h(mul_rn(static_cast<float>(code), sm1j[i]));
+        if (xO != nullptr) xO[m * ldO + j] = f2h_mul(static_cast<float>(code), sm1j[i]);
       }
     }
   } else {
@@ -270,7 +325,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
         if (xO != nullptr) sm1 = sub_rn(s[o], 1.0f);
       }
       if (qO != nullptr) qO[m * ldO + j] = static_cast<int8_t>(code);
-      if (xO != nullptr) xO[m * ldO + j] = f2h(mul_rn(static_cast<float>(code), sm1));
+      if (xO != nullptr) xO[m * ldO + j] = f2h_mul(static_cast<float>(code), sm1);
     }
   }
 }
@@ -544,11 +599,27 @@ qlin_status launch_quant_grad(const uint16_t* dy, int64_t M, int64_t N, const ui
   const dim3 grid(static_cast<unsigned>((M + kQuantTokens - 1) / kQuantTokens));
   if (N <= 4096)
     quant_act_kernel<true, false, 4, uint16_t><<<grid, kQuantThreads, 0, st>>>(dy, M, N, sw, gq, gs, nullptr, 0, 0,
-                                                                                 nullptr, nullptr, nullptr);
+                                                                                 nullptr, nullptr, nullptr, MomFold{});
   else
     quant_act_kernel<true, false, 8, uint16_t><<<grid, kQuantThreads, 0, st>>>(dy, M, N, sw, gq, gs, nullptr, 0, 0,
-                                                                                  nullptr, nullptr, nullptr);
+                                                                                  nullptr, nullptr, nullptr, MomFold{});
   QLIN_LAUNCH_CHECK("quant_act_kernel (gradient)");
+  return QLIN_OK;
+}
+
+qlin_status launch_quant_momentum(const uint16_t* x, int64_t M, int64_t K, const float* r, int8_t* q, float* scale,
+                                  const int32_t* O, int32_t nO, uint16_t* xO, const MomFold& mf, hipStream_t st) {
+  const int ldO = static_cast<int>(outlier_ld(nO));
+  const dim3 grid(static_cast<unsigned>((M + kQuantTokens - 1) / kQuantTokens));
+  // The two tokens' rows, then the new r by slot.
+  const size_t lds = static_cast<size_t>(kQuantTokens) * 2 * static_cast<size_t>(K) + 4 * kOutlierLdMax;
+  if (K <= 4096)
+    quant_act_kernel<true, true, 4, float, true><<<grid, kQuantThreads, lds, st>>>(x, M, K, r, q, scale, O, nO, ldO,
+                                                                                 nullptr, nullptr, xO, mf);
+  else
+    quant_act_kernel<true, true, 8, float, true><<<grid, kQuantThreads, lds, st>>>(x, M, K, r, q, scale, O, nO, ldO,
+                                                                                 nullptr, nullptr, xO, mf);
+  QLIN_LAUNCH_CHECK("quant_act_kernel (momentum folded)");
   return QLIN_OK;
 }
 
@@ -589,7 +660,7 @@ extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, c
     constexpr bool HR = decltype(has_r)::value, OLc = decltype(ol_c)::value;
     constexpr int CH = decltype(ch)::value;
     quant_act_kernel<HR, OLc, CH><<<grid, kQuantThreads, OLc ? ol_lds : 0, st>>>(x, M, K, r, q, scale, O, nO, ldO, s,
-                                                                                qO, xO);
+                                                                                qO, xO, MomFold{});
   };
   auto go_ch = [&](auto has_r, auto ol_c) {
     if (K <= 4096)

@@ -82,6 +82,17 @@ __device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
 
+// fp16 of the fp32 product a * b: rounded to fp32, then to fp16, as written.
+// Left alone, the compiler turns the product and the conversion into one
+// mixed-precision fma with a +0 addend, whatever the contraction setting,
+// which (at least) turns a -0 product into +0; the empty asm keeps the
+// product in a register of its own.
+__device__ __forceinline__ uint16_t f2h_mul(float a, float b) {
+  float p = __fmul_rn(a, b);
+  asm volatile("" : "+v"(p));
+  return f2h(p);
+}
+
 // IEEE single-precision operations with one rounding each (never contracted).
 __device__ __forceinline__ float mul_rn(float a, float b) { return __fmul_rn(a, b); }
 __device__ __forceinline__ float add_rn(float a, float b) { return __fadd_rn(a, b); }
@@ -93,6 +104,23 @@ __device__ __forceinline__ float div_rn(float a, float b) { return a / b; }
 // neighbours), and '/' to the IEEE division sequence.
 __device__ __forceinline__ float sqrt_rn(float a) { return __builtin_sqrtf(a); }
 __device__ __forceinline__ float rint_f(float a) { return __builtin_rintf(a); }
+
+// Quaff targeted momentum scaling for one outlier channel ("Quaff" paper
+// notes, key design): c = max_m |x[m, o]|, wm = max_n |W[o, n]|,
+// beta = max(1, sqrt(c / wm)) (1 when wm == 0), s' = gamma s + (1 - gamma) beta
+// and r' = 1 / s', one rounding per operation.
+__device__ __forceinline__ void momentum_step(float c, float wm, float gamma, float s, float& sn, float& rn) {
+  float beta = 1.0f;
+  if (wm != 0.0f) beta = fmaxf(1.0f, sqrt_rn(div_rn(c, wm)));
+  const float g1 = sub_rn(1.0f, gamma);
+  sn = add_rn(mul_rn(gamma, s), mul_rn(g1, beta));
+  rn = div_rn(1.0f, sn);
+}
+
+// Workgroup barrier for LDS only: waits for this wave's LDS traffic, then for
+// every wave of the group.  Outstanding global loads are not waited for
+// (__syncthreads() waits for every memory operation of the wave first).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Wavefront (64 lanes) reductions.
 __device__ __forceinline__ float wave_max(float v) {

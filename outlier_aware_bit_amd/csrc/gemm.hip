@@ -172,12 +172,6 @@ __device__ __forceinline__ float col_scale(const GemmArgs& g, int64_t n) {
     return h2f(g.sw_h[n]);
 }
 
-__device__ __forceinline__ void lds_barrier() {
-  // Waits for this wave's LDS traffic, then for every wave of the group.
-  // Outstanding global loads (the prefetched stages) are not waited for.
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // ============================================================ tiled kernel
 constexpr int kBN = 256, kBK = 128, kTileThreads = 256;
 

@@ -122,12 +122,10 @@ __global__ __launch_bounds__(kStripThreads) void momentum_kernel(
     for (int w = 0; w < kStripThreads / 64; ++w) c = fmaxf(c, red[w][tid]);
     const int64_t k = strip * 64 + tid;
     if (own != 0) {
-      float beta = 1.0f;
-      if (wm != 0.0f) beta = fmaxf(1.0f, sqrt_rn(div_rn(c, wm)));
-      const float g1 = sub_rn(1.0f, gamma);
-      const float sn = add_rn(mul_rn(gamma, s_k), mul_rn(g1, beta));
+      float sn, rn;
+      momentum_step(c, wm, gamma, s_k, sn, rn);
       s[k] = sn;
-      r[k] = div_rn(1.0f, sn);
+      r[k] = rn;
     } else {
       r[k] = div_rn(1.0f, s_k);
     }
@@ -216,13 +214,104 @@ __global__ __launch_bounds__(kMomThreads) void momentum_fold_kernel(
   if (o < 0 || o >= K) return;
   float c = 0.0f;
   for (int b = 0; b < rblocks; ++b) c = fmaxf(c, part[static_cast<int64_t>(b) * nO + j]);
-  const float wm = wmax[j];
-  float beta = 1.0f;
-  if (wm != 0.0f) beta = fmaxf(1.0f, sqrt_rn(div_rn(c, wm)));
-  const float g1 = sub_rn(1.0f, gamma);
-  const float sn = add_rn(mul_rn(gamma, s[o]), mul_rn(g1, beta));
+  float sn, rn;
+  momentum_step(c, wmax[j], gamma, s[o], sn, rn);
   s[o] = sn;
-  r[o] = div_rn(1.0f, sn);
+  r[o] = rn;
+}
+
+// Momentum maxima for the quantizer's fold: workgroup (strip, b) takes the 64
+// channels of a strip over the rows of block b of kMomFoldBlocks, 16 rows in
+// flight per thread (one pass of 512 rows), and writes the maxima of the
+// strip's outlier channels to part[b * nO + j]; block 0 also copies s[O[j]]
+// to part[kMomFoldBlocks * nO + j] (the quantizer reads the old s there
+// while its first workgroup writes the new one), writes r = 1 / s for the
+// strip's other channels and the marker of slot j at r[O[j]] (nO <= 256).  As in momentum_kernel, every load is issued
+// before the outlier bookkeeping, from clamped in-range addresses.
+constexpr int kBlkThreads = 256;  // 8 lanes per row, 32 rows per load
+constexpr int kBlkLoads = 16;
+constexpr int kBlkRows = kBlkThreads / 8 * kBlkLoads;
+
+__global__ __launch_bounds__(kBlkThreads) void momentum_block_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const int32_t* __restrict__ O, int nO,
+    const float* __restrict__ s, float* __restrict__ r, int64_t rows, float* __restrict__ part) {
+  __shared__ float red[kBlkThreads / 64][64];
+  __shared__ int owner[64];  // 1 + index into O of the outlier at this channel, or 0
+  const int64_t strip = blockIdx.x, rb = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int o_raw = O[(tid < nO) ? tid : 0];
+  const float s_k = s[strip * 64 + lane];
+  const uint16_t* const col = x + strip * 64 + (tid & 7) * 8;
+  // Rows past the block (or the batch) repeat its last row, or row 0 for a
+  // block past the batch: in range, and the maximum over all blocks is
+  // unchanged.
+  const int64_t m_lo = rb * rows, m_hi = (m_lo + rows < M) ? m_lo + rows : M;
+  const int64_t last = (m_hi > m_lo) ? m_hi - 1 : 0;
+  v4i v[kBlkLoads];
+  auto load_rows = [&](int64_t mb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kBlkLoads; ++i) {
+      int64_t m = mb + (tid >> 3) + static_cast<int64_t>(kBlkThreads / 8) * i;
+      m = m < m_hi ? m : last;
+      v[i] = *reinterpret_cast<const v4i*>(col + m * K);
+    }
+  };
+  float cm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // channels 8*(tid&7) + [0, 8)
+  auto fold_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kBlkLoads; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t u = static_cast<uint32_t>(v[i][w]);
+        cm[2 * w] = fmaxf(cm[2 * w], fabsf(h2f(static_cast<uint16_t>(u & 0xffffu))));
+        cm[2 * w + 1] = fmaxf(cm[2 * w + 1], fabsf(h2f(static_cast<uint16_t>(u >> 16))));
+      }
+  };
+  load_rows(m_lo);
+  if (tid < 64) owner[tid] = 0;
+  __syncthreads();
+  const int o0 = (tid < nO) ? o_raw : -1;
+  if (o0 >= 0 && o0 < K && o0 / 64 == strip) owner[o0 % 64] = tid + 1;
+  for (int j = tid + kBlkThreads; j < nO; j += kBlkThreads) {
+    const int o = O[j];
+    if (o >= 0 && o < K && o / 64 == strip) owner[o % 64] = j + 1;
+  }
+  __syncthreads();
+  fold_rows();
+  for (int64_t mb = m_lo + kBlkRows; mb < m_hi; mb += kBlkRows) {
+    load_rows(mb);
+    __builtin_amdgcn_sched_barrier(0);  // all of a pass's loads before any use
+    fold_rows();
+  }
+  // Lanes with equal (lane & 7) hold the same channels: combine over lane bits 3..5.
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float t = cm[c];
+    t = fmaxf(t, __shfl_xor(t, 8));
+    t = fmaxf(t, __shfl_xor(t, 16));
+    t = fmaxf(t, __shfl_xor(t, 32));
+    cm[c] = t;
+  }
+  if (lane < 8) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) red[wave][lane * 8 + c] = cm[c];
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int own = owner[tid];
+    if (own != 0) {
+      float c = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kBlkThreads / 64; ++w) c = fmaxf(c, red[w][tid]);
+      part[rb * nO + own - 1] = c;
+      if (rb == 0) {
+        part[static_cast<int64_t>(kMomFoldBlocks) * nO + own - 1] = s_k;
+        r[strip * 64 + tid] = mom_slot_marker(own - 1);
+      }
+    } else if (rb == 0) {
+      r[strip * 64 + tid] = div_rn(1.0f, s_k);
+    }
+  }
 }
 
 // The two-launch form is used from kWorkMinRows tokens: below, one workgroup
@@ -573,6 +662,55 @@ extern "C" qlin_status qlin_momentum_update(const uint16_t* x, int64_t M, int64_
   }
   QLIN_REQUIRE(K / 64 <= 0x7fffffffLL, QLIN_ERR_SHAPE, "K too large");
   return launch_momentum(x, M, K, O, nO, wmax_O, gamma, s, r, work, as_stream(stream));
+}
+
+extern "C" size_t qlin_quaff_momentum_quant_work_bytes(int64_t M, int32_t nO) {
+  if (M < 0 || nO < 0) return 0;
+  const size_t fused = static_cast<size_t>(kMomFoldBlocks + 1) * static_cast<size_t>(nO) * sizeof(float);
+  const size_t two = qlin_momentum_work_bytes(M, nO);
+  return fused > two ? fused : two;
+}
+
+extern "C" qlin_status qlin_quaff_momentum_quant(const uint16_t* x, int64_t M, int64_t K, const int32_t* O,
+                                                 int32_t nO, const float* wmax_O, float gamma, float* s, float* r,
+                                                 float* work, int8_t* q, float* scale, uint16_t* xO,
+                                                 void* stream) {
+  QLIN_REQUIRE(M >= 0, QLIN_ERR_INVALID_ARG, "M=%lld is negative", (long long)M);
+  QLIN_REQUIRE(K > 0 && K % 128 == 0, QLIN_ERR_SHAPE, "K=%lld must be a positive multiple of 128", (long long)K);
+  QLIN_DIMS(M, K);
+  QLIN_REQUIRE(nO >= 0 && nO <= K, QLIN_ERR_SHAPE, "nO=%d must be in [0, K]", nO);
+  QLIN_REQUIRE(gamma >= 0.0f && gamma <= 1.0f, QLIN_ERR_INVALID_ARG, "gamma=%g must be in [0, 1]", (double)gamma);
+  QLIN_PTR(s);
+  QLIN_PTR(r);
+  QLIN_OPT_PTR(work);
+  if (nO > 0) {
+    QLIN_PTR(O);
+    QLIN_PTR(wmax_O);
+    if (M > 0) QLIN_PTR(xO);
+  } else {
+    QLIN_REQUIRE(O == nullptr && xO == nullptr, QLIN_ERR_INVALID_ARG, "O and xO must be NULL when nO == 0");
+  }
+  if (M > 0) {
+    QLIN_PTR(x);
+    QLIN_PTR(q);
+    QLIN_PTR(scale);
+  }
+  QLIN_REQUIRE(K / 64 <= 0x7fffffffLL && M / 2 < 0x7fffffffLL, QLIN_ERR_SHAPE, "M or K too large");
+  // The folded form needs a workspace, the outlier slots of the quantizer's
+  // LDS path and rows that fit its registers; otherwise the two calls it
+  // stands for, which give the same result.
+  const bool fold = work != nullptr && M > 0 && nO > 0 && outlier_ld(nO) <= 256 && K <= 8192;
+  if (!fold) {
+    const qlin_status st = qlin_momentum_update(x, M, K, O, nO, wmax_O, gamma, s, r, work, stream);
+    if (st != QLIN_OK) return st;
+    return qlin_quant_act(x, M, K, r, q, scale, O, nO, s, nullptr, xO, stream);
+  }
+  hipStream_t st = as_stream(stream);
+  const int64_t rows = (M + kMomFoldBlocks - 1) / kMomFoldBlocks;
+  momentum_block_kernel<<<dim3(static_cast<unsigned>(K / 64), kMomFoldBlocks), kBlkThreads, 0, st>>>(
+      x, M, K, O, nO, s, r, rows, work);
+  QLIN_LAUNCH_CHECK("momentum_block_kernel");
+  return launch_quant_momentum(x, M, K, r, q, scale, O, nO, xO, MomFold{work, wmax_O, gamma, s, r}, st);
 }
 
 extern "C" qlin_status qlin_momentum_update_noalloc(const uint16_t* x, int64_t M, int64_t K, const int32_t* O,

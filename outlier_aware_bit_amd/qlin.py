@@ -149,6 +149,42 @@ def qlin_momentum_update(x, O, wmax_O, gamma, s, r, work=None):
     return s, r
 
 
+def qlin_quaff_momentum_quant_work_bytes(M, nO) -> int:
+    return int(_lib.load().qlin_quaff_momentum_quant_work_bytes(M, nO))
+
+
+def qlin_quaff_momentum_quant(x, O, wmax_O, gamma, s, r, work=None, q=None, scale=None, xO=None):
+    """Quaff's momentum update (s in place, r written), then the per-token
+    int8 of x * r and xO = fp16(q[:, O] * (s[O] - 1)) with the new s and r.
+    work: a float32 device workspace of at least
+    qlin_quaff_momentum_quant_work_bytes(M, nO) bytes, or None.
+    Returns (q, scale, xO)."""
+    lib = _lib.load()
+    _req(x, "x", torch.float16)
+    M, K = x.shape
+    _req(O, "O", torch.int32)
+    nO = O.numel()
+    _req(wmax_O, "wmax_O", torch.float32, (nO,))
+    _req(s, "s", torch.float32, (K,))
+    _req(r, "r", torch.float32, (K,))
+    q = _req(q, "q", torch.int8, (M, K)) if q is not None else _empty((M, K), torch.int8, x)
+    scale = _req(scale, "scale", torch.float32, (M,)) if scale is not None else _empty((M,), torch.float32, x)
+    if nO:
+        ld = qlin_outlier_ld(nO)
+        xO = _req(xO, "xO", torch.float16, (M, ld)) if xO is not None else _empty((M, ld), torch.float16, x)
+    else:
+        xO = None
+    if work is not None:
+        _req(work, "work", torch.float32)
+        need = qlin_quaff_momentum_quant_work_bytes(M, nO)
+        if work.numel() * 4 < need:
+            raise ValueError(f"work holds {work.numel() * 4} bytes, {need} needed")
+    _lib.check("qlin_quaff_momentum_quant", lib.qlin_quaff_momentum_quant(
+        x.data_ptr(), M, K, O.data_ptr() if nO else None, nO, wmax_O.data_ptr() if nO else None, float(gamma),
+        s.data_ptr(), r.data_ptr(), _ptr(work), q.data_ptr(), scale.data_ptr(), _ptr(xO), _stream()))
+    return q, scale, xO
+
+
 def qlin_weight_row_absmax(w_rows, out=None):
     lib = _lib.load()
     _req(w_rows, "w_rows", torch.float16)

@@ -136,6 +136,27 @@ void momentum() {
   EXPECT(qlin_momentum_update_noalloc(x, 8, 256, O, 8193, wm, 0.9f, s, r, nullptr), QLIN_ERR_SHAPE);
   EXPECT(qlin_momentum_update_noalloc(x, 8, 256, O, 4, wm, 1.5f, s, r, nullptr), QLIN_ERR_INVALID_ARG);
   EXPECT(qlin_momentum_update_noalloc(x, kHuger, 256, O, 4, wm, 0.9f, s, r, nullptr), QLIN_ERR_SHAPE);
+  // The momentum update and the quantization in one call.
+  int8_t* q = at<int8_t>(kA);
+  float* sc = at<float>(kB);
+  uint16_t* xO = at<uint16_t>(kA);
+  auto mq = [&](int64_t M, int64_t K, int32_t nO, float gamma, float* work, uint16_t* xo) {
+    return qlin_quaff_momentum_quant(x, M, K, O, nO, wm, gamma, s, r, work, q, sc, xo, nullptr);
+  };
+  EXPECT(mq(8, 256, 4, 1.5f, nullptr, xO), QLIN_ERR_INVALID_ARG);
+  EXPECT(mq(8, 256, 400, 0.9f, nullptr, xO), QLIN_ERR_SHAPE);
+  EXPECT(mq(8, 200, 4, 0.9f, nullptr, xO), QLIN_ERR_SHAPE);
+  EXPECT(mq(-1, 256, 4, 0.9f, nullptr, xO), QLIN_ERR_INVALID_ARG);
+  EXPECT(mq(8, 256, 4, 0.9f, nullptr, nullptr), QLIN_ERR_INVALID_ARG);
+  EXPECT(mq(8, 256, 4, 0.9f, at<float>(kA + 4), xO), QLIN_ERR_ALIGN);
+  EXPECT(mq(kHuger, 256, 4, 0.9f, nullptr, xO), QLIN_ERR_SHAPE);
+  EXPECT(mq(kHuge, kHuge, 4, 0.9f, nullptr, xO), QLIN_ERR_SHAPE);
+  if (qlin_quaff_momentum_quant_work_bytes(128, 205) != 5 * 205 * 4 ||
+      qlin_quaff_momentum_quant_work_bytes(2048, 205) != 16 * 205 * 4 ||
+      qlin_quaff_momentum_quant_work_bytes(-1, 7) != 0 || qlin_quaff_momentum_quant_work_bytes(kHuger, 7) != 16 * 7 * 4) {
+    ++g_failures;
+    printf("FAIL qlin_quaff_momentum_quant_work_bytes\n");
+  }
 }
 
 void weights() {

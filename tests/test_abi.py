@@ -130,6 +130,31 @@ def test_momentum_validation():
     assert lib.qlin_momentum_work_bytes(-1, 7) == 0
 
 
+def test_momentum_quant_validation():
+    lib = _lib.load()
+    def mq(x=A, M=8, K=256, O=A, nO=4, wm=A, gamma=0.9, s=A, r=B, work=None, q=A, scale=B, xO=A):
+        return lib.qlin_quaff_momentum_quant(x, M, K, O, nO, wm, gamma, s, r, work, q, scale, xO, None)
+    _err(mq(gamma=1.5), _lib.QLIN_ERR_INVALID_ARG)
+    _err(mq(nO=400), _lib.QLIN_ERR_SHAPE)
+    _err(mq(K=200), _lib.QLIN_ERR_SHAPE)
+    _err(mq(M=-1), _lib.QLIN_ERR_INVALID_ARG)
+    _err(mq(O=None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(mq(wm=None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(mq(xO=None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(mq(nO=0, O=None, wm=None), _lib.QLIN_ERR_INVALID_ARG)  # xO given without outliers
+    _err(mq(q=None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(mq(scale=None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(mq(s=None), _lib.QLIN_ERR_INVALID_ARG)
+    _err(mq(x=MIS), _lib.QLIN_ERR_ALIGN)
+    _err(mq(work=A + 4), _lib.QLIN_ERR_ALIGN)
+    # Workspace: five rows of nO floats (four row blocks and the old s), or
+    # what the momentum update's two-launch form needs, if more.
+    assert lib.qlin_quaff_momentum_quant_work_bytes(128, 205) == 5 * 205 * 4
+    assert lib.qlin_quaff_momentum_quant_work_bytes(2048, 205) == 16 * 205 * 4
+    assert lib.qlin_quaff_momentum_quant_work_bytes(0, 7) == 5 * 7 * 4
+    assert lib.qlin_quaff_momentum_quant_work_bytes(-1, 7) == 0
+
+
 def test_weight_prep_validation():
     lib = _lib.load()
     _err(lib.qlin_quant_weight_sym(A, 256, 128, 3, A, B, None), _lib.QLIN_ERR_UNSUPPORTED)
