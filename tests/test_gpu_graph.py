@@ -1,6 +1,8 @@
 """The Quaff layer step (momentum update -> quantization with the compensation
 operand -> fused W8A8 GEMM) captured into HIP graphs and replayed, checked
-bit for bit against the same step launched eagerly from the same state.
+bit for bit against the same step launched eagerly from the same state; the
+first two as separate calls, or as one qlin_quaff_momentum_quant call with a
+workspace (its maxima kernel leaves markers in r that the quantizer reads).
 
 The momentum state s is updated in place by every step, so the eager and the
 graph paths each own a copy of it.  Replays alternate between two activation
@@ -17,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 
 class _Step:
-    def __init__(self, q, d, w8, sw, WOp, wmax, O, nO):
+    def __init__(self, q, d, w8, sw, WOp, wmax, O, nO, fold):
         import torch
         M, K = d.xs[0].shape
         N = d.w.shape[1]
@@ -28,22 +30,29 @@ class _Step:
         self.sa = torch.empty((M,), dtype=torch.float32, device="cuda")
         self.xO = torch.empty((M, q.qlin_outlier_ld(nO)), dtype=torch.float16, device="cuda")
         self.y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        self.work = (torch.empty((q.qlin_quaff_momentum_quant_work_bytes(M, nO) // 4,), dtype=torch.float32,
+                                 device="cuda") if fold else None)
 
     def run(self, x):
         q = self.q
-        q.qlin_momentum_update(x, self.O, self.wmax, 0.9, self.s, self.r)
-        q.qlin_quant_act(x, self.r, self.O, s=self.s, q=self.qa, scale=self.sa, xO=self.xO, want_qO=False)
+        if self.work is not None:
+            q.qlin_quaff_momentum_quant(x, self.O, self.wmax, 0.9, self.s, self.r, work=self.work, q=self.qa,
+                                        scale=self.sa, xO=self.xO)
+        else:
+            q.qlin_momentum_update(x, self.O, self.wmax, 0.9, self.s, self.r)
+            q.qlin_quant_act(x, self.r, self.O, s=self.s, q=self.qa, scale=self.sa, xO=self.xO, want_qO=False)
         q.qlin_gemm_w8a8(self.qa, self.sa, self.w8, self.sw, self.N, xO=self.xO, nO=self.nO, WO=self.WOp, y=self.y)
 
     def state(self):
         return [host(t) for t in (self.s, self.r, self.qa, self.sa, self.xO, self.y)]
 
 
-def test_quaff_step_graph_replays_match_eager():
+@pytest.mark.parametrize("fold", [False, True], ids=["two_calls", "folded"])
+def test_quaff_step_graph_replays_match_eager(fold):
     import torch
     from outlier_aware_bit_amd import qlin as q
     M, K, N, nO = 1024, 1024, 512, 51
-    log(f"graph replay of the Quaff step M={M} K={K} N={N} |O|={nO}")
+    log(f"graph replay of the Quaff step M={M} K={K} N={N} |O|={nO} fold={fold}")
     d = synth.quaff_steps(M=M, K=K, N=N, n_outliers=nO, steps=2, seed=11)
     codes, sw = q.qlin_quant_weight_sym(dev(d.w), 8)
     w8 = q.qlin_pack_weight(q.QLIN_LAYOUT_W8, codes)
@@ -52,8 +61,8 @@ def test_quaff_step_graph_replays_match_eager():
     wmax = q.qlin_weight_row_absmax(WO)
     O = dev(d.outliers)
     xs = [dev(x) for x in d.xs]
-    eager = _Step(q, d, w8, sw, WOp, wmax, O, nO)
-    graphed = _Step(q, d, w8, sw, WOp, wmax, O, nO)
+    eager = _Step(q, d, w8, sw, WOp, wmax, O, nO, fold)
+    graphed = _Step(q, d, w8, sw, WOp, wmax, O, nO, fold)
     torch.cuda.synchronize()
 
     graphs = []
