@@ -102,11 +102,15 @@ __device__ __forceinline__ uint2 sym_codes8(const float (&v)[8], float inv) {
 // MF (the momentum step folded in; HAS_R, OL, K <= 512 * CH): r[O[j]] and
 // s[O[j]] are not read but formed from the momentum step's row-block maxima
 // (mf.part), which each lane folds for its own slots; the first workgroup
-// writes them to mf.s and mf.r.  The maxima kernel leaves a marker in r at
-// each outlier channel, a NaN carrying the slot (mom_slot_marker); r read
-// for the row is replaced there by the new r of that slot, from an LDS
-// table (one barrier).  A lane that reads r[O[j]] after the first workgroup
-// has written it gets the same new r, which it keeps.
+// writes them to mf.s and mf.r.  The maxima kernel leaves a NaN in r at
+// each outlier channel (mom_slot_marker), so x * r there is NaN, which the
+// maximum (fmaxf) passes over; each lane adds |x[O[j]] * r'| of its own
+// slots, gathering x[O[j]] from the row.  The codes of a token go to an LDS
+// row first; after a barrier the slots' codes overwrite the outlier
+// channels' there, and after another the row is written out.  (A lane that
+// reads r[O[j]] after the first workgroup has written the new r gets a
+// number instead of the NaN: the maximum is then the same, and the code is
+// overwritten all the same.)
 constexpr int kOutlierLdMax = 256;
 constexpr int kQuantTokens = kQuantThreads / 128;  // tokens per workgroup
 
@@ -179,14 +183,14 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
   // NULL without xO: the load then reads O[0] instead and is not used.
   [[maybe_unused]] float rj[kSl], sm1j[kSl];
   [[maybe_unused]] uint16_t* const rowl = reinterpret_cast<uint16_t*>(qlds + tok * 2 * K);
+  [[maybe_unused]] uint16_t xg[MF ? kSl : 1];
   if constexpr (MF) {
-    // The momentum step of the lane's slots and the new r by slot in LDS
-    // (the first token's lanes write it), then the lane's chunks take the
-    // new r at their outlier channels.
-    float* const rn_of = reinterpret_cast<float*>(qlds + kQuantTokens * 2 * K);
+    // The slots' values x[O[j]] (their lines are on the way with the row),
+    // then the momentum step of the lane's slots.
+#pragma unroll
+    for (int i = 0; i < kSl; ++i) xg[i] = xr[oj[i] >= 0 ? oj[i] : 0];
 #pragma unroll
     for (int i = 0; i < kSl; ++i) {
-      const int j = lane + 64 * (2 * i + half);
       float c = fpart[i][0];
 #pragma unroll
       for (int b = 1; b < kMomFoldBlocks; ++b) c = fmaxf(c, fpart[i][b]);
@@ -194,22 +198,13 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
       momentum_step(c, fw[i], mf.gamma, fs[i], sn, rn);
       rj[i] = rn;
       sm1j[i] = (oj[i] >= 0) ? sub_rn(sn, 1.0f) : 0.0f;
-      if (tok == 0) rn_of[j] = rn;
       if (blockIdx.x == 0 && tok == 0 && oj[i] >= 0) {
         mf.s[oj[i]] = sn;
         mf.r[oj[i]] = rn;
       }
     }
-    lds_barrier();  // (not __syncthreads(), which would wait for the row first)
-#pragma unroll
-    for (int i = 0; i < CH; ++i)
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const uint32_t u = __builtin_bit_cast(uint32_t, rch[i][w]);
-        if ((u & ~kMomSlotMask) == kMomSlotTag) rch[i][w] = rn_of[u & kMomSlotMask];
-      }
   }
-  if constexpr (OL) {
+  if constexpr (OL && !MF) {
     const bool wx = xO != nullptr;
     [[maybe_unused]] const float* const sp = wx ? s : reinterpret_cast<const float*>(O);
     if constexpr (!MF) {
@@ -264,10 +259,43 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
       for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
     }
   }
+  if constexpr (MF) {
+    // The outlier channels, left out above (NaN), with the new r.
+#pragma unroll
+    for (int i = 0; i < kSl; ++i) amax = fmaxf(amax, oj[i] >= 0 ? fabsf(mul_rn(h2f(xg[i]), rj[i])) : 0.0f);
+  }
   amax = wave_max(amax);
   if (lane == 0) red[wave] = amax;
   __syncthreads();  // both halves' maxima, and (OL) the whole staged row
   const float a = fmaxf(red[2 * tok], red[2 * tok + 1]);
+  if constexpr (MF) {
+    // Every wave stays for the barriers below; a token past M stores nothing.
+    const float inv = (a == 0.0f) ? 0.0f : div_rn(127.0f, a);
+    if (valid && lane == 0 && half == 0) scale[m] = (a == 0.0f) ? 0.0f : div_rn(a, 127.0f);
+    int8_t* const qrow = reinterpret_cast<int8_t*>(qlds) + tok * K;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = chunk(i);
+      if (c < nchunks) *reinterpret_cast<uint2*>(qrow + c * 8) = sym_codes8<true>(vr[i], inv);
+    }
+    lds_barrier();
+    int code[kSl];
+#pragma unroll
+    for (int i = 0; i < kSl; ++i) {
+      code[i] = (oj[i] >= 0) ? sym_code(mul_rn(h2f(xg[i]), rj[i]), inv) : 0;
+      if (oj[i] >= 0) qrow[oj[i]] = static_cast<int8_t>(code[i]);
+    }
+    lds_barrier();
+    if (!valid) return;
+    for (int c = lane + 64 * half; c < static_cast<int>(K / 16); c += 128)
+      *reinterpret_cast<v4i*>(q + m * K + 16 * c) = *reinterpret_cast<const v4i*>(qrow + 16 * c);
+#pragma unroll
+    for (int i = 0; i < kSl; ++i) {
+      const int j = lane + 64 * (2 * i + half);
+      if (j < ldO) xO[m * ldO + j] = f2h_mul(static_cast<float>(code[i]), sm1j[i]);
+    }
+    return;
+  }
   if (!valid) return;
   const float inv = (a == 0.0f) ? 0.0f : div_rn(127.0f, a);
   if (lane == 0 && half == 0) scale[m] = (a == 0.0f) ? 0.0f : div_rn(a, 127.0f);
@@ -611,8 +639,8 @@ qlin_status launch_quant_momentum(const uint16_t* x, int64_t M, int64_t K, const
                                   const int32_t* O, int32_t nO, uint16_t* xO, const MomFold& mf, hipStream_t st) {
   const int ldO = static_cast<int>(outlier_ld(nO));
   const dim3 grid(static_cast<unsigned>((M + kQuantTokens - 1) / kQuantTokens));
-  // The two tokens' rows, then the new r by slot.
-  const size_t lds = static_cast<size_t>(kQuantTokens) * 2 * static_cast<size_t>(K) + 4 * kOutlierLdMax;
+  // The two tokens' rows of codes.
+  const size_t lds = static_cast<size_t>(kQuantTokens) * static_cast<size_t>(K);
   if (K <= 4096)
     quant_act_kernel<true, true, 4, float, true><<<grid, kQuantThreads, lds, st>>>(x, M, K, r, q, scale, O, nO, ldO,
                                                                                  nullptr, nullptr, xO, mf);
