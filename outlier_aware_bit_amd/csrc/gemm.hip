@@ -685,7 +685,7 @@ constexpr int kXOLdsLd = 208;
 // columns, two per SIMD, so that each CU has twice the operand loads in
 // flight.
 template <BOp B, AOp A, int TM, int BD, int COMP, int WV = 4>
-__global__ __launch_bounds__(64 * WV, (A == AOp::U4G) ? 2 : 1) void gemm_tile(GemmArgs g) {
+__global__ __launch_bounds__(64 * WV, (A == AOp::U4G || (A == AOp::U4 && TM == 4)) ? 2 : 1) void gemm_tile(GemmArgs g) {
   using T = Tile<B, A, TM, WV>;
   constexpr int NTW = T::kNTW;
   static_assert(WV == 4 || (B == BOp::W8 && A == AOp::I8 && (COMP == 0 || COMP == 5)),
@@ -1551,8 +1551,10 @@ qlin_status launch_tile(const GemmArgs& g, hipStream_t st) {
   // per-group requantized weights, where register room leaves one.
   // Group-wise W4A4 keeps one (its group constants and fp32 sums take the
   // room), and so do eight-wave tiles, where it measured faster (two waves
-  // per SIMD cover the weights' latency).
-  constexpr int BD = (((B == BOp::W8 || B == BOp::W4Group) && TM == 8) || A == AOp::U4G || WV == 8) ? 1 : 2;
+  // per SIMD cover the weights' latency), and the W4A4 tiles that run two
+  // workgroups per CU (101 against 101-107 us with two stages).
+  constexpr int BD = (((B == BOp::W8 || B == BOp::W4Group) && TM == 8) || A == AOp::U4G || WV == 8 ||
+                      (A == AOp::U4 && TM == 4)) ? 1 : 2;
   const int64_t tiles = ((g.M + 32 * TM - 1) / (32 * TM)) * ((g.N + kBN - 1) / kBN);
   QLIN_REQUIRE(tiles <= 0x7fffffffLL, QLIN_ERR_SHAPE, "M=%lld too large", (long long)g.M);
   gemm_tile<B, A, TM, BD, COMP, WV><<<dim3(static_cast<unsigned>(tiles)), 64 * WV, 0, st>>>(g);
@@ -1608,9 +1610,13 @@ qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
       }
     }
     // 256-row tiles when they still give every CU a tile: per weight byte
-    // streamed (and unpacked) they do twice the matrix-core work.
+    // streamed (and unpacked) they do twice the matrix-core work.  W4A4
+    // instead runs 128-row tiles two workgroups per CU at every M, so that
+    // each SIMD holds two waves whose unpacking and waits overlap the other's
+    // matrix-core work (2048 x 4096 x 14336: 112 -> 101 us).
     const int64_t tiles_n = (g.N + kBN - 1) / kBN;
-    if (((g.M + 255) / 256) * tiles_n >= 256) return launch_tile<B, A, 8, 0>(g, st);
+    if constexpr (B != BOp::W4U)
+      if (((g.M + 255) / 256) * tiles_n >= 256) return launch_tile<B, A, 8, 0>(g, st);
     // 128-row int8 tiles: eight waves (2048 x 4096 x 4096: 41.8 -> 37.2 us
     // in one comparison).
     if constexpr (B == BOp::W8 && A == AOp::I8)
