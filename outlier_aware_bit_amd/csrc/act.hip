@@ -85,11 +85,13 @@ __device__ __forceinline__ uint2 sym_codes8(const float (&v)[8], float inv) {
 }
 
 // Per-token symmetric int8: a = max|v|, inv = 127/a, q = clamp(rint(v*inv)).
-// Two wavefronts per token: wave half h takes the 64-chunk blocks h, h + 2,
-// ... of the row (chunks of 8 values), the first CH of them held in
-// registers as raw fp16 between the absmax and the coding pass (CH = 4 up to
-// K = 4096, 8 up to 8192; longer rows re-read the tail from cache).  The two
-// halves' maxima meet in LDS across one workgroup barrier.
+// WPT wavefronts per token: wave h of a token takes the 64-chunk blocks h,
+// h + WPT, ... of the row (chunks of 8 values), the first CH of them held in
+// registers as raw fp16 between the absmax and the coding pass (with four
+// waves per token, CH = 2 up to K = 4096, 4 up to 8192; longer rows re-read
+// the tail from cache).  The waves' maxima meet in LDS across one workgroup
+// barrier.  (Four waves per token, one token per workgroup, against two:
+// 8.1 -> 7.8 us at 2048 x 4096 with r and xO, 26.3 -> 25.2 at 4096 x 11008.)
 //
 // Outlier columns (row stride ldO, zero padded): the code of x[m, O[j]], and
 // the compensation operand fp16(code * (s[O[j]] - 1)).  With OL (ldO <= 256
@@ -97,7 +99,7 @@ __device__ __forceinline__ uint2 sym_codes8(const float (&v)[8], float inv) {
 // row is needed, and the row is staged in LDS (each wave its own blocks; the
 // barrier makes the whole row visible), so that the outlier values are read
 // from there; otherwise they are re-read from memory.  Each wave takes every
-// other block of 64 outlier slots.
+// WPT-th block of 64 outlier slots.
 //
 // MF (the momentum step folded in; HAS_R, OL, K <= 512 * CH): r[O[j]] and
 // s[O[j]] are not read but formed from the momentum step's row-block maxima
@@ -112,9 +114,14 @@ __device__ __forceinline__ uint2 sym_codes8(const float (&v)[8], float inv) {
 // number instead of the NaN: the maximum is then the same, and the code is
 // overwritten all the same.)
 constexpr int kOutlierLdMax = 256;
-constexpr int kQuantTokens = kQuantThreads / 128;  // tokens per workgroup
+// Tokens per workgroup with WPT wavefronts per token.
+constexpr int quant_tokens(int wpt) { return kQuantThreads / 64 / wpt; }
+constexpr int kQuantWpt = 4;  // wavefronts per token in the launches below
+constexpr int kQuantTokens = quant_tokens(kQuantWpt);
+// Register chunks per lane that hold rows of up to 4096 / 8192 channels.
+constexpr int kQuantCh4k = 4096 / (512 * kQuantWpt), kQuantCh8k = 8192 / (512 * kQuantWpt);
 
-template <bool HAS_R, bool OL, int CH, typename RT = float, bool MF = false>
+template <bool HAS_R, bool OL, int CH, typename RT = float, bool MF = false, int WPT = 2>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const RT* __restrict__ r, int8_t* __restrict__ q,
     float* __restrict__ scale, const int32_t* __restrict__ O, int nO, int ldO,
@@ -122,26 +129,27 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
   static_assert(!MF || (HAS_R && OL && std::is_same_v<RT, float>), "the momentum fold needs r and the LDS row");
   extern __shared__ __attribute__((aligned(16))) uint8_t qlds[];
   __shared__ float red[kQuantThreads / 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = wave & 1, tok = wave >> 1;
-  const int64_t m = static_cast<int64_t>(blockIdx.x) * kQuantTokens + tok;
+  constexpr int kTok = quant_tokens(WPT);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = wave % WPT, tok = wave / WPT;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * kTok + tok;
   // A token past M still takes part in the workgroup barrier (on row M - 1's
   // data) and stores nothing.
   const bool valid = m < M;
   const uint16_t* xr = x + (valid ? m : M - 1) * K;
   const int nchunks = static_cast<int>(K / 8);
-  auto chunk = [&](int i) { return 64 * (2 * i + half) + lane; };  // this lane's i-th chunk
+  auto chunk = [&](int i) { return 64 * (WPT * i + half) + lane; };  // this lane's i-th chunk
 
-  // Outlier slots of this lane (j = lane + 64 (2 i + half)): their channel
+  // Outlier slots of this lane (j = lane + 64 (WPT i + half)): their channel
   // indices are loaded first, so that the loads of r[O[j]] and s[O[j]] below
   // wait only for them and not for the row issued after them (a wait for a
   // load also waits for every load issued before it).  Unconditional, from
   // a clamped index (a guarded load is a branch that waits for it).
-  constexpr int kSl = kOutlierLdMax / 128;
+  constexpr int kSl = kOutlierLdMax / (64 * WPT);
   [[maybe_unused]] int oj[kSl];
   if constexpr (OL) {
 #pragma unroll
     for (int i = 0; i < kSl; ++i) {
-      const int j = lane + 64 * (2 * i + half);
+      const int j = lane + 64 * (WPT * i + half);
       const int o = O[j < nO ? j : nO - 1];
       oj[i] = (j < nO && o >= 0 && o < K) ? o : -1;
     }
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
   if constexpr (MF) {
 #pragma unroll
     for (int i = 0; i < kSl; ++i) {
-      const int j = lane + 64 * (2 * i + half), jc = j < nO ? j : nO - 1;
+      const int j = lane + 64 * (WPT * i + half), jc = j < nO ? j : nO - 1;
 #pragma unroll
       for (int b = 0; b < kMomFoldBlocks; ++b) fpart[i][b] = mf.part[b * nO + jc];
       fw[i] = mf.wmax[jc];
@@ -267,7 +275,9 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
   amax = wave_max(amax);
   if (lane == 0) red[wave] = amax;
   __syncthreads();  // both halves' maxima, and (OL) the whole staged row
-  const float a = fmaxf(red[2 * tok], red[2 * tok + 1]);
+  float a = red[WPT * tok];
+#pragma unroll
+  for (int w = 1; w < WPT; ++w) a = fmaxf(a, red[WPT * tok + w]);
   if constexpr (MF) {
     // Every wave stays for the barriers below; a token past M stores nothing.
     const float inv = (a == 0.0f) ? 0.0f : div_rn(127.0f, a);
@@ -287,11 +297,11 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     }
     lds_barrier();
     if (!valid) return;
-    for (int c = lane + 64 * half; c < static_cast<int>(K / 16); c += 128)
+    for (int c = lane + 64 * half; c < static_cast<int>(K / 16); c += 64 * WPT)
       *reinterpret_cast<v4i*>(q + m * K + 16 * c) = *reinterpret_cast<const v4i*>(qrow + 16 * c);
 #pragma unroll
     for (int i = 0; i < kSl; ++i) {
-      const int j = lane + 64 * (2 * i + half);
+      const int j = lane + 64 * (WPT * i + half);
       if (j < ldO) xO[m * ldO + j] = f2h_mul(static_cast<float>(code[i]), sm1j[i]);
     }
     return;
@@ -329,7 +339,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
   if constexpr (OL) {
 #pragma unroll
     for (int i = 0; i < kSl; ++i) {
-      const int j = lane + 64 * (2 * i + half);
+      const int j = lane + 64 * (WPT * i + half);
       if (j < ldO) {
         int code = 0;
         if (oj[i] >= 0) {
@@ -342,7 +352,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
       }
     }
   } else {
-    for (int j = lane + 64 * half; j < ldO; j += 128) {
+    for (int j = lane + 64 * half; j < ldO; j += 64 * WPT) {
       const int o = j < nO ? O[j] : -1;
       int code = 0;
       float sm1 = 0.0f;
@@ -626,11 +636,11 @@ qlin_status launch_quant_grad(const uint16_t* dy, int64_t M, int64_t N, const ui
                               hipStream_t st) {
   const dim3 grid(static_cast<unsigned>((M + kQuantTokens - 1) / kQuantTokens));
   if (N <= 4096)
-    quant_act_kernel<true, false, 4, uint16_t><<<grid, kQuantThreads, 0, st>>>(dy, M, N, sw, gq, gs, nullptr, 0, 0,
-                                                                                 nullptr, nullptr, nullptr, MomFold{});
+    quant_act_kernel<true, false, kQuantCh4k, uint16_t, false, kQuantWpt><<<grid, kQuantThreads, 0, st>>>(
+        dy, M, N, sw, gq, gs, nullptr, 0, 0, nullptr, nullptr, nullptr, MomFold{});
   else
-    quant_act_kernel<true, false, 8, uint16_t><<<grid, kQuantThreads, 0, st>>>(dy, M, N, sw, gq, gs, nullptr, 0, 0,
-                                                                                  nullptr, nullptr, nullptr, MomFold{});
+    quant_act_kernel<true, false, kQuantCh8k, uint16_t, false, kQuantWpt><<<grid, kQuantThreads, 0, st>>>(
+        dy, M, N, sw, gq, gs, nullptr, 0, 0, nullptr, nullptr, nullptr, MomFold{});
   QLIN_LAUNCH_CHECK("quant_act_kernel (gradient)");
   return QLIN_OK;
 }
@@ -642,11 +652,11 @@ qlin_status launch_quant_momentum(const uint16_t* x, int64_t M, int64_t K, const
   // The two tokens' rows of codes.
   const size_t lds = static_cast<size_t>(kQuantTokens) * static_cast<size_t>(K);
   if (K <= 4096)
-    quant_act_kernel<true, true, 4, float, true><<<grid, kQuantThreads, lds, st>>>(x, M, K, r, q, scale, O, nO, ldO,
-                                                                                 nullptr, nullptr, xO, mf);
+    quant_act_kernel<true, true, kQuantCh4k, float, true, kQuantWpt><<<grid, kQuantThreads, lds, st>>>(
+        x, M, K, r, q, scale, O, nO, ldO, nullptr, nullptr, xO, mf);
   else
-    quant_act_kernel<true, true, 8, float, true><<<grid, kQuantThreads, lds, st>>>(x, M, K, r, q, scale, O, nO, ldO,
-                                                                                 nullptr, nullptr, xO, mf);
+    quant_act_kernel<true, true, kQuantCh8k, float, true, kQuantWpt><<<grid, kQuantThreads, lds, st>>>(
+        x, M, K, r, q, scale, O, nO, ldO, nullptr, nullptr, xO, mf);
   QLIN_LAUNCH_CHECK("quant_act_kernel (momentum folded)");
   return QLIN_OK;
 }
@@ -687,14 +697,14 @@ extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, c
   auto go = [&](auto has_r, auto ol_c, auto ch) {
     constexpr bool HR = decltype(has_r)::value, OLc = decltype(ol_c)::value;
     constexpr int CH = decltype(ch)::value;
-    quant_act_kernel<HR, OLc, CH><<<grid, kQuantThreads, OLc ? ol_lds : 0, st>>>(x, M, K, r, q, scale, O, nO, ldO, s,
-                                                                                qO, xO, MomFold{});
+    quant_act_kernel<HR, OLc, CH, float, false, kQuantWpt><<<grid, kQuantThreads, OLc ? ol_lds : 0, st>>>(
+        x, M, K, r, q, scale, O, nO, ldO, s, qO, xO, MomFold{});
   };
   auto go_ch = [&](auto has_r, auto ol_c) {
     if (K <= 4096)
-      go(has_r, ol_c, std::integral_constant<int, 4>{});
+      go(has_r, ol_c, std::integral_constant<int, kQuantCh4k>{});
     else
-      go(has_r, ol_c, std::integral_constant<int, 8>{});
+      go(has_r, ol_c, std::integral_constant<int, kQuantCh8k>{});
   };
   auto go_ol = [&](auto has_r) {
     if (ol)
