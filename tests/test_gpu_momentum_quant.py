@@ -38,6 +38,8 @@ def _steps(M, K, nO, seed):
 
 @pytest.mark.parametrize("M,K,nO,work", [
     (1, 256, 3, True),        # fewer tokens than row blocks
+    (5, 128, 7, True),        # the shortest rows (two 64-channel strips)
+    (2, 384, 1, True),        # one outlier channel
     (3, 1024, 16, True),
     (70, 1024, 13, True),
     (513, 4096, 205, True),   # ragged, the q_proj channel count
