@@ -185,12 +185,14 @@ size_t qlin_momentum_work_bytes(int64_t M, int32_t nO);
  *   work    device workspace of qlin_quaff_momentum_quant_work_bytes(M, nO)
  *           bytes, or NULL.  With it (and 1 <= nO <= 256, K <= 8192) the
  *           maxima are taken by every CU over 4 row blocks per 64-channel
- *           strip, and each quantizer wave folds them into the new s[O],
- *           r[O] itself (two launches in all, no launch for the fold);
- *           otherwise the two calls above are made.  Calls that overlap
- *           must not share it.
+ *           strip, and each quantizer lane folds them for its outlier
+ *           slots into the new s[O], r[O] (two launches in all, none for
+ *           the fold); otherwise the two calls above are made.  Calls that
+ *           overlap must not share it.  Between the two launches r holds a
+ *           marker (a NaN) at each outlier channel; s must hold finite
+ *           positive values, as the momentum update keeps them.
  *   q, scale, xO   as in qlin_quant_act (xO required when nO > 0, NULL
- *           otherwise; the codes of the outlier columns are not written)
+ *           otherwise; qO, the outlier columns' codes alone, is not offered)
  * M == 0 runs the momentum update alone.
  */
 qlin_status qlin_quaff_momentum_quant(const uint16_t* x, int64_t M, int64_t K, const int32_t* O,
