@@ -101,7 +101,7 @@ __device__ __forceinline__ uint2 sym_codes8(const float (&v)[8], float inv) {
 // from there; otherwise they are re-read from memory.  Each wave takes every
 // WPT-th block of 64 outlier slots.
 //
-// MF (the momentum step folded in; HAS_R, OL, K <= 512 * CH): r[O[j]] and
+// MF (the momentum step folded in; HAS_R, OL, K <= 512 * WPT * CH): r[O[j]] and
 // s[O[j]] are not read but formed from the momentum step's row-block maxima
 // (mf.part), which each lane folds for its own slots; the first workgroup
 // writes them to mf.s and mf.r.  The maxima kernel leaves a NaN in r at
