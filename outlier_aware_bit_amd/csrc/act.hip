@@ -88,8 +88,9 @@ __device__ __forceinline__ uint2 sym_codes8(const float (&v)[8], float inv) {
 // WPT wavefronts per token: wave h of a token takes the 64-chunk blocks h,
 // h + WPT, ... of the row (chunks of 8 values), the first CH of them held in
 // registers as raw fp16 between the absmax and the coding pass (with four
-// waves per token, CH = 2 up to K = 4096, 4 up to 8192; longer rows re-read
-// the tail from cache).  The waves' maxima meet in LDS across one workgroup
+// waves per token, CH = 2 up to K = 4096, 4 up to 8192, 6 up to 12288;
+// longer rows re-read the tail from cache: at 4096 x 11008 that re-read
+// took 25.1 against 22.9 us with CH = 6).  The waves' maxima meet in LDS across one workgroup
 // barrier.  (Four waves per token, one token per workgroup, against two:
 // 8.1 -> 7.8 us at 2048 x 4096 with r and xO, 26.3 -> 25.2 at 4096 x 11008.)
 //
@@ -120,6 +121,7 @@ constexpr int kQuantWpt = 4;  // wavefronts per token in the launches below
 constexpr int kQuantTokens = quant_tokens(kQuantWpt);
 // Register chunks per lane that hold rows of up to 4096 / 8192 channels.
 constexpr int kQuantCh4k = 4096 / (512 * kQuantWpt), kQuantCh8k = 8192 / (512 * kQuantWpt);
+constexpr int kQuantCh12k = 12288 / (512 * kQuantWpt);
 
 template <bool HAS_R, bool OL, int CH, typename RT = float, bool MF = false, int WPT = 2>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
@@ -703,8 +705,10 @@ extern "C" qlin_status qlin_quant_act(const uint16_t* x, int64_t M, int64_t K, c
   auto go_ch = [&](auto has_r, auto ol_c) {
     if (K <= 4096)
       go(has_r, ol_c, std::integral_constant<int, kQuantCh4k>{});
-    else
+    else if (K <= 8192)
       go(has_r, ol_c, std::integral_constant<int, kQuantCh8k>{});
+    else
+      go(has_r, ol_c, std::integral_constant<int, kQuantCh12k>{});
   };
   auto go_ol = [&](auto has_r) {
     if (ol)
