@@ -1224,22 +1224,25 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny(GemmArgs g) {
     for (int uu = 0; uu < U; ++uu) {
       const int u = base + WAVES * uu;
       const bool ok_u = u < KU;
+      // Weights and ratios come from clamped, in-bounds indices with no
+      // condition: a unit past K meets zero activations below, and a strip
+      // past N is never stored.  Under a condition, the compiler sinks the
+      // per-group requantization into the branch, where it waits for each
+      // load before issuing the next.
+      const int uc = ok_u ? u : KU - 1;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const bool ok = ok_u && (nt0 + nt) < tiles_n;
+        const int64_t strip = (nt0 + nt) < tiles_n ? nt0 + nt : tiles_n - 1;
 #pragma unroll
         for (int h = 0; h < NBU; ++h) {
-          const int64_t tile_k = (B == BOp::W8) ? (2 * static_cast<int64_t>(u) + h) : static_cast<int64_t>(u);
-          const int64_t tix = (nt0 + nt) * ((B == BOp::W8) ? g.K / 32 : g.K / 64) + tile_k;
-          rb[uu][nt][h] = ok ? *reinterpret_cast<const uint4*>(g.b + (tix << 10) + lane * 16)
-                             : make_uint4(0, 0, 0, 0);
+          const int64_t tile_k = (B == BOp::W8) ? (2 * static_cast<int64_t>(uc) + h) : static_cast<int64_t>(uc);
+          const int64_t tix = strip * ((B == BOp::W8) ? g.K / 32 : g.K / 64) + tile_k;
+          rb[uu][nt][h] = *reinterpret_cast<const uint4*>(g.b + (tix << 10) + lane * 16);
         }
         rr[uu][nt] = v2h{static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f)};
         if constexpr (B == BOp::W4Group) {
-          if (ok) {
-            const _Float16 r = __builtin_bit_cast(_Float16, g.ratio[static_cast<int64_t>(u / 2) * g.N + (nt0 + nt) * 32 + arow]);
-            rr[uu][nt] = v2h{r, r};
-          }
+          const _Float16 r = __builtin_bit_cast(_Float16, g.ratio[static_cast<int64_t>(uc / 2) * g.N + strip * 32 + arow]);
+          rr[uu][nt] = v2h{r, r};
         }
       }
 #pragma unroll
@@ -1347,9 +1350,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny(GemmArgs g) {
 // 8U r + w + 8j, j < U.  Activations are loaded two rounds ahead and stored
 // to the other of two LDS buffers one round ahead; weights are loaded two
 // rounds ahead into two register sets.  Units past K (a partial last round)
-// get zero weights, and their activation chunks are read from a clamped,
-// in-bounds address: they add exactly zero.  Rows past M are read from row
-// M - 1 and their outputs are not stored.
+// read their weights from the last unit and their activation chunks from a
+// clamped, in-bounds address; their activation fragments are zeroed, so they
+// add exactly zero.  Rows past M are read from row M - 1 and their outputs
+// are not stored.
 template <BOp B, int MT, int U>
 __global__ __launch_bounds__(512) void gemm_skinny_lds(GemmArgs g) {
   constexpr int NT = 2, WAVES = 8;
@@ -1394,16 +1398,18 @@ __global__ __launch_bounds__(512) void gemm_skinny_lds(GemmArgs g) {
   auto load_w = [&](int r, uint4 (&rb)[U][NT][NBU], v2h (&rr)[U][NT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
+      // Unconditional loads from a clamped unit: the fragments of a unit
+      // past K are zeroed on the activation side instead (a select on the
+      // weights becomes a branch around the load and, per group, around the
+      // requantization, which then waits for each load in turn).
       const int u = 8 * U * r + wave + 8 * j;
-      const bool ok = u < KU;
-      const int uc = ok ? u : KU - 1;
+      const int uc = u < KU ? u : KU - 1;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
         for (int h = 0; h < NBU; ++h) {
           const int64_t tix = (nt0 + nt) * KT + ((B == BOp::W8) ? 2 * static_cast<int64_t>(uc) + h : uc);
-          const uint4 w = *reinterpret_cast<const uint4*>(g.b + (tix << 10) + lane * 16);
-          rb[j][nt][h] = ok ? w : make_uint4(0, 0, 0, 0);
+          rb[j][nt][h] = *reinterpret_cast<const uint4*>(g.b + (tix << 10) + lane * 16);
         }
         if constexpr (B == BOp::W4Group) {
           const _Float16 q = __builtin_bit_cast(
@@ -1440,12 +1446,14 @@ __global__ __launch_bounds__(512) void gemm_skinny_lds(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       v4i af[MT][2];
+      const bool uok = 8 * U * r + wave + 8 * j < KU;  // a unit past K adds zero
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int row = 32 * mt + arow, c = 4 * (wave + 8 * j) + 2 * h + ahalf;
-          af[mt][h] = *reinterpret_cast<const v4i*>(cur + row * kRowB + ((c ^ (row & 15)) << 4));
+          const v4i f = *reinterpret_cast<const v4i*>(cur + row * kRowB + ((c ^ (row & 15)) << 4));
+          af[mt][h] = uok ? f : v4i{};
         }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
