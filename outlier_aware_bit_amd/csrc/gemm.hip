@@ -1586,9 +1586,19 @@ qlin_status launch(const GemmArgs& g, bool comp, hipStream_t st) {
       // int8 activations from 33 tokens: staged through LDS (measured at
       // 4096 x 11008: M = 64 per channel 16.8 -> 13.3 us, M = 128 26.4 ->
       // 18.7 us), except where the direct form measured faster: the
-      // requantizing per-group weights at 128 rows, whose registers spill,
-      // and int8 weights at 128 rows up to 96 tokens.
+      // requantizing per-group weights at every such M, and int8 weights at
+      // 128 rows up to 96 tokens.
       const int64_t dgrid = g.N / 64;
+      if constexpr (A == AOp::I8 && B == BOp::W4Group) {
+        // 33-64 tokens: two 64-k units in flight per wave (at 4096 x 11008,
+        // M = 48 / 64: 18.2 / 18.7 us against 20.4 / 20.8 through LDS; the
+        // vector requantization, not the activation loads, sets the pace).
+        if (g.M > 32 && g.M <= 64) {
+          launch_skinny<B, A, 2, 2, 8, 2>(g, st);
+          QLIN_LAUNCH_CHECK("gemm_skinny");
+          return QLIN_OK;
+        }
+      }
       if constexpr (A == AOp::I8) {
         if (g.M > 32 && g.M <= 64) {
           gemm_skinny_lds<B, 2, 2><<<dim3(static_cast<unsigned>(dgrid)), 512, 0, st>>>(g);
