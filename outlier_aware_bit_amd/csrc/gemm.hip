@@ -91,6 +91,7 @@ __device__ __forceinline__ uint32_t mask_hi(uint32_t w) { return (w >> 4) & 0x0F
 // 1536.0 (spacing 1 on [1024, 2048)) rounds to an integer n with ties to even
 // and leaves n's two's complement in the low byte of the fp16 pattern.
 __device__ __forceinline__ void requant_word(uint32_t w, v2h rr, uint32_t& out_lo, uint32_t& out_hi) {
+  const v2h r2 = __builtin_shufflevector(rr, rr, 0, 0);  // the ratio is the low half of rr
   const uint32_t xw = w ^ 0x88888888u;
   const v2h off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
   const v2h lo = {static_cast<_Float16>(-127.0f), static_cast<_Float16>(-127.0f)};
@@ -102,7 +103,7 @@ __device__ __forceinline__ void requant_word(uint32_t w, v2h rr, uint32_t& out_l
     const uint32_t bits = ((xw >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
     v2h h = __builtin_bit_cast(v2h, bits);
     h = h - off;
-    h = h * rr;
+    h = h * r2;
     h = __builtin_elementwise_min(__builtin_elementwise_max(h, lo), hi);
     h = h + magic;
     pr[p] = __builtin_bit_cast(uint32_t, h);
@@ -273,11 +274,12 @@ __device__ __forceinline__ void load_b_part(const TilePtrs<B, A, TM, WV>& p, int
     constexpr int kp = KS >> 1, nt = KS & 1;
     rb[kp * 2 + nt] = *reinterpret_cast<const v4i*>(p.b + ((static_cast<int64_t>(2 * s + kp) + nt * kt) << 10));
     if constexpr (B == BOp::W4Group && KS == 0) {
+      // The ratio stays in the low half as loaded (zero-extended, no
+      // instruction): packing it into both halves here, next to its load in
+      // the k step's schedule, waited for every load in flight.
 #pragma unroll
-      for (int n2 = 0; n2 < 2; ++n2) {
-        const _Float16 r = __builtin_bit_cast(_Float16, p.ratio[static_cast<int64_t>(s) * N + n2 * 32]);
-        rr[n2] = v2h{r, r};
-      }
+      for (int n2 = 0; n2 < 2; ++n2)
+        rr[n2] = __builtin_bit_cast(v2h, static_cast<uint32_t>(p.ratio[static_cast<int64_t>(s) * N + n2 * 32]));
     }
   }
 }
